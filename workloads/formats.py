@@ -1,0 +1,66 @@
+"""Storage formats of the inputs: bf16 (round to nearest even) and OCP fp8 e4m3.
+
+These are input-preparation encoders only.  The oracle and the GPU library
+each decode the stored bytes with their own code.
+
+Dtype codes match the C-ABI enum: 0 = fp32, 1 = bf16, 2 = fp8 e4m3 (OCP
+"e4m3fn": bias 7, no infinities, max finite 448).
+"""
+import numpy as np
+
+DT_F32, DT_BF16, DT_E4M3 = 0, 1, 2
+_NAMES = {DT_F32: "f32", DT_BF16: "bf16", DT_E4M3: "e4m3"}
+
+
+def dtype_name(dt):
+    return _NAMES[dt]
+
+
+def bf16_bits(a):
+    """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    """bf16 bit patterns (uint16) -> exact fp32 values."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32)
+    return (b << np.uint32(16)).view(np.float32)
+
+
+def _e4m3_positive_table():
+    """All non-negative finite e4m3 values, indexed by code 0..126."""
+    vals = np.empty(127, dtype=np.float64)
+    for code in range(127):
+        e, mnt = code >> 3, code & 7
+        vals[code] = (mnt / 8.0) * 2.0 ** -6 if e == 0 else (1 + mnt / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_E4M3_POS = _e4m3_positive_table()
+E4M3_MAX = 448.0
+
+
+def e4m3_scale(a):
+    """Per-tensor scale so that max|a| maps to the largest finite e4m3 (448)."""
+    amax = float(np.max(np.abs(np.asarray(a, dtype=np.float64))))
+    return amax / E4M3_MAX if amax > 0 else 1.0
+
+
+def e4m3_encode(a, scale):
+    """Encode a/scale to e4m3 codes (uint8): nearest value, ties to the even
+    code, saturating at +-448 (never produces the NaN code)."""
+    v = np.asarray(a, dtype=np.float64) / float(scale)
+    mag = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, mag, side="left")        # first value >= mag
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = mag - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(v < 0, code | np.uint8(0x80), code).astype(np.uint8)
+    # -0 is stored as +0 so that equal values have equal codes
+    code = np.where(code == 0x80, np.uint8(0), code).astype(np.uint8)
+    return code
