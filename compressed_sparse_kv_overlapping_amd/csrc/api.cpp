@@ -1,0 +1,242 @@
+// C-ABI entry points of libcskv: argument validation, launch configuration,
+// workspace carving and the per-thread error message.  Every check runs
+// before any launch, so a rejected call writes nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/cskv.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return CSKV_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CSKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kD = 512;
+
+}  // namespace
+
+extern "C" {
+
+int cskv_version(void) { return CSKV_VERSION; }
+
+const char* cskv_status_string(int status) {
+  switch (status) {
+    case CSKV_OK: return "ok";
+    case CSKV_ERR_INVALID_ARG: return "invalid argument";
+    case CSKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case CSKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSKV_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* cskv_last_error(void) { return g_last_error.c_str(); }
+
+int cskv_compress(const void* raw_kv, const void* score_logits, const float* pos_bias, int64_t T,
+                  int32_t m, int64_t entry_begin, int64_t entry_end, void* out, int64_t ld_out,
+                  cskv_dtype dt, void* stream) {
+  if (T < 0 || m < 1) return fail(CSKV_ERR_INVALID_ARG, "cskv_compress: T=%lld m=%d", (long long)T, m);
+  const int64_t N = T / m;
+  if (entry_begin < 0 || entry_end < entry_begin || entry_end > N)
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_compress: entry range [%lld, %lld) outside [0, %lld]",
+                (long long)entry_begin, (long long)entry_end, (long long)N);
+  if (ld_out < kD || ld_out % 8 != 0)
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_compress: ld_out=%lld (need >= 512, multiple of 8)",
+                (long long)ld_out);
+  if (dt != CSKV_F32 && dt != CSKV_BF16)
+    return fail(CSKV_ERR_UNSUPPORTED, "cskv_compress: dtype %d (F32 or BF16)", (int)dt);
+  if (entry_end == entry_begin) return ok();   // nothing to write: pointers are not used
+  if (!raw_kv || !score_logits || !pos_bias || !out)
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_compress: null pointer");
+  if (!aligned16(raw_kv) || !aligned16(score_logits) || !aligned16(pos_bias) || !aligned16(out))
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_compress: tensors must be 16-byte aligned");
+  return hip_status(cskv::launch_compress((int)dt, raw_kv, score_logits, pos_bias, m, entry_begin,
+                                          entry_end, out, ld_out, (hipStream_t)stream),
+                    "cskv_compress");
+}
+
+size_t cskv_index_topk_workspace_size(int64_t B, int64_t N, int32_t k) {
+  if (B < 1 || N < 1 || k < 1) return 0;
+  return cskv::topk_workspace_bytes(B, N, k);
+}
+
+static int check_topk(const char* fn, const void* q_idx, const void* idx_keys, int64_t B, int64_t N,
+                      int32_t k, int64_t key_bstride, const int64_t* q_pos, int32_t m,
+                      float idx_scale, cskv_dtype idx_dt, const int32_t* idx_out) {
+  if (!q_idx || !idx_keys || !idx_out) return fail(CSKV_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (B < 1 || N < 1 || k < 1 || key_bstride < 0)
+    return fail(CSKV_ERR_INVALID_ARG, "%s: B=%lld N=%lld k=%d key_bstride=%lld", fn, (long long)B,
+                (long long)N, k, (long long)key_bstride);
+  if (q_pos && m < 1) return fail(CSKV_ERR_INVALID_ARG, "%s: m=%d with q_pos", fn, m);
+  if (!(idx_scale > 0.f) || idx_scale > 3.0e38f)
+    return fail(CSKV_ERR_INVALID_ARG, "%s: idx_scale must be positive and finite", fn);
+  if (idx_dt != CSKV_F32 && idx_dt != CSKV_BF16 && idx_dt != CSKV_FP8_E4M3)
+    return fail(CSKV_ERR_UNSUPPORTED, "%s: idx dtype %d", fn, (int)idx_dt);
+  if (k > cskv::topk_max_k())
+    return fail(CSKV_ERR_UNSUPPORTED, "%s: k=%d > %d", fn, k, cskv::topk_max_k());
+  if (N > cskv::topk_max_entries() || B > (int64_t)1 << 30)
+    return fail(CSKV_ERR_UNSUPPORTED, "%s: N=%lld (max %lld) B=%lld", fn, (long long)N,
+                (long long)cskv::topk_max_entries(), (long long)B);
+  if (key_bstride % 64 != 0) return fail(CSKV_ERR_INVALID_ARG, "%s: key_bstride %% 64 != 0", fn);
+  if (!aligned16(q_idx) || !aligned16(idx_keys))
+    return fail(CSKV_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  return CSKV_OK;
+}
+
+int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t N, int32_t k,
+                    int64_t key_bstride, const int64_t* q_pos, int32_t m, float idx_scale,
+                    cskv_dtype idx_dt, int32_t* idx_out, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  int st = check_topk("cskv_index_topk", q_idx, idx_keys, B, N, k, key_bstride, q_pos, m,
+                      idx_scale, idx_dt, idx_out);
+  if (st) return st;
+  const size_t need = cskv::topk_workspace_bytes(B, N, k);
+  if (!workspace || ws_bytes < need || !aligned16(workspace))
+    return fail(CSKV_ERR_WORKSPACE, "cskv_index_topk: workspace %zu bytes, need %zu", ws_bytes, need);
+  cskv::TopkParams p{(int)idx_dt, q_idx, idx_keys, q_pos, key_bstride, B, N, k, m, idx_scale, idx_out};
+  return hip_status(cskv::launch_topk(p, workspace, (hipStream_t)stream), "cskv_index_topk");
+}
+
+size_t cskv_attend_workspace_size(int64_t B, int32_t H, int64_t rows_per_query) {
+  if (B < 1 || H < 1 || rows_per_query < 0) return 0;
+  // the larger of the fp32 and bf16 layouts, so one size serves both
+  size_t a = cskv::attend_partial_bytes(0, B, H, rows_per_query);
+  size_t b = cskv::attend_partial_bytes(1, B, H, rows_per_query);
+  return a > b ? a : b;
+}
+
+static int check_attend(const char* fn, const void* q, const void* entries, const void* window,
+                        int64_t B, int32_t H, int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
+                        int64_t win_bstride, int64_t win_rows, cskv_dtype dt, const void* out) {
+  if (!q || !entries || !out) return fail(CSKV_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (W > 0 && !window) return fail(CSKV_ERR_INVALID_ARG, "%s: W=%d without a window", fn, W);
+  if (B < 1 || H < 1 || N < 0 || W < 0 || k < 0 || ent_bstride < 0 || win_bstride < 0 ||
+      win_rows < 0)
+    return fail(CSKV_ERR_INVALID_ARG, "%s: B=%lld H=%d N=%lld W=%d k=%d", fn, (long long)B, H,
+                (long long)N, W, k);
+  if (dt != CSKV_F32 && dt != CSKV_BF16)
+    return fail(CSKV_ERR_UNSUPPORTED, "%s: dtype %d (F32 or BF16)", fn, (int)dt);
+  if (N > (int64_t)1 << 31 || (int64_t)k + W > (int64_t)1 << 30 || B > (int64_t)1 << 30)
+    return fail(CSKV_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+  if (ent_bstride % 8 != 0 || win_bstride % 8 != 0)
+    return fail(CSKV_ERR_INVALID_ARG, "%s: batch strides must be multiples of 8", fn);
+  if (!aligned16(q) || !aligned16(entries) || (window && !aligned16(window)) || !aligned16(out))
+    return fail(CSKV_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  return CSKV_OK;
+}
+
+int cskv_sparse_attend(const void* q, const void* entries, const void* window, const int32_t* idx,
+                       int64_t B, int32_t H, int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
+                       int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
+                       int64_t win_pos0, float scale, cskv_dtype dt, void* out, float* lse,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_attend("cskv_sparse_attend", q, entries, window, B, H, N, W, k, ent_bstride,
+                        win_bstride, win_rows, dt, out);
+  if (st) return st;
+  if (k > 0 && !idx) return fail(CSKV_ERR_INVALID_ARG, "cskv_sparse_attend: null idx");
+  if (!q_pos && W > win_rows)
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_sparse_attend: W=%d > window rows %lld", W,
+                (long long)win_rows);
+  const size_t need = cskv::attend_partial_bytes((int)dt, B, H, (int64_t)k + W);
+  if (need && (!workspace || ws_bytes < need || !aligned16(workspace)))
+    return fail(CSKV_ERR_WORKSPACE, "cskv_sparse_attend: workspace %zu bytes, need %zu", ws_bytes,
+                need);
+  cskv::AttendParams p{(int)dt, q, entries, window, idx, q_pos, B, N, ent_bstride, win_bstride,
+                       win_pos0, win_rows, H, W, k, scale, out, lse, 0};
+  return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), "cskv_sparse_attend");
+}
+
+size_t cskv_csa_workspace_size(int64_t B, int32_t H, int64_t N, int32_t W, int32_t k) {
+  if (B < 1 || H < 1 || N < 1 || k < 1 || W < 0) return 0;
+  return cskv::topk_workspace_bytes(B, N, k) + 256 +
+         cskv_attend_workspace_size(B, H, (int64_t)k + W);
+}
+
+int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const void* idx_keys,
+                    const void* window, int64_t B, int32_t H, int64_t N, int32_t W, int32_t k,
+                    int32_t m, int64_t ent_bstride, int64_t key_bstride, int64_t win_bstride,
+                    int64_t win_rows, const int64_t* q_pos, int64_t win_pos0, float scale,
+                    float idx_scale, cskv_dtype dt, cskv_dtype idx_dt, void* out, float* lse,
+                    int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_topk("cskv_csa_attend", q_idx, idx_keys, B, N, k, key_bstride, q_pos, m,
+                      idx_scale, idx_dt, idx_out);
+  if (st) return st;
+  st = check_attend("cskv_csa_attend", q, entries, window, B, H, N, W, k, ent_bstride, win_bstride,
+                    win_rows, dt, out);
+  if (st) return st;
+  if (!q_pos && W > win_rows)
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_csa_attend: W=%d > window rows %lld", W,
+                (long long)win_rows);
+  const size_t need = cskv_csa_workspace_size(B, H, N, W, k);
+  if (!workspace || ws_bytes < need || !aligned16(workspace))
+    return fail(CSKV_ERR_WORKSPACE, "cskv_csa_attend: workspace %zu bytes, need %zu", ws_bytes, need);
+  const size_t topk_bytes = (cskv::topk_workspace_bytes(B, N, k) + 255) / 256 * 256;
+  cskv::TopkParams tp{(int)idx_dt, q_idx, idx_keys, q_pos, key_bstride, B, N, k, m, idx_scale,
+                      idx_out};
+  hipError_t e = cskv::launch_topk(tp, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "cskv_csa_attend (top-k)");
+  cskv::AttendParams ap{(int)dt, q, entries, window, idx_out, q_pos, B, N, ent_bstride,
+                        win_bstride, win_pos0, win_rows, H, W, k, scale, out, lse, 0};
+  return hip_status(cskv::launch_attend(ap, (char*)workspace + topk_bytes, (hipStream_t)stream),
+                    "cskv_csa_attend (attention)");
+}
+
+size_t cskv_hca_workspace_size(int64_t B, int32_t H, int64_t N) {
+  if (B < 1 || H < 1 || N < 0) return 0;
+  return cskv_attend_workspace_size(B, H, N);
+}
+
+int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, int64_t N,
+                    int64_t ent_bstride, float scale, cskv_dtype dt, void* out, float* lse,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_attend("cskv_hca_attend", q, entries, nullptr, B, H, N, 0, 0, ent_bstride, 0, 0,
+                        dt, out);
+  if (st) return st;
+  const size_t need = cskv::attend_partial_bytes((int)dt, B, H, N);
+  if (need && (!workspace || ws_bytes < need || !aligned16(workspace)))
+    return fail(CSKV_ERR_WORKSPACE, "cskv_hca_attend: workspace %zu bytes, need %zu", ws_bytes, need);
+  cskv::AttendParams p{(int)dt, q, entries, nullptr, nullptr, nullptr, B, N, ent_bstride, 0, 0, 0,
+                       H, 0, 0, scale, out, lse, 1};
+  return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), "cskv_hca_attend");
+}
+
+int cskv_merge(const float* o_part, const float* lse_part, int64_t B, int32_t H, int32_t S,
+               void* out, float* lse, cskv_dtype dt, void* stream) {
+  if (!o_part || !lse_part || !out) return fail(CSKV_ERR_INVALID_ARG, "cskv_merge: null pointer");
+  if (B < 1 || H < 1 || S < 1) return fail(CSKV_ERR_INVALID_ARG, "cskv_merge: B=%lld H=%d S=%d",
+                                           (long long)B, H, S);
+  if (dt != CSKV_F32 && dt != CSKV_BF16)
+    return fail(CSKV_ERR_UNSUPPORTED, "cskv_merge: dtype %d (F32 or BF16)", (int)dt);
+  if (!aligned16(o_part) || !aligned16(out))
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_merge: tensors must be 16-byte aligned");
+  return hip_status(cskv::launch_merge((int)dt, o_part, lse_part, B * H, S, out, lse,
+                                       (hipStream_t)stream),
+                    "cskv_merge");
+}
+
+}  // extern "C"

@@ -1,0 +1,444 @@
+// Indexer scoring and top-k selection for gfx950.
+//
+// Method: "Frontier Techniques: NTK RoPE, CSA+HCA, QAT, MTP" 2.1 (entries
+// scored cheaply by the indexer, the top 1024 kept per query) and "DeepSeek
+// V4 comprimeix el context", section "CSA: buscar primer i atendre despres"
+// (a light indexer scores every compressed entry and keeps the most relevant
+// ones).  Score s[b][i] = scale * dot(q_idx[b], key[i]) over 64 dims; the
+// selection is the first k visible entries in the order (score descending,
+// index ascending).
+//
+// Selection without storing the B x N score matrix:
+//  1. score pass (MFMA): scores are reduced to the maximum of every group of
+//     GS consecutive entries.  The k-th largest group maximum is a score that
+//     at least k entries reach, so it is a lower bound of the k-th best score.
+//  2. threshold: per query, radix select of the k-th largest group maximum.
+//  3. collect pass (MFMA again): every visible entry scoring at least the
+//     threshold is appended to the query's candidate list (typically ~1.2 k
+//     candidates for unstructured scores).
+//  4. final: per query, exact radix select over (score key, ~index) 64-bit
+//     composite keys of the candidates, then the chosen indices are sorted
+//     ascending and written.  If the candidate list overflowed (e.g. massive
+//     score ties), the query is resolved by a self-contained streaming radix
+//     select over all its entries instead.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace cskv {
+
+constexpr int kI = 64;
+constexpr int kCap = 8192;           // candidate capacity per query
+constexpr int kMaxK = 4096;
+constexpr int kMaxGroups = 16384;
+
+struct IdxArgs {
+  const void* q;              // [B][64]
+  const void* keys;           // [N][64] (+ b * key_bstride)
+  const int64_t* q_pos;       // NULL at decode
+  int64_t key_bstride;
+  int B, N, k, m, GS, G, qpb, tiles_per_wave;
+  float scale;
+  uint32_t* gmax;             // [B][G]
+  uint32_t* thr;              // [B]
+  uint32_t* cnt;              // [B]
+  uint64_t* cand;             // [B][kCap]
+  int32_t* out;               // [B][k]
+};
+
+__device__ __forceinline__ int n_visible(const IdxArgs& a, int b) {
+  if (!a.q_pos) return a.N;
+  const int64_t v = (a.q_pos[b] + 1) / a.m;                 // entries with (i+1)m <= pos+1
+  return (int)(v < 0 ? 0 : (v > a.N ? a.N : v));
+}
+
+template <class T> struct KeyFrag;
+template <> struct KeyFrag<bf16_t> { static constexpr int bytes = 2; };
+template <> struct KeyFrag<float> { static constexpr int bytes = 4; };
+template <> struct KeyFrag<e4m3_t> { static constexpr int bytes = 1; };
+
+// MODE 0: group maxima.  MODE 1: collect candidates >= threshold.
+template <class T, int NQB, int MODE>
+__global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int q0 = blockIdx.y * a.qpb;
+  const T* qbase = reinterpret_cast<const T*>(a.q);
+  const T* kbase = reinterpret_cast<const T*>(a.keys) + (int64_t)q0 * a.key_bstride;
+
+  // this lane's queries (one per 16-column block) and their query fragments
+  Frag<T> qf[NQB][2];
+  int qb[NQB], nvis[NQB];
+  float tscore[NQB];
+  int blk_vis = 0;
+#pragma unroll
+  for (int j = 0; j < NQB; ++j) {
+    const int c = 16 * j + col;
+    const bool ok = c < a.qpb && q0 + c < a.B;
+    qb[j] = ok ? q0 + c : -1;
+    nvis[j] = ok ? n_visible(a, q0 + c) : 0;
+    blk_vis = max(blk_vis, nvis[j]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ok) {
+        frag_load(qf[j][ks], qbase + (int64_t)(q0 + c) * kI + 32 * ks + 8 * g);
+      } else {
+        Frag<T> z{};
+        qf[j][ks] = z;
+      }
+    }
+    tscore[j] = -INFINITY;                                       // threshold 0: take all
+    if (MODE == 1 && ok && a.thr[q0 + c] != 0u) tscore[j] = key_score(a.thr[q0 + c]);
+  }
+  // the largest visible prefix over the block's queries bounds the tiles
+  for (int off = 32; off >= 1; off >>= 1) blk_vis = max(blk_vis, __shfl_xor(blk_vis, off, 64));
+
+  // group maxima are written for every group (0 when nothing is visible);
+  // candidates are only looked for in the visible prefix
+  const int e_w0 = (blockIdx.x * 4 + wave) * a.tiles_per_wave * 16;
+  const int e_w1 = min(e_w0 + a.tiles_per_wave * 16, MODE == 0 ? a.G * a.GS : blk_vis);
+  float gm[NQB][4];
+#pragma unroll
+  for (int j = 0; j < NQB; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gm[j][i] = -INFINITY;
+
+  for (int et = e_w0; et < e_w1; et += 16) {
+   if (et < blk_vis) {                                         // skip invisible tiles
+    Frag<T> kf[2];
+    const int er = et + col;                                   // A row of this lane
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (er < a.N) {
+        frag_load(kf[ks], kbase + (int64_t)er * kI + 32 * ks + 8 * g);
+      } else {
+        Frag<T> z{};
+        kf[ks] = z;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NQB; ++j) {
+      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+      mma16(S, kf[0], qf[j][0]);
+      mma16(S, kf[1], qf[j][1]);
+      // S[i]: query qb[j], entry et + 4g + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = et + 4 * g + i;
+        const bool vis = e < nvis[j];
+        if (MODE == 0) {
+          gm[j][i] = fmaxf(gm[j][i], vis ? S[i] : -INFINITY);
+        } else if (vis) {
+          const float s = S[i] * a.scale;
+          if (s >= tscore[j]) {
+            const uint32_t slot = atomicAdd(a.cnt + qb[j], 1u);
+            if (slot < (uint32_t)kCap)
+              a.cand[(int64_t)qb[j] * kCap + slot] =
+                  ((uint64_t)score_key(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+          }
+        }
+      }
+    }
+   }
+    if (MODE == 0) {
+      // group boundaries coincide with tile boundaries for GS >= 16
+      const int GS = a.GS;
+      if (GS <= 8 || ((et + 16) % GS) == 0) {
+#pragma unroll
+        for (int j = 0; j < NQB; ++j) {
+          float v = fmaxf(fmaxf(gm[j][0], gm[j][1]), fmaxf(gm[j][2], gm[j][3]));
+          int grp;
+          bool writer;
+          if (GS == 4) {
+            grp = (et + 4 * g) / 4;
+            writer = true;
+          } else if (GS == 8) {
+            v = fmaxf(v, shfl_xor(v, 16));
+            grp = (et + 8 * (g >> 1)) / 8;
+            writer = (g & 1) == 0;
+          } else {
+            v = fmaxf(v, shfl_xor(v, 16));
+            v = fmaxf(v, shfl_xor(v, 32));
+            grp = et / GS;
+            writer = g == 0;
+          }
+          if (writer && qb[j] >= 0 && grp < a.G)
+            a.gmax[(int64_t)qb[j] * a.G + grp] = (v == -INFINITY) ? 0u : score_key(v * a.scale);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gm[j][i] = -INFINITY;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------- block-wide radix helpers
+
+// Block of 256 threads: position of the digit holding the kk-th largest key
+// among the counted ones.  hist[256] in LDS (already filled); on return
+// *digit and *above (count of keys in higher digits) are in LDS scratch.
+__device__ void find_digit(const uint32_t* hist, int nbins, uint32_t kk, uint32_t* sh_digit,
+                           uint32_t* sh_above, uint32_t* scan) {
+  // suffix sums (from the top bin down), one bin chunk per thread
+  const int t = threadIdx.x;
+  const int per = nbins / 256;
+  uint32_t local = 0;
+  for (int i = 0; i < per; ++i) local += hist[nbins - 1 - (t * per + i)];
+  scan[t] = local;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    uint32_t v = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
+  }
+  // scan[t] = keys in the top (t+1)*per bins
+  const uint32_t before = t ? scan[t - 1] : 0;
+  if (before < kk && kk <= scan[t]) {
+    uint32_t cum = before;
+    for (int i = 0; i < per; ++i) {
+      const int bin = nbins - 1 - (t * per + i);
+      if (cum + hist[bin] >= kk) {
+        *sh_digit = (uint32_t)bin;
+        *sh_above = cum;
+        break;
+      }
+      cum += hist[bin];
+    }
+  }
+  __syncthreads();
+}
+
+// k-th largest of the G group maxima of each query (0 if fewer than k
+// non-empty groups or fewer than k visible entries).
+__global__ __launch_bounds__(256) void idx_threshold_kernel(IdxArgs a) {
+  __shared__ uint32_t keys[kMaxGroups];
+  __shared__ uint32_t hist[256], scan[256];
+  __shared__ uint32_t sh_digit, sh_above, sh_nonempty;
+  const int b = blockIdx.x;
+  if (threadIdx.x == 0) sh_nonempty = 0;
+  __syncthreads();
+  uint32_t ne = 0;
+  for (int i = threadIdx.x; i < a.G; i += 256) {
+    const uint32_t v = a.gmax[(int64_t)b * a.G + i];
+    keys[i] = v;
+    ne += v != 0u;
+  }
+  atomicAdd(&sh_nonempty, ne);
+  __syncthreads();
+  const int nv = n_visible(a, b);
+  if (nv <= a.k || sh_nonempty < (uint32_t)a.k) {
+    if (threadIdx.x == 0) { a.thr[b] = 0u; a.cnt[b] = 0u; }
+    return;
+  }
+  uint32_t prefix = 0, mask = 0, kk = (uint32_t)a.k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.G; i += 256) {
+      const uint32_t v = keys[i];
+      if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    find_digit(hist, 256, kk, &sh_digit, &sh_above, scan);
+    kk -= sh_above;
+    prefix |= sh_digit << shift;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) { a.thr[b] = prefix; a.cnt[b] = 0u; }
+}
+
+// ----------------------------------------------------------------- final
+
+constexpr int kFinalThreads = 256;
+
+// 64-bit composite of the scored entry e: score key high, ~e low (so that
+// larger composite = higher score, then lower index).
+__device__ __forceinline__ uint64_t composite(uint32_t key, int e) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+
+template <class T>
+__device__ __forceinline__ float dot64(const T* qrow, const T* krow);
+template <> __device__ __forceinline__ float dot64<float>(const float* q, const float* k) {
+  float s = 0.f;
+  for (int r = 0; r < kI; ++r) s = fmaf(q[r], k[r], s);
+  return s;
+}
+template <> __device__ __forceinline__ float dot64<bf16_t>(const bf16_t* q, const bf16_t* k) {
+  float s = 0.f;
+  for (int r = 0; r < kI; ++r)
+    s = fmaf(__uint_as_float((uint32_t)q[r].u << 16), __uint_as_float((uint32_t)k[r].u << 16), s);
+  return s;
+}
+template <> __device__ __forceinline__ float dot64<e4m3_t>(const e4m3_t* q, const e4m3_t* k) {
+  float s = 0.f;
+  for (int r = 0; r < kI; ++r)
+    s = fmaf(__builtin_amdgcn_cvt_f32_fp8((int)q[r].u, 0), __builtin_amdgcn_cvt_f32_fp8((int)k[r].u, 0), s);
+  return s;
+}
+
+// Exact selection for one query.  Candidates are either the collected list
+// (in LDS) or, on overflow, every visible entry with its score recomputed.
+template <class T>
+__global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
+  __shared__ uint64_t cand[kCap];
+  __shared__ int32_t sel[kMaxK];
+  __shared__ uint32_t hist[2048], scan[256];
+  __shared__ uint32_t sh_digit, sh_above, sh_nsel;
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const int nv = n_visible(a, b);
+  int32_t* out = a.out + (int64_t)b * a.k;
+  if (nv <= a.k) {
+    for (int j = t; j < a.k; j += kFinalThreads) out[j] = j < nv ? j : -1;
+    return;
+  }
+  const uint32_t c = a.cnt[b];
+  const bool overflow = c > (uint32_t)kCap;
+  const int nc = overflow ? 0 : (int)c;
+  for (int j = t; j < nc; j += kFinalThreads) cand[j] = a.cand[(int64_t)b * kCap + j];
+  const T* kb = reinterpret_cast<const T*>(a.keys) + (int64_t)b * a.key_bstride;
+  const T* qrow = reinterpret_cast<const T*>(a.q) + (int64_t)b * kI;
+  __syncthreads();
+
+  // radix select of the k-th largest composite, most significant digit first
+  uint64_t prefix = 0, mask = 0;
+  uint32_t kk = (uint32_t)a.k;
+  int shift = 64;
+  bool done = false;
+  for (int p = 0; p < 6 && !done; ++p) {
+    const int bits = (p % 3 == 2) ? 10 : 11;                 // 11+11+10 bits per 32-bit half
+    shift -= bits;
+    const uint32_t nb = 1u << bits;
+    for (int i = t; i < 2048; i += kFinalThreads) hist[i] = 0;
+    __syncthreads();
+    if (!overflow) {
+      for (int j = t; j < nc; j += kFinalThreads) {
+        const uint64_t v = cand[j];
+        if ((v & mask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & (nb - 1)], 1u);
+      }
+    } else {
+      for (int e = t; e < nv; e += kFinalThreads) {
+        const float s = dot64<T>(qrow, kb + (int64_t)e * kI) * a.scale;
+        const uint64_t v = composite(score_key(s), e);
+        if ((v & mask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & (nb - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    find_digit(hist, 2048, kk, &sh_digit, &sh_above, scan);
+    // bins above 2^bits are empty, so the digit lies below nb
+    kk -= sh_above;
+    const uint32_t bucket = hist[sh_digit];
+    prefix |= (uint64_t)sh_digit << shift;
+    mask |= (uint64_t)(nb - 1) << shift;
+    done = bucket == kk;                 // every key in the bucket is selected
+    __syncthreads();
+  }
+  // threshold: lowest composite in the final bucket (remaining bits zero)
+  const uint64_t thr = prefix;
+  if (t == 0) sh_nsel = 0;
+  __syncthreads();
+  if (!overflow) {
+    for (int j = t; j < nc; j += kFinalThreads) {
+      const uint64_t v = cand[j];
+      if (v >= thr) {
+        const uint32_t at = atomicAdd(&sh_nsel, 1u);
+        if (at < (uint32_t)kMaxK) sel[at] = (int32_t)(0xffffffffu - (uint32_t)v);
+      }
+    }
+  } else {
+    for (int e = t; e < nv; e += kFinalThreads) {
+      const float s = dot64<T>(qrow, kb + (int64_t)e * kI) * a.scale;
+      if (composite(score_key(s), e) >= thr) {
+        const uint32_t at = atomicAdd(&sh_nsel, 1u);
+        if (at < (uint32_t)kMaxK) sel[at] = e;
+      }
+    }
+  }
+  __syncthreads();
+  // bitonic sort of the k selected indices (ascending), padded to 2^p
+  int n2 = 1;
+  while (n2 < a.k) n2 <<= 1;
+  for (int j = a.k + t; j < n2; j += kFinalThreads) sel[j] = 0x7fffffff;
+  __syncthreads();
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = t; i < n2 / 2; i += kFinalThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const int32_t x = sel[lo], y = sel[hi];
+        if ((x > y) == up) { sel[lo] = y; sel[hi] = x; }
+      }
+      __syncthreads();
+    }
+  }
+  for (int j = t; j < a.k; j += kFinalThreads) out[j] = sel[j];
+}
+
+// ------------------------------------------------------------------ host
+
+// Group size: about 4k groups per query (so the k-th largest group maximum
+// sits near the top quarter of the groups), at most kMaxGroups groups.
+int topk_group_size(int64_t N, int k) {
+  int64_t target = N / (4 * (int64_t)k);
+  int gs = 4;
+  while (gs < 64 && (int64_t)gs * 2 <= target) gs *= 2;
+  while (gs < 64 && (N + gs - 1) / gs > kMaxGroups) gs *= 2;
+  return gs;
+}
+
+size_t topk_workspace_bytes(int64_t B, int64_t N, int k) {
+  const int GS = topk_group_size(N, k);
+  const int64_t G = (N + GS - 1) / GS;
+  size_t bytes = 0;
+  bytes += (size_t)B * kCap * 8;                        // candidates
+  bytes += (size_t)B * G * 4;                           // group maxima
+  bytes += (size_t)B * 8;                               // threshold + count
+  return bytes + 256;
+}
+
+int topk_max_k() { return kMaxK; }
+int64_t topk_max_entries() { return (int64_t)kMaxGroups * 64; }
+
+template <class T>
+static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t stream) {
+  IdxArgs a;
+  a.q = p.q; a.keys = p.keys; a.q_pos = p.q_pos; a.key_bstride = p.key_bstride;
+  a.B = (int)p.B; a.N = (int)p.N; a.k = p.k; a.m = p.m; a.scale = p.scale; a.out = p.out;
+  a.GS = topk_group_size(p.N, p.k);
+  a.G = (int)((p.N + a.GS - 1) / a.GS);
+  char* w = (char*)ws;
+  a.cand = (uint64_t*)w;            w += (size_t)p.B * kCap * 8;
+  a.gmax = (uint32_t*)w;            w += (size_t)p.B * a.G * 4;
+  a.thr = (uint32_t*)w;             w += (size_t)p.B * 4;
+  a.cnt = (uint32_t*)w;
+  const bool per_seq = p.key_bstride != 0;
+  int nqb = per_seq ? 1 : (p.B <= 16 ? 1 : (p.B <= 32 ? 2 : 4));
+  a.qpb = per_seq ? 1 : 16 * nqb;
+  const int qblocks = (int)((p.B + a.qpb - 1) / a.qpb);
+  // tiles per wave: a multiple of GS/16, enough blocks to fill the GPU
+  const int min_tpw = a.GS >= 16 ? a.GS / 16 : 1;
+  int tpw = 64;
+  while (tpw > min_tpw && (int64_t)qblocks * ((p.N + tpw * 64 - 1) / (tpw * 64)) < 1024) tpw /= 2;
+  a.tiles_per_wave = tpw;
+  const int chunks = (int)((p.N + tpw * 64 - 1) / (tpw * 64));
+  dim3 grid(chunks, qblocks);
+#define CSKV_SCORE(NQB, MODE) \
+  hipLaunchKernelGGL((idx_score_kernel<T, NQB, MODE>), grid, dim3(256), 0, stream, a)
+  if (nqb == 1) CSKV_SCORE(1, 0); else if (nqb == 2) CSKV_SCORE(2, 0); else CSKV_SCORE(4, 0);
+  hipLaunchKernelGGL(idx_threshold_kernel, dim3((unsigned)p.B), dim3(256), 0, stream, a);
+  if (nqb == 1) CSKV_SCORE(1, 1); else if (nqb == 2) CSKV_SCORE(2, 1); else CSKV_SCORE(4, 1);
+#undef CSKV_SCORE
+  hipLaunchKernelGGL(idx_final_kernel<T>, dim3((unsigned)p.B), dim3(kFinalThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkParams& p, void* ws, hipStream_t stream) {
+  if (p.dt == 0) return launch_topk_t<float>(p, ws, stream);
+  if (p.dt == 1) return launch_topk_t<bf16_t>(p, ws, stream);
+  return launch_topk_t<e4m3_t>(p, ws, stream);
+}
+
+}  // namespace cskv

@@ -1,0 +1,51 @@
+// Launchers of the gfx950 kernels (host side).  Each returns the HIP status
+// of its launches; argument checking happens before, in api.cpp.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cskv {
+
+hipError_t launch_compress(int dt, const void* x, const void* z, const float* bias, int m,
+                           int64_t e_begin, int64_t e_end, void* out, int64_t ld_out,
+                           hipStream_t stream);
+
+struct AttendParams {
+  int dt;                    // 0 fp32, 1 bf16
+  const void* q;             // [B][H][576]
+  const void* entries;       // [N][576] (+ b * ent_bstride)
+  const void* window;        // rows of 576 (+ b * win_bstride)
+  const int32_t* idx;        // [B][k] selected entries (unused when dense)
+  const int64_t* q_pos;      // NULL = decode window
+  int64_t B, N, ent_bstride, win_bstride, win_pos0, win_rows;
+  int H, W, k;
+  float scale;
+  void* out;                 // [B][H][512]
+  float* lse;                // [B][H] or NULL
+  int dense;                 // 1: rows = all N entries, no window
+};
+
+int attend_splits(int dt, int64_t B, int H, int64_t nslots);
+size_t attend_partial_bytes(int dt, int64_t B, int H, int64_t nslots);
+hipError_t launch_attend(const AttendParams& p, void* ws, hipStream_t stream);
+hipError_t launch_merge(int dt, const float* o_part, const float* lse_part, int64_t BH, int S,
+                        void* out, float* lse, hipStream_t stream);
+
+struct TopkParams {
+  int dt;                    // 0 fp32, 1 bf16, 2 fp8 e4m3
+  const void* q;             // [B][64]
+  const void* keys;          // [N][64] (+ b * key_bstride)
+  const int64_t* q_pos;      // NULL at decode
+  int64_t key_bstride, B, N;
+  int k, m;
+  float scale;
+  int32_t* out;              // [B][k]
+};
+
+int topk_max_k();
+int64_t topk_max_entries();
+size_t topk_workspace_bytes(int64_t B, int64_t N, int k);
+hipError_t launch_topk(const TopkParams& p, void* ws, hipStream_t stream);
+
+}  // namespace cskv

@@ -1,0 +1,184 @@
+/*
+ * cskv: token-axis compressed attention (CSA / HCA) for AMD MI355X (gfx950).
+ *
+ * The method is described by the pages
+ *   "Frontier Techniques: NTK RoPE, CSA+HCA, QAT, MTP" (section 2, CSA + HCA),
+ *   "DeepSeek V4 comprimeix el context: aixi funcionen CSA i HCA",
+ *   "The State and Signal Problem: MLA and Multi-Token Prediction" (section
+ *   "MLA compresses what generation must remember": 512-dim shared latent plus
+ *   a decoupled 64-dim RoPE key),
+ *   "Compressed attention - CSA / HCA" (sections 1-4: token-axis compression,
+ *   recent window plus compressed history, cache budgeting).
+ *
+ * Data layout (row-major, element counts; D = 512, R = 64, E = D + R = 576):
+ *   raw_kv, score_logits [T][512]   raw shared-KV rows and compressor logits
+ *   pos_bias             [2m][512]  fp32 per-window-position bias
+ *   entries              [N][576]   compressed entries: dims 0..511 content
+ *                                    (the attention value), 512..575 RoPE part
+ *   idx_keys             [N][64]    indexer keys;   q_idx [B][64] queries
+ *   window               [rows][576] raw recent rows (512 content + 64 RoPE)
+ *   q                    [B][H][576] attention queries
+ *   out                  [B][H][512] attention output;  lse [B][H] fp32
+ *   idx_out              [B][k]     int32 selected entries: valid indices in
+ *                                    ascending order, then -1 padding
+ * Per-query caches: *_bstride gives the element offset between the caches of
+ * consecutive queries (0 = one cache shared by all queries).
+ *
+ * Conventions
+ *  - Every pointer argument except `stream` is device memory (or host-pinned
+ *    memory the GPU can read), owned by the caller; the library allocates and
+ *    frees nothing and keeps no state between calls.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronize the device.
+ *  - All arguments are validated before anything is launched: on error
+ *    nothing is written and a negative status is returned; the message is
+ *    kept per thread in cskv_last_error().
+ *  - Inputs outside what the kernels are built for are rejected with
+ *    CSKV_ERR_UNSUPPORTED; there is no fallback path.
+ *  - Results are deterministic for fixed shapes (fixed split counts and merge
+ *    order; the selected set is fully ordered by score then index).
+ *  - Tensors must be 16-byte aligned.
+ */
+#ifndef CSKV_H
+#define CSKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSKV_VERSION 10000
+
+typedef enum cskv_dtype {
+  CSKV_F32 = 0,       /* IEEE binary32 */
+  CSKV_BF16 = 1,      /* bfloat16 */
+  CSKV_FP8_E4M3 = 2   /* OCP fp8 E4M3 (max 448); indexer keys/queries only */
+} cskv_dtype;
+
+typedef enum cskv_status {
+  CSKV_OK = 0,
+  CSKV_ERR_INVALID_ARG = -1,  /* null pointer, bad size, range out of bounds */
+  CSKV_ERR_UNSUPPORTED = -2,  /* valid but outside the compiled kernels */
+  CSKV_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+  CSKV_ERR_HIP = -4           /* launch failure; HIP message in cskv_last_error() */
+} cskv_status;
+
+int cskv_version(void);
+const char* cskv_status_string(int status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* cskv_last_error(void);
+
+/*
+ * Compression ("DeepSeek V4 comprimeix el context", sections "DeepSeek
+ * comprimeix la dimensio temporal" and "Finestres solapades per evitar
+ * fronteres artificials"; "Frontier Techniques", 2.1 m = 4 and 2.2 m' = 128).
+ *
+ * For entries i in [entry_begin, entry_end) and d < 512:
+ *   out[i*ld_out + d] = sum_p w_p[d] * raw_kv[j][d],   j = (i-1)*m + p,
+ *   w[d] = softmax over the present p in [0, 2m) (j >= 0) of
+ *          score_logits[j][d] + pos_bias[p][d].
+ * Entry count N = floor(T/m); tokens past N*m are not compressed (they stay
+ * in the raw window).  Only columns 0..511 of each out row are written, so
+ * out may be the packed 576-wide entry buffer (ld_out = 576).  Bulk use is
+ * (0, N); streaming decode appends one entry per completed block with
+ * (N-1, N).
+ *   raw_kv, score_logits: [T][512] in dt (F32 or BF16); pos_bias: [2m][512]
+ *   fp32; out: rows of ld_out >= 512 elements in dt (ld_out % 8 == 0).
+ * An empty entry range is a no-op (the pointers are then not used).
+ * Errors: INVALID_ARG for null pointers, T < 0, m < 1, entry range outside
+ * [0, N], ld_out < 512; UNSUPPORTED for dt not F32/BF16.
+ */
+int cskv_compress(const void* raw_kv, const void* score_logits, const float* pos_bias, int64_t T,
+                  int32_t m, int64_t entry_begin, int64_t entry_end, void* out, int64_t ld_out,
+                  cskv_dtype dt, void* stream);
+
+/*
+ * Indexer scoring and top-k selection ("Frontier Techniques", 2.1: entries
+ * scored cheaply by the indexer, top-1024 kept; "DeepSeek V4 comprimeix el
+ * context", section "CSA: buscar primer i atendre despres").
+ *
+ *   s[b][i] = idx_scale * sum_{r<64} q_idx[b][r] * idx_keys[b*key_bstride + i*64 + r]
+ * Visible entries: all N at decode (q_pos == NULL); for a causal prefill
+ * query at position q_pos[b], entry i is visible iff (i+1)*m <= q_pos[b]+1.
+ * idx_out[b] receives the min(k, visible) visible entries that come first in
+ * the order (score descending, index ascending), as ascending indices,
+ * followed by -1 padding.
+ *   q_idx [B][64], idx_keys [N][64] (per query if key_bstride > 0), both in
+ *   idx_dt (F32, BF16 or FP8_E4M3; for FP8 pass idx_scale = scale_q*scale_k).
+ *   workspace: at least cskv_index_topk_workspace_size(B, N, k) bytes.
+ * Errors: INVALID_ARG (null pointers, B < 1, N < 1, k < 1, m < 1 with q_pos);
+ * UNSUPPORTED (k > 4096); WORKSPACE.
+ */
+size_t cskv_index_topk_workspace_size(int64_t B, int64_t N, int32_t k);
+int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t N, int32_t k,
+                    int64_t key_bstride, const int64_t* q_pos, int32_t m, float idx_scale,
+                    cskv_dtype idx_dt, int32_t* idx_out, void* workspace, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * Sparse attention over selected entries plus the raw window ("Frontier
+ * Techniques", 2.1: attention over the top entries plus a 128-token raw
+ * window; "DeepSeek V4 comprimeix el context", section "CSA: ...": full
+ * attention over the chosen blocks and the local window).
+ *
+ * Rows of query b: entries[b*ent_bstride + idx[b][j]*576] for idx[b][j] >= 0,
+ * then the window rows: at decode (q_pos == NULL) rows 0..W-1 of
+ * window + b*win_bstride; at prefill the raw rows at positions
+ * max(0, q_pos[b]-W+1) .. q_pos[b], where row 0 of the window buffer holds
+ * position win_pos0 (the buffer has win_rows rows).  For every head h:
+ *   l_r = scale * sum_{e<576} q[b][h][e] * row_r[e],
+ *   out[b][h][d] = sum_r softmax(l)_r * row_r[d]  (d < 512),
+ *   lse[b][h] = ln sum_r exp(l_r)   (lse may be NULL).
+ * One softmax covers the selected entries and the window together.
+ *   idx [B][k] int32 (-1 = no entry; any order); q, entries, window, out in dt
+ *   (F32 or BF16); workspace: cskv_attend_workspace_size(...) bytes.
+ * Errors: INVALID_ARG (null pointers, sizes < 0, window positions outside the
+ * buffer); UNSUPPORTED (dt not F32/BF16); WORKSPACE.
+ */
+size_t cskv_attend_workspace_size(int64_t B, int32_t H, int64_t rows_per_query);
+int cskv_sparse_attend(const void* q, const void* entries, const void* window, const int32_t* idx,
+                       int64_t B, int32_t H, int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
+                       int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
+                       int64_t win_pos0, float scale, cskv_dtype dt, void* out, float* lse,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * CSA: cskv_index_topk followed by cskv_sparse_attend, on one stream, with
+ * one workspace of cskv_csa_workspace_size(B, H, N, W, k) bytes.  idx_out
+ * ([B][k] int32) receives the selection.
+ */
+size_t cskv_csa_workspace_size(int64_t B, int32_t H, int64_t N, int32_t W, int32_t k);
+int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const void* idx_keys,
+                    const void* window, int64_t B, int32_t H, int64_t N, int32_t W, int32_t k,
+                    int32_t m, int64_t ent_bstride, int64_t key_bstride, int64_t win_bstride,
+                    int64_t win_rows, const int64_t* q_pos, int64_t win_pos0, float scale,
+                    float idx_scale, cskv_dtype dt, cskv_dtype idx_dt, void* out, float* lse,
+                    int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * HCA ("Frontier Techniques", 2.2; "DeepSeek V4 comprimeix el context",
+ * section "HCA: un resum global 128 vegades mes curt"): every query attends
+ * densely over all N entries, no selection and no window.  Same formulas as
+ * cskv_sparse_attend with rows = entries[b*ent_bstride + i*576], i < N.
+ */
+size_t cskv_hca_workspace_size(int64_t B, int32_t H, int64_t N);
+int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, int64_t N,
+                    int64_t ent_bstride, float scale, cskv_dtype dt, void* out, float* lse,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Merge of split-KV partial results: for each (b, h) with S partial results
+ * o_part[b][h][s][512] (fp32, each normalised over its own rows) and
+ * lse_part[b][h][s]:  lse = ln sum_s exp(lse_s),  out = sum_s exp(lse_s - lse)
+ * * o_s.  A split with no rows has lse_s = -inf and contributes nothing.
+ * out [B][H][512] in dt; lse may be NULL.
+ */
+int cskv_merge(const float* o_part, const float* lse_part, int64_t B, int32_t H, int32_t S,
+               void* out, float* lse, cskv_dtype dt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSKV_H */

@@ -1,0 +1,32 @@
+"""Shared helpers of the GPU parity tests: upload stored inputs, compare
+against the oracle with the normwise relative error."""
+import numpy as np
+import torch
+
+import workloads as wl
+
+TOL = {wl.DT_F32: 1e-4, wl.DT_BF16: 2e-2}
+
+
+def dev(t, device="cuda"):
+    """Upload a stored input (workloads.Tensor or raw numpy) as a torch tensor
+    of the matching dtype."""
+    raw, dt = (t.raw, t.dt) if isinstance(t, wl.Tensor) else (t, None)
+    if raw.dtype == np.uint16:
+        return torch.from_numpy(raw.view(np.int16)).to(device).view(torch.bfloat16)
+    if raw.dtype == np.uint8:
+        return torch.from_numpy(raw).to(device).view(torch.float8_e4m3fn)
+    return torch.from_numpy(np.ascontiguousarray(raw)).to(device)
+
+
+def host_f64(t):
+    """GPU tensor -> float64 numpy (exact decode of bf16/fp32)."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rowwise_err(got, ref):
+    """max over rows of max|got - ref| / max|ref| (one row = last axis)."""
+    got = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return float((np.abs(got - ref).max(axis=1) / den).max())

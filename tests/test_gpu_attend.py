@@ -1,0 +1,193 @@
+"""GPU parity of the attention entry points (HCA, sparse attention over a
+given selection, fused CSA, merge) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests.helpers import TOL, dev, host_f64, rowwise_err
+from tests.selection import check_selection
+
+pytestmark = pytest.mark.gpu
+E = 576
+
+
+def _cskv():
+    import compressed_sparse_kv_overlapping_amd as cskv
+    return cskv
+
+
+def _rand(cfg_id, seed, tid, shape, dt, std=1.0):
+    return wl.encode(wl.normal(cfg_id, seed, tid, shape, std), dt).raw
+
+
+def _check_attn(out, lse, ref_out, ref_lse, dt):
+    assert rowwise_err(host_f64(out), ref_out) <= TOL[dt]
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-4 if dt == wl.DT_F32 else 2e-3,
+                               atol=1e-4 if dt == wl.DT_F32 else 2e-3)
+
+
+@pytest.mark.parametrize("dt", [wl.DT_F32, wl.DT_BF16])
+@pytest.mark.parametrize("B,H,N", [(1, 16, 32), (2, 128, 1000), (3, 48, 33), (1, 16, 1), (4, 130, 300)])
+def test_hca_matches_oracle(dt, B, H, N):
+    q = _rand(94, N, 1, (B, H, E), dt, 1 / 24)
+    ent = _rand(94, N, 2, (N, E), dt)
+    out, lse = _cskv().hca_attend(dev(q), dev(ent))
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q, ent, dt)
+    _check_attn(out, lse, ro, rl, dt)
+
+
+def test_hca_decode_workload_sampled():
+    """16 queries x 128 heads over 8,192 bf16 entries; queries 0 and 15 checked."""
+    cfg = wl.CONFIGS["hca_decode"]
+    inp = wl.make_inputs(cfg, seed=0)
+    out, lse = _cskv().hca_attend(dev(inp["q_hca"]), dev(inp["entries_hca"]))
+    torch.cuda.synchronize()
+    rows = [0, cfg.B - 1]
+    ro, rl = oracle.hca_attend(inp["q_hca"].raw[rows], inp["entries_hca"].raw, wl.DT_BF16)
+    _check_attn(out[rows], lse[rows], ro, rl, wl.DT_BF16)
+
+
+def test_hca_per_sequence_caches():
+    B, H, N, dt = 3, 64, 700, wl.DT_BF16
+    q = _rand(95, 0, 1, (B, H, E), dt, 1 / 24)
+    ent = _rand(95, 0, 2, (B, N, E), dt)
+    out, lse = _cskv().hca_attend(dev(q), dev(ent), per_seq=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q, ent, dt, per_seq=True)
+    _check_attn(out, lse, ro, rl, dt)
+
+
+@pytest.mark.parametrize("dt", [wl.DT_F32, wl.DT_BF16])
+def test_sparse_attend_given_selection(dt):
+    """Attention over a given index list (with -1 holes, unsorted) plus the window."""
+    B, H, N, W, k = 3, 128 if dt == wl.DT_BF16 else 16, 5000, 128, 200
+    q = _rand(96, 0, 1, (B, H, E), dt, 1 / 24)
+    ent = _rand(96, 0, 2, (N, E), dt)
+    win = _rand(96, 0, 3, (W, E), dt)
+    rng = np.random.default_rng(0)
+    idx = np.stack([rng.choice(N, k, replace=False) for _ in range(B)]).astype(np.int32)
+    idx[0, 5:40] = -1
+    idx[2, :] = -1
+    out, lse = _cskv().sparse_attend(dev(q), dev(ent), dev(win), torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend(q, ent, win, dt, idx)
+    _check_attn(out, lse, ro, rl, dt)
+
+
+def test_sparse_attend_special_cases():
+    cskv = _cskv()
+    dt = wl.DT_BF16
+    B, H, N, W, k = 2, 64, 300, 128, 1024
+    ent = _rand(97, 0, 2, (N, E), dt)
+    win = _rand(97, 0, 3, (W, E), dt)
+    idx = np.full((B, k), -1, np.int32)
+    idx[:, :N] = np.arange(N)                                   # k >= N: all entries
+    q = np.zeros((B, H, E), np.uint16)                          # q = 0: uniform weights
+    out, lse = cskv.sparse_attend(dev(q), dev(ent), dev(win), torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    rows = np.concatenate([oracle.decode(ent, dt), oracle.decode(win, dt)])
+    assert rowwise_err(host_f64(out)[0], np.tile(rows[:, :512].mean(0), (H, 1))) <= 2e-2
+    np.testing.assert_allclose(lse.cpu().numpy(), np.log(N + W), rtol=1e-5)
+    # no rows at all: zero output, lse = -inf
+    q2 = _rand(97, 0, 1, (B, H, E), dt, 1 / 24)
+    none = np.full((B, 4), -1, np.int32)
+    out, lse = cskv.sparse_attend(dev(q2), dev(ent), dev(win), torch.from_numpy(none).cuda(), W=0)
+    torch.cuda.synchronize()
+    assert (host_f64(out) == 0).all() and np.isneginf(lse.cpu().numpy()).all()
+    out, lse = cskv.hca_attend(dev(q2), dev(ent), scale=0.0)       # scale 0: uniform weights
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(lse.cpu().numpy(), np.log(N), rtol=1e-5)
+
+
+def test_merge_of_split_partials():
+    """cskv_merge combines oracle partials over a row partition into the
+    oracle's unsplit result."""
+    B, H, N, S = 2, 32, 300, 7
+    q = _rand(98, 0, 1, (B, H, E), wl.DT_F32, 1 / 24)
+    ent = _rand(98, 0, 2, (N, E), wl.DT_F32)
+    parts = np.array_split(np.arange(N), S - 1)
+    parts.insert(3, np.arange(0))                               # plus one empty split
+    po, pl = [], []
+    for p in parts:
+        if len(p):
+            o, l = oracle.hca_attend(q, ent[p], wl.DT_F32)
+        else:
+            o, l = np.zeros((B, H, 512)), np.full((B, H), -np.inf)
+        po.append(o)
+        pl.append(l)
+    o_part = torch.from_numpy(np.stack(po, 2).astype(np.float32)).cuda()      # [B, H, S, 512]
+    l_part = torch.from_numpy(np.stack(pl, 2).astype(np.float32)).cuda()
+    out, lse = _cskv().merge(o_part, l_part, dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q, ent, wl.DT_F32)
+    assert rowwise_err(host_f64(out), ro) <= 1e-5
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=1e-5)
+
+
+@pytest.mark.parametrize("name", ["tiny", "csa_decode"])
+def test_csa_decode_matches_oracle(name):
+    """Fused CSA decode: selection within the tie band, then attention over
+    the selection plus the window equal to the oracle's."""
+    cfg = wl.CONFIGS[name]
+    inp = wl.make_inputs(cfg, seed=0)
+    cskv = _cskv()
+    if cfg.T:
+        ent = np.empty((cfg.N_csa, E), np.float32 if cfg.dt == wl.DT_F32 else np.uint16)
+        c = oracle.compress(inp["x"].raw, inp["z"].raw, cfg.dt, inp["b4"].raw, 4)
+        ent[:, :512] = c if cfg.dt == wl.DT_F32 else wl.bf16_bits(c.astype(np.float32))
+        ent[:, 512:] = inp["rope4"].raw
+    else:
+        ent = inp["entries"].raw
+    out, lse, idx = cskv.csa_attend(dev(inp["q"]), dev(inp["qI"]), dev(ent), dev(inp["kI"]),
+                                    dev(inp["window"]), cfg.k)
+    torch.cuda.synchronize()
+    s, v = oracle.index_scores(inp["qI"].raw, inp["kI"].raw, cfg.idx_dt)
+    idx = idx.cpu().numpy()
+    check_selection(idx, s, v, cfg.k)
+    ref_idx = np.sort(oracle.topk(s, v, cfg.k), axis=1)
+    same = [b for b in range(cfg.B) if np.array_equal(ref_idx[b], idx[b])]
+    assert len(same) >= cfg.B - 1
+    ro, rl = oracle.csa_attend(inp["q"].raw[same], ent, inp["window"].raw, cfg.dt, ref_idx[same])
+    _check_attn(out[same], lse[same], ro, rl, cfg.dt)
+
+
+def test_csa_prefill_attention_sampled():
+    """Prefill attention with per-query causal windows, on the 1M-context
+    chunk shapes (sampled queries), using the oracle's own selection."""
+    cfg = wl.CONFIGS["csa_prefill"]
+    inp = wl.make_inputs(cfg, seed=0)
+    rows = np.array([0, 1, 2047, cfg.B - 1])
+    qI, kI = inp["qI"], inp["kI"]
+    s, v = oracle.index_scores(qI.raw[rows], kI.raw, wl.DT_E4M3, qI.scale * kI.scale,
+                               q_pos=inp["q_pos"][rows], m=4)
+    idx = np.sort(oracle.topk(s, v, cfg.k), axis=1)
+    qp = inp["q_pos"][rows]
+    out, lse = _cskv().sparse_attend(dev(inp["q"].raw[rows]), dev(inp["entries"]), dev(inp["window"]),
+                                     torch.from_numpy(idx).cuda(), q_pos=torch.from_numpy(qp).cuda(),
+                                     win_pos0=inp["win_pos0"], W=cfg.W)
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend(inp["q"].raw[rows], inp["entries"].raw, inp["window"].raw, wl.DT_BF16,
+                               idx, q_pos=qp, win_pos0=inp["win_pos0"], W=cfg.W)
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+
+
+def test_csa_per_sequence_decode():
+    B, H, N, W, k, dt = 4, 128, 6000, 128, 512, wl.DT_BF16
+    q = _rand(99, 0, 1, (B, H, E), dt, 1 / 24)
+    ent = _rand(99, 0, 2, (B, N, E), dt)
+    win = _rand(99, 0, 3, (B, W, E), dt)
+    qI = _rand(99, 0, 4, (B, 64), dt)
+    kI = _rand(99, 0, 5, (B, N, 64), dt)
+    out, lse, idx = _cskv().csa_attend(dev(q), dev(qI), dev(ent), dev(kI), dev(win), k, per_seq=True)
+    torch.cuda.synchronize()
+    s, v = oracle.index_scores(qI, kI, dt, per_seq=True)
+    idx = idx.cpu().numpy()
+    check_selection(idx, s, v, k)
+    ref_idx = np.sort(oracle.topk(s, v, k), 1)
+    ro, rl = oracle.csa_attend(q, ent, win, dt, ref_idx, per_seq=True)
+    same = [b for b in range(B) if np.array_equal(ref_idx[b], idx[b])]
+    assert len(same) >= B - 1
+    _check_attn(out[same], lse[same], ro[same], rl[same], dt)

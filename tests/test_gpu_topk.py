@@ -1,0 +1,120 @@
+"""GPU parity of cskv_index_topk: indexer scores and top-k selection."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests.helpers import dev
+from tests.selection import check_selection
+
+pytestmark = pytest.mark.gpu
+
+
+def _cskv():
+    import compressed_sparse_kv_overlapping_amd as cskv
+    return cskv
+
+
+def _run(qI, kI, dt, k, scale=1.0, q_pos=None, m=4, per_seq=False):
+    cskv = _cskv()
+    qp = None if q_pos is None else torch.from_numpy(np.asarray(q_pos, np.int64)).cuda()
+    idx = cskv.index_topk(dev(qI), dev(kI), k, q_pos=qp, m=m, idx_scale=scale, per_seq=per_seq)
+    torch.cuda.synchronize()
+    s, v = oracle.index_scores(qI, kI, dt, scale, q_pos=q_pos, m=m, per_seq=per_seq)
+    return idx.cpu().numpy(), s, v
+
+
+@pytest.mark.parametrize("dt", [wl.DT_F32, wl.DT_BF16])
+@pytest.mark.parametrize("B,N,k", [(1, 1024, 64), (8, 16384, 1024), (3, 5000, 100), (40, 3001, 17),
+                                   (2, 70000, 7), (5, 777, 1), (1, 4096, 4096)])
+def test_topk_matches_oracle(dt, B, N, k):
+    rng_cfg = 91
+    qI = wl.encode(wl.normal(rng_cfg, N, 1, (B, 64)), dt).raw
+    kI = wl.encode(wl.normal(rng_cfg, N, 2, (N, 64)), dt).raw
+    idx, s, v = _run(qI, kI, dt, k)
+    exact = check_selection(idx, s, v, k)
+    assert exact >= B - 1          # near-ties inside the band are rare for random scores
+
+
+def test_topk_workload_sizes():
+    """The decode selections of the workloads: top-64 of 1,024 (fp32),
+    top-1024 of 16,384 (bf16, 8 queries) and of 262,144 (bf16, 32 queries)."""
+    for name in ("tiny", "csa_decode"):
+        inp = wl.make_inputs(name, seed=0)
+        cfg = wl.CONFIGS[name]
+        idx, s, v = _run(inp["qI"].raw, inp["kI"].raw, cfg.idx_dt, cfg.k)
+        check_selection(idx, s, v, cfg.k)
+    cfg = wl.CONFIGS["layer_1m"]
+    inp = wl.make_inputs(cfg, seed=0, with_compress_source=False)
+    idx, s, v = _run(inp["qI"].raw, inp["kI"].raw, wl.DT_BF16, cfg.k)
+    check_selection(idx, s, v, cfg.k)
+
+
+def test_topk_exact_ties_resolve_by_index():
+    """Small-integer inputs: exact scores with many ties; the order (score
+    descending, index ascending) makes the set unique."""
+    rng = np.random.default_rng(5)
+    B, N, k = 4, 20000, 300
+    qI = rng.integers(-2, 3, (B, 64)).astype(np.float32)
+    kI = rng.integers(-2, 3, (N, 64)).astype(np.float32)
+    for dt in (wl.DT_F32, wl.DT_BF16):
+        idx, s, v = _run(wl.encode(qI, dt).raw, wl.encode(kI, dt).raw, dt, k)
+        ref = oracle.topk(s, v, k)
+        np.testing.assert_array_equal(idx, np.sort(ref, axis=1))
+
+
+def test_topk_all_equal_scores_takes_lowest_indices():
+    """Every score equal: the candidate list overflows and the streaming path
+    must return entries 0..k-1."""
+    B, N, k = 3, 30000, 50
+    qI = np.zeros((B, 64), np.float32)
+    kI = np.random.default_rng(6).standard_normal((N, 64)).astype(np.float32)
+    idx, _, _ = _run(wl.bf16_bits(qI), wl.bf16_bits(kI), wl.DT_BF16, k)
+    np.testing.assert_array_equal(idx, np.tile(np.arange(k, dtype=np.int32), (B, 1)))
+
+
+def test_topk_fewer_entries_than_k():
+    qI = np.ones((2, 64), np.float32)
+    kI = np.random.default_rng(7).standard_normal((10, 64)).astype(np.float32)
+    idx, _, _ = _run(qI, kI, wl.DT_F32, 16)
+    np.testing.assert_array_equal(idx[:, :10], np.tile(np.arange(10), (2, 1)))
+    assert (idx[:, 10:] == -1).all()
+
+
+def test_topk_per_sequence_keys():
+    rng_cfg = 92
+    B, N, k = 6, 9000, 256
+    qI = wl.bf16_bits(wl.normal(rng_cfg, 0, 1, (B, 64)))
+    kI = wl.bf16_bits(wl.normal(rng_cfg, 0, 2, (B, N, 64)))
+    idx, s, v = _run(qI, kI, wl.DT_BF16, k, per_seq=True)
+    check_selection(idx, s, v, k)
+
+
+def test_topk_prefill_fp8_causal():
+    """fp8 e4m3 indexer with per-tensor scales and a causal mask: queries at
+    the end of a context whose visible entry count varies per query."""
+    rng_cfg = 93
+    B, N, k, m = 64, 40000, 1024, 4
+    q = wl.normal(rng_cfg, 0, 1, (B, 64))
+    kk = wl.normal(rng_cfg, 0, 2, (N, 64))
+    sq, sk = wl.e4m3_scale(q), wl.e4m3_scale(kk)
+    qI, kI = wl.e4m3_encode(q, sq), wl.e4m3_encode(kk, sk)
+    pos = np.concatenate([[0, 3, 4, 100, 4099], np.arange(N * m - B + 5, N * m)])[:B]
+    idx, s, v = _run(qI, kI, wl.DT_E4M3, k, scale=sq * sk, q_pos=pos, m=m)
+    check_selection(idx, s, v, k)
+
+
+def test_topk_prefill_workload_sampled():
+    """The 4,096-query fp8 prefill chunk over 262,144 entries, checked on a
+    sample of queries (first, last and evenly spaced positions)."""
+    cfg = wl.CONFIGS["csa_prefill"]
+    inp = wl.make_inputs(cfg, seed=0)
+    qI, kI = inp["qI"], inp["kI"]
+    scale = qI.scale * kI.scale
+    cskv = _cskv()
+    qp = torch.from_numpy(inp["q_pos"]).cuda()
+    idx = cskv.index_topk(dev(qI), dev(kI), cfg.k, q_pos=qp, m=4, idx_scale=scale).cpu().numpy()
+    rows = np.unique(np.concatenate([[0, 1, cfg.B - 1], np.linspace(0, cfg.B - 1, 29).astype(int)]))
+    s, v = oracle.index_scores(qI.raw[rows], kI.raw, wl.DT_E4M3, scale, q_pos=inp["q_pos"][rows], m=4)
+    check_selection(idx[rows], s, v, cfg.k)
