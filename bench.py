@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the compressed sparse KV attention hot path on one MI355X.
+
+One step = the 1M-token layer pair: compress the raw bf16 KV [2^20, 512] at
+m = 4 (262,144 entries) and m' = 128 (8,192 entries) into 576-wide entry
+buffers, then CSA decode (indexer top-1024 + 128-token window) and HCA decode
+(dense over all 8,192 entries) for 32 queries x 128 heads.  Inputs are seeded
+synthetic tensors already resident in HBM; every kernel of the step runs in
+the timed region.
+
+Metric: compressed-KV entries attended per second, counted as (query,
+compressed entry) pairs: 32 x 1024 (CSA) + 32 x 8192 (HCA) per step.
+
+Prints one JSON line.  Per-kernel durations come from HIP events recorded on
+the launch stream around each launch inside the timed steps; the roofline of
+the dominant kernel divides its algorithmic bytes by its average duration.
+The CPU baseline times the oracle on a bounded sample of the same step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+D, R, E, I = 512, 64, 576, 64
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "compressed_sparse_kv_overlapping_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get("kernels", {}).get(kernel)
+    if not entry or t.get("source_digest") != source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is described in DESIGN.md, not built.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import compressed_sparse_kv_overlapping_amd as cskv
+    import workloads as wl
+    from tests.helpers import dev
+
+    torch.cuda.set_device(0)
+    cfg = wl.CONFIGS["layer_1m"]
+    t_gen = time.time()
+    inp = wl.make_inputs(cfg, seed=args.seed)
+    T, B, H, k, W = cfg.T, cfg.B, cfg.H, cfg.k, cfg.W
+    N4, N128 = T // cfg.m_csa, T // cfg.m_hca
+    x, z = dev(inp["x"]), dev(inp["z"])
+    b4, b128 = dev(inp["b4"]), dev(inp["b128"])
+    ent4 = torch.empty((N4, E), dtype=torch.bfloat16, device="cuda")
+    ent128 = torch.empty((N128, E), dtype=torch.bfloat16, device="cuda")
+    ent4[:, D:] = dev(inp["rope4"])
+    ent128[:, D:] = dev(inp["rope128"])
+    win, q, q_hca = dev(inp["window"]), dev(inp["q"]), dev(inp["q_hca"])
+    qI, kI = dev(inp["qI"]), dev(inp["kI"])
+    out_csa = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    out_hca = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    lse_csa = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    lse_hca = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    ws_topk = torch.empty(cskv.index_topk_workspace_size(B, N4, k), dtype=torch.uint8, device="cuda")
+    ws_csa = torch.empty(max(1, cskv.attend_workspace_size(B, H, k + W)), dtype=torch.uint8, device="cuda")
+    ws_hca = torch.empty(max(1, cskv.hca_workspace_size(B, H, N128)), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    gen_s = time.time() - t_gen
+
+    parts = ["compress_m4", "compress_m128", "csa_topk", "csa_attend", "hca_attend"]
+
+    def step(ev):
+        ev[0].record()
+        cskv.compress(x, z, b4, cfg.m_csa, out=ent4)
+        ev[1].record()
+        cskv.compress(x, z, b128, cfg.m_hca, out=ent128)
+        ev[2].record()
+        cskv.index_topk(qI, kI, k, idx_out=idx, workspace=ws_topk)
+        ev[3].record()
+        cskv.sparse_attend(q, ent4, win, idx, out=out_csa, lse=lse_csa, workspace=ws_csa)
+        ev[4].record()
+        cskv.hca_attend(q_hca, ent128, out=out_hca, lse=lse_hca, workspace=ws_hca)
+        ev[5].record()
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
+
+    for _ in range(args.warmup):
+        step(events())
+    torch.cuda.synchronize()
+    evs = [events() for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+    part_ms = {p: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+               for j, p in enumerate(parts)}
+
+    pairs = B * k + B * N128
+    value = pairs / (ms_step * 1e-3)
+
+    # algorithmic bytes / flops per launch (inputs once, outputs once, gathers per query)
+    bx = 2 * T * D * 2
+    alg = {
+        "compress_m4": {"bytes": bx + N4 * D * 2},
+        "compress_m128": {"bytes": bx + N128 * D * 2},
+        "csa_topk": {"bytes": N4 * I * 2 + B * I * 2 + B * k * 4, "flops": 2 * B * N4 * I},
+        "csa_attend": {"bytes": B * (k + W) * E * 2 + B * H * E * 2 + B * H * D * 2,
+                       "flops": 2 * B * H * (k + W) * (E + D)},
+        "hca_attend": {"bytes": N128 * E * 2 + B * H * E * 2 + B * H * D * 2,
+                       "flops": 2 * B * H * N128 * (E + D)},
+    }
+    detail = {}
+    for p in parts:
+        t = part_ms[p] * 1e-3
+        d = {"ms": round(part_ms[p], 4), "GB/s": round(alg[p]["bytes"] / t / 1e9, 1),
+             "hbm_frac": round(alg[p]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4)}
+        if "flops" in alg[p]:
+            d["TFLOP/s"] = round(alg[p]["flops"] / t / 1e12, 2)
+            d["bf16_mfma_frac"] = round(alg[p]["flops"] / t / 1e12 / BF16_PEAK_TFLOPS, 4)
+        detail[p] = d
+    dom = max(parts, key=lambda p: part_ms[p])
+    ach = alg[dom]["bytes"] / (part_ms[dom] * 1e-3) / 1e9
+    traffic = measured_traffic(dom)
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "alg_bytes_per_launch": alg[dom]["bytes"]}
+
+    comp_ms = part_ms["compress_m4"] + part_ms["compress_m128"]
+    attn_ms = part_ms["csa_topk"] + part_ms["csa_attend"] + part_ms["hca_attend"]
+    comp_bytes = alg["compress_m4"]["bytes"] + alg["compress_m128"]["bytes"]
+    attn_bytes = alg["csa_topk"]["bytes"] + alg["csa_attend"]["bytes"] + alg["hca_attend"]["bytes"]
+
+    result = {
+        "metric": "compressed-KV entries attended/sec + % HBM peak, CSA/HCA decode at 1M ctx",
+        "value": round(value, 1), "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "layer_1m", "raw_tokens": T, "entries_m4": N4, "entries_m128": N128,
+                   "queries": B, "heads": H, "top_k": k, "window": W,
+                   "pairs_per_step": pairs, "kv": "shared context"},
+        "roofline": roofline,
+        "compressor_GBps": round(comp_bytes / (comp_ms * 1e-3) / 1e9, 1),
+        "attention_GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
+        "decode_only_entries_per_s": round(pairs / (attn_ms * 1e-3), 1),
+        "parts": detail,
+        "wall_s_timed": round(wall, 3), "input_gen_s": round(gen_s, 1),
+    }
+    del x, z
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(args, cskv, wl, dev, torch, np)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, inp, cfg, ms_step, np)
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(args, cskv, wl, dev, torch, np):
+    """The 4,096-query causal prefill chunk at positions 1,044,480..1,048,575
+    over 262,144 entries (fp8 indexer, bf16 attention)."""
+    cfg = wl.CONFIGS["csa_prefill"]
+    inp = wl.make_inputs(cfg, seed=args.seed)
+    B, H, k, W, N = cfg.B, cfg.H, cfg.k, cfg.W, cfg.N_csa
+    q, ent, win = dev(inp["q"]), dev(inp["entries"]), dev(inp["window"])
+    qI, kI = dev(inp["qI"]), dev(inp["kI"])
+    scale = inp["qI"].scale * inp["kI"].scale
+    qp = torch.from_numpy(inp["q_pos"]).cuda()
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws_t = torch.empty(cskv.index_topk_workspace_size(B, N, k), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(max(1, cskv.attend_workspace_size(B, H, k + W)), dtype=torch.uint8, device="cuda")
+
+    def run(ev):
+        ev[0].record()
+        cskv.index_topk(qI, kI, k, q_pos=qp, m=4, idx_scale=scale, idx_out=idx, workspace=ws_t)
+        ev[1].record()
+        cskv.sparse_attend(q, ent, win, idx, q_pos=qp, win_pos0=inp["win_pos0"], W=W, out=out,
+                           lse=lse, workspace=ws_a)
+        ev[2].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for _ in range(2):
+        run(mk())
+    steps = max(3, args.steps // 4)
+    evs = [mk() for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    t_sel = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_att = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    n_vis = np.minimum((inp["q_pos"] + 1) // 4, N)
+    pairs = int(n_vis.sum())                                   # visible (query, entry) scores
+    idx_flops = 2 * pairs * I
+    att_flops = 2 * B * H * (k + W) * (E + D)
+    return {
+        "workload": "csa_prefill", "queries": B, "entries": N, "top_k": k, "window": W,
+        "ms": round(t_sel + t_att, 4),
+        "entries_attended_per_s": round(B * k / ((t_sel + t_att) * 1e-3), 1),
+        "indexer_topk_ms": round(t_sel, 4),
+        "indexer_TFLOPs": round(idx_flops / (t_sel * 1e-3) / 1e12, 2),
+        "indexer_frac_bf16_peak": round(idx_flops / (t_sel * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "indexer_frac_fp8_peak": round(idx_flops / (t_sel * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "attention_ms": round(t_att, 4),
+        "attention_roofline": {"bound": "mfma", "achieved": round(att_flops / (t_att * 1e-3) / 1e12, 1),
+                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(att_flops / (t_att * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+    }
+
+
+def cpu_baseline(args, inp, cfg, gpu_ms, np):
+    """The oracle (plain fp64 C, OpenMP over independent outputs) on a bounded
+    sample of the same step, extrapolated to a whole step."""
+    import oracle
+    import workloads as wl
+    threads = oracle.max_threads()
+    T, B, H, k = cfg.T, cfg.B, cfg.H, cfg.k
+    N4, N128 = T // 4, T // 128
+    rng = np.random.default_rng(0)
+    budget = args.cpu_seconds
+    # compress: a sample of entries at each scale
+    n4, n128 = 4096, 64
+    t = time.perf_counter()
+    oracle.compress(inp["x"].raw, inp["z"].raw, wl.DT_BF16, inp["b4"].raw, 4,
+                    entry_ids=rng.choice(N4, n4, replace=False))
+    t_c4 = (time.perf_counter() - t) * N4 / n4
+    t = time.perf_counter()
+    oracle.compress(inp["x"].raw, inp["z"].raw, wl.DT_BF16, inp["b128"].raw, 128,
+                    entry_ids=rng.choice(N128, n128, replace=False))
+    t_c128 = (time.perf_counter() - t) * N128 / n128
+    # CSA and HCA: one query with all its heads (the oracle's cost does not
+    # depend on the entry values, so the content dims are a constant here)
+    ent = np.empty((N4, E), np.uint16)
+    ent[:, :D] = 0x3f80
+    ent[:, D:] = inp["rope4"].raw
+    t = time.perf_counter()
+    s, v = oracle.index_scores(inp["qI"].raw[:1], inp["kI"].raw, wl.DT_BF16)
+    sel = oracle.topk(s, v, k)
+    t_sel = (time.perf_counter() - t) * B
+    t = time.perf_counter()
+    oracle.csa_attend(inp["q"].raw[:1], ent, inp["window"].raw, wl.DT_BF16, sel)
+    t_csa = (time.perf_counter() - t) * B
+    ent128 = np.empty((N128, E), np.uint16)
+    ent128[:, :D] = 0x3f80
+    ent128[:, D:] = inp["rope128"].raw
+    nh = 16
+    t = time.perf_counter()
+    oracle.hca_attend(inp["q_hca"].raw[:1, :nh], ent128, wl.DT_BF16)
+    t_hca = (time.perf_counter() - t) * B * H / nh
+    step_s = t_c4 + t_c128 + t_sel + t_csa + t_hca
+    pairs = B * k + B * N128
+    return {
+        "value": round(pairs / step_s, 2), "unit": "entries/s", "cores": threads, "kind": "oracle",
+        "sample": (f"compress {n4} of {N4} m=4 entries and {n128} of {N128} m'=128 entries; "
+                   f"indexer+top-k and CSA attention for 1 of {B} queries (all {H} heads); HCA for "
+                   f"1 query x {nh} of {H} heads; each part scaled to the full step"),
+        "step_s_extrapolated": round(step_s, 2),
+        "parts_s": {"compress_m4": round(t_c4, 2), "compress_m128": round(t_c128, 2),
+                    "csa_topk": round(t_sel, 2), "csa_attend": round(t_csa, 2),
+                    "hca_attend": round(t_hca, 2)},
+        "gpu_speedup": round(step_s / (gpu_ms * 1e-3), 1),
+    }
+
+
+if __name__ == "__main__":
+    main()
