@@ -71,6 +71,101 @@ template <> struct Row8<bf16_t> {
   }
 };
 
+// 8 consecutive elements kept in their storage format (16 bytes of bf16 or
+// 32 bytes of fp32) and widened on use.
+template <class T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float operator[](int i) const {
+    const uint32_t w = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
+    return (i & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ float operator[](int i) const {
+    return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : i == 3 ? a.w
+         : i == 4 ? b.x : i == 5 ? b.y : i == 6 ? b.z : b.w;
+  }
+};
+
+// 4 consecutive elements in storage format (8 bytes bf16, 16 bytes fp32).
+template <class T> struct Raw4;
+template <> struct Raw4<bf16_t> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ float operator[](int i) const {
+    const uint32_t w = i < 2 ? v.x : v.y;
+    return (i & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+};
+template <> struct Raw4<float> {
+  float4 a;
+  __device__ __forceinline__ void load(const float* p) { a = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ float operator[](int i) const {
+    return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : a.w;
+  }
+};
+template <class T, int N> struct RawN;
+template <class T> struct RawN<T, 8> : Raw8<T> {};
+template <class T> struct RawN<T, 4> : Raw4<T> {};
+
+// N consecutive fp32 stored as the output dtype.
+template <class T, int N> struct StoreN;
+template <class T> struct StoreN<T, 8> {
+  static __device__ __forceinline__ void store(T* p, const float* v) { Row8<T>::store(p, v); }
+};
+template <> struct StoreN<bf16_t, 4> {
+  static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+};
+template <> struct StoreN<float, 4> {
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+// Raw buffer stores: the hardware drops stores whose offset is at or past
+// num_records, so a store can be issued unconditionally and masked by its
+// offset (keeps loops free of conditional memory operations).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+template <class T, int N> struct BufStoreN;
+template <> struct BufStoreN<bf16_t, 4> {
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+  }
+};
+template <> struct BufStoreN<bf16_t, 8> {
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v) {
+    u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+               pack_bf16x2(v[6], v[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+  }
+};
+template <> struct BufStoreN<float, 4> {
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v) {
+    u32x4 w = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+  }
+};
+template <> struct BufStoreN<float, 8> {
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v) {
+    BufStoreN<float, 4>::store(r, off, v);
+    BufStoreN<float, 4>::store(r, off + 16, v + 4);
+  }
+};
+
 // ---------------------------------------------------------------- shuffles
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 

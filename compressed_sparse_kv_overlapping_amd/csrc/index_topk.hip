@@ -40,9 +40,10 @@ struct IdxArgs {
   float scale;
   uint32_t* gmax;             // [B][G]
   uint32_t* thr;              // [B]
-  uint32_t* cnt;              // [B]
-  uint64_t* cand;             // [B][kCap]
+  uint32_t* cnt;              // [B][chunks] candidates found per (query, chunk)
+  uint64_t* cand;             // [B][chunks][region] candidate regions
   int32_t* out;               // [B][k]
+  int chunks, region;         // score-pass chunks; slots per (query, chunk)
 };
 
 __device__ __forceinline__ int n_visible(const IdxArgs& a, int b) {
@@ -56,10 +57,16 @@ template <> struct KeyFrag<bf16_t> { static constexpr int bytes = 2; };
 template <> struct KeyFrag<float> { static constexpr int bytes = 4; };
 template <> struct KeyFrag<e4m3_t> { static constexpr int bytes = 1; };
 
-// MODE 0: group maxima.  MODE 1: collect candidates >= threshold.
+// MODE 0: group maxima.  MODE 1: collect candidates >= threshold into this
+// chunk's region of each query (counted in LDS, no global atomics).
 template <class T, int NQB, int MODE>
 __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
+  __shared__ uint32_t lcnt[16 * NQB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (MODE == 1) {
+    if (threadIdx.x < 16 * NQB) lcnt[threadIdx.x] = 0;
+    __syncthreads();
+  }
   const int col = lane & 15, g = lane >> 4;
   const int q0 = blockIdx.y * a.qpb;
   const T* qbase = reinterpret_cast<const T*>(a.q);
@@ -130,9 +137,9 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
         } else if (vis) {
           const float s = S[i] * a.scale;
           if (s >= tscore[j]) {
-            const uint32_t slot = atomicAdd(a.cnt + qb[j], 1u);
-            if (slot < (uint32_t)kCap)
-              a.cand[(int64_t)qb[j] * kCap + slot] =
+            const uint32_t slot = atomicAdd(&lcnt[16 * j + col], 1u);
+            if (slot < (uint32_t)a.region)
+              a.cand[((int64_t)qb[j] * a.chunks + blockIdx.x) * a.region + slot] =
                   ((uint64_t)score_key(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
           }
         }
@@ -167,6 +174,13 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
           for (int i = 0; i < 4; ++i) gm[j][i] = -INFINITY;
         }
       }
+    }
+  }
+  if (MODE == 1) {
+    __syncthreads();
+    if (threadIdx.x < 16 * NQB) {
+      const int c = threadIdx.x;
+      if (c < a.qpb && q0 + c < a.B) a.cnt[(int64_t)(q0 + c) * a.chunks + blockIdx.x] = lcnt[c];
     }
   }
 }
@@ -227,7 +241,7 @@ __global__ __launch_bounds__(256) void idx_threshold_kernel(IdxArgs a) {
   __syncthreads();
   const int nv = n_visible(a, b);
   if (nv <= a.k || sh_nonempty < (uint32_t)a.k) {
-    if (threadIdx.x == 0) { a.thr[b] = 0u; a.cnt[b] = 0u; }
+    if (threadIdx.x == 0) a.thr[b] = 0u;
     return;
   }
   uint32_t prefix = 0, mask = 0, kk = (uint32_t)a.k;
@@ -245,7 +259,7 @@ __global__ __launch_bounds__(256) void idx_threshold_kernel(IdxArgs a) {
     mask |= 255u << shift;
     __syncthreads();
   }
-  if (threadIdx.x == 0) { a.thr[b] = prefix; a.cnt[b] = 0u; }
+  if (threadIdx.x == 0) a.thr[b] = prefix;
 }
 
 // ----------------------------------------------------------------- final
@@ -294,10 +308,34 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
     for (int j = t; j < a.k; j += kFinalThreads) out[j] = j < nv ? j : -1;
     return;
   }
-  const uint32_t c = a.cnt[b];
-  const bool overflow = c > (uint32_t)kCap;
-  const int nc = overflow ? 0 : (int)c;
-  for (int j = t; j < nc; j += kFinalThreads) cand[j] = a.cand[(int64_t)b * kCap + j];
+  // gather the chunk regions into LDS (prefix sums of the chunk counts);
+  // a full region or more than kCap candidates in total means overflow
+  __shared__ uint32_t sh_total, sh_over;
+  if (t == 0) { sh_total = 0; sh_over = 0; }
+  __syncthreads();
+  for (int c0 = 0; c0 < a.chunks; c0 += kFinalThreads) {
+    const int c = c0 + t;
+    const uint32_t n = c < a.chunks ? a.cnt[(int64_t)b * a.chunks + c] : 0u;
+    if (n > (uint32_t)a.region) atomicOr(&sh_over, 1u);
+    scan[t] = n;
+    __syncthreads();
+    for (int off = 1; off < kFinalThreads; off <<= 1) {
+      const uint32_t v = t >= off ? scan[t - off] : 0u;
+      __syncthreads();
+      scan[t] += v;
+      __syncthreads();
+    }
+    const uint32_t base = sh_total + (t ? scan[t - 1] : 0u);
+    if (!sh_over && c < a.chunks && base + n <= (uint32_t)kCap) {
+      const uint64_t* src = a.cand + ((int64_t)b * a.chunks + c) * a.region;
+      for (uint32_t i = 0; i < n; ++i) cand[base + i] = src[i];
+    }
+    __syncthreads();
+    if (t == kFinalThreads - 1) sh_total += scan[t];
+    __syncthreads();
+  }
+  const bool overflow = sh_over || sh_total > (uint32_t)kCap;
+  const int nc = overflow ? 0 : (int)sh_total;
   const T* kb = reinterpret_cast<const T*>(a.keys) + (int64_t)b * a.key_bstride;
   const T* qrow = reinterpret_cast<const T*>(a.q) + (int64_t)b * kI;
   __syncthreads();
@@ -389,13 +427,42 @@ int topk_group_size(int64_t N, int k) {
   return gs;
 }
 
+// Launch geometry of the score passes, shared by the workspace query and the
+// launcher: entry chunks of tiles_per_wave * 64 entries (4 waves x 16-entry
+// tiles), and the candidate region of each (query, chunk).
+struct TopkGeom { int GS, G, qpb, nqb, qblocks, tpw, chunks, region; };
+
+static TopkGeom topk_geom(int64_t B, int64_t N, int k, bool per_seq) {
+  TopkGeom g;
+  g.GS = topk_group_size(N, k);
+  g.G = (int)((N + g.GS - 1) / g.GS);
+  g.nqb = per_seq ? 1 : (B <= 16 ? 1 : (B <= 32 ? 2 : 4));
+  g.qpb = per_seq ? 1 : 16 * g.nqb;
+  g.qblocks = (int)((B + g.qpb - 1) / g.qpb);
+  const int min_tpw = g.GS >= 16 ? g.GS / 16 : 1;
+  g.tpw = 64;
+  while (g.tpw > min_tpw && (int64_t)g.qblocks * ((N + g.tpw * 64 - 1) / (g.tpw * 64)) < 1024) g.tpw /= 2;
+  g.chunks = (int)((N + g.tpw * 64 - 1) / (g.tpw * 64));
+  // about 1.2k candidates per query are expected; give each chunk room for
+  // 16x its share (at least 32 slots), capped by the chunk size
+  int64_t r = (16 * (int64_t)k + g.chunks - 1) / g.chunks;
+  r = r < 32 ? 32 : r;
+  const int64_t csize = (int64_t)g.tpw * 64;
+  g.region = (int)(r > csize ? csize : r);
+  return g;
+}
+
 size_t topk_workspace_bytes(int64_t B, int64_t N, int k) {
-  const int GS = topk_group_size(N, k);
-  const int64_t G = (N + GS - 1) / GS;
+  // per-sequence keys use one query per block, which has the most chunks
+  const TopkGeom g1 = topk_geom(B, N, k, false), g2 = topk_geom(B, N, k, true);
+  const int64_t slots = (int64_t)g1.chunks * g1.region > (int64_t)g2.chunks * g2.region
+                            ? (int64_t)g1.chunks * g1.region : (int64_t)g2.chunks * g2.region;
+  const int64_t chunks = g1.chunks > g2.chunks ? g1.chunks : g2.chunks;
   size_t bytes = 0;
-  bytes += (size_t)B * kCap * 8;                        // candidates
-  bytes += (size_t)B * G * 4;                           // group maxima
-  bytes += (size_t)B * 8;                               // threshold + count
+  bytes += (size_t)B * slots * 8;                       // candidate regions
+  bytes += (size_t)B * g1.G * 4;                        // group maxima
+  bytes += (size_t)B * 4;                               // thresholds
+  bytes += (size_t)B * chunks * 4;                      // counts per (query, chunk)
   return bytes + 256;
 }
 
@@ -407,23 +474,16 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
   IdxArgs a;
   a.q = p.q; a.keys = p.keys; a.q_pos = p.q_pos; a.key_bstride = p.key_bstride;
   a.B = (int)p.B; a.N = (int)p.N; a.k = p.k; a.m = p.m; a.scale = p.scale; a.out = p.out;
-  a.GS = topk_group_size(p.N, p.k);
-  a.G = (int)((p.N + a.GS - 1) / a.GS);
+  const bool per_seq = p.key_bstride != 0;
+  const TopkGeom g = topk_geom(p.B, p.N, p.k, per_seq);
+  a.GS = g.GS; a.G = g.G; a.qpb = g.qpb; a.tiles_per_wave = g.tpw;
+  a.chunks = g.chunks; a.region = g.region;
   char* w = (char*)ws;
-  a.cand = (uint64_t*)w;            w += (size_t)p.B * kCap * 8;
+  a.cand = (uint64_t*)w;            w += (size_t)p.B * g.chunks * g.region * 8;
   a.gmax = (uint32_t*)w;            w += (size_t)p.B * a.G * 4;
   a.thr = (uint32_t*)w;             w += (size_t)p.B * 4;
   a.cnt = (uint32_t*)w;
-  const bool per_seq = p.key_bstride != 0;
-  int nqb = per_seq ? 1 : (p.B <= 16 ? 1 : (p.B <= 32 ? 2 : 4));
-  a.qpb = per_seq ? 1 : 16 * nqb;
-  const int qblocks = (int)((p.B + a.qpb - 1) / a.qpb);
-  // tiles per wave: a multiple of GS/16, enough blocks to fill the GPU
-  const int min_tpw = a.GS >= 16 ? a.GS / 16 : 1;
-  int tpw = 64;
-  while (tpw > min_tpw && (int64_t)qblocks * ((p.N + tpw * 64 - 1) / (tpw * 64)) < 1024) tpw /= 2;
-  a.tiles_per_wave = tpw;
-  const int chunks = (int)((p.N + tpw * 64 - 1) / (tpw * 64));
+  const int nqb = g.nqb, qblocks = g.qblocks, chunks = g.chunks;
   dim3 grid(chunks, qblocks);
 #define CSKV_SCORE(NQB, MODE) \
   hipLaunchKernelGGL((idx_score_kernel<T, NQB, MODE>), grid, dim3(256), 0, stream, a)
