@@ -34,6 +34,9 @@ _SIGS = {
     "cskv_last_error": ([], ctypes.c_char_p),
     "cskv_compress": ([_vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp, _i64, ctypes.c_int, _vp],
                       ctypes.c_int),
+    "cskv_compress2_workspace_size": ([_i32], _sz),
+    "cskv_compress2": ([_vp, _vp, _i64, _vp, _i32, _vp, _i64, _vp, _i32, _vp, _i64, ctypes.c_int,
+                        _vp, _sz, _vp], ctypes.c_int),
     "cskv_index_topk_workspace_size": ([_i64, _i64, _i32], _sz),
     "cskv_index_topk": ([_vp, _vp, _i64, _i64, _i32, _i64, _vp, _i32, _f32, ctypes.c_int, _vp,
                          _vp, _sz, _vp], ctypes.c_int),
@@ -124,6 +127,34 @@ def compress(x, z, bias, m, out=None, entry_begin=0, entry_end=None, stream=None
     _call("cskv_compress", _ptr(x), _ptr(z), _ptr(bias), T, m, entry_begin, entry_end, _ptr(out),
           out.stride(0), _dt(x), _stream(stream))
     return out
+
+
+def compress2_workspace_size(m_large):
+    return library().cskv_compress2_workspace_size(m_large)
+
+
+def compress2(x, z, bias_small, m_small, bias_large, m_large, out_small=None, out_large=None,
+              workspace=None, stream=None):
+    """Both scales in one pass: returns (out_small, out_large), each either
+    given (e.g. [N, 576] entry buffers; columns 0..511 written) or allocated
+    as [N, 512]."""
+    _dev(x, z, bias_small, bias_large)
+    T = x.shape[0]
+    if out_small is None:
+        out_small = torch.empty((T // m_small, D), dtype=x.dtype, device=x.device)
+    if out_large is None:
+        out_large = torch.empty((T // m_large, D), dtype=x.dtype, device=x.device)
+    for o in (out_small, out_large):
+        if o.dim() != 2 or o.stride(1) != 1 or o.dtype != x.dtype:
+            raise ValueError("outputs must be row-major 2-D tensors of the input dtype")
+    if x.dtype != z.dtype or bias_small.dtype != torch.float32 or bias_large.dtype != torch.float32:
+        raise ValueError("x and z must share a dtype; biases must be fp32")
+    if workspace is None:
+        workspace = _workspace(compress2_workspace_size(m_large), x.device)
+    _call("cskv_compress2", _ptr(x), _ptr(z), T, _ptr(bias_small), m_small, _ptr(out_small),
+          out_small.stride(0), _ptr(bias_large), m_large, _ptr(out_large), out_large.stride(0),
+          _dt(x), _ptr(workspace), workspace.numel(), _stream(stream))
+    return out_small, out_large
 
 
 # -------------------------------------------------------------- indexer/top-k

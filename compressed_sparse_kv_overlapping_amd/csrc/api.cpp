@@ -80,6 +80,45 @@ int cskv_compress(const void* raw_kv, const void* score_logits, const float* pos
                     "cskv_compress");
 }
 
+size_t cskv_compress2_workspace_size(int32_t m_large) {
+  if (m_large < 1 || m_large > 65536) return 0;
+  return cskv::compress_fused_workspace_bytes(m_large);
+}
+
+int cskv_compress2(const void* raw_kv, const void* score_logits, int64_t T,
+                   const float* bias_small, int32_t m_small, void* out_small, int64_t ld_small,
+                   const float* bias_large, int32_t m_large, void* out_large, int64_t ld_large,
+                   cskv_dtype dt, void* workspace, size_t ws_bytes, void* stream) {
+  if (T < 0 || m_small < 1 || m_large < 1)
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_compress2: T=%lld m_small=%d m_large=%d", (long long)T,
+                m_small, m_large);
+  if (m_large % m_small != 0 || m_large == m_small)
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_compress2: m_large=%d must be a multiple (> 1) of m_small=%d",
+                m_large, m_small);
+  if (ld_small < kD || ld_small % 8 != 0 || ld_large < kD || ld_large % 8 != 0)
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_compress2: ld_small=%lld ld_large=%lld", (long long)ld_small,
+                (long long)ld_large);
+  if (m_small > 4 || m_large > 65536)
+    return fail(CSKV_ERR_UNSUPPORTED, "cskv_compress2: m_small=%d (max 4) m_large=%d (max 65536)",
+                m_small, m_large);
+  if (dt != CSKV_F32 && dt != CSKV_BF16)
+    return fail(CSKV_ERR_UNSUPPORTED, "cskv_compress2: dtype %d (F32 or BF16)", (int)dt);
+  if (T / m_small == 0) return ok();           // nothing to write
+  const bool large = T / m_large > 0;           // the large-scale pointers are used only then
+  if (!raw_kv || !score_logits || !bias_small || !out_small || (large && (!bias_large || !out_large)))
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_compress2: null pointer");
+  if (!aligned16(raw_kv) || !aligned16(score_logits) || !aligned16(bias_small) ||
+      !aligned16(out_small) || (large && (!aligned16(bias_large) || !aligned16(out_large))))
+    return fail(CSKV_ERR_INVALID_ARG, "cskv_compress2: tensors must be 16-byte aligned");
+  const size_t need = cskv::compress_fused_workspace_bytes(m_large);
+  if (!workspace || ws_bytes < need || !aligned16(workspace))
+    return fail(CSKV_ERR_WORKSPACE, "cskv_compress2: workspace %zu bytes, need %zu", ws_bytes, need);
+  return hip_status(cskv::launch_compress_fused((int)dt, raw_kv, score_logits, T, bias_small, m_small,
+                                                out_small, ld_small, bias_large, m_large, out_large,
+                                                ld_large, workspace, (hipStream_t)stream),
+                    "cskv_compress2");
+}
+
 size_t cskv_index_topk_workspace_size(int64_t B, int64_t N, int32_t k) {
   if (B < 1 || N < 1 || k < 1) return 0;
   return cskv::topk_workspace_bytes(B, N, k);

@@ -166,8 +166,8 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
   constexpr int NDB = kDv / MN;                              // output d-blocks
   __shared__ __attribute__((aligned(16))) T Ks[kTile * C::KP];
   __shared__ __attribute__((aligned(16))) T Vt[kDv * C::VP];
-  __shared__ int64_t row_off[kTile];
-  __shared__ int row_ok[kTile];
+  __shared__ int64_t row_off[2][kTile];
+  __shared__ int row_ok[2][kTile];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
@@ -211,8 +211,13 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
   const int s_begin = split * a.slots_per_split;
   const int s_end = min(a.nslots, s_begin + a.slots_per_split);
 
-  for (int t0 = s_begin; t0 < s_end; t0 += kTile) {
-    // row addresses of this tile
+  // Software pipeline: while tile i is multiplied out of LDS, the rows of
+  // tile i+1 are already in flight into registers (their addresses were
+  // resolved into the other row_off slot).
+  constexpr int kVTasks = 8 * (kDv / 8);                      // 4-row x 8-dim value tasks
+  constexpr int kRTasks = kTile * ((kE - kDv) / 8);           // RoPE chunks
+  constexpr int kVPer = (kVTasks + NT - 1) / NT, kRPer = (kRTasks + NT - 1) / NT;
+  auto resolve = [&](int t0, int slot) {
     if (threadIdx.x < kTile) {
       const int s = t0 + threadIdx.x;
       int64_t off = 0;
@@ -232,44 +237,85 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
           off = -1 - ((int64_t)b * a.win_bstride + (ok ? r : 0) * kE);   // negative: window row
         }
       }
-      row_off[threadIdx.x] = off;
-      row_ok[threadIdx.x] = ok;
+      row_off[slot][threadIdx.x] = off;
+      row_ok[slot][threadIdx.x] = ok;
     }
-    __syncthreads();
-    // gather: value part (dims 0..511) as 4-row x 8-dim tasks, written to K
-    // row-major and to V^T; RoPE part (dims 512..575) to K only
-    for (int task = threadIdx.x; task < 8 * (kDv / 8); task += NT) {
-      const int qd = task & 7, cc = task >> 3;
-      Chunk8<T> c4[4];
+  };
+  Chunk8<T> pv[kVPer][4], pr[kRPer];
+  auto fetch = [&](int slot) {
+#pragma unroll
+    for (int u = 0; u < kVPer; ++u) {
+      const int task = threadIdx.x + u * NT;
+      const int qd = task & 7, cc = (task >> 3) & 63;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * qd + i;
-        if (row_ok[r]) {
-          const int64_t off = row_off[r];
+        if (task < kVTasks && row_ok[slot][r]) {
+          const int64_t off = row_off[slot][r];
           const T* src = off >= 0 ? ent + off : win + (-1 - off);
-          c4[i].load(src + cc * 8);
+          pv[u][i].load(src + cc * 8);
         } else {
-          c4[i].zero();
+          pv[u][i].zero();
         }
-        c4[i].store(Ks + r * C::KP + cc * 8);
       }
+    }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) Quad<T>::store(Vt + (cc * 8 + t) * C::VP + 4 * qd, c4, t);
-    }
-    for (int task = threadIdx.x; task < kTile * ((kE - kDv) / 8); task += NT) {
-      const int r = task >> 3, cc = kDv / 8 + (task & 7);
-      Chunk8<T> c;
-      if (row_ok[r]) {
-        const int64_t off = row_off[r];
+    for (int u = 0; u < kRPer; ++u) {
+      const int task = threadIdx.x + u * NT;
+      const int r = (task >> 3) & (kTile - 1), cc = kDv / 8 + (task & 7);
+      if (task < kRTasks && row_ok[slot][r]) {
+        const int64_t off = row_off[slot][r];
         const T* src = off >= 0 ? ent + off : win + (-1 - off);
-        c.load(src + cc * 8);
+        pr[u].load(src + cc * 8);
       } else {
-        c.zero();
+        pr[u].zero();
       }
-      c.store(Ks + r * C::KP + cc * 8);
     }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int u = 0; u < kVPer; ++u) {
+      const int task = threadIdx.x + u * NT;
+      if (task < kVTasks) {
+        const int qd = task & 7, cc = task >> 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[u][i].store(Ks + (4 * qd + i) * C::KP + cc * 8);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) Quad<T>::store(Vt + (cc * 8 + t) * C::VP + 4 * qd, pv[u], t);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRPer; ++u) {
+      const int task = threadIdx.x + u * NT;
+      if (task < kRTasks) {
+        const int r = task >> 3, cc = kDv / 8 + (task & 7);
+        pr[u].store(Ks + r * C::KP + cc * 8);
+      }
+    }
+  };
+  // bf16 keeps the next tile in flight; fp32 (a single wave holding a whole
+  // tile) fetches and stages back to back
+  constexpr bool kOverlap = sizeof(T) == 2;
+  int slot = 0;
+  if (kOverlap && s_begin < s_end) {
+    resolve(s_begin, 0);
     __syncthreads();
-
+    fetch(0);
+  }
+  for (int t0 = s_begin; t0 < s_end; t0 += kTile) {
+    if constexpr (kOverlap) {
+      stage();                                                 // tile t0 -> LDS
+      if (t0 + kTile < s_end) resolve(t0 + kTile, slot ^ 1);
+      __syncthreads();
+      if (t0 + kTile < s_end) fetch(slot ^ 1);                 // next tile in flight
+    } else {
+      resolve(t0, slot);
+      __syncthreads();
+      fetch(slot);
+      stage();
+      __syncthreads();
+    }
+    const int* tile_ok = row_ok[slot];
     // logits S^T[row, head]
     float sv[NS];
     if constexpr (MN == 32) {
@@ -305,7 +351,7 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int r = srow<MN>(g, i);
-      sv[i] = row_ok[r] ? sv[i] * a.c : -INFINITY;
+      sv[i] = tile_ok[r] ? sv[i] * a.c : -INFINITY;
       tmax = fmaxf(tmax, sv[i]);
     }
     if constexpr (MN == 32) {
@@ -363,6 +409,7 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
       }
     }
     __syncthreads();
+    if constexpr (kOverlap) slot ^= 1;
   }
 
   // finish: total row sum of this head over the lane groups

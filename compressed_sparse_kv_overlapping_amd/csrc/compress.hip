@@ -18,6 +18,7 @@
 // one XCD and share its L2.
 #include "common.hpp"
 #include "kernels.hpp"
+#include <cmath>
 
 namespace cskv {
 
@@ -99,16 +100,14 @@ __global__ __launch_bounds__(64 * kCompressWaves) void compress_kernel(
 // A wave streams a contiguous range of entries and reads every token once.
 // Block b (tokens [bm, bm+m)) feeds two windows: the second half of entry b
 // (window positions m..2m-1) and the first half of entry b+1 (positions
-// 0..m-1).  With a reference r per dimension, a token's weight in either
-// window factors as
+// 0..m-1).  With the block maximum r of z (per dimension), a token's weight
+// in either window factors as
 //     exp(z + b_p - M) = 2^(z*log2e - r) * 2^((b_p - bmax)*log2e) * const,
 // so each element needs one exp2, shared by both windows, times a
-// per-position factor beta_p <= 1 precomputed once (in registers).  The
-// constant cancels in the normalisation as long as both halves of an entry
-// use the same r.  r moves only when a block maximum leaves [r - kBand,
-// r + kBand] (log2 units); then the carried half is rescaled.  So weights
-// stay in (2^-kBand-ish, 2^kBand] without a per-window maximum, and the
-// result equals the exact softmax up to rounding.
+// per-position factor beta_p <= 1 precomputed once per block of waves (in
+// LDS).  The two halves of an entry carry the references of their blocks
+// and are joined with one exp2 per dimension, so the result equals the
+// exact softmax up to rounding for any logit range.
 constexpr float kBand = 8.f;
 constexpr float kDown = 100.f;
 
@@ -164,9 +163,10 @@ __global__ __launch_bounds__(256) void compress_small_kernel(
   }
   __syncthreads();
   if (e0 >= e1) return;
-  // carried first half (for the next entry) and the shared reference
-  float cS[DPL], cA[DPL], ref[DPL];
-  bool have_ref = false;
+  // carried first half (for the next entry) and its reference
+  float cS[DPL], cA[DPL], cr[DPL];
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) { cS[d] = 0.f; cA[d] = 0.f; cr[d] = 0.f; }
   int64_t bk = e0 > 0 ? e0 - 1 : 0;
   // ring of kRing register buffers (storage format): blocks are loaded
   // kRing - 1 blocks ahead of the one being folded
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void compress_small_kernel(
     }
   };
   auto fold_block = [&](int64_t b, const RawN<T, DPL>* zc, const RawN<T, DPL>* xc) {
-    // block maximum of z (log2 units) and the reference update
+    // block maximum of z (log2 units): the reference of this block's sums
     float bmx[DPL];
 #pragma unroll
     for (int d = 0; d < DPL; ++d) {
@@ -193,25 +193,6 @@ __global__ __launch_bounds__(256) void compress_small_kernel(
 #pragma unroll
       for (int t = 1; t < M; ++t) v = fmaxf(v, zc[t][d]);
       bmx[d] = v * L2E;
-    }
-    bool move = !have_ref;
-    if (have_ref) {
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) move |= (bmx[d] > ref[d] + kBand) || (bmx[d] < ref[d] - kBand);
-    }
-    if (__any(move)) {
-      // rescale the carried half to the new reference (exactly)
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) {
-        const float nr = next_ref(ref[d], bmx[d], have_ref);
-        if (have_ref) {
-          const float f = __builtin_amdgcn_exp2f(ref[d] - nr);
-          cS[d] *= f;
-          cA[d] *= f;
-        }
-        ref[d] = nr;
-      }
-      have_ref = true;
     }
     float sA[DPL], aA[DPL], sB[DPL], aB[DPL];
 #pragma unroll
@@ -228,7 +209,7 @@ __global__ __launch_bounds__(256) void compress_small_kernel(
       }
 #pragma unroll
       for (int d = 0; d < DPL; ++d) {
-        const float u = __builtin_amdgcn_exp2f(fmaf(zc[t][d], L2E, -ref[d]));
+        const float u = __builtin_amdgcn_exp2f(fmaf(zc[t][d], L2E, -bmx[d]));
         const float xv = xc[t][d];
         const float wa = u * ba[d];
         const float wb = u * bb[d];
@@ -244,9 +225,12 @@ __global__ __launch_bounds__(256) void compress_small_kernel(
       const bool first = b == 0;               // entry 0 has no previous block
 #pragma unroll
       for (int d = 0; d < DPL; ++d) {
-        const float S = first ? sB[d] : cS[d] + sB[d];
-        const float A = first ? aB[d] : cA[d] + aB[d];
-        o[d] = A * __builtin_amdgcn_rcpf(S);
+        // join the two halves at the larger of their references
+        const float dl = cr[d] - bmx[d];
+        const float g = __builtin_amdgcn_exp2f(-fabsf(dl));
+        const float fc = first ? 0.f : (dl >= 0.f ? 1.f : g);
+        const float fb = (first || dl < 0.f) ? 1.f : g;
+        o[d] = (cA[d] * fc + aB[d] * fb) * __builtin_amdgcn_rcpf(cS[d] * fc + sB[d] * fb);
       }
       // rows outside [e0, e1) fall past the buffer record and are dropped
       const uint32_t off = (b >= e0 && b < e1) ? (uint32_t)((b - e0) * ld_out + d0) * sizeof(T)
@@ -254,7 +238,7 @@ __global__ __launch_bounds__(256) void compress_small_kernel(
       BufStoreN<T, DPL>::store(orsrc, off, o);
     }
 #pragma unroll
-    for (int d = 0; d < DPL; ++d) { cS[d] = sA[d]; cA[d] = aA[d]; }
+    for (int d = 0; d < DPL; ++d) { cS[d] = sA[d]; cA[d] = aA[d]; cr[d] = bmx[d]; }
   };
 #pragma unroll
   for (int i = 0; i < kRing - 1; ++i) load_block(bk + i, zb[i], xb[i]);
@@ -461,6 +445,380 @@ static hipError_t launch_large_t(const void* x, const void* z, const float* bias
                      e_end, kLargeEpw, (T*)out, ld_out);
   return hipGetLastError();
 }
+
+// ---------------------------------------------------------------------------
+// Fused two-scale compressor: one pass over x and z produces the entries of
+// a small block size MS (<= 4, the CSA scale) and of a large block size ML =
+// R * MS (the HCA scale), since both read the same raw rows.
+//
+// Weights share one exp2 per element: with a per-dimension reference r,
+//   small window:  2^(z*log2e - r) * beta_s[p],   beta_s = 2^((b_s - max b_s) log2e)
+//   large window:  2^(z*log2e - r) * beta_l[p],   beta_l = 2^((b_l - max b_l) log2e)
+// (the constant factors cancel in each normalisation).  beta_s (2*MS rows)
+// sits in LDS for the whole block; beta_l (2*ML rows, precomputed into the
+// workspace) is staged in LDS MS positions at a time: the waves of a block
+// stream their large blocks in lockstep, so they need the same beta_l rows
+// at the same time.  r is the small-scale lazily moved reference of the
+// streaming small compressor; when it moves, every running sum is rescaled.
+// Wave ranges hand their carried halves to the next wave through LDS as in
+// the large compressor.
+constexpr int kFusedWaves = 4;
+#ifndef CSKV_FUSED_EPW
+#define CSKV_FUSED_EPW 4
+#endif
+constexpr int kFusedEpw = CSKV_FUSED_EPW;     // large entries per wave (wave 0: one less)
+constexpr int kFusedDpl = 4;
+
+__global__ void beta_table_kernel(const float* __restrict__ bias, int rows, float* __restrict__ beta) {
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= kD) return;
+  const float L2E = 1.4426950408889634f;
+  float bm = bias[d];
+  for (int p = 1; p < rows; ++p) bm = fmaxf(bm, bias[(int64_t)p * kD + d]);
+  for (int p = 0; p < rows; ++p)
+    beta[(int64_t)p * kD + d] = __builtin_amdgcn_exp2f((bias[(int64_t)p * kD + d] - bm) * L2E);
+}
+
+template <class T, int MS, int DPL>
+__global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
+    const T* __restrict__ x, const T* __restrict__ z, const float* __restrict__ bias_s,
+    const float* __restrict__ beta_l, int R, int64_t NL, int epw, T* __restrict__ out_s,
+    int64_t ld_s, T* __restrict__ out_l, int64_t ld_l) {
+  constexpr int kSlices = kD / (64 * DPL);
+  constexpr int kSW = 64 * DPL;                   // dims of this block's slice
+  const int ML = R * MS;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int blk = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int slice = blk % kSlices;
+  const int64_t group = blk / kSlices;
+  const int dl = lane * DPL;                      // dim within the slice
+  const int d0 = slice * kSW + dl;
+  const float L2E = 1.4426950408889634f;
+  // large entries of this wave: [E0, E1); wave 0 also streams E0-1 (the block halo)
+  const int64_t g0 = group * ((int64_t)kFusedWaves * epw - 1);
+  const int64_t E0 = wave == 0 ? g0 : g0 + (int64_t)wave * epw - 1;
+  const int64_t E1r = g0 + (int64_t)(wave + 1) * epw - 1;
+  const int64_t E1 = E1r < NL ? E1r : NL;
+  const int64_t LB0 = (wave == 0) ? E0 - 1 : E0;  // first large block streamed (-1: none)
+  const int nblocks = epw;                        // large blocks streamed by every wave
+  const int64_t NS = NL * R;                      // small entries
+  const int64_t S0 = E0 * R, S1 = E1 * R;         // small entries written by this wave
+
+  __shared__ __attribute__((aligned(16))) float bs_lds[2 * MS][kSW];
+  __shared__ __attribute__((aligned(16))) float bl_lds[2][2 * MS][kSW];
+  __shared__ float xch[kFusedWaves][6][kSW];
+  for (int i = threadIdx.x; i < 2 * MS * kSW; i += 64 * kFusedWaves) {
+    const int p = i / kSW, d = i % kSW;
+    float bm = bias_s[slice * kSW + d];
+    for (int q = 1; q < 2 * MS; ++q) bm = fmaxf(bm, bias_s[(int64_t)q * kD + slice * kSW + d]);
+    bs_lds[p][d] = __builtin_amdgcn_exp2f((bias_s[(int64_t)p * kD + slice * kSW + d] - bm) * L2E);
+  }
+  // beta_l rows for positions [t, t+MS) of both halves: loaded into
+  // registers one step before they are written to LDS, so that the wait for
+  // them never drains the raw-row loads issued after them
+  constexpr int kBlQuads = 2 * MS * kSW / 4;
+  static_assert(kBlQuads <= 2 * 64 * kFusedWaves, "two quads per thread");
+  // thread's two quads (clamped: surplus threads repeat the last one)
+  const int q0 = (int)threadIdx.x < kBlQuads ? (int)threadIdx.x : kBlQuads - 1;
+  const int q1 = (int)threadIdx.x + 64 * kFusedWaves < kBlQuads ? (int)threadIdx.x + 64 * kFusedWaves
+                                                                 : kBlQuads - 1;
+  auto bl_src = [&](int t, int i) {
+    const int row = (i * 4) / kSW, d = (i * 4) % kSW;
+    const int p = row < MS ? t + row : ML + t + (row - MS);
+    return reinterpret_cast<const float4*>(beta_l + (int64_t)p * kD + slice * kSW + d);
+  };
+  float4 bq0, bq1;
+  auto load_bl = [&](int t) { bq0 = *bl_src(t, q0); bq1 = *bl_src(t, q1); };
+  auto write_bl = [&](int k) {
+    *reinterpret_cast<float4*>(&bl_lds[k][(q0 * 4) / kSW][(q0 * 4) % kSW]) = bq0;
+    *reinterpret_cast<float4*>(&bl_lds[k][(q1 * 4) / kSW][(q1 * 4) % kSW]) = bq1;
+  };
+  load_bl(0);
+  write_bl(0);
+
+  // Small scale: running reference ref (lazily moved, may go down), carried
+  // first half cS/cA.  Large scale: reference rl of the current large block
+  // (raise-only within the block; both halves of the block use it), carried
+  // first half lcS/lcA with its own reference lcr, and G = 2^(ref - rl) that
+  // turns a small-scale factor u into a large-scale one.
+  float cS[DPL], cA[DPL], cr[DPL];
+  float rl[DPL], G[DPL], lcS[DPL], lcA[DPL], lcr[DPL];
+  float lsA[DPL], laA[DPL], lsB[DPL], laB[DPL];   // large: halves of the current block
+  float fS[DPL], fA[DPL], fr[DPL];                // small: second half of the first entry
+  float gS[DPL], gA[DPL], gr[DPL];                // large: second half of the first entry
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) {
+    cr[d] = 0.f; cS[d] = cA[d] = 0.f;
+    rl[d] = 0.f; G[d] = 0.f; lcS[d] = lcA[d] = lcr[d] = 0.f;
+    lsA[d] = laA[d] = lsB[d] = laB[d] = 0.f;
+    fS[d] = fA[d] = fr[d] = gS[d] = gA[d] = gr[d] = 0.f;
+  }
+  // Every wave streams nblocks large blocks from LB0 (which is -1 for the
+  // very first wave: that virtual block re-reads block 0, stores nothing, and
+  // its carried halves are discarded because entry 0 has no first half).
+  const int64_t sbegin = LB0 * R;                            // first small block streamed
+  const int nsteps = nblocks * R;
+  const int64_t sb_last = NS - 1;                            // last small block inside NL large blocks
+  auto load_sb = [&](int64_t sb, RawN<T, DPL>* zz, RawN<T, DPL>* xx) {
+    if (sb > sb_last) sb = sb_last;
+    if (sb < 0) sb = 0;
+#pragma unroll
+    for (int t = 0; t < MS; ++t) {
+      const int64_t j = sb * MS + t;
+      zz[t].load(z + j * kD + d0);
+      xx[t].load(x + j * kD + d0);
+    }
+  };
+  const __amdgpu_buffer_rsrc_t rsrc_s =
+      make_rsrc(out_s + (S0 < S1 ? S0 : 0) * ld_s, S0 < S1 ? (uint32_t)((S1 - S0) * ld_s * sizeof(T)) : 0u);
+  const __amdgpu_buffer_rsrc_t rsrc_l =
+      make_rsrc(out_l + (E0 < E1 ? E0 : 0) * ld_l, E0 < E1 ? (uint32_t)((E1 - E0) * ld_l * sizeof(T)) : 0u);
+
+  constexpr int kRing = 3;
+  RawN<T, DPL> zb[kRing][MS], xb[kRing][MS];
+  if (nsteps > 1) load_bl((1 % R) * MS);                     // rows of step 1
+#pragma unroll
+  for (int i = 0; i < kRing - 1; ++i) load_sb(sbegin + i, zb[i], xb[i]);
+  __syncthreads();                                           // bs_lds and bl_lds[0] ready
+
+  for (int st0 = 0; st0 < nsteps; st0 += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      const int st = st0 + i;                                // step = small block of the stream
+      const int nx = (i + kRing - 1) % kRing;
+      if (st < nsteps) {
+        const int64_t sb = sbegin + st;                      // global small block (may be < 0)
+        const int j = st % R;                                // position within the large block
+        const int64_t lb = LB0 + st / R;                     // large block (may be -1)
+        const int kb = st & 1;
+        // the next step's beta_l rows go to the other buffer (read by every
+        // wave before the barrier that ended the previous step)
+        if (st + 1 < nsteps) write_bl(kb ^ 1);
+        if (st + 2 < nsteps) load_bl(((st + 2) % R) * MS);
+        load_sb(sbegin + st + kRing - 1, zb[nx], xb[nx]);
+        const RawN<T, DPL>* zc = zb[i];
+        const RawN<T, DPL>* xc = xb[i];
+        // reference update from the small block maximum
+        float bmx[DPL];
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) {
+          float v = zc[0][d];
+#pragma unroll
+          for (int t = 1; t < MS; ++t) v = fmaxf(v, zc[t][d]);
+          bmx[d] = v * L2E;
+        }
+        // the small sums of this block use its maximum bmx as reference; the
+        // large block's reference rl is raise-only
+        if (j == 0) {                                        // a large block starts
+#pragma unroll
+          for (int d = 0; d < DPL; ++d) rl[d] = bmx[d];
+        } else {
+          bool up = false;
+#pragma unroll
+          for (int d = 0; d < DPL; ++d) up |= bmx[d] > rl[d] + kBand;
+          if (__any(up)) {
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) {
+              const float na = bmx[d] > rl[d] + kBand ? bmx[d] : rl[d];
+              const float f = __builtin_amdgcn_exp2f(rl[d] - na);
+              lsA[d] *= f; laA[d] *= f; lsB[d] *= f; laB[d] *= f;
+              rl[d] = na;
+            }
+          }
+        }
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) G[d] = __builtin_amdgcn_exp2f(bmx[d] - rl[d]);
+        float sA[DPL], aA[DPL], sB[DPL], aB[DPL];
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) { sA[d] = 0.f; aA[d] = 0.f; sB[d] = 0.f; aB[d] = 0.f; }
+#pragma unroll
+        for (int t = 0; t < MS; ++t) {
+          float ba[DPL], bb[DPL], la[DPL], lbv[DPL];
+#pragma unroll
+          for (int d = 0; d < DPL; d += 4) {
+            const float4 v0 = *reinterpret_cast<const float4*>(&bs_lds[t][dl + d]);
+            const float4 v1 = *reinterpret_cast<const float4*>(&bs_lds[MS + t][dl + d]);
+            const float4 v2 = *reinterpret_cast<const float4*>(&bl_lds[kb][t][dl + d]);
+            const float4 v3 = *reinterpret_cast<const float4*>(&bl_lds[kb][MS + t][dl + d]);
+            ba[d] = v0.x; ba[d + 1] = v0.y; ba[d + 2] = v0.z; ba[d + 3] = v0.w;
+            bb[d] = v1.x; bb[d + 1] = v1.y; bb[d + 2] = v1.z; bb[d + 3] = v1.w;
+            la[d] = v2.x; la[d + 1] = v2.y; la[d + 2] = v2.z; la[d + 3] = v2.w;
+            lbv[d] = v3.x; lbv[d + 1] = v3.y; lbv[d + 2] = v3.z; lbv[d + 3] = v3.w;
+          }
+#pragma unroll
+          for (int d = 0; d < DPL; ++d) {
+            const float u = __builtin_amdgcn_exp2f(fmaf(zc[t][d], L2E, -bmx[d]));
+            const float xv = xc[t][d];
+            const float wa = u * ba[d], wb = u * bb[d];
+            sA[d] += wa;
+            aA[d] = fmaf(wa, xv, aA[d]);
+            sB[d] += wb;
+            aB[d] = fmaf(wb, xv, aB[d]);
+            const float ul = u * G[d];
+            const float va = ul * la[d], vb = ul * lbv[d];
+            lsA[d] += va;
+            laA[d] = fmaf(va, xv, laA[d]);
+            lsB[d] += vb;
+            laB[d] = fmaf(vb, xv, laB[d]);
+          }
+          asm volatile("" ::: "memory");
+        }
+        // small entry sb: carried first half + this second half
+        {
+          float o[DPL];
+          const bool first = sb == 0;
+#pragma unroll
+          for (int d = 0; d < DPL; ++d) {
+            const float dl = cr[d] - bmx[d];
+            const float g = __builtin_amdgcn_exp2f(-fabsf(dl));
+            const float fc = first ? 0.f : (dl >= 0.f ? 1.f : g);
+            const float fb = (first || dl < 0.f) ? 1.f : g;
+            o[d] = (cA[d] * fc + aB[d] * fb) * __builtin_amdgcn_rcpf(cS[d] * fc + sB[d] * fb);
+          }
+          const bool defer = wave > 0 && sb == S0;           // first half comes from wave-1
+          if (defer) {
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) { fS[d] = sB[d]; fA[d] = aB[d]; fr[d] = bmx[d]; }
+          }
+          const uint32_t off = (sb >= S0 && sb < S1 && !defer)
+                                   ? (uint32_t)((sb - S0) * ld_s + d0) * sizeof(T) : 0xffffffffu;
+          BufStoreN<T, DPL>::store(rsrc_s, off, o);
+#pragma unroll
+          for (int d = 0; d < DPL; ++d) { cS[d] = sA[d]; cA[d] = aA[d]; cr[d] = bmx[d]; }
+        }
+        // end of a large block: large entry lb closes
+        if (j == R - 1) {
+          float o[DPL];
+          const bool first = lb == 0;
+#pragma unroll
+          for (int d = 0; d < DPL; ++d) {
+            const float mx = fmaxf(lcr[d], rl[d]);
+            const float fc = first ? 0.f : __builtin_amdgcn_exp2f(lcr[d] - mx);
+            const float fb = __builtin_amdgcn_exp2f(rl[d] - mx);
+            o[d] = (lcA[d] * fc + laB[d] * fb) * __builtin_amdgcn_rcpf(lcS[d] * fc + lsB[d] * fb);
+          }
+          const bool defer = wave > 0 && lb == E0;
+          if (defer) {
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) { gS[d] = lsB[d]; gA[d] = laB[d]; gr[d] = rl[d]; }
+          }
+          const uint32_t off = (lb >= E0 && lb < E1 && !defer)
+                                   ? (uint32_t)((lb - E0) * ld_l + d0) * sizeof(T) : 0xffffffffu;
+          BufStoreN<T, DPL>::store(rsrc_l, off, o);
+#pragma unroll
+          for (int d = 0; d < DPL; ++d) {
+            lcS[d] = lsA[d]; lcA[d] = laA[d]; lcr[d] = rl[d];
+            lsA[d] = 0.f; laA[d] = 0.f; lsB[d] = 0.f; laB[d] = 0.f;
+          }
+        }
+        __syncthreads();                                     // next beta_l rows staged
+      }
+    }
+  }
+  // hand both carried first halves (and the reference) to the next wave
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) {
+    xch[wave][0][dl + d] = cS[d];
+    xch[wave][1][dl + d] = cA[d];
+    xch[wave][2][dl + d] = lcS[d];
+    xch[wave][3][dl + d] = lcA[d];
+    xch[wave][4][dl + d] = cr[d];
+    xch[wave][5][dl + d] = lcr[d];
+  }
+  __syncthreads();
+  if (wave > 0) {
+    float os[DPL], ol[DPL];
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) {
+      const float pr = xch[wave - 1][4][dl + d];
+      float mx = fmaxf(pr, fr[d]);
+      float fp = __builtin_amdgcn_exp2f(pr - mx), fc = __builtin_amdgcn_exp2f(fr[d] - mx);
+      os[d] = (xch[wave - 1][1][dl + d] * fp + fA[d] * fc) *
+              __builtin_amdgcn_rcpf(xch[wave - 1][0][dl + d] * fp + fS[d] * fc);
+      const float plr = xch[wave - 1][5][dl + d];
+      mx = fmaxf(plr, gr[d]);
+      fp = __builtin_amdgcn_exp2f(plr - mx);
+      fc = __builtin_amdgcn_exp2f(gr[d] - mx);
+      ol[d] = (xch[wave - 1][3][dl + d] * fp + gA[d] * fc) *
+              __builtin_amdgcn_rcpf(xch[wave - 1][2][dl + d] * fp + gS[d] * fc);
+    }
+    BufStoreN<T, DPL>::store(rsrc_s, S0 < S1 ? (uint32_t)(d0 * sizeof(T)) : 0xffffffffu, os);
+    BufStoreN<T, DPL>::store(rsrc_l, E0 < E1 ? (uint32_t)(d0 * sizeof(T)) : 0xffffffffu, ol);
+  }
+}
+
+template <class T>
+static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens, const float* bias_s,
+                                 int ms, void* out_s, int64_t ld_s, const float* bias_l, int ml,
+                                 void* out_l, int64_t ld_l, void* ws, hipStream_t stream) {
+  constexpr int kSlices = kD / (64 * kFusedDpl);
+  const int64_t NL = T_tokens / ml;
+  const int R = ml / ms;
+  float* beta_l = (float*)ws;
+  hipLaunchKernelGGL(beta_table_kernel, dim3(kD / 256), dim3(256), 0, stream, bias_l, 2 * ml, beta_l);
+  const T* xp = (const T*)x;
+  const T* zp = (const T*)z;
+  int epw = kFusedEpw;
+  int64_t groups = 0;
+  auto pick = [&](const void* kern, int msel) {
+    // Large entries per wave: every block streams kFusedWaves*epw large
+    // blocks for kFusedWaves*epw-1 entries (one halo block), and the grid
+    // runs in rounds of the blocks that fit on the chip at once.  Take the
+    // epw that wastes least of both.
+    static int slots_by_ms[5] = {0, 0, 0, 0, 0};
+    int& slots = slots_by_ms[msel];
+    if (slots == 0) {
+      int nb = 0, dev = 0, cus = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 64 * kFusedWaves, 0) != hipSuccess ||
+          hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        nb = 0;
+      slots = nb > 0 && cus > 0 ? nb * cus : 512;
+    }
+    double best = -1.0;
+    for (int e = 2; e <= 16; ++e) {
+      const int64_t per = (int64_t)kFusedWaves * e - 1;
+      const int64_t g = (NL + per - 1) / per;
+      const double rounds = (double)(g * kSlices) / slots;
+      const double eff = rounds / std::ceil(rounds) * (double)(NL) / (double)(g * (per + 1));
+      if (eff > best + 1e-9) { best = eff; epw = e; groups = g; }
+    }
+  };
+#define CSKV_FUSED(MS)                                                                            \
+  pick((const void*)compress_fused_kernel<T, MS, kFusedDpl>, MS);                                 \
+  hipLaunchKernelGGL((compress_fused_kernel<T, MS, kFusedDpl>), dim3((unsigned)(groups * kSlices)), \
+                     dim3(64 * kFusedWaves), 0, stream, xp, zp, bias_s, beta_l, R, NL, epw,        \
+                     (T*)out_s, ld_s, (T*)out_l, ld_l)
+  switch (ms) {
+    case 1: CSKV_FUSED(1); break;
+    case 2: CSKV_FUSED(2); break;
+    case 3: CSKV_FUSED(3); break;
+    default: CSKV_FUSED(4); break;
+  }
+#undef CSKV_FUSED
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_fused(int dt, const void* x, const void* z, int64_t T_tokens,
+                                 const float* bias_s, int ms, void* out_s, int64_t ld_s,
+                                 const float* bias_l, int ml, void* out_l, int64_t ld_l, void* ws,
+                                 hipStream_t stream) {
+  const int64_t NL = T_tokens / ml, NSall = T_tokens / ms, NSf = NL * (ml / ms);
+  hipError_t e = hipSuccess;
+  if (NL > 0) {
+    e = dt == 0 ? launch_fused_t<float>(x, z, T_tokens, bias_s, ms, out_s, ld_s, bias_l, ml, out_l,
+                                        ld_l, ws, stream)
+                : launch_fused_t<bf16_t>(x, z, T_tokens, bias_s, ms, out_s, ld_s, bias_l, ml, out_l,
+                                         ld_l, ws, stream);
+    if (e != hipSuccess) return e;
+  }
+  // small entries past the last whole large block
+  if (NSall > NSf) e = launch_compress(dt, x, z, bias_s, ms, NSf, NSall, out_s, ld_s, stream);
+  return e;
+}
+
+size_t compress_fused_workspace_bytes(int ml) { return (size_t)2 * ml * kD * sizeof(float) + 256; }
 
 template <class T>
 static hipError_t launch_compress_t(const void* x, const void* z, const float* bias, int m,

@@ -10,6 +10,11 @@ namespace cskv {
 hipError_t launch_compress(int dt, const void* x, const void* z, const float* bias, int m,
                            int64_t e_begin, int64_t e_end, void* out, int64_t ld_out,
                            hipStream_t stream);
+hipError_t launch_compress_fused(int dt, const void* x, const void* z, int64_t T_tokens,
+                                 const float* bias_s, int ms, void* out_s, int64_t ld_s,
+                                 const float* bias_l, int ml, void* out_l, int64_t ld_l, void* ws,
+                                 hipStream_t stream);
+size_t compress_fused_workspace_bytes(int ml);
 
 struct AttendParams {
   int dt;                    // 0 fp32, 1 bf16

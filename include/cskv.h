@@ -95,6 +95,27 @@ int cskv_compress(const void* raw_kv, const void* score_logits, const float* pos
                   cskv_dtype dt, void* stream);
 
 /*
+ * Two-scale compression in one pass over the raw rows (the CSA scale
+ * m_small and the HCA scale m_large = R * m_small, "Frontier Techniques" 2.1
+ * and 2.2 compress the same history at m = 4 and m' = 128).  Writes exactly
+ * what cskv_compress(.., m_small, 0, floor(T/m_small), out_small, ..) and
+ * cskv_compress(.., m_large, 0, floor(T/m_large), out_large, ..) write, with
+ * one read of raw_kv and score_logits instead of two.
+ *   bias_small [2*m_small][512], bias_large [2*m_large][512] fp32;
+ *   out_small / out_large rows of ld >= 512 (multiple of 8) in dt.
+ *   workspace: cskv_compress2_workspace_size(m_large) bytes (exp'd bias table).
+ * bias_large and out_large are not used (may be NULL) when T < m_large.
+ * Errors: INVALID_ARG (null pointers, T < 0, m_large not a multiple of
+ * m_small, ld < 512); UNSUPPORTED (m_small > 4, m_large > 65536, dt not
+ * F32/BF16); WORKSPACE.
+ */
+size_t cskv_compress2_workspace_size(int32_t m_large);
+int cskv_compress2(const void* raw_kv, const void* score_logits, int64_t T,
+                   const float* bias_small, int32_t m_small, void* out_small, int64_t ld_small,
+                   const float* bias_large, int32_t m_large, void* out_large, int64_t ld_large,
+                   cskv_dtype dt, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Indexer scoring and top-k selection ("Frontier Techniques", 2.1: entries
  * scored cheaply by the indexer, top-1024 kept; "DeepSeek V4 comprimeix el
  * context", section "CSA: buscar primer i atendre despres").

@@ -27,7 +27,7 @@ def declared():
 
 def test_header_functions_are_exported(lib):
     names = declared()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), f"{n} declared in cskv.h but not exported"
     from compressed_sparse_kv_overlapping_amd import binding
@@ -54,6 +54,21 @@ def test_compress_errors(lib):
     assert b"null" in lib.cskv_last_error()
     assert c(P, P, P, 16, 4, 0, 4, ctypes.c_void_p(0x100008), 576, 1, NULL) == INVALID  # alignment
     assert c(NULL, NULL, NULL, 3, 4, 0, 0, NULL, 512, 1, NULL) == OK    # empty range: no-op
+
+
+def test_compress2_errors(lib):
+    f = lib.cskv_compress2
+    ws = lib.cskv_compress2_workspace_size(128)
+    assert ws >= 256 * 512 * 4
+    assert f(P, P, 4096, P, 4, P, 576, P, 130, P, 576, 1, P, ws, NULL) == INVALID      # 130 % 4
+    assert f(P, P, 4096, P, 4, P, 576, P, 4, P, 576, 1, P, ws, NULL) == INVALID        # equal sizes
+    assert f(P, P, 4096, P, 8, P, 576, P, 128, P, 576, 1, P, ws, NULL) == UNSUPPORTED  # m_small > 4
+    assert f(P, P, 4096, P, 4, P, 576, P, 128, P, 576, 2, P, ws, NULL) == UNSUPPORTED  # fp8
+    assert f(P, P, 4096, P, 4, P, 500, P, 128, P, 576, 1, P, ws, NULL) == INVALID      # ld
+    assert f(P, P, 4096, P, 4, P, 576, P, 128, P, 576, 1, NULL, ws, NULL) == WORKSPACE
+    assert f(P, P, 4096, P, 4, P, 576, P, 128, P, 576, 1, P, ws - 1, NULL) == WORKSPACE
+    assert f(NULL, P, 4096, P, 4, P, 576, P, 128, P, 576, 1, P, ws, NULL) == INVALID
+    assert f(NULL, NULL, 3, NULL, 4, NULL, 512, NULL, 128, NULL, 512, 1, NULL, 0, NULL) == OK  # T < m
 
 
 def test_index_topk_errors(lib):

@@ -120,3 +120,60 @@ def test_compress_1m_tokens_sampled():
         ref = oracle.compress(inp["x"].raw, inp["z"].raw, wl.DT_BF16, inp[bname].raw, m, entry_ids=ids)
         got = host_f64(ent[torch.from_numpy(ids).cuda(), :512])
         assert rowwise_err(got, ref) <= 2e-2
+
+
+@pytest.mark.parametrize("dt", [wl.DT_F32, wl.DT_BF16])
+@pytest.mark.parametrize("ms,ml,T", [(4, 128, 4096), (4, 128, 4099), (4, 128, 4196), (2, 16, 1000),
+                                     (1, 8, 517), (3, 12, 600), (4, 8, 333), (4, 128, 100),
+                                     (4, 64, 64 * 61 + 7), (4, 128, 128 * 40)])
+def test_compress2_matches_oracle(dt, ms, ml, T):
+    """Both scales in one pass equal the oracle at each scale (ragged T,
+    a whole number of blocks of waves or not)."""
+    cskv = _cskv()
+    x, z, _ = _inputs(T, ms, dt, seed=ms * 31 + ml * 7 + T)
+    bs = wl.normal(90, T, 5, (2 * ms, D), 0.1)
+    bl = wl.normal(90, T, 6, (2 * ml, D), 0.1)
+    os_, ol = cskv.compress2(dev(x), dev(z), dev(bs), ms, dev(bl), ml)
+    torch.cuda.synchronize()
+    assert os_.shape == (T // ms, D) and ol.shape == (T // ml, D)
+    assert rowwise_err(host_f64(os_), oracle.compress(x.raw, z.raw, dt, bs, ms)) <= TOL[dt]
+    if T // ml:
+        assert rowwise_err(host_f64(ol), oracle.compress(x.raw, z.raw, dt, bl, ml)) <= TOL[dt]
+
+
+def test_compress2_large_logits():
+    cskv = _cskv()
+    T, ms, ml = 4096 + 64, 4, 128
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((T, D)).astype(np.float32)
+    z = (30 * rng.standard_normal((T, D))).clip(-80, 80).astype(np.float32)
+    bs = (3 * rng.standard_normal((2 * ms, D))).astype(np.float32)
+    bl = (10 * rng.standard_normal((2 * ml, D))).clip(-20, 20).astype(np.float32)
+    os_, ol = cskv.compress2(dev(x), dev(z), dev(bs), ms, dev(bl), ml)
+    torch.cuda.synchronize()
+    got_s, got_l = host_f64(os_), host_f64(ol)
+    assert np.isfinite(got_s).all() and np.isfinite(got_l).all()
+    assert rowwise_err(got_s, oracle.compress(x, z, wl.DT_F32, bs, ms)) <= 1e-4
+    assert rowwise_err(got_l, oracle.compress(x, z, wl.DT_F32, bl, ml)) <= 1e-4
+
+
+def test_compress2_1m_tokens_sampled():
+    """The 1M-token bf16 layer: both scales from one pass, sampled entries,
+    and equal (to bf16 rounding) to the single-scale kernels."""
+    cskv = _cskv()
+    inp = wl.make_inputs("layer_1m", seed=0)
+    X, Z = dev(inp["x"]), dev(inp["z"])
+    e4 = torch.empty(((1 << 20) // 4, 576), dtype=torch.bfloat16, device="cuda")
+    e128 = torch.empty(((1 << 20) // 128, 576), dtype=torch.bfloat16, device="cuda")
+    cskv.compress2(X, Z, dev(inp["b4"]), 4, dev(inp["b128"]), 128, out_small=e4, out_large=e128)
+    s4 = cskv.compress(X, Z, dev(inp["b4"]), 4)
+    s128 = cskv.compress(X, Z, dev(inp["b128"]), 128)
+    torch.cuda.synchronize()
+    assert rowwise_err(host_f64(e4[:, :512]), host_f64(s4)) <= 1e-2
+    assert rowwise_err(host_f64(e128[:, :512]), host_f64(s128)) <= 1e-2
+    rng = np.random.default_rng(1)
+    for m, ent, bname in ((4, e4, "b4"), (128, e128, "b128")):
+        N = (1 << 20) // m
+        ids = np.unique(np.concatenate([[0, 1, N - 2, N - 1], rng.integers(0, N, 300)]))
+        ref = oracle.compress(inp["x"].raw, inp["z"].raw, wl.DT_BF16, inp[bname].raw, m, entry_ids=ids)
+        assert rowwise_err(host_f64(ent[torch.from_numpy(ids).cuda(), :512]), ref) <= 2e-2
