@@ -3,7 +3,7 @@
 
 One step = the 1M-token layer pair: compress the raw bf16 KV [2^20, 512] at
 m = 4 (262,144 entries) and m' = 128 (8,192 entries) into 576-wide entry
-buffers, then CSA decode (indexer top-1024 + 128-token window) and HCA decode
+buffers in one fused pass over the raw rows, then CSA decode (indexer top-1024 + 128-token window) and HCA decode
 (dense over all 8,192 entries) for 32 queries x 128 heads.  Inputs are seeded
 synthetic tensors already resident in HBM; every kernel of the step runs in
 the timed region.
@@ -104,23 +104,23 @@ def main():
     ws_topk = torch.empty(cskv.index_topk_workspace_size(B, N4, k), dtype=torch.uint8, device="cuda")
     ws_csa = torch.empty(max(1, cskv.attend_workspace_size(B, H, k + W)), dtype=torch.uint8, device="cuda")
     ws_hca = torch.empty(max(1, cskv.hca_workspace_size(B, H, N128)), dtype=torch.uint8, device="cuda")
+    ws_c = torch.empty(cskv.compress2_workspace_size(cfg.m_hca), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     gen_s = time.time() - t_gen
 
-    parts = ["compress_m4", "compress_m128", "csa_topk", "csa_attend", "hca_attend"]
+    parts = ["compress", "csa_topk", "csa_attend", "hca_attend"]
 
     def step(ev):
         ev[0].record()
-        cskv.compress(x, z, b4, cfg.m_csa, out=ent4)
+        cskv.compress2(x, z, b4, cfg.m_csa, b128, cfg.m_hca, out_small=ent4, out_large=ent128,
+                       workspace=ws_c)
         ev[1].record()
-        cskv.compress(x, z, b128, cfg.m_hca, out=ent128)
-        ev[2].record()
         cskv.index_topk(qI, kI, k, idx_out=idx, workspace=ws_topk)
-        ev[3].record()
+        ev[2].record()
         cskv.sparse_attend(q, ent4, win, idx, out=out_csa, lse=lse_csa, workspace=ws_csa)
-        ev[4].record()
+        ev[3].record()
         cskv.hca_attend(q_hca, ent128, out=out_hca, lse=lse_hca, workspace=ws_hca)
-        ev[5].record()
+        ev[4].record()
 
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
@@ -148,8 +148,7 @@ def main():
     # algorithmic bytes / flops per launch (inputs once, outputs once, gathers per query)
     bx = 2 * T * D * 2
     alg = {
-        "compress_m4": {"bytes": bx + N4 * D * 2},
-        "compress_m128": {"bytes": bx + N128 * D * 2},
+        "compress": {"bytes": bx + (N4 + N128) * D * 2},
         "csa_topk": {"bytes": N4 * I * 2 + B * I * 2 + B * k * 4, "flops": 2 * B * N4 * I},
         "csa_attend": {"bytes": B * (k + W) * E * 2 + B * H * E * 2 + B * H * D * 2,
                        "flops": 2 * B * H * (k + W) * (E + D)},
@@ -172,9 +171,9 @@ def main():
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": alg[dom]["bytes"]}
 
-    comp_ms = part_ms["compress_m4"] + part_ms["compress_m128"]
+    comp_ms = part_ms["compress"]
     attn_ms = part_ms["csa_topk"] + part_ms["csa_attend"] + part_ms["hca_attend"]
-    comp_bytes = alg["compress_m4"]["bytes"] + alg["compress_m128"]["bytes"]
+    comp_bytes = alg["compress"]["bytes"]
     attn_bytes = alg["csa_topk"]["bytes"] + alg["csa_attend"]["bytes"] + alg["hca_attend"]["bytes"]
 
     result = {

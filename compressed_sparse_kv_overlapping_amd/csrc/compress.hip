@@ -469,13 +469,26 @@ constexpr int kFusedWaves = 4;
 constexpr int kFusedEpw = CSKV_FUSED_EPW;     // large entries per wave (wave 0: one less)
 constexpr int kFusedDpl = 4;
 
-__global__ void beta_table_kernel(const float* __restrict__ bias, int rows, float* __restrict__ beta) {
-  const int d = blockIdx.x * blockDim.x + threadIdx.x;
-  if (d >= kD) return;
+// beta[p][d] = 2^((bias[p][d] - max_p bias[p][d]) * log2e): a block takes 64
+// dimensions, its 16 row slices take every 16th row, and the column maxima
+// meet in LDS.
+constexpr int kBetaDims = 64, kBetaSlices = 16;
+__global__ __launch_bounds__(kBetaDims* kBetaSlices) void beta_table_kernel(
+    const float* __restrict__ bias, int rows, float* __restrict__ beta) {
+  __shared__ float part[kBetaSlices][kBetaDims];
+  const int dl = threadIdx.x % kBetaDims, sl = threadIdx.x / kBetaDims;
+  const int d = blockIdx.x * kBetaDims + dl;
   const float L2E = 1.4426950408889634f;
-  float bm = bias[d];
-  for (int p = 1; p < rows; ++p) bm = fmaxf(bm, bias[(int64_t)p * kD + d]);
-  for (int p = 0; p < rows; ++p)
+  float bm = -INFINITY;
+#pragma unroll 4
+  for (int p = sl; p < rows; p += kBetaSlices) bm = fmaxf(bm, bias[(int64_t)p * kD + d]);
+  part[sl][dl] = bm;
+  __syncthreads();
+  bm = part[0][dl];
+#pragma unroll
+  for (int i = 1; i < kBetaSlices; ++i) bm = fmaxf(bm, part[i][dl]);
+#pragma unroll 4
+  for (int p = sl; p < rows; p += kBetaSlices)
     beta[(int64_t)p * kD + d] = __builtin_amdgcn_exp2f((bias[(int64_t)p * kD + d] - bm) * L2E);
 }
 
@@ -756,7 +769,8 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
   const int64_t NL = T_tokens / ml;
   const int R = ml / ms;
   float* beta_l = (float*)ws;
-  hipLaunchKernelGGL(beta_table_kernel, dim3(kD / 256), dim3(256), 0, stream, bias_l, 2 * ml, beta_l);
+  hipLaunchKernelGGL(beta_table_kernel, dim3(kD / kBetaDims), dim3(kBetaDims * kBetaSlices), 0, stream,
+                     bias_l, 2 * ml, beta_l);
   const T* xp = (const T*)x;
   const T* zp = (const T*)z;
   int epw = kFusedEpw;
