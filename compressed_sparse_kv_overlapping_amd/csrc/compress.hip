@@ -451,17 +451,19 @@ static hipError_t launch_large_t(const void* x, const void* z, const float* bias
 // a small block size MS (<= 4, the CSA scale) and of a large block size ML =
 // R * MS (the HCA scale), since both read the same raw rows.
 //
-// Weights share one exp2 per element: with a per-dimension reference r,
+// Weights share one exp2 per element: with r the maximum of z over the small
+// block being read (per dimension),
 //   small window:  2^(z*log2e - r) * beta_s[p],   beta_s = 2^((b_s - max b_s) log2e)
 //   large window:  2^(z*log2e - r) * beta_l[p],   beta_l = 2^((b_l - max b_l) log2e)
-// (the constant factors cancel in each normalisation).  beta_s (2*MS rows)
-// sits in LDS for the whole block; beta_l (2*ML rows, precomputed into the
-// workspace) is staged in LDS MS positions at a time: the waves of a block
-// stream their large blocks in lockstep, so they need the same beta_l rows
-// at the same time.  r is the small-scale lazily moved reference of the
-// streaming small compressor; when it moves, every running sum is rescaled.
-// Wave ranges hand their carried halves to the next wave through LDS as in
-// the large compressor.
+// (the constant factors cancel in each normalisation).  With ux = u x every
+// accumulation is one FMA.  beta_s (2*MS rows) sits in LDS for the whole
+// block; beta_l (2*ML rows, precomputed into the workspace) is staged in LDS
+// MS positions at a time: the waves of a block stream their large blocks in
+// lockstep, so they need the same beta_l rows at the same time.  A small
+// block's large sums join the running sums of its large block once, scaled
+// by 2^(r - rl) with rl the large block's raise-only reference.  Wave ranges
+// hand their carried halves to the next wave through LDS as in the large
+// compressor.
 constexpr int kFusedWaves = 4;
 #ifndef CSKV_FUSED_EPW
 #define CSKV_FUSED_EPW 4
@@ -521,6 +523,9 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
   __shared__ __attribute__((aligned(16))) float bs_lds[2 * MS][kSW];
   __shared__ __attribute__((aligned(16))) float bl_lds[2][2 * MS][kSW];
   __shared__ float xch[kFusedWaves][6][kSW];
+  // second halves of a wave's first small and large entries (waves > 0),
+  // completed with the previous wave's carried halves at the end
+  __shared__ float dfr[kFusedWaves][6][kSW];
   for (int i = threadIdx.x; i < 2 * MS * kSW; i += 64 * kFusedWaves) {
     const int p = i / kSW, d = i % kSW;
     float bm = bias_s[slice * kSW + d];
@@ -550,22 +555,20 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
   load_bl(0);
   write_bl(0);
 
-  // Small scale: running reference ref (lazily moved, may go down), carried
-  // first half cS/cA.  Large scale: reference rl of the current large block
-  // (raise-only within the block; both halves of the block use it), carried
-  // first half lcS/lcA with its own reference lcr, and G = 2^(ref - rl) that
-  // turns a small-scale factor u into a large-scale one.
+  // Small scale: carried first half cS/cA of the next entry with its
+  // reference cr (the maximum of the block it came from).  Large scale:
+  // reference rl of the current large block (raise-only within the block;
+  // both halves of the block use it), running halves lsA/laA, lsB/laB, and
+  // the carried first half lcS/lcA of the next large entry with its
+  // reference lcr.
   float cS[DPL], cA[DPL], cr[DPL];
-  float rl[DPL], G[DPL], lcS[DPL], lcA[DPL], lcr[DPL];
+  float rl[DPL], lcS[DPL], lcA[DPL], lcr[DPL];
   float lsA[DPL], laA[DPL], lsB[DPL], laB[DPL];   // large: halves of the current block
-  float fS[DPL], fA[DPL], fr[DPL];                // small: second half of the first entry
-  float gS[DPL], gA[DPL], gr[DPL];                // large: second half of the first entry
 #pragma unroll
   for (int d = 0; d < DPL; ++d) {
     cr[d] = 0.f; cS[d] = cA[d] = 0.f;
-    rl[d] = 0.f; G[d] = 0.f; lcS[d] = lcA[d] = lcr[d] = 0.f;
+    rl[d] = -INFINITY; lcS[d] = lcA[d] = lcr[d] = 0.f;
     lsA[d] = laA[d] = lsB[d] = laB[d] = 0.f;
-    fS[d] = fA[d] = fr[d] = gS[d] = gA[d] = gr[d] = 0.f;
   }
   // Every wave streams nblocks large blocks from LB0 (which is -1 for the
   // very first wave: that virtual block re-reads block 0, stores nothing, and
@@ -588,144 +591,156 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
   const __amdgpu_buffer_rsrc_t rsrc_l =
       make_rsrc(out_l + (E0 < E1 ? E0 : 0) * ld_l, E0 < E1 ? (uint32_t)((E1 - E0) * ld_l * sizeof(T)) : 0u);
 
-  constexpr int kRing = 3;
-  RawN<T, DPL> zb[kRing][MS], xb[kRing][MS];
+  // Two register slots of raw rows: the step reading one loads the next
+  // block into the other.  A wave streams its large blocks in an outer loop
+  // and their R (even) small blocks in an inner loop unrolled by two, so that
+  // the slots and the beta_l buffers are fixed per unrolled step and a large
+  // entry closes outside the inner loop.
+  RawN<T, DPL> zb[2][MS], xb[2][MS];
   if (nsteps > 1) load_bl((1 % R) * MS);                     // rows of step 1
-#pragma unroll
-  for (int i = 0; i < kRing - 1; ++i) load_sb(sbegin + i, zb[i], xb[i]);
+  load_sb(sbegin, zb[0], xb[0]);
   __syncthreads();                                           // bs_lds and bl_lds[0] ready
 
-  for (int st0 = 0; st0 < nsteps; st0 += kRing) {
+  auto step = [&](const int st, const int kb, const RawN<T, DPL>* zc, const RawN<T, DPL>* xc,
+                  RawN<T, DPL>* zn, RawN<T, DPL>* xn) {
+    const int64_t sb = sbegin + st;                          // global small block (may be < 0)
+    // the next step's beta_l rows go to the other buffer (read by every
+    // wave before the barrier that ended the previous step)
+    if (st + 1 < nsteps) write_bl(kb ^ 1);
+    if (st + 2 < nsteps) load_bl(((st + 2) % R) * MS);
+    load_sb(sb + 1, zn, xn);
+    // reference update from the small block maximum
+    float bmx[DPL];
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) {
-      const int st = st0 + i;                                // step = small block of the stream
-      const int nx = (i + kRing - 1) % kRing;
-      if (st < nsteps) {
-        const int64_t sb = sbegin + st;                      // global small block (may be < 0)
-        const int j = st % R;                                // position within the large block
-        const int64_t lb = LB0 + st / R;                     // large block (may be -1)
-        const int kb = st & 1;
-        // the next step's beta_l rows go to the other buffer (read by every
-        // wave before the barrier that ended the previous step)
-        if (st + 1 < nsteps) write_bl(kb ^ 1);
-        if (st + 2 < nsteps) load_bl(((st + 2) % R) * MS);
-        load_sb(sbegin + st + kRing - 1, zb[nx], xb[nx]);
-        const RawN<T, DPL>* zc = zb[i];
-        const RawN<T, DPL>* xc = xb[i];
-        // reference update from the small block maximum
-        float bmx[DPL];
+    for (int d = 0; d < DPL; ++d) {
+      float v = zc[0][d];
+#pragma unroll
+      for (int t = 1; t < MS; ++t) v = fmaxf(v, zc[t][d]);
+      bmx[d] = v * L2E;
+    }
+    // This block's sums, all against its maximum bmx: the small halves
+    // (sA/aA: first half of entry sb + 1, sB/aB: second half of entry
+    // sb) and the large block's two halves (pA/qA, pB/qB).  ux = u x
+    // turns every accumulation into one FMA.
+    float sA[DPL], aA[DPL], sB[DPL], aB[DPL], pA[DPL], qA[DPL], pB[DPL], qB[DPL];
+#pragma unroll
+    for (int t = 0; t < MS; ++t) {
+      float ba[DPL], bb[DPL], la[DPL], lbv[DPL];
+#pragma unroll
+      for (int d = 0; d < DPL; d += 4) {
+        const float4 v0 = *reinterpret_cast<const float4*>(&bs_lds[t][dl + d]);
+        const float4 v1 = *reinterpret_cast<const float4*>(&bs_lds[MS + t][dl + d]);
+        const float4 v2 = *reinterpret_cast<const float4*>(&bl_lds[kb][t][dl + d]);
+        const float4 v3 = *reinterpret_cast<const float4*>(&bl_lds[kb][MS + t][dl + d]);
+        ba[d] = v0.x; ba[d + 1] = v0.y; ba[d + 2] = v0.z; ba[d + 3] = v0.w;
+        bb[d] = v1.x; bb[d + 1] = v1.y; bb[d + 2] = v1.z; bb[d + 3] = v1.w;
+        la[d] = v2.x; la[d + 1] = v2.y; la[d + 2] = v2.z; la[d + 3] = v2.w;
+        lbv[d] = v3.x; lbv[d + 1] = v3.y; lbv[d + 2] = v3.z; lbv[d + 3] = v3.w;
+      }
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) {
+        const float u = __builtin_amdgcn_exp2f(fmaf(zc[t][d], L2E, -bmx[d]));
+        const float ux = u * xc[t][d];
+        if (t == 0) {
+          sA[d] = u * ba[d]; aA[d] = ux * ba[d]; sB[d] = u * bb[d]; aB[d] = ux * bb[d];
+          pA[d] = u * la[d]; qA[d] = ux * la[d]; pB[d] = u * lbv[d]; qB[d] = ux * lbv[d];
+        } else {
+          sA[d] = fmaf(u, ba[d], sA[d]);
+          aA[d] = fmaf(ux, ba[d], aA[d]);
+          sB[d] = fmaf(u, bb[d], sB[d]);
+          aB[d] = fmaf(ux, bb[d], aB[d]);
+          pA[d] = fmaf(u, la[d], pA[d]);
+          qA[d] = fmaf(ux, la[d], qA[d]);
+          pB[d] = fmaf(u, lbv[d], pB[d]);
+          qB[d] = fmaf(ux, lbv[d], qB[d]);
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
+    // The large block's reference rl is raise-only within the block (it
+    // is -inf before the block's first small block); this block's large sums
+    // join the running sums scaled by G = 2^(bmx - rl) <= 2^kBand.  Raising
+    // rl (rare, and at every large block's start) rescales the running sums.
+    bool up = false;
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) up |= bmx[d] > rl[d] + kBand;
+    if (__any(up)) {
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) {
+        const float na = bmx[d] > rl[d] + kBand ? bmx[d] : rl[d];
+        const float f = __builtin_amdgcn_exp2f(rl[d] - na);
+        lsA[d] *= f; laA[d] *= f; lsB[d] *= f; laB[d] *= f;
+        rl[d] = na;
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) {
+      const float G = __builtin_amdgcn_exp2f(bmx[d] - rl[d]);
+      lsA[d] = fmaf(G, pA[d], lsA[d]);
+      laA[d] = fmaf(G, qA[d], laA[d]);
+      lsB[d] = fmaf(G, pB[d], lsB[d]);
+      laB[d] = fmaf(G, qB[d], laB[d]);
+    }
+    // small entry sb: carried first half + this second half
+    {
+      float o[DPL];
+      const bool first = sb == 0;
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) {
+        const float dl = cr[d] - bmx[d];
+        const float g = __builtin_amdgcn_exp2f(-fabsf(dl));
+        const float fc = first ? 0.f : (dl >= 0.f ? 1.f : g);
+        const float fb = (first || dl < 0.f) ? 1.f : g;
+        o[d] = (cA[d] * fc + aB[d] * fb) * __builtin_amdgcn_rcpf(cS[d] * fc + sB[d] * fb);
+      }
+      const bool defer = wave > 0 && sb == S0;           // first half comes from wave-1
+      if (defer) {
 #pragma unroll
         for (int d = 0; d < DPL; ++d) {
-          float v = zc[0][d];
-#pragma unroll
-          for (int t = 1; t < MS; ++t) v = fmaxf(v, zc[t][d]);
-          bmx[d] = v * L2E;
+          dfr[wave][0][dl + d] = sB[d]; dfr[wave][1][dl + d] = aB[d]; dfr[wave][2][dl + d] = bmx[d];
         }
-        // the small sums of this block use its maximum bmx as reference; the
-        // large block's reference rl is raise-only
-        if (j == 0) {                                        // a large block starts
+      }
+      const uint32_t off = (sb >= S0 && sb < S1 && !defer)
+                               ? (uint32_t)((sb - S0) * ld_s + d0) * sizeof(T) : 0xffffffffu;
+      BufStoreN<T, DPL>::store(rsrc_s, off, o);
 #pragma unroll
-          for (int d = 0; d < DPL; ++d) rl[d] = bmx[d];
-        } else {
-          bool up = false;
+      for (int d = 0; d < DPL; ++d) { cS[d] = sA[d]; cA[d] = aA[d]; cr[d] = bmx[d]; }
+    }
+    __syncthreads();                                         // next beta_l rows staged
+  };
+
+  for (int bi = 0; bi < nblocks; ++bi) {
+    const int64_t lb = LB0 + bi;                             // large block (may be -1)
+    for (int j = 0; j < R; j += 2) {
+      step(bi * R + j, 0, zb[0], xb[0], zb[1], xb[1]);
+      step(bi * R + j + 1, 1, zb[1], xb[1], zb[0], xb[0]);
+    }
+    // end of a large block: large entry lb closes
+    {
+      float o[DPL];
+      const bool first = lb == 0;
 #pragma unroll
-          for (int d = 0; d < DPL; ++d) up |= bmx[d] > rl[d] + kBand;
-          if (__any(up)) {
+      for (int d = 0; d < DPL; ++d) {
+        const float mx = fmaxf(lcr[d], rl[d]);
+        const float fc = first ? 0.f : __builtin_amdgcn_exp2f(lcr[d] - mx);
+        const float fb = __builtin_amdgcn_exp2f(rl[d] - mx);
+        o[d] = (lcA[d] * fc + laB[d] * fb) * __builtin_amdgcn_rcpf(lcS[d] * fc + lsB[d] * fb);
+      }
+      const bool defer = wave > 0 && lb == E0;
+      if (defer) {
 #pragma unroll
-            for (int d = 0; d < DPL; ++d) {
-              const float na = bmx[d] > rl[d] + kBand ? bmx[d] : rl[d];
-              const float f = __builtin_amdgcn_exp2f(rl[d] - na);
-              lsA[d] *= f; laA[d] *= f; lsB[d] *= f; laB[d] *= f;
-              rl[d] = na;
-            }
-          }
+        for (int d = 0; d < DPL; ++d) {
+          dfr[wave][3][dl + d] = lsB[d]; dfr[wave][4][dl + d] = laB[d]; dfr[wave][5][dl + d] = rl[d];
         }
+      }
+      const uint32_t off = (lb >= E0 && lb < E1 && !defer)
+                               ? (uint32_t)((lb - E0) * ld_l + d0) * sizeof(T) : 0xffffffffu;
+      BufStoreN<T, DPL>::store(rsrc_l, off, o);
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) G[d] = __builtin_amdgcn_exp2f(bmx[d] - rl[d]);
-        float sA[DPL], aA[DPL], sB[DPL], aB[DPL];
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) { sA[d] = 0.f; aA[d] = 0.f; sB[d] = 0.f; aB[d] = 0.f; }
-#pragma unroll
-        for (int t = 0; t < MS; ++t) {
-          float ba[DPL], bb[DPL], la[DPL], lbv[DPL];
-#pragma unroll
-          for (int d = 0; d < DPL; d += 4) {
-            const float4 v0 = *reinterpret_cast<const float4*>(&bs_lds[t][dl + d]);
-            const float4 v1 = *reinterpret_cast<const float4*>(&bs_lds[MS + t][dl + d]);
-            const float4 v2 = *reinterpret_cast<const float4*>(&bl_lds[kb][t][dl + d]);
-            const float4 v3 = *reinterpret_cast<const float4*>(&bl_lds[kb][MS + t][dl + d]);
-            ba[d] = v0.x; ba[d + 1] = v0.y; ba[d + 2] = v0.z; ba[d + 3] = v0.w;
-            bb[d] = v1.x; bb[d + 1] = v1.y; bb[d + 2] = v1.z; bb[d + 3] = v1.w;
-            la[d] = v2.x; la[d + 1] = v2.y; la[d + 2] = v2.z; la[d + 3] = v2.w;
-            lbv[d] = v3.x; lbv[d + 1] = v3.y; lbv[d + 2] = v3.z; lbv[d + 3] = v3.w;
-          }
-#pragma unroll
-          for (int d = 0; d < DPL; ++d) {
-            const float u = __builtin_amdgcn_exp2f(fmaf(zc[t][d], L2E, -bmx[d]));
-            const float xv = xc[t][d];
-            const float wa = u * ba[d], wb = u * bb[d];
-            sA[d] += wa;
-            aA[d] = fmaf(wa, xv, aA[d]);
-            sB[d] += wb;
-            aB[d] = fmaf(wb, xv, aB[d]);
-            const float ul = u * G[d];
-            const float va = ul * la[d], vb = ul * lbv[d];
-            lsA[d] += va;
-            laA[d] = fmaf(va, xv, laA[d]);
-            lsB[d] += vb;
-            laB[d] = fmaf(vb, xv, laB[d]);
-          }
-          asm volatile("" ::: "memory");
-        }
-        // small entry sb: carried first half + this second half
-        {
-          float o[DPL];
-          const bool first = sb == 0;
-#pragma unroll
-          for (int d = 0; d < DPL; ++d) {
-            const float dl = cr[d] - bmx[d];
-            const float g = __builtin_amdgcn_exp2f(-fabsf(dl));
-            const float fc = first ? 0.f : (dl >= 0.f ? 1.f : g);
-            const float fb = (first || dl < 0.f) ? 1.f : g;
-            o[d] = (cA[d] * fc + aB[d] * fb) * __builtin_amdgcn_rcpf(cS[d] * fc + sB[d] * fb);
-          }
-          const bool defer = wave > 0 && sb == S0;           // first half comes from wave-1
-          if (defer) {
-#pragma unroll
-            for (int d = 0; d < DPL; ++d) { fS[d] = sB[d]; fA[d] = aB[d]; fr[d] = bmx[d]; }
-          }
-          const uint32_t off = (sb >= S0 && sb < S1 && !defer)
-                                   ? (uint32_t)((sb - S0) * ld_s + d0) * sizeof(T) : 0xffffffffu;
-          BufStoreN<T, DPL>::store(rsrc_s, off, o);
-#pragma unroll
-          for (int d = 0; d < DPL; ++d) { cS[d] = sA[d]; cA[d] = aA[d]; cr[d] = bmx[d]; }
-        }
-        // end of a large block: large entry lb closes
-        if (j == R - 1) {
-          float o[DPL];
-          const bool first = lb == 0;
-#pragma unroll
-          for (int d = 0; d < DPL; ++d) {
-            const float mx = fmaxf(lcr[d], rl[d]);
-            const float fc = first ? 0.f : __builtin_amdgcn_exp2f(lcr[d] - mx);
-            const float fb = __builtin_amdgcn_exp2f(rl[d] - mx);
-            o[d] = (lcA[d] * fc + laB[d] * fb) * __builtin_amdgcn_rcpf(lcS[d] * fc + lsB[d] * fb);
-          }
-          const bool defer = wave > 0 && lb == E0;
-          if (defer) {
-#pragma unroll
-            for (int d = 0; d < DPL; ++d) { gS[d] = lsB[d]; gA[d] = laB[d]; gr[d] = rl[d]; }
-          }
-          const uint32_t off = (lb >= E0 && lb < E1 && !defer)
-                                   ? (uint32_t)((lb - E0) * ld_l + d0) * sizeof(T) : 0xffffffffu;
-          BufStoreN<T, DPL>::store(rsrc_l, off, o);
-#pragma unroll
-          for (int d = 0; d < DPL; ++d) {
-            lcS[d] = lsA[d]; lcA[d] = laA[d]; lcr[d] = rl[d];
-            lsA[d] = 0.f; laA[d] = 0.f; lsB[d] = 0.f; laB[d] = 0.f;
-          }
-        }
-        __syncthreads();                                     // next beta_l rows staged
+      for (int d = 0; d < DPL; ++d) {
+        lcS[d] = lsA[d]; lcA[d] = laA[d]; lcr[d] = rl[d];
+        lsA[d] = 0.f; laA[d] = 0.f; lsB[d] = 0.f; laB[d] = 0.f;
+        rl[d] = -INFINITY;
       }
     }
   }
@@ -744,17 +759,19 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
     float os[DPL], ol[DPL];
 #pragma unroll
     for (int d = 0; d < DPL; ++d) {
+      const float fS = dfr[wave][0][dl + d], fA = dfr[wave][1][dl + d], fr = dfr[wave][2][dl + d];
+      const float gS = dfr[wave][3][dl + d], gA = dfr[wave][4][dl + d], gr = dfr[wave][5][dl + d];
       const float pr = xch[wave - 1][4][dl + d];
-      float mx = fmaxf(pr, fr[d]);
-      float fp = __builtin_amdgcn_exp2f(pr - mx), fc = __builtin_amdgcn_exp2f(fr[d] - mx);
-      os[d] = (xch[wave - 1][1][dl + d] * fp + fA[d] * fc) *
-              __builtin_amdgcn_rcpf(xch[wave - 1][0][dl + d] * fp + fS[d] * fc);
+      float mx = fmaxf(pr, fr);
+      float fp = __builtin_amdgcn_exp2f(pr - mx), fc = __builtin_amdgcn_exp2f(fr - mx);
+      os[d] = (xch[wave - 1][1][dl + d] * fp + fA * fc) *
+              __builtin_amdgcn_rcpf(xch[wave - 1][0][dl + d] * fp + fS * fc);
       const float plr = xch[wave - 1][5][dl + d];
-      mx = fmaxf(plr, gr[d]);
+      mx = fmaxf(plr, gr);
       fp = __builtin_amdgcn_exp2f(plr - mx);
-      fc = __builtin_amdgcn_exp2f(gr[d] - mx);
-      ol[d] = (xch[wave - 1][3][dl + d] * fp + gA[d] * fc) *
-              __builtin_amdgcn_rcpf(xch[wave - 1][2][dl + d] * fp + gS[d] * fc);
+      fc = __builtin_amdgcn_exp2f(gr - mx);
+      ol[d] = (xch[wave - 1][3][dl + d] * fp + gA * fc) *
+              __builtin_amdgcn_rcpf(xch[wave - 1][2][dl + d] * fp + gS * fc);
     }
     BufStoreN<T, DPL>::store(rsrc_s, S0 < S1 ? (uint32_t)(d0 * sizeof(T)) : 0xffffffffu, os);
     BufStoreN<T, DPL>::store(rsrc_l, E0 < E1 ? (uint32_t)(d0 * sizeof(T)) : 0xffffffffu, ol);
@@ -820,6 +837,13 @@ hipError_t launch_compress_fused(int dt, const void* x, const void* z, int64_t T
                                  hipStream_t stream) {
   const int64_t NL = T_tokens / ml, NSall = T_tokens / ms, NSf = NL * (ml / ms);
   hipError_t e = hipSuccess;
+  if ((ml / ms) % 2 != 0) {
+    // the fused kernel streams an even number of small blocks per large
+    // block; otherwise each scale gets its own streaming kernel
+    e = launch_compress(dt, x, z, bias_s, ms, 0, NSall, out_s, ld_s, stream);
+    if (e == hipSuccess && NL > 0) e = launch_compress(dt, x, z, bias_l, ml, 0, NL, out_l, ld_l, stream);
+    return e;
+  }
   if (NL > 0) {
     e = dt == 0 ? launch_fused_t<float>(x, z, T_tokens, bias_s, ms, out_s, ld_s, bias_l, ml, out_l,
                                         ld_l, ws, stream)
