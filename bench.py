@@ -17,7 +17,6 @@ the dominant kernel divides its algorithmic bytes by its average duration.
 The CPU baseline times the oracle on a bounded sample of the same step.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -45,15 +44,6 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "compressed_sparse_kv_overlapping_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources (else None)."""
@@ -63,6 +53,7 @@ def measured_traffic(kernel):
             t = json.load(f)
     except (OSError, ValueError):
         return None
+    from compressed_sparse_kv_overlapping_amd.profiling import source_digest
     entry = t.get("kernels", {}).get(kernel)
     if not entry or t.get("source_digest") != source_digest():
         return None

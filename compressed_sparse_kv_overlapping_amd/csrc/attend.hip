@@ -888,7 +888,10 @@ int attend_splits(int dt, int64_t B, int H, int64_t nslots) {
   const int64_t blocks = B * ((H + hpb - 1) / hpb);
   const int64_t tiles = (nslots + kTile - 1) / kTile;
   if (tiles == 0) return 1;
-  int64_t s = (512 + blocks - 1) / blocks;
+  // about one round of resident blocks (the bf16 kernel holds one block per
+  // compute unit): more splits than that only add partial outputs
+  const int64_t target = dt == 0 ? 512 : 256;
+  int64_t s = (target + blocks - 1) / blocks;
   const int64_t cap = tiles / 2 > 1 ? tiles / 2 : 1;
   if (s > cap) s = cap;
   if (s > 64) s = 64;
