@@ -438,13 +438,18 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
 //
 // Tiles are gathered from HBM straight into LDS (global_load_lds, 16 bytes
 // per lane, no registers), one tile ahead into the other of two buffers.  A
-// tile is 32 rows x 1152 bytes stored row-major; within each row the 16-byte
-// chunks are XOR-permuted inside aligned groups of 8 by a function of the
-// row, so that both LDS read patterns are free of bank conflicts:
-//   logits: 16 rows x one chunk (ds_read_b128),
-//   values: 4 rows x two chunks, read transposed (ds_read_b64_tr_b16), which
-//           hands each lane four consecutive rows of one value dimension: the
-//           A operand of O^T += V^T P^T, taken from the row-major tile.
+// tile holds 32 rows x 72 chunks of 16 bytes.  Copy n fills slots
+// [64 n, 64 n + 64): lanes 0..31 take chunk 2n of rows 0..31, lanes 32..63
+// chunk 2n + 1 of the rows rotated by 8, so that chunk c of row r sits in slot
+//   64 (c / 2) + 32 (c % 2) + ((r + 8 (c % 2)) % 32)
+// and every lane copies a single row.  Both LDS read patterns then touch
+// distinct banks (64 banks of 4 bytes, 16 lanes a pass):
+//   logits: 16 rows x one chunk (ds_read_b128): one 256-byte run, or two
+//           128-byte runs that do not alias,
+//   values: 4 rows x two chunks, read transposed (ds_read_b64_tr_b16): runs in
+//           distinct banks; the transposed read hands each lane four
+//           consecutive rows of one value dimension, the A operand of
+//           O^T += V^T P^T.
 // The gather is issued from inline assembly, so the compiler does not see
 // an LDS write in flight; the loop waits for it explicitly before the
 // barrier that opens each tile.
@@ -461,9 +466,10 @@ constexpr int kRowBytes = kE * 2, kRowChunks = kE / 8, kTileBytes = kTile * kRow
 constexpr int kTileLoads = kTile * kRowChunks / 64;          // 64-lane loads per tile (36)
 static_assert(kTileLoads % kWideWaves == 0, "whole loads per wave");
 
-__device__ __forceinline__ int chunk_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-// physical chunk of logical chunk c in row r (an involution for fixed r)
-__device__ __forceinline__ int chunk_phys(int c, int r) { return (c & ~7) | ((c ^ chunk_swz(r)) & 7); }
+// byte offset of chunk c of row r in a tile
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return 1024 * (c >> 1) + 512 * (c & 1) + 16 * ((r + 8 * (c & 1)) & 31);
+}
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
@@ -475,10 +481,13 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
 __device__ __forceinline__ unsigned lds_offset(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
-// 16 bytes per lane from src into LDS at m0 + 16 * lane (m0 wave-uniform)
+// 16 bytes per lane from src into LDS at m0 + 16 * lane (m0 wave-uniform).
+// No memory clobber: the buffer it fills is read only after the explicit
+// wait and barrier that open the next tile, so other loads (the row
+// addresses of the following copies among them) may move across it.
 __device__ __forceinline__ void dma16(const char* src, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_base) : "memory", "m0");
+               :: "v"(src), "s"(lds_base) : "m0");
 }
 
 struct WideShared {
@@ -599,49 +608,40 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
       if (threadIdx.x == 0) row_mask[t % 3] = (uint32_t)m;
     }
   };
-  // gather tile t into buffer k: load n (64 lanes x 16 bytes) fills LDS bytes
-  // [1024 n, 1024 n + 1024) of the buffer; its lane i takes physical chunk
-  // 64 n + i of the tile
+  // gather tile t into buffer k: copy n (64 lanes x 16 bytes) fills LDS bytes
+  // [1024 n, 1024 n + 1024) of the buffer with chunks 2n (lanes 0..31) and
+  // 2n + 1 (lanes 32..63); a lane's copies all come from one row
   auto issue = [&](int t, int k) {
-    const int slot = t % 3;
     const unsigned base = lds_offset(kbuf[k]);
-    // load i of this wave takes physical chunk 64 (wave + 4 i) + lane; consecutive
-    // loads are 256 chunks = 3 rows + 40 chunks apart
-    const int s0 = 64 * wave + lane;
-    int r = s0 / kRowChunks, pc = s0 - r * kRowChunks;
+    const int par = lane >> 5;
+    const int r = ((lane & 31) - 8 * par) & 31;
+    const char* rowp = row_ptr[t % 3][r] + 16 * par;
 #pragma unroll
     for (int i = 0; i < kTileLoads / kWideWaves; ++i) {
       const int n = wave + i * kWideWaves;
-      dma16(row_ptr[slot][r] + chunk_phys(pc, r) * 16,
-            (unsigned)__builtin_amdgcn_readfirstlane(base + 1024 * n));
-      pc += 256 - 3 * kRowChunks;
-      r += 3;
-      if (pc >= kRowChunks) { pc -= kRowChunks; r += 1; }
+      dma16(rowp + 32 * n, (unsigned)__builtin_amdgcn_readfirstlane(base + 1024 * n));
     }
   };
-  static_assert(64 * kWideWaves == 3 * kRowChunks + 40, "load stride");
 
   // Lane offsets of the LDS read patterns, derived from the lane id each
   // time a tile starts: nothing lane-dependent stays in a register across
   // the loop.
   struct LaneOffs {
-    int koff0, koff1;      // logit rows col and 16 + col, logical chunk low bits g / 4 + g
-    int vbase, vlow, sw_v; // value rows 4g + col/4 and 16 + that
-    int qoff;              // second head block's queries in LDS
-    int g4;                // 4 g
+    int k0, k1;        // logit rows col and 16 + col at chunk g (+ 2048 per 32-dim step)
+    int v0, v1;        // value rows 4g + col/4 and 16 + that (+ 1024 per 16-dim block)
+    int qoff;          // second head block's queries in LDS
+    int g4;            // 4 g
   };
   auto lane_offs = [&]() {
     int lid;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
     const int c = lid & 15, gg = lid >> 4;
     LaneOffs o;
-    const int sk = chunk_swz(c);
-    o.koff0 = c * kRowBytes + ((gg ^ sk) << 4);
-    o.koff1 = c * kRowBytes + (((4 + gg) ^ sk) << 4);
-    const int vr = 4 * gg + (c >> 2);
-    o.vbase = vr * kRowBytes + ((c & 1) << 3);
-    o.vlow = (c & 3) >> 1;
-    o.sw_v = chunk_swz(vr);
+    o.k0 = tile_off(c, gg);
+    o.k1 = tile_off(16 + c, gg);
+    const int vr = 4 * gg + (c >> 2), vc = (c & 3) >> 1;     // chunk 2 db + vc, half c & 1
+    o.v0 = tile_off(vr, vc) + ((c & 1) << 3);
+    o.v1 = tile_off(16 + vr, vc) + ((c & 1) << 3);
     o.qoff = (int)lds_offset(&qs[wave][c][8 * gg]);
     o.g4 = 4 * gg;
     return o;
@@ -656,9 +656,8 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     // second head block's queries; double-buffered one step ahead
     Frag<bf16_t> A0[2], A1[2], Q1[2];
     auto kfrag = [&](int ks, int u) {
-      const char* p = kb + ((ks & 1) ? L.koff1 : L.koff0) + 128 * (ks >> 1);
-      const uint4 x0 = *reinterpret_cast<const uint4*>(p);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(p + 16 * kRowBytes);
+      const uint4 x0 = *reinterpret_cast<const uint4*>(kb + L.k0 + 2048 * ks);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(kb + L.k1 + 2048 * ks);
       const u32x4 y = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
           (const __attribute__((address_space(3))) char*)(uintptr_t)(L.qoff + 64 * ks));
       A0[u].v = u32x4{x0.x, x0.y, x0.z, x0.w};
@@ -688,8 +687,7 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
       sv[i] = ((m >> bit) & 1u) ? x * c_log2 : -INFINITY;
       tmax = fmaxf(tmax, sv[i]);
     }
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    return fmaxf(tmax, shfl_xor(tmax, 32));
+    return max_xor32(max_xor16(tmax));
   };
   // one tile of the accumulation (check: the main pass, which sets the
   // references and flags logits past the band)
@@ -720,8 +718,7 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     // 16-dim block db (chunks 2 db, 2 db + 1) run three blocks ahead
     Frag<bf16_t> VF[4];
     auto vfrag = [&](int db) {
-      const char* p = kb + L.vbase + (((2 * (db & 3) + L.vlow) ^ L.sw_v) << 4) + 128 * (db >> 2);
-      const uint2 v0 = lds_read_tr(p), v1 = lds_read_tr(p + 16 * kRowBytes);
+      const uint2 v0 = lds_read_tr(kb + L.v0 + 1024 * db), v1 = lds_read_tr(kb + L.v1 + 1024 * db);
       VF[db & 3].v = u32x4{v0.x, v0.y, v1.x, v1.y};
     };
     vfrag(0);
@@ -802,9 +799,7 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   const float LN2 = 0.6931471805599453f;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    float l = l_run[j];
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
+    const float l = sum_xor32(sum_xor16(l_run[j]));
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const float lse2 = l > 0.f ? m_ref[j] + __log2f(l) : -INFINITY;
     if (!hok[j]) continue;

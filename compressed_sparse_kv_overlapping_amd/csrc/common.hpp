@@ -169,6 +169,26 @@ template <> struct BufStoreN<float, 8> {
 // ---------------------------------------------------------------- shuffles
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Combine a value with the one held by lane ^ 16 (or ^ 32) through the gfx950
+// lane-half swaps (plain VALU, no LDS round trip).  Both lanes of a pair see
+// the two values in the same order, so they get bitwise equal results.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key);
 // -0 is folded onto +0 so equal values get equal keys.
 __device__ __forceinline__ uint32_t score_key(float s) {
