@@ -17,8 +17,9 @@
 //     threshold is appended to the query's candidate list (typically ~1.2 k
 //     candidates for unstructured scores).
 //  4. final: per query, exact radix select over (score key, ~index) 64-bit
-//     composite keys of the candidates, then the chosen indices are sorted
-//     ascending and written.  If the candidate list overflowed (e.g. massive
+//     composite keys of the candidates; the chosen indices are written in
+//     ascending order (candidates are kept in entry-range order and sorted
+//     only within each range).  If the candidate list overflowed (e.g. massive
 //     score ties), the query is resolved by a self-contained streaming radix
 //     select over all its entries instead.
 #include "common.hpp"
@@ -187,27 +188,42 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
 
 // ------------------------------------------------- block-wide radix helpers
 
-// Block of 256 threads: position of the digit holding the kk-th largest key
-// among the counted ones.  hist[256] in LDS (already filled); on return
-// *digit and *above (count of keys in higher digits) are in LDS scratch.
-__device__ void find_digit(const uint32_t* hist, int nbins, uint32_t kk, uint32_t* sh_digit,
-                           uint32_t* sh_above, uint32_t* scan) {
-  // suffix sums (from the top bin down), one bin chunk per thread
+// Exclusive prefix sum over the block (256 threads): wave scans, then the
+// wave totals.  *total receives the block sum.  part[] holds 4 values.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* part, uint32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) part[w] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t p = part[i];
+    base += i < w ? p : 0u;
+    tot += p;
+  }
+  __syncthreads();                                           // part[] free again
+  *total = tot;
+  return base + incl - x;
+}
+
+// Bin of hist[nbins] (nbins a multiple of 256, 256 threads) that holds the
+// kk-th largest counted key: thread t owns the t-th group of nbins/256 bins
+// from the top.  *sh_digit gets the bin, *sh_above the keys in higher bins.
+__device__ void find_kth_bin(const uint32_t* hist, int nbins, uint32_t kk, uint32_t* sh_digit,
+                             uint32_t* sh_above, uint32_t* part) {
   const int t = threadIdx.x;
   const int per = nbins / 256;
   uint32_t local = 0;
   for (int i = 0; i < per; ++i) local += hist[nbins - 1 - (t * per + i)];
-  scan[t] = local;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    uint32_t v = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += v;
-    __syncthreads();
-  }
-  // scan[t] = keys in the top (t+1)*per bins
-  const uint32_t before = t ? scan[t - 1] : 0;
-  if (before < kk && kk <= scan[t]) {
+  uint32_t tot;
+  const uint32_t before = block_excl_scan(local, part, &tot);
+  if (before < kk && kk <= before + local) {
     uint32_t cum = before;
     for (int i = 0; i < per; ++i) {
       const int bin = nbins - 1 - (t * per + i);
@@ -222,44 +238,88 @@ __device__ void find_digit(const uint32_t* hist, int nbins, uint32_t kk, uint32_
   __syncthreads();
 }
 
-// k-th largest of the G group maxima of each query (0 if fewer than k
-// non-empty groups or fewer than k visible entries).
-__global__ __launch_bounds__(256) void idx_threshold_kernel(IdxArgs a) {
-  __shared__ uint32_t keys[kMaxGroups];
-  __shared__ uint32_t hist[256], scan[256];
-  __shared__ uint32_t sh_digit, sh_above, sh_nonempty;
-  const int b = blockIdx.x;
-  if (threadIdx.x == 0) sh_nonempty = 0;
-  __syncthreads();
-  uint32_t ne = 0;
-  for (int i = threadIdx.x; i < a.G; i += 256) {
-    const uint32_t v = a.gmax[(int64_t)b * a.G + i];
-    keys[i] = v;
-    ne += v != 0u;
+// Block min and max of the valid keys (256 threads; part[] holds 8 values).
+__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, uint32_t* part, uint32_t* out_mn,
+                                             uint32_t* out_mx) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
   }
-  atomicAdd(&sh_nonempty, ne);
+  if (lane == 0) { part[w] = mn; part[4 + w] = mx; }
   __syncthreads();
+  mn = min(min(part[0], part[1]), min(part[2], part[3]));
+  mx = max(max(part[4], part[5]), max(part[6], part[7]));
+  __syncthreads();
+  *out_mn = mn;
+  *out_mx = mx;
+}
+
+// kk-th largest (1-based) of the 32-bit keys that key_at(i) yields as valid,
+// i in [0, n), given their min lo and max hi.  Every pass spreads the
+// remaining range over 2^BB bins of equal width, so keys crowded into a few
+// high bits still fall into distinct bins (few colliding LDS atomics) and a
+// range of 2^r takes ceil(r / BB) passes.  *above_out: valid keys greater
+// than the result.
+template <int BB, class KeyAt>
+__device__ uint32_t block_kth_largest(KeyAt key_at, int n, uint32_t kk, uint32_t lo, uint32_t hi,
+                                      uint32_t* hist, uint32_t* part, uint32_t* sh_digit,
+                                      uint32_t* sh_above, uint32_t* above_out) {
+  uint32_t above_total = 0;
+  for (;;) {
+    const uint32_t range = hi - lo;
+    if (range == 0) break;
+    const int bits = 32 - __clz((int)range);              // range < 2^bits
+    const int shift = bits > BB ? bits - BB : 0;
+    for (int i = threadIdx.x; i < (1 << BB); i += 256) hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) {
+      uint32_t key;
+      if (key_at(i, key) && key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> shift], 1u);
+    }
+    __syncthreads();
+    find_kth_bin(hist, 1 << BB, kk, sh_digit, sh_above, part);
+    const uint32_t bin = *sh_digit;
+    kk -= *sh_above;
+    above_total += *sh_above;
+    __syncthreads();
+    lo += bin << shift;
+    const uint32_t top = lo + ((1u << shift) - 1u);
+    hi = top < hi ? top : hi;
+    if (shift == 0) break;
+  }
+  *above_out = above_total;
+  return lo;
+}
+
+// k-th largest of the G group maxima of each query (0 if fewer than k
+// non-empty groups or fewer than k visible entries).  The maxima are read
+// from L2 on every pass; only the histogram lives in LDS.
+__global__ __launch_bounds__(256) void idx_threshold_kernel(IdxArgs a) {
+  __shared__ uint32_t hist[4096], part[8];
+  __shared__ uint32_t sh_digit, sh_above;
+  const int b = blockIdx.x;
+  const uint32_t* gm = a.gmax + (int64_t)b * a.G;
+  uint32_t ne = 0, mn = 0xffffffffu, mx = 0u;
+  for (int i = threadIdx.x; i < a.G; i += 256) {
+    const uint32_t v = gm[i];
+    if (v != 0u) { ++ne; mn = min(mn, v); mx = max(mx, v); }
+  }
+  uint32_t nonempty;
+  block_excl_scan(ne, part, &nonempty);
+  uint32_t lo, hi;
+  block_minmax(mn, mx, part, &lo, &hi);
   const int nv = n_visible(a, b);
-  if (nv <= a.k || sh_nonempty < (uint32_t)a.k) {
+  if (nv <= a.k || nonempty < (uint32_t)a.k) {
     if (threadIdx.x == 0) a.thr[b] = 0u;
     return;
   }
-  uint32_t prefix = 0, mask = 0, kk = (uint32_t)a.k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < a.G; i += 256) {
-      const uint32_t v = keys[i];
-      if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    find_digit(hist, 256, kk, &sh_digit, &sh_above, scan);
-    kk -= sh_above;
-    prefix |= sh_digit << shift;
-    mask |= 255u << shift;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) a.thr[b] = prefix;
+  uint32_t above;
+  const uint32_t thr = block_kth_largest<12>(
+      [&](int i, uint32_t& key) { key = gm[i]; return key != 0u; }, a.G, (uint32_t)a.k, lo, hi,
+      hist, part, &sh_digit, &sh_above, &above);
+  if (threadIdx.x == 0) a.thr[b] = thr;
 }
 
 // ----------------------------------------------------------------- final
@@ -294,12 +354,31 @@ template <> __device__ __forceinline__ float dot64<e4m3_t>(const e4m3_t* q, cons
 
 // Exact selection for one query.  Candidates are either the collected list
 // (in LDS) or, on overflow, every visible entry with its score recomputed.
+//
+// Collected list: the candidate regions are gathered in chunk order, i.e. in
+// ascending entry ranges.  The k-th largest composite is found with one
+// histogram of the score words over 2048 bins of their range; the few
+// candidates in the bin that holds it are ranked exactly by composite (a
+// crowded bin falls back to further passes).  Each selected candidate is then
+// written at its chunk's output offset plus its rank by index among the
+// chunk's selected ones, so the output is ascending without a global sort.
+constexpr int kMaxChunks = 2048;
+constexpr int kFinalBB = 11;                 // histogram of 2^11 bins
+constexpr int kMem = 512;                    // bin members ranked exactly
 template <class T>
 __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
-  __shared__ uint64_t cand[kCap];
-  __shared__ int32_t sel[kMaxK];
-  __shared__ uint32_t hist[2048], scan[256];
-  __shared__ uint32_t sh_digit, sh_above, sh_nsel;
+  // candidates (list) or, on overflow, the k selected indices
+  __shared__ union { uint64_t cand[kCap]; int32_t sel[kMaxK]; } cs;
+  // the histogram, then the members of the k-th bin, then the chunks' output
+  // offsets
+  __shared__ union { uint32_t hist[1 << kFinalBB]; uint64_t mem[kMem]; uint16_t csel[kMaxChunks]; } hs;
+  __shared__ uint16_t coff[kMaxChunks + 1];                  // list offset of each chunk
+  __shared__ uint32_t part[8];
+  __shared__ uint32_t sh_digit, sh_above, sh_nsel, sh_over;
+  __shared__ uint64_t sh_thr;
+  uint64_t* cand = cs.cand;
+  int32_t* sel = cs.sel;
+  uint32_t* hist = hs.hist;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   const int nv = n_visible(a, b);
@@ -308,94 +387,195 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
     for (int j = t; j < a.k; j += kFinalThreads) out[j] = j < nv ? j : -1;
     return;
   }
-  // gather the chunk regions into LDS (prefix sums of the chunk counts);
-  // a full region or more than kCap candidates in total means overflow
-  __shared__ uint32_t sh_total, sh_over;
-  if (t == 0) { sh_total = 0; sh_over = 0; }
-  __syncthreads();
-  for (int c0 = 0; c0 < a.chunks; c0 += kFinalThreads) {
-    const int c = c0 + t;
-    const uint32_t n = c < a.chunks ? a.cnt[(int64_t)b * a.chunks + c] : 0u;
-    if (n > (uint32_t)a.region) atomicOr(&sh_over, 1u);
-    scan[t] = n;
-    __syncthreads();
-    for (int off = 1; off < kFinalThreads; off <<= 1) {
-      const uint32_t v = t >= off ? scan[t - off] : 0u;
-      __syncthreads();
-      scan[t] += v;
-      __syncthreads();
-    }
-    const uint32_t base = sh_total + (t ? scan[t - 1] : 0u);
-    if (!sh_over && c < a.chunks && base + n <= (uint32_t)kCap) {
-      const uint64_t* src = a.cand + ((int64_t)b * a.chunks + c) * a.region;
-      for (uint32_t i = 0; i < n; ++i) cand[base + i] = src[i];
-    }
-    __syncthreads();
-    if (t == kFinalThreads - 1) sh_total += scan[t];
-    __syncthreads();
+  // gather: thread t owns chunks [c0, c1); a full region or more than kCap
+  // candidates in total means overflow
+  if (t == 0) sh_over = 0;
+  const bool listed = a.chunks <= kMaxChunks;               // else: streaming path
+  const int cpt = (a.chunks + kFinalThreads - 1) / kFinalThreads;
+  const int c0 = listed ? min(a.chunks, t * cpt) : 0, c1 = listed ? min(a.chunks, c0 + cpt) : 0;
+  uint32_t mine = 0;
+  bool full = !listed;
+  for (int c = c0; c < c1; ++c) {
+    const uint32_t n = a.cnt[(int64_t)b * a.chunks + c];
+    full |= n > (uint32_t)a.region;
+    mine += n > (uint32_t)a.region ? (uint32_t)a.region : n;
   }
-  const bool overflow = sh_over || sh_total > (uint32_t)kCap;
-  const int nc = overflow ? 0 : (int)sh_total;
+  __syncthreads();
+  if (full) sh_over = 1;
+  uint32_t total;
+  const uint32_t base = block_excl_scan(mine, part, &total);
+  const bool overflow = sh_over != 0 || total > (uint32_t)kCap;
+  if (!overflow) {
+    // chunk offsets in the list, then a copy spread over the whole block:
+    // list slot j belongs to the last chunk whose offset is <= j
+    uint32_t at = base;
+    for (int c = c0; c < c1; ++c) {
+      coff[c] = (uint16_t)at;
+      const uint32_t n = a.cnt[(int64_t)b * a.chunks + c];
+      at += n > (uint32_t)a.region ? (uint32_t)a.region : n;
+    }
+    if (t == 0) coff[a.chunks] = (uint16_t)total;
+    __syncthreads();
+    for (uint32_t j = t; j < total; j += kFinalThreads) {
+      int lo = 0, hi = a.chunks;                             // coff[lo] <= j < coff[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (coff[mid] <= j) lo = mid; else hi = mid;
+      }
+      cand[j] = a.cand[((int64_t)b * a.chunks + lo) * a.region + (j - coff[lo])];
+    }
+  }
+  const int nc = overflow ? 0 : (int)total;
   const T* kb = reinterpret_cast<const T*>(a.keys) + (int64_t)b * a.key_bstride;
   const T* qrow = reinterpret_cast<const T*>(a.q) + (int64_t)b * kI;
   __syncthreads();
 
-  // radix select of the k-th largest composite, most significant digit first
-  uint64_t prefix = 0, mask = 0;
-  uint32_t kk = (uint32_t)a.k;
-  int shift = 64;
-  bool done = false;
-  for (int p = 0; p < 6 && !done; ++p) {
-    const int bits = (p % 3 == 2) ? 10 : 11;                 // 11+11+10 bits per 32-bit half
-    shift -= bits;
-    const uint32_t nb = 1u << bits;
-    for (int i = t; i < 2048; i += kFinalThreads) hist[i] = 0;
+  // the k-th largest composite
+  uint64_t prefix = 0;
+  if (!overflow) {
+    uint32_t mn = 0xffffffffu, mx = 0u;
+    for (int j = t; j < nc; j += kFinalThreads) {
+      const uint32_t h = (uint32_t)(cand[j] >> 32);
+      mn = min(mn, h);
+      mx = max(mx, h);
+    }
+    uint32_t lo, hi;
+    block_minmax(mn, mx, part, &lo, &hi);
+    const uint32_t range = hi - lo;
+    const int bits = range ? 32 - __clz((int)range) : 0;   // range < 2^bits
+    const int shift = bits > kFinalBB ? bits - kFinalBB : 0;
+    for (int i = t; i < (1 << kFinalBB); i += kFinalThreads) hist[i] = 0;
+    if (t == 0) { sh_nsel = 0; sh_thr = 0; }
     __syncthreads();
-    if (!overflow) {
+    for (int j = t; j < nc; j += kFinalThreads)
+      atomicAdd(&hist[((uint32_t)(cand[j] >> 32) - lo) >> shift], 1u);
+    __syncthreads();
+    find_kth_bin(hist, 1 << kFinalBB, (uint32_t)a.k, &sh_digit, &sh_above, part);
+    const uint32_t bin = sh_digit, kk = (uint32_t)a.k - sh_above, nbin = hist[bin];
+    __syncthreads();                                         // hist is read; mem reuses it
+    if (nbin <= (uint32_t)kMem) {
+      // the bin's members; the one with exactly kk - 1 larger members is
+      // the k-th largest overall (composites are distinct)
       for (int j = t; j < nc; j += kFinalThreads) {
         const uint64_t v = cand[j];
-        if ((v & mask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & (nb - 1)], 1u);
+        if ((((uint32_t)(v >> 32) - lo) >> shift) == bin) hs.mem[atomicAdd(&sh_nsel, 1u)] = v;
       }
+      __syncthreads();
+      for (uint32_t i = t; i < nbin; i += kFinalThreads) {
+        const uint64_t v = hs.mem[i];
+        uint32_t r = 0;
+        for (uint32_t j = 0; j < nbin; ++j) r += hs.mem[j] > v;
+        if (r == kk - 1) sh_thr = v;
+      }
+      __syncthreads();
+      prefix = sh_thr;
     } else {
+      // a crowded bin: the score word by further passes, then the index
+      // word among the candidates tied on that score
+      uint32_t above;
+      const uint32_t th = block_kth_largest<kFinalBB>(
+          [&](int j, uint32_t& key) { key = (uint32_t)(cand[j] >> 32); return true; }, nc,
+          (uint32_t)a.k, lo, hi, hist, part, &sh_digit, &sh_above, &above);
+      const uint32_t kt = (uint32_t)a.k - above;             // to take among score th
+      mn = 0xffffffffu;
+      mx = 0u;
+      for (int j = t; j < nc; j += kFinalThreads) {
+        const uint64_t v = cand[j];
+        if ((uint32_t)(v >> 32) == th) {
+          mn = min(mn, (uint32_t)v);
+          mx = max(mx, (uint32_t)v);
+        }
+      }
+      block_minmax(mn, mx, part, &lo, &hi);
+      const uint32_t tl = block_kth_largest<kFinalBB>(
+          [&](int j, uint32_t& key) {
+            const uint64_t v = cand[j];
+            key = (uint32_t)v;
+            return (uint32_t)(v >> 32) == th;
+          },
+          nc, kt, lo, hi, hist, part, &sh_digit, &sh_above, &above);
+      prefix = ((uint64_t)th << 32) | tl;
+      __syncthreads();                                       // hist is read; csel reuses it
+    }
+  } else {
+    // radix select over the recomputed composites, digits of 11, 11 and 10
+    // bits per 32-bit word
+    uint64_t mask = 0;
+    uint32_t kk = (uint32_t)a.k;
+    bool done = false;
+    for (int p = 0; p < 6 && !done; ++p) {
+      const int bits = (p % 3 == 2) ? 10 : 11;
+      const int shift = 64 - 32 * (p / 3) - (p % 3 == 0 ? 11 : (p % 3 == 1 ? 22 : 32));
+      const uint32_t nb = 1u << bits;
+      for (int i = t; i < (int)nb; i += kFinalThreads) hist[i] = 0;
+      __syncthreads();
       for (int e = t; e < nv; e += kFinalThreads) {
         const float s = dot64<T>(qrow, kb + (int64_t)e * kI) * a.scale;
         const uint64_t v = composite(score_key(s), e);
         if ((v & mask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & (nb - 1)], 1u);
       }
+      __syncthreads();
+      find_kth_bin(hist, (int)nb, kk, &sh_digit, &sh_above, part);
+      kk -= sh_above;
+      const uint32_t bucket = hist[sh_digit];
+      prefix |= (uint64_t)sh_digit << shift;
+      mask |= (uint64_t)(nb - 1) << shift;
+      done = bucket == kk;               // every key in the bucket is selected
+      __syncthreads();
+    }
+  }
+  // threshold: the k-th largest composite (on overflow the lowest one of
+  // the final bucket); composites are distinct, so exactly k reach it
+  const uint64_t thr = prefix;
+  if (!overflow) {
+    // per-chunk counts of selected candidates -> output offsets; then each
+    // selected candidate goes to its chunk's offset plus its rank by index
+    // among the chunk's selected ones (chunks are ascending entry ranges)
+    uint32_t mine_sel = 0;
+    for (int c = c0; c < c1; ++c) {
+      uint32_t m = 0;
+      for (uint32_t j = coff[c]; j < coff[c + 1]; ++j) m += cand[j] >= thr;
+      hs.csel[c] = (uint16_t)m;
+      mine_sel += m;
+    }
+    uint32_t nsel;
+    uint32_t ob = block_excl_scan(mine_sel, part, &nsel);
+    for (int c = c0; c < c1; ++c) {
+      const uint32_t m = hs.csel[c];
+      hs.csel[c] = (uint16_t)ob;
+      ob += m;
     }
     __syncthreads();
-    find_digit(hist, 2048, kk, &sh_digit, &sh_above, scan);
-    // bins above 2^bits are empty, so the digit lies below nb
-    kk -= sh_above;
-    const uint32_t bucket = hist[sh_digit];
-    prefix |= (uint64_t)sh_digit << shift;
-    mask |= (uint64_t)(nb - 1) << shift;
-    done = bucket == kk;                 // every key in the bucket is selected
-    __syncthreads();
+    for (uint32_t j = t; j < total; j += kFinalThreads) {
+      const uint64_t v = cand[j];
+      if (v < thr) continue;
+      int lo = 0, hi = a.chunks;                             // chunk of slot j
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (coff[mid] <= j) lo = mid; else hi = mid;
+      }
+      uint32_t rank = 0;                                     // selected with a smaller index
+      for (uint32_t i = coff[lo]; i < coff[lo + 1]; ++i) {
+        const uint64_t w = cand[i];
+        rank += (w >= thr) && ((uint32_t)w > (uint32_t)v);  // larger low word = smaller index
+      }
+      const uint32_t o = hs.csel[lo] + rank;
+      if (o < (uint32_t)a.k) out[o] = (int32_t)(0xffffffffu - (uint32_t)v);
+    }
+    for (int j = (int)nsel + t; j < a.k; j += kFinalThreads) out[j] = -1;
+    return;
   }
-  // threshold: lowest composite in the final bucket (remaining bits zero)
-  const uint64_t thr = prefix;
+  // overflow: collect the selected indices by streaming, then sort them
   if (t == 0) sh_nsel = 0;
   __syncthreads();
-  if (!overflow) {
-    for (int j = t; j < nc; j += kFinalThreads) {
-      const uint64_t v = cand[j];
-      if (v >= thr) {
-        const uint32_t at = atomicAdd(&sh_nsel, 1u);
-        if (at < (uint32_t)kMaxK) sel[at] = (int32_t)(0xffffffffu - (uint32_t)v);
-      }
-    }
-  } else {
-    for (int e = t; e < nv; e += kFinalThreads) {
-      const float s = dot64<T>(qrow, kb + (int64_t)e * kI) * a.scale;
-      if (composite(score_key(s), e) >= thr) {
-        const uint32_t at = atomicAdd(&sh_nsel, 1u);
-        if (at < (uint32_t)kMaxK) sel[at] = e;
-      }
+  for (int e = t; e < nv; e += kFinalThreads) {
+    const float s = dot64<T>(qrow, kb + (int64_t)e * kI) * a.scale;
+    if (composite(score_key(s), e) >= thr) {
+      const uint32_t at = atomicAdd(&sh_nsel, 1u);
+      if (at < (uint32_t)kMaxK) sel[at] = e;
     }
   }
   __syncthreads();
-  // bitonic sort of the k selected indices (ascending), padded to 2^p
   int n2 = 1;
   while (n2 < a.k) n2 <<= 1;
   for (int j = a.k + t; j < n2; j += kFinalThreads) sel[j] = 0x7fffffff;

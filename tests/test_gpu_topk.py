@@ -64,6 +64,23 @@ def test_topk_exact_ties_resolve_by_index():
         np.testing.assert_array_equal(idx, np.sort(ref, axis=1))
 
 
+def test_topk_crowded_bin_in_list():
+    """Three score values only: every entry of the top score is a candidate
+    (about 6k, within the list's capacity), and the k-th one sits in a bin far
+    too crowded to rank member by member, so the select narrows it by further
+    passes and the index word."""
+    rng = np.random.default_rng(8)
+    B, N, k = 2, 20000, 1000
+    qI = np.zeros((B, 64), np.float32)
+    qI[:, 0] = 1.0
+    kI = np.zeros((N, 64), np.float32)
+    kI[:, 0] = rng.choice([0.0, 1.0, 2.0], size=N, p=[0.4, 0.3, 0.3])
+    for dt in (wl.DT_F32, wl.DT_BF16):
+        idx, s, v = _run(wl.encode(qI, dt).raw, wl.encode(kI, dt).raw, dt, k)
+        ref = oracle.topk(s, v, k)
+        np.testing.assert_array_equal(idx, np.sort(ref, axis=1))
+
+
 def test_topk_all_equal_scores_takes_lowest_indices():
     """Every score equal: the candidate list overflows and the streaming path
     must return entries 0..k-1."""
