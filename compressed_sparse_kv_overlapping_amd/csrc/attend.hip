@@ -478,17 +478,6 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
   const v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)p);
   return __builtin_bit_cast(uint2, r);
 }
-__device__ __forceinline__ unsigned lds_offset(const void* p) {
-  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-// 16 bytes per lane from src into LDS at m0 + 16 * lane (m0 wave-uniform).
-// No memory clobber: the buffer it fills is read only after the explicit
-// wait and barrier that open the next tile, so other loads (the row
-// addresses of the following copies among them) may move across it.
-__device__ __forceinline__ void dma16(const char* src, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_base) : "m0");
-}
 
 struct WideShared {
   __attribute__((aligned(16))) char kbuf[2][kTileBytes];

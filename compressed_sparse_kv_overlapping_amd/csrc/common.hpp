@@ -200,6 +200,21 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// ------------------------------------------------------------ LDS copies
+// One 16-byte copy per lane from global memory straight into LDS: lane i's
+// bytes land at lds_base + 16 i (lds_base wave-uniform).  Issued through
+// inline asm so that the compiler adds no waits of its own before LDS reads:
+// a buffer filled this way is read only after an explicit
+// "s_waitcnt vmcnt(0)" and a barrier.  No memory clobber, so other loads may
+// move across it.
+__device__ __forceinline__ unsigned lds_offset(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void dma16(const char* src, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_base) : "m0");
+}
+
 // ---------------------------------------------------------------- MFMA
 // A fragment is 8 "k-slots" per lane.  For an MxN MFMA tile (M = N = MN) the
 // lane l supplies row (A) / column (B) l % MN and the k-slots of lane group

@@ -58,33 +58,112 @@ template <> struct KeyFrag<bf16_t> { static constexpr int bytes = 2; };
 template <> struct KeyFrag<float> { static constexpr int bytes = 4; };
 template <> struct KeyFrag<e4m3_t> { static constexpr int bytes = 1; };
 
+// Maximum of two scores in one instruction: the median of (a, b, +inf),
+// which skips the quieting of signalling NaNs that the compiler puts before
+// an IEEE-mode maximum (scores of finite inputs are never NaN).  pinf holds
+// +inf in a register the compiler cannot see into, so that it keeps the
+// median instead of turning it back into a maximum.
+__device__ __forceinline__ float max_raw(float a, float b, float pinf) {
+  return __builtin_amdgcn_fmed3f(a, b, pinf);
+}
+
+// Neighbours of a float in the total order of finite values (zero steps to
+// the smallest denormal of the other side).
+__device__ __forceinline__ float next_up(float x) {
+  if (x != x || x == INFINITY) return x;
+  if (x == 0.f) return __uint_as_float(1u);
+  const uint32_t u = __float_as_uint(x);
+  return __uint_as_float(x > 0.f ? u + 1u : u - 1u);
+}
+__device__ __forceinline__ float next_down(float x) { return -next_up(-x); }
+
+// The smallest raw dot product S with fl(S * scale) >= t (scale > 0): the
+// product is monotone in S, so S >= this bound exactly when the scaled score
+// reaches t.  Starts from fl(t / scale), within an ulp or two of the bound;
+// if the search does not settle (only for absurd scales) every score
+// qualifies, which is still exact (the final select sorts it out).
+__device__ float raw_threshold(float t, float scale) {
+  if (t == -INFINITY) return -INFINITY;
+  float s = t / scale;
+  for (int i = 0; i < 8 && !(s * scale >= t); ++i) s = next_up(s);
+  for (int i = 0; i < 8; ++i) {
+    const float p = next_down(s);
+    if (p * scale >= t) s = p; else break;
+  }
+  const bool ok = s * scale >= t && !(next_down(s) * scale >= t);
+  return ok ? s : -INFINITY;
+}
+
+// Key rows staged in LDS for the many-query score passes: 16 KB stages of
+// whole 64-dim rows (kRow bytes each), the 16-byte chunks of row r stored at
+// chunk c ^ swz(r).  16 consecutive rows then put a lane group's fragment
+// reads on distinct banks (rows per 256 bytes: 4 fp8, 2 bf16, 1 fp32).
+template <class T> struct KeyTiles {
+  static constexpr int kRow = 64 * (int)sizeof(T);
+  static constexpr int kChunks = kRow / 16;
+  static constexpr int kRowsPer256 = 256 / kRow;
+  static constexpr int kStage = 16384;
+  static constexpr int kTiles = kStage / (16 * kRow);        // 16-row tiles per stage
+  static __device__ __forceinline__ int swz(int r) { return (r / kRowsPer256) % kChunks; }
+  // the 8-element fragment at byte offset off of a staged row
+  static __device__ __forceinline__ void load(Frag<T>& f, const char* row, int off, int sw);
+};
+template <> __device__ __forceinline__ void KeyTiles<e4m3_t>::load(Frag<e4m3_t>& f, const char* row,
+                                                                   int off, int sw) {
+  f.v = *reinterpret_cast<const uint64_t*>(row + 16 * ((off >> 4) ^ sw) + (off & 15));
+}
+template <> __device__ __forceinline__ void KeyTiles<bf16_t>::load(Frag<bf16_t>& f, const char* row,
+                                                                   int off, int sw) {
+  f.v = *reinterpret_cast<const u32x4*>(row + 16 * ((off >> 4) ^ sw));
+}
+template <> __device__ __forceinline__ void KeyTiles<float>::load(Frag<float>& f, const char* row,
+                                                                  int off, int sw) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(row + 16 * ((off >> 4) ^ sw));
+  const u32x4 b = *reinterpret_cast<const u32x4*>(row + 16 * (((off >> 4) + 1) ^ sw));
+  f.v[0] = __uint_as_float(a.x); f.v[1] = __uint_as_float(a.y);
+  f.v[2] = __uint_as_float(a.z); f.v[3] = __uint_as_float(a.w);
+  f.v[4] = __uint_as_float(b.x); f.v[5] = __uint_as_float(b.y);
+  f.v[6] = __uint_as_float(b.z); f.v[7] = __uint_as_float(b.w);
+}
+
 // MODE 0: group maxima.  MODE 1: collect candidates >= threshold into this
 // chunk's region of each query (counted in LDS, no global atomics).
-template <class T, int NQB, int MODE>
+//
+// WQ = 1: the block's waves share 16*NQB queries and split the chunk's
+// entries.  WQ = 4: each wave owns 16*NQB queries of its own and all four
+// stream the same entry tiles (read once from L2 per block, then hit in L1),
+// which divides the key traffic of many-query launches by four.
+//
+// Tiles that every query of the wave sees entirely take a fast epilogue: a
+// running maximum (MODE 0), or one comparison of the raw MFMA score against
+// the threshold divided by the scale (MODE 1).
+template <class T, int NQB, int MODE, int WQ>
 __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
-  __shared__ uint32_t lcnt[16 * NQB];
+  __shared__ uint32_t lcnt[WQ * 16 * NQB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int qw = WQ == 4 ? wave : 0;                         // this wave's query set
   if (MODE == 1) {
-    if (threadIdx.x < 16 * NQB) lcnt[threadIdx.x] = 0;
+    if (threadIdx.x < WQ * 16 * NQB) lcnt[threadIdx.x] = 0;
     __syncthreads();
   }
   const int col = lane & 15, g = lane >> 4;
-  const int q0 = blockIdx.y * a.qpb;
+  const int q0 = blockIdx.y * a.qpb + qw * 16 * NQB;
   const T* qbase = reinterpret_cast<const T*>(a.q);
   const T* kbase = reinterpret_cast<const T*>(a.keys) + (int64_t)q0 * a.key_bstride;
 
   // this lane's queries (one per 16-column block) and their query fragments
   Frag<T> qf[NQB][2];
   int qb[NQB], nvis[NQB];
-  float tscore[NQB];
-  int blk_vis = 0;
+  float tscore[NQB], traw[NQB];
+  int blk_vis = 0, min_vis = 0x7fffffff;
 #pragma unroll
   for (int j = 0; j < NQB; ++j) {
     const int c = 16 * j + col;
-    const bool ok = c < a.qpb && q0 + c < a.B;
+    const bool ok = (WQ == 4 || c < a.qpb) && q0 + c < a.B;
     qb[j] = ok ? q0 + c : -1;
     nvis[j] = ok ? n_visible(a, q0 + c) : 0;
     blk_vis = max(blk_vis, nvis[j]);
+    min_vis = min(min_vis, ok ? nvis[j] : 0x7fffffff);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       if (ok) {
@@ -96,49 +175,81 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
     }
     tscore[j] = -INFINITY;                                       // threshold 0: take all
     if (MODE == 1 && ok && a.thr[q0 + c] != 0u) tscore[j] = key_score(a.thr[q0 + c]);
+    traw[j] = MODE == 1 && ok ? raw_threshold(tscore[j], a.scale) : INFINITY;   // absent: none
   }
-  // the largest visible prefix over the block's queries bounds the tiles
-  for (int off = 32; off >= 1; off >>= 1) blk_vis = max(blk_vis, __shfl_xor(blk_vis, off, 64));
+  // the largest visible prefix over the wave's queries bounds the tiles; up
+  // to the smallest one every tile is fully visible
+  for (int off = 32; off >= 1; off >>= 1) {
+    blk_vis = max(blk_vis, __shfl_xor(blk_vis, off, 64));
+    min_vis = min(min_vis, __shfl_xor(min_vis, off, 64));
+  }
 
   // group maxima are written for every group (0 when nothing is visible);
   // candidates are only looked for in the visible prefix
-  const int e_w0 = (blockIdx.x * 4 + wave) * a.tiles_per_wave * 16;
+  const int e_w0 = (WQ == 4 ? blockIdx.x : blockIdx.x * 4 + wave) * a.tiles_per_wave * 16;
   const int e_w1 = min(e_w0 + a.tiles_per_wave * 16, MODE == 0 ? a.G * a.GS : blk_vis);
-  float gm[NQB][4];
+  float pinf = INFINITY;
+  asm volatile("" : "+v"(pinf));
+  // running group maximum of this lane's query per 16-column block (a lane's
+  // four entries of a tile always lie in one group: GS >= 4)
+  float gm[NQB];
 #pragma unroll
-  for (int j = 0; j < NQB; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) gm[j][i] = -INFINITY;
+  for (int j = 0; j < NQB; ++j) gm[j] = -INFINITY;
 
-  for (int et = e_w0; et < e_w1; et += 16) {
+  // group maxima (GS >= 16): lane g keeps the maximum of group 4n + g, and
+  // every fourth group (or the range's last) the lanes write the 16 bytes of
+  // up to four consecutive groups of their query at once
+  float held[NQB];
+  const int grp_first = e_w0 / a.GS, grp_last = (e_w1 - 1) / a.GS;
+  auto tile = [&](const int et, const Frag<T>* kf) {
    if (et < blk_vis) {                                         // skip invisible tiles
-    Frag<T> kf[2];
-    const int er = et + col;                                   // A row of this lane
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (er < a.N) {
-        frag_load(kf[ks], kbase + (int64_t)er * kI + 32 * ks + 8 * g);
-      } else {
-        Frag<T> z{};
-        kf[ks] = z;
-      }
-    }
+    f32x4 S[NQB];
 #pragma unroll
     for (int j = 0; j < NQB; ++j) {
-      f32x4 S = {0.f, 0.f, 0.f, 0.f};
-      mma16(S, kf[0], qf[j][0]);
-      mma16(S, kf[1], qf[j][1]);
-      // S[i]: query qb[j], entry et + 4g + i
+      S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma16(S[j], kf[0], qf[j][0]);
+      mma16(S[j], kf[1], qf[j][1]);
+    }
+    // S[j][i]: query qb[j], entry et + 4g + i
+    if (et + 16 <= min_vis) {
+      if (MODE == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = et + 4 * g + i;
-        const bool vis = e < nvis[j];
-        if (MODE == 0) {
-          gm[j][i] = fmaxf(gm[j][i], vis ? S[i] : -INFINITY);
-        } else if (vis) {
-          const float s = S[i] * a.scale;
-          if (s >= tscore[j]) {
-            const uint32_t slot = atomicAdd(&lcnt[16 * j + col], 1u);
+        for (int j = 0; j < NQB; ++j)
+          gm[j] = max_raw(max_raw(gm[j], max_raw(S[j][0], S[j][1], pinf), pinf),
+                          max_raw(S[j][2], S[j][3], pinf), pinf);
+      } else {
+        bool hit = false;
+#pragma unroll
+        for (int j = 0; j < NQB; ++j)
+          hit |= max_raw(max_raw(S[j][0], S[j][1], pinf), max_raw(S[j][2], S[j][3], pinf), pinf) >= traw[j];
+        if (__any(hit)) {
+#pragma unroll
+          for (int j = 0; j < NQB; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (S[j][i] >= traw[j] && qb[j] >= 0) {
+                const int e = et + 4 * g + i;
+                const float s = S[j][i] * a.scale;
+                const uint32_t slot = atomicAdd(&lcnt[qw * 16 * NQB + 16 * j + col], 1u);
+                if (slot < (uint32_t)a.region)
+                  a.cand[((int64_t)qb[j] * a.chunks + blockIdx.x) * a.region + slot] =
+                      ((uint64_t)score_key(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+              }
+            }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NQB; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = et + 4 * g + i;
+          const bool vis = e < nvis[j];
+          if (MODE == 0) {
+            gm[j] = fmaxf(gm[j], vis ? S[j][i] : -INFINITY);
+          } else if (vis && S[j][i] >= traw[j]) {
+            const float s = S[j][i] * a.scale;
+            const uint32_t slot = atomicAdd(&lcnt[qw * 16 * NQB + 16 * j + col], 1u);
             if (slot < (uint32_t)a.region)
               a.cand[((int64_t)qb[j] * a.chunks + blockIdx.x) * a.region + slot] =
                   ((uint64_t)score_key(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
@@ -153,35 +264,119 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
       if (GS <= 8 || ((et + 16) % GS) == 0) {
 #pragma unroll
         for (int j = 0; j < NQB; ++j) {
-          float v = fmaxf(fmaxf(gm[j][0], gm[j][1]), fmaxf(gm[j][2], gm[j][3]));
-          int grp;
-          bool writer;
-          if (GS == 4) {
-            grp = (et + 4 * g) / 4;
-            writer = true;
-          } else if (GS == 8) {
-            v = fmaxf(v, shfl_xor(v, 16));
-            grp = (et + 8 * (g >> 1)) / 8;
-            writer = (g & 1) == 0;
+          float v = gm[j];
+          if (GS <= 8) {
+            int grp;
+            bool writer;
+            if (GS == 4) {
+              grp = (et + 4 * g) / 4;
+              writer = true;
+            } else {
+              v = fmaxf(v, shfl_xor(v, 16));
+              grp = (et + 8 * (g >> 1)) / 8;
+              writer = (g & 1) == 0;
+            }
+            if (writer && qb[j] >= 0 && grp < a.G)
+              a.gmax[(int64_t)qb[j] * a.G + grp] = (v == -INFINITY) ? 0u : score_key(v * a.scale);
           } else {
             v = fmaxf(v, shfl_xor(v, 16));
             v = fmaxf(v, shfl_xor(v, 32));
-            grp = et / GS;
-            writer = g == 0;
+            const int grp = et / GS;
+            if (g == (grp & 3)) held[j] = v;
+            if ((grp & 3) == 3 || grp == grp_last) {
+              const int gw = (grp & ~3) + g;                   // this lane's group
+              if (gw >= grp_first && gw <= grp && qb[j] >= 0 && gw < a.G)
+                a.gmax[(int64_t)qb[j] * a.G + gw] =
+                    (held[j] == -INFINITY) ? 0u : score_key(held[j] * a.scale);
+            }
           }
-          if (writer && qb[j] >= 0 && grp < a.G)
-            a.gmax[(int64_t)qb[j] * a.G + grp] = (v == -INFINITY) ? 0u : score_key(v * a.scale);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) gm[j][i] = -INFINITY;
+          gm[j] = -INFINITY;
         }
+      }
+    }
+  };
+
+  if constexpr (WQ == 1) {
+    // key fragments of the next PF - 1 tiles are in flight while a tile is
+    // computed (register ring, the loop unrolled by PF so slots are fixed)
+    constexpr int PF = 4;
+    Frag<T> kr[PF][2];
+    auto load_tile = [&](const int et, Frag<T>* kf) {
+      const int er = et + col;                                 // A row of this lane
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (et < e_w1 && et < blk_vis && er < a.N) {
+          frag_load(kf[ks], kbase + (int64_t)er * kI + 32 * ks + 8 * g);
+        } else {
+          Frag<T> z{};
+          kf[ks] = z;
+        }
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < PF - 1; ++p) load_tile(e_w0 + 16 * p, kr[p]);
+    for (int et = e_w0; et < e_w1; et += 16 * PF) {
+      load_tile(et + 48, kr[3]);
+      tile(et, kr[0]);
+      if (et + 16 >= e_w1) break;
+      load_tile(et + 64, kr[0]);
+      tile(et + 16, kr[1]);
+      if (et + 32 >= e_w1) break;
+      load_tile(et + 80, kr[1]);
+      tile(et + 32, kr[2]);
+      if (et + 48 >= e_w1) break;
+      load_tile(et + 96, kr[2]);
+      tile(et + 48, kr[3]);
+    }
+  } else {
+    // The block's key rows pass through LDS in stages of 16 KB, copied by
+    // all four waves straight from global memory while the previous stage is
+    // computed.  Rows are kept whole with their 16-byte chunks XOR-swizzled
+    // by row, so the fragment reads of 16 consecutive rows hit distinct banks.
+    using KT = KeyTiles<T>;
+    __shared__ __attribute__((aligned(16))) char kst[2][KT::kStage];
+    __shared__ int sh_end[4];
+    if (lane == 0) sh_end[wave] = e_w1;
+    __syncthreads();
+    const int e_b1 = max(max(sh_end[0], sh_end[1]), max(sh_end[2], sh_end[3]));
+    const int nst = e_b1 > e_w0 ? (e_b1 - e_w0 + 16 * KT::kTiles - 1) / (16 * KT::kTiles) : 0;
+    const char* keys = reinterpret_cast<const char*>(a.keys);
+    auto issue = [&](const int st) {
+      char* buf = kst[st & 1];
+#pragma unroll
+      for (int n = 0; n < KT::kStage / 4096; ++n) {
+        const int pos = (n * 4 + wave) * 1024 + lane * 16;     // byte in the stage
+        const int r = pos / KT::kRow, c = (pos % KT::kRow) / 16;
+        int row = e_w0 + st * 16 * KT::kTiles + r;
+        row = row < a.N ? row : a.N - 1;
+        const char* src = keys + (int64_t)row * KT::kRow + 16 * (c ^ KT::swz(r));
+        dma16(src, (unsigned)__builtin_amdgcn_readfirstlane(lds_offset(buf + (n * 4 + wave) * 1024)));
+      }
+    };
+    if (nst > 0) issue(0);
+    const int swz = KT::swz(col);
+    for (int st = 0; st < nst; ++st) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();                                         // stage st landed; st - 1 read
+      if (st + 1 < nst) issue(st + 1);
+      const char* buf = kst[st & 1];
+      for (int t = 0; t < KT::kTiles; ++t) {
+        const int et = e_w0 + (st * KT::kTiles + t) * 16;
+        if (et >= e_w1) break;
+        Frag<T> kf[2];
+        const char* rowp = buf + (t * 16 + col) * KT::kRow;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) KT::load(kf[ks], rowp, (32 * ks + 8 * g) * (int)sizeof(T), swz);
+        tile(et, kf);
       }
     }
   }
   if (MODE == 1) {
     __syncthreads();
-    if (threadIdx.x < 16 * NQB) {
+    if (threadIdx.x < WQ * 16 * NQB) {
       const int c = threadIdx.x;
-      if (c < a.qpb && q0 + c < a.B) a.cnt[(int64_t)(q0 + c) * a.chunks + blockIdx.x] = lcnt[c];
+      const int q = blockIdx.y * a.qpb + c;
+      if ((WQ == 4 || c < a.qpb) && q < a.B) a.cnt[(int64_t)q * a.chunks + blockIdx.x] = lcnt[c];
     }
   }
 }
@@ -608,26 +803,33 @@ int topk_group_size(int64_t N, int k) {
 }
 
 // Launch geometry of the score passes, shared by the workspace query and the
-// launcher: entry chunks of tiles_per_wave * 64 entries (4 waves x 16-entry
-// tiles), and the candidate region of each (query, chunk).
-struct TopkGeom { int GS, G, qpb, nqb, qblocks, tpw, chunks, region; };
+// launcher: entry chunks of tiles_per_wave 16-entry tiles per wave (times 4
+// when the waves split the chunk), and the candidate region of each (query,
+// chunk).
+struct TopkGeom { int GS, G, qpb, nqb, wq, qblocks, tpw, chunks, region; };
 
 static TopkGeom topk_geom(int64_t B, int64_t N, int k, bool per_seq) {
   TopkGeom g;
   g.GS = topk_group_size(N, k);
   g.G = (int)((N + g.GS - 1) / g.GS);
   g.nqb = per_seq ? 1 : (B <= 16 ? 1 : (B <= 32 ? 2 : 4));
-  g.qpb = per_seq ? 1 : 16 * g.nqb;
+  // many queries: the four waves of a block take a query set each and share
+  // the entry tiles; otherwise they share the queries and split the entries
+  g.wq = (!per_seq && B >= 1024) ? 4 : 1;
+  g.qpb = per_seq ? 1 : 16 * g.nqb * g.wq;
   g.qblocks = (int)((B + g.qpb - 1) / g.qpb);
   const int min_tpw = g.GS >= 16 ? g.GS / 16 : 1;
-  g.tpw = 64;
-  while (g.tpw > min_tpw && (int64_t)g.qblocks * ((N + g.tpw * 64 - 1) / (g.tpw * 64)) < 1024) g.tpw /= 2;
-  g.chunks = (int)((N + g.tpw * 64 - 1) / (g.tpw * 64));
+  const int wsplit = g.wq == 4 ? 1 : 4;                      // waves splitting a chunk
+  g.tpw = g.wq == 4 ? 256 : 64;
+  while (g.tpw > min_tpw &&
+         (int64_t)g.qblocks * ((N + (int64_t)g.tpw * 16 * wsplit - 1) / ((int64_t)g.tpw * 16 * wsplit)) < 1024)
+    g.tpw /= 2;
+  g.chunks = (int)((N + (int64_t)g.tpw * 16 * wsplit - 1) / ((int64_t)g.tpw * 16 * wsplit));
   // about 1.2k candidates per query are expected; give each chunk room for
   // 16x its share (at least 32 slots), capped by the chunk size
   int64_t r = (16 * (int64_t)k + g.chunks - 1) / g.chunks;
   r = r < 32 ? 32 : r;
-  const int64_t csize = (int64_t)g.tpw * 64;
+  const int64_t csize = (int64_t)g.tpw * 16 * wsplit;
   g.region = (int)(r > csize ? csize : r);
   return g;
 }
@@ -665,11 +867,17 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
   a.cnt = (uint32_t*)w;
   const int nqb = g.nqb, qblocks = g.qblocks, chunks = g.chunks;
   dim3 grid(chunks, qblocks);
-#define CSKV_SCORE(NQB, MODE) \
-  hipLaunchKernelGGL((idx_score_kernel<T, NQB, MODE>), grid, dim3(256), 0, stream, a)
-  if (nqb == 1) CSKV_SCORE(1, 0); else if (nqb == 2) CSKV_SCORE(2, 0); else CSKV_SCORE(4, 0);
+#define CSKV_SCORE(NQB, MODE, WQ) \
+  hipLaunchKernelGGL((idx_score_kernel<T, NQB, MODE, WQ>), grid, dim3(256), 0, stream, a)
+#define CSKV_SCORE_PASS(MODE)                                                  \
+  if (g.wq == 4) CSKV_SCORE(4, MODE, 4);                                       \
+  else if (nqb == 1) CSKV_SCORE(1, MODE, 1);                                   \
+  else if (nqb == 2) CSKV_SCORE(2, MODE, 1);                                   \
+  else CSKV_SCORE(4, MODE, 1)
+  CSKV_SCORE_PASS(0);
   hipLaunchKernelGGL(idx_threshold_kernel, dim3((unsigned)p.B), dim3(256), 0, stream, a);
-  if (nqb == 1) CSKV_SCORE(1, 1); else if (nqb == 2) CSKV_SCORE(2, 1); else CSKV_SCORE(4, 1);
+  CSKV_SCORE_PASS(1);
+#undef CSKV_SCORE_PASS
 #undef CSKV_SCORE
   hipLaunchKernelGGL(idx_final_kernel<T>, dim3((unsigned)p.B), dim3(kFinalThreads), 0, stream, a);
   return hipGetLastError();

@@ -37,6 +37,27 @@ def test_topk_matches_oracle(dt, B, N, k):
     assert exact >= B - 1          # near-ties inside the band are rare for random scores
 
 
+@pytest.mark.parametrize("dt", [wl.DT_F32, wl.DT_BF16, wl.DT_E4M3])
+def test_topk_many_queries(dt):
+    """1,536 queries: the score passes give each wave its own query set and
+    share the entry tiles; a causal mask leaves some tiles partly visible."""
+    rng_cfg = 94
+    B, N, k, m = 1536, 6000, 256, 4
+    q = wl.normal(rng_cfg, 0, 1, (B, 64))
+    kk = wl.normal(rng_cfg, 0, 2, (N, 64))
+    pos = np.random.default_rng(3).integers(0, N * m, B)
+    pos[:4] = [0, 3, 4, N * m - 1]
+    if dt == wl.DT_E4M3:
+        sq, sk = wl.e4m3_scale(q), wl.e4m3_scale(kk)
+        qI, kI, scale = wl.e4m3_encode(q, sq), wl.e4m3_encode(kk, sk), sq * sk
+    else:
+        qI, kI, scale = wl.encode(q, dt).raw, wl.encode(kk, dt).raw, 0.37
+    idx, s, v = _run(qI, kI, dt, k, scale=scale, q_pos=pos, m=m)
+    check_selection(idx, s, v, k)
+    idx, s, v = _run(qI, kI, dt, k, scale=scale)
+    check_selection(idx, s, v, k)
+
+
 def test_topk_workload_sizes():
     """The decode selections of the workloads: top-64 of 1,024 (fp32),
     top-1024 of 16,384 (bf16, 8 queries) and of 262,144 (bf16, 32 queries)."""
