@@ -95,7 +95,7 @@ def main():
     ws_topk = torch.empty(cskv.index_topk_workspace_size(B, N4, k), dtype=torch.uint8, device="cuda")
     ws_csa = torch.empty(max(1, cskv.attend_workspace_size(B, H, k + W)), dtype=torch.uint8, device="cuda")
     ws_hca = torch.empty(max(1, cskv.hca_workspace_size(B, H, N128)), dtype=torch.uint8, device="cuda")
-    ws_c = torch.empty(cskv.compress2_workspace_size(cfg.m_hca), dtype=torch.uint8, device="cuda")
+    ws_c = torch.empty(cskv.compress2_workspace_size(T, cfg.m_hca), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     gen_s = time.time() - t_gen
 

@@ -34,7 +34,7 @@ _SIGS = {
     "cskv_last_error": ([], ctypes.c_char_p),
     "cskv_compress": ([_vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp, _i64, ctypes.c_int, _vp],
                       ctypes.c_int),
-    "cskv_compress2_workspace_size": ([_i32], _sz),
+    "cskv_compress2_workspace_size": ([_i64, _i32], _sz),
     "cskv_compress2": ([_vp, _vp, _i64, _vp, _i32, _vp, _i64, _vp, _i32, _vp, _i64, ctypes.c_int,
                         _vp, _sz, _vp], ctypes.c_int),
     "cskv_index_topk_workspace_size": ([_i64, _i64, _i32], _sz),
@@ -129,8 +129,8 @@ def compress(x, z, bias, m, out=None, entry_begin=0, entry_end=None, stream=None
     return out
 
 
-def compress2_workspace_size(m_large):
-    return library().cskv_compress2_workspace_size(m_large)
+def compress2_workspace_size(T, m_large):
+    return library().cskv_compress2_workspace_size(T, m_large)
 
 
 def compress2(x, z, bias_small, m_small, bias_large, m_large, out_small=None, out_large=None,
@@ -150,7 +150,7 @@ def compress2(x, z, bias_small, m_small, bias_large, m_large, out_small=None, ou
     if x.dtype != z.dtype or bias_small.dtype != torch.float32 or bias_large.dtype != torch.float32:
         raise ValueError("x and z must share a dtype; biases must be fp32")
     if workspace is None:
-        workspace = _workspace(compress2_workspace_size(m_large), x.device)
+        workspace = _workspace(compress2_workspace_size(T, m_large), x.device)
     _call("cskv_compress2", _ptr(x), _ptr(z), T, _ptr(bias_small), m_small, _ptr(out_small),
           out_small.stride(0), _ptr(bias_large), m_large, _ptr(out_large), out_large.stride(0),
           _dt(x), _ptr(workspace), workspace.numel(), _stream(stream))

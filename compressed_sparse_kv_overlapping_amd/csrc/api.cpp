@@ -80,9 +80,9 @@ int cskv_compress(const void* raw_kv, const void* score_logits, const float* pos
                     "cskv_compress");
 }
 
-size_t cskv_compress2_workspace_size(int32_t m_large) {
-  if (m_large < 1 || m_large > 65536) return 0;
-  return cskv::compress_fused_workspace_bytes(m_large);
+size_t cskv_compress2_workspace_size(int64_t T, int32_t m_large) {
+  if (T < 0 || m_large < 1 || m_large > 65536) return 0;
+  return cskv::compress_fused_workspace_bytes(T, m_large);
 }
 
 int cskv_compress2(const void* raw_kv, const void* score_logits, int64_t T,
@@ -110,7 +110,7 @@ int cskv_compress2(const void* raw_kv, const void* score_logits, int64_t T,
   if (!aligned16(raw_kv) || !aligned16(score_logits) || !aligned16(bias_small) ||
       !aligned16(out_small) || (large && (!aligned16(bias_large) || !aligned16(out_large))))
     return fail(CSKV_ERR_INVALID_ARG, "cskv_compress2: tensors must be 16-byte aligned");
-  const size_t need = cskv::compress_fused_workspace_bytes(m_large);
+  const size_t need = cskv::compress_fused_workspace_bytes(T, m_large);
   if (!workspace || ws_bytes < need || !aligned16(workspace))
     return fail(CSKV_ERR_WORKSPACE, "cskv_compress2: workspace %zu bytes, need %zu", ws_bytes, need);
   return hip_status(cskv::launch_compress_fused((int)dt, raw_kv, score_logits, T, bias_small, m_small,

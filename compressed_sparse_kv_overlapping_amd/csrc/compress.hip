@@ -464,6 +464,16 @@ static hipError_t launch_large_t(const void* x, const void* z, const float* bias
 // by 2^(r - rl) with rl the large block's raise-only reference.  Wave ranges
 // hand their carried halves to the next wave through LDS as in the large
 // compressor.
+// One entry from its two half-window sums, each with its own reference
+// (log2 domain): both are brought to the larger reference.
+__device__ __forceinline__ float join_halves(float pS, float pA, float pr, float sS, float sA, float sr) {
+  const float mx = fmaxf(pr, sr);
+  const float fp = __builtin_amdgcn_exp2f(pr - mx), fc = __builtin_amdgcn_exp2f(sr - mx);
+  return (pA * fp + sA * fc) * __builtin_amdgcn_rcpf(pS * fp + sS * fc);
+}
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_elem(bf16_t* p, float v) { p->u = (uint16_t)f32_to_bf16(v); }
+
 constexpr int kFusedWaves = 4;
 #ifndef CSKV_FUSED_EPW
 #define CSKV_FUSED_EPW 4
@@ -498,7 +508,7 @@ template <class T, int MS, int DPL>
 __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
     const T* __restrict__ x, const T* __restrict__ z, const float* __restrict__ bias_s,
     const float* __restrict__ beta_l, int R, int64_t NL, int epw, T* __restrict__ out_s,
-    int64_t ld_s, T* __restrict__ out_l, int64_t ld_l) {
+    int64_t ld_s, T* __restrict__ out_l, int64_t ld_l, float* __restrict__ bnd) {
   constexpr int kSlices = kD / (64 * DPL);
   constexpr int kSW = 64 * DPL;                   // dims of this block's slice
   const int ML = R * MS;
@@ -510,21 +520,23 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
   const int dl = lane * DPL;                      // dim within the slice
   const int d0 = slice * kSW + dl;
   const float L2E = 1.4426950408889634f;
-  // large entries of this wave: [E0, E1); wave 0 also streams E0-1 (the block halo)
-  const int64_t g0 = group * ((int64_t)kFusedWaves * epw - 1);
-  const int64_t E0 = wave == 0 ? g0 : g0 + (int64_t)wave * epw - 1;
-  const int64_t E1r = g0 + (int64_t)(wave + 1) * epw - 1;
-  const int64_t E1 = E1r < NL ? E1r : NL;
-  const int64_t LB0 = (wave == 0) ? E0 - 1 : E0;  // first large block streamed (-1: none)
+  // large entries of this wave: [E0, E1), streamed as large blocks from E0
+  const int64_t E0 = (group * kFusedWaves + wave) * (int64_t)epw;
+  const int64_t E1 = E0 + epw < NL ? E0 + epw : NL;
+  const int64_t LB0 = E0;                         // first large block streamed
   const int nblocks = epw;                        // large blocks streamed by every wave
+  // the first entries of a range wait for the previous range's carried
+  // halves: through LDS inside the block, through the workspace (and the
+  // join kernel) across blocks; entry 0 has no first half
+  const bool deferred = wave > 0 || group > 0;
   const int64_t NS = NL * R;                      // small entries
   const int64_t S0 = E0 * R, S1 = E1 * R;         // small entries written by this wave
 
   __shared__ __attribute__((aligned(16))) float bs_lds[2 * MS][kSW];
   __shared__ __attribute__((aligned(16))) float bl_lds[2][2 * MS][kSW];
   __shared__ float xch[kFusedWaves][6][kSW];
-  // second halves of a wave's first small and large entries (waves > 0),
-  // completed with the previous wave's carried halves at the end
+  // second halves of a wave's first small and large entries (all but the
+  // very first range), completed with the previous range's carried halves
   __shared__ float dfr[kFusedWaves][6][kSW];
   for (int i = threadIdx.x; i < 2 * MS * kSW; i += 64 * kFusedWaves) {
     const int p = i / kSW, d = i % kSW;
@@ -570,9 +582,6 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
     rl[d] = -INFINITY; lcS[d] = lcA[d] = lcr[d] = 0.f;
     lsA[d] = laA[d] = lsB[d] = laB[d] = 0.f;
   }
-  // Every wave streams nblocks large blocks from LB0 (which is -1 for the
-  // very first wave: that virtual block re-reads block 0, stores nothing, and
-  // its carried halves are discarded because entry 0 has no first half).
   const int64_t sbegin = LB0 * R;                            // first small block streamed
   const int nsteps = nblocks * R;
   const int64_t sb_last = NS - 1;                            // last small block inside NL large blocks
@@ -693,7 +702,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
         const float fb = (first || dl < 0.f) ? 1.f : g;
         o[d] = (cA[d] * fc + aB[d] * fb) * __builtin_amdgcn_rcpf(cS[d] * fc + sB[d] * fb);
       }
-      const bool defer = wave > 0 && sb == S0;           // first half comes from wave-1
+      const bool defer = deferred && sb == S0;            // first half comes from the previous range
       if (defer) {
 #pragma unroll
         for (int d = 0; d < DPL; ++d) {
@@ -726,7 +735,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
         const float fb = __builtin_amdgcn_exp2f(rl[d] - mx);
         o[d] = (lcA[d] * fc + laB[d] * fb) * __builtin_amdgcn_rcpf(lcS[d] * fc + lsB[d] * fb);
       }
-      const bool defer = wave > 0 && lb == E0;
+      const bool defer = deferred && lb == E0;
       if (defer) {
 #pragma unroll
         for (int d = 0; d < DPL; ++d) {
@@ -744,7 +753,9 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
       }
     }
   }
-  // hand both carried first halves (and the reference) to the next wave
+  // hand both carried first halves (and the references) to the next wave;
+  // the last wave's go to the workspace for the next block's first wave,
+  // which leaves its deferred halves there too
 #pragma unroll
   for (int d = 0; d < DPL; ++d) {
     xch[wave][0][dl + d] = cS[d];
@@ -754,28 +765,59 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
     xch[wave][4][dl + d] = cr[d];
     xch[wave][5][dl + d] = lcr[d];
   }
+  float* bg = bnd + group * (int64_t)(12 * kD);
+  if (wave == kFusedWaves - 1) {
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) {
+      bg[0 * kD + d0 + d] = cS[d];
+      bg[1 * kD + d0 + d] = cA[d];
+      bg[2 * kD + d0 + d] = cr[d];
+      bg[3 * kD + d0 + d] = lcS[d];
+      bg[4 * kD + d0 + d] = lcA[d];
+      bg[5 * kD + d0 + d] = lcr[d];
+    }
+  }
+  if (wave == 0 && group > 0) {
+#pragma unroll
+    for (int d = 0; d < DPL; ++d)
+#pragma unroll
+      for (int f = 0; f < 6; ++f) bg[(6 + f) * kD + d0 + d] = dfr[0][f][dl + d];
+  }
   __syncthreads();
   if (wave > 0) {
     float os[DPL], ol[DPL];
 #pragma unroll
     for (int d = 0; d < DPL; ++d) {
-      const float fS = dfr[wave][0][dl + d], fA = dfr[wave][1][dl + d], fr = dfr[wave][2][dl + d];
-      const float gS = dfr[wave][3][dl + d], gA = dfr[wave][4][dl + d], gr = dfr[wave][5][dl + d];
-      const float pr = xch[wave - 1][4][dl + d];
-      float mx = fmaxf(pr, fr);
-      float fp = __builtin_amdgcn_exp2f(pr - mx), fc = __builtin_amdgcn_exp2f(fr - mx);
-      os[d] = (xch[wave - 1][1][dl + d] * fp + fA * fc) *
-              __builtin_amdgcn_rcpf(xch[wave - 1][0][dl + d] * fp + fS * fc);
-      const float plr = xch[wave - 1][5][dl + d];
-      mx = fmaxf(plr, gr);
-      fp = __builtin_amdgcn_exp2f(plr - mx);
-      fc = __builtin_amdgcn_exp2f(gr - mx);
-      ol[d] = (xch[wave - 1][3][dl + d] * fp + gA * fc) *
-              __builtin_amdgcn_rcpf(xch[wave - 1][2][dl + d] * fp + gS * fc);
+      os[d] = join_halves(xch[wave - 1][0][dl + d], xch[wave - 1][1][dl + d], xch[wave - 1][4][dl + d],
+                          dfr[wave][0][dl + d], dfr[wave][1][dl + d], dfr[wave][2][dl + d]);
+      ol[d] = join_halves(xch[wave - 1][2][dl + d], xch[wave - 1][3][dl + d], xch[wave - 1][5][dl + d],
+                          dfr[wave][3][dl + d], dfr[wave][4][dl + d], dfr[wave][5][dl + d]);
     }
     BufStoreN<T, DPL>::store(rsrc_s, S0 < S1 ? (uint32_t)(d0 * sizeof(T)) : 0xffffffffu, os);
     BufStoreN<T, DPL>::store(rsrc_l, E0 < E1 ? (uint32_t)(d0 * sizeof(T)) : 0xffffffffu, ol);
   }
+}
+
+// The first small and large entries of every block but the first: the
+// previous block's carried first halves joined with this block's deferred
+// second halves (both in the workspace).  One thread per dimension.
+template <class T>
+__global__ __launch_bounds__(256) void compress_join_kernel(const float* __restrict__ bnd, int64_t groups,
+                                                            int per, int R, int64_t NL,
+                                                            T* __restrict__ out_s, int64_t ld_s,
+                                                            T* __restrict__ out_l, int64_t ld_l) {
+  const int64_t g = 1 + blockIdx.x / (kD / 256);
+  const int d = (blockIdx.x % (kD / 256)) * 256 + threadIdx.x;
+  const int64_t E = g * per;                                 // the block's first large entry
+  if (g >= groups || E >= NL) return;
+  const float* c = bnd + (g - 1) * (int64_t)(12 * kD);       // carried by the previous block
+  const float* f = bnd + g * (int64_t)(12 * kD);             // deferred by this block
+  const float os = join_halves(c[0 * kD + d], c[1 * kD + d], c[2 * kD + d],
+                               f[6 * kD + d], f[7 * kD + d], f[8 * kD + d]);
+  const float ol = join_halves(c[3 * kD + d], c[4 * kD + d], c[5 * kD + d],
+                               f[9 * kD + d], f[10 * kD + d], f[11 * kD + d]);
+  store_elem(out_s + (E * R) * ld_s + d, os);
+  store_elem(out_l + E * ld_l + d, ol);
 }
 
 template <class T>
@@ -786,6 +828,7 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
   const int64_t NL = T_tokens / ml;
   const int R = ml / ms;
   float* beta_l = (float*)ws;
+  float* bnd = beta_l + (size_t)2 * ml * kD;                 // per block: 12 x 512 boundary halves
   hipLaunchKernelGGL(beta_table_kernel, dim3(kD / kBetaDims), dim3(kBetaDims * kBetaSlices), 0, stream,
                      bias_l, 2 * ml, beta_l);
   const T* xp = (const T*)x;
@@ -793,10 +836,9 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
   int epw = kFusedEpw;
   int64_t groups = 0;
   auto pick = [&](const void* kern, int msel) {
-    // Large entries per wave: every block streams kFusedWaves*epw large
-    // blocks for kFusedWaves*epw-1 entries (one halo block), and the grid
-    // runs in rounds of the blocks that fit on the chip at once.  Take the
-    // epw that wastes least of both.
+    // Large entries per wave: the grid runs in rounds of the blocks that fit
+    // on the chip at once; take the epw (at least 2) that fills its last
+    // round best, the largest of equals (fewest block boundaries to join).
     static int slots_by_ms[5] = {0, 0, 0, 0, 0};
     int& slots = slots_by_ms[msel];
     if (slots == 0) {
@@ -809,18 +851,18 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
     }
     double best = -1.0;
     for (int e = 2; e <= 16; ++e) {
-      const int64_t per = (int64_t)kFusedWaves * e - 1;
+      const int64_t per = (int64_t)kFusedWaves * e;
       const int64_t g = (NL + per - 1) / per;
       const double rounds = (double)(g * kSlices) / slots;
-      const double eff = rounds / std::ceil(rounds) * (double)(NL) / (double)(g * (per + 1));
-      if (eff > best + 1e-9) { best = eff; epw = e; groups = g; }
+      const double eff = rounds / std::ceil(rounds) * (double)NL / (double)(g * per);
+      if (eff >= best - 1e-9) { best = eff; epw = e; groups = g; }
     }
   };
 #define CSKV_FUSED(MS)                                                                            \
   pick((const void*)compress_fused_kernel<T, MS, kFusedDpl>, MS);                                 \
   hipLaunchKernelGGL((compress_fused_kernel<T, MS, kFusedDpl>), dim3((unsigned)(groups * kSlices)), \
                      dim3(64 * kFusedWaves), 0, stream, xp, zp, bias_s, beta_l, R, NL, epw,        \
-                     (T*)out_s, ld_s, (T*)out_l, ld_l)
+                     (T*)out_s, ld_s, (T*)out_l, ld_l, bnd)
   switch (ms) {
     case 1: CSKV_FUSED(1); break;
     case 2: CSKV_FUSED(2); break;
@@ -828,6 +870,9 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
     default: CSKV_FUSED(4); break;
   }
 #undef CSKV_FUSED
+  if (groups > 1)
+    hipLaunchKernelGGL(compress_join_kernel<T>, dim3((unsigned)((groups - 1) * (kD / 256))), dim3(256), 0,
+                       stream, bnd, groups, kFusedWaves * epw, R, NL, (T*)out_s, ld_s, (T*)out_l, ld_l);
   return hipGetLastError();
 }
 
@@ -856,7 +901,13 @@ hipError_t launch_compress_fused(int dt, const void* x, const void* z, int64_t T
   return e;
 }
 
-size_t compress_fused_workspace_bytes(int ml) { return (size_t)2 * ml * kD * sizeof(float) + 256; }
+// The pooling-weight table plus the boundary halves of every block (at
+// most one block per 2 * kFusedWaves large entries).
+size_t compress_fused_workspace_bytes(int64_t T_tokens, int ml) {
+  const int64_t NL = T_tokens / ml;
+  const int64_t groups = (NL + 2 * kFusedWaves - 1) / (2 * kFusedWaves);
+  return (size_t)2 * ml * kD * sizeof(float) + (size_t)groups * 12 * kD * sizeof(float) + 256;
+}
 
 template <class T>
 static hipError_t launch_compress_t(const void* x, const void* z, const float* bias, int m,

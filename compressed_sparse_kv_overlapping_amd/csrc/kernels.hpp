@@ -14,7 +14,7 @@ hipError_t launch_compress_fused(int dt, const void* x, const void* z, int64_t T
                                  const float* bias_s, int ms, void* out_s, int64_t ld_s,
                                  const float* bias_l, int ml, void* out_l, int64_t ld_l, void* ws,
                                  hipStream_t stream);
-size_t compress_fused_workspace_bytes(int ml);
+size_t compress_fused_workspace_bytes(int64_t T_tokens, int ml);
 
 struct AttendParams {
   int dt;                    // 0 fp32, 1 bf16

@@ -58,7 +58,7 @@ def run():
     b128 = 0.1 * torch.randn(256, D, device="cuda", generator=g)
     e4 = torch.empty(T_TOKENS // 4, 576, dtype=torch.bfloat16, device="cuda")
     e128 = torch.empty(T_TOKENS // 128, 576, dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(cskv.compress2_workspace_size(128), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(cskv.compress2_workspace_size(T_TOKENS, 128), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     for _ in range(3):
         dst.copy_(src)

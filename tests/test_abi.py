@@ -58,7 +58,7 @@ def test_compress_errors(lib):
 
 def test_compress2_errors(lib):
     f = lib.cskv_compress2
-    ws = lib.cskv_compress2_workspace_size(128)
+    ws = lib.cskv_compress2_workspace_size(4096, 128)
     assert ws >= 256 * 512 * 4
     assert f(P, P, 4096, P, 4, P, 576, P, 130, P, 576, 1, P, ws, NULL) == INVALID      # 130 % 4
     assert f(P, P, 4096, P, 4, P, 576, P, 4, P, 576, 1, P, ws, NULL) == INVALID        # equal sizes
