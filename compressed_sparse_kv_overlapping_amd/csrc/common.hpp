@@ -77,6 +77,10 @@ template <class T> struct Raw8;
 template <> struct Raw8<bf16_t> {
   uint4 v;
   __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load_nt(const bf16_t* p) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    v = make_uint4(a.x, a.y, a.z, a.w);
+  }
   __device__ __forceinline__ float operator[](int i) const {
     const uint32_t w = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
     return (i & 1) ? bf16_hi(w) : bf16_lo(w);
@@ -87,6 +91,12 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void load(const float* p) {
     a = reinterpret_cast<const float4*>(p)[0];
     b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
+    a = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+    b = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
   }
   __device__ __forceinline__ float operator[](int i) const {
     return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : i == 3 ? a.w
@@ -99,6 +109,11 @@ template <class T> struct Raw4;
 template <> struct Raw4<bf16_t> {
   uint2 v;
   __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void load_nt(const bf16_t* p) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 a = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    v = make_uint2(a.x, a.y);
+  }
   __device__ __forceinline__ float operator[](int i) const {
     const uint32_t w = i < 2 ? v.x : v.y;
     return (i & 1) ? bf16_hi(w) : bf16_lo(w);
@@ -107,6 +122,10 @@ template <> struct Raw4<bf16_t> {
 template <> struct Raw4<float> {
   float4 a;
   __device__ __forceinline__ void load(const float* p) { a = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    a = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+  }
   __device__ __forceinline__ float operator[](int i) const {
     return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : a.w;
   }

@@ -591,8 +591,8 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
 #pragma unroll
     for (int t = 0; t < MS; ++t) {
       const int64_t j = sb * MS + t;
-      zz[t].load(z + j * kD + d0);
-      xx[t].load(x + j * kD + d0);
+      zz[t].load_nt(z + j * kD + d0);                        // read once: no cache allocation
+      xx[t].load_nt(x + j * kD + d0);
     }
   };
   const __amdgpu_buffer_rsrc_t rsrc_s =
