@@ -130,7 +130,30 @@ template <> struct Raw4<float> {
     return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : a.w;
   }
 };
+// 2 consecutive elements in storage format (4 bytes bf16, 8 bytes fp32).
+template <class T> struct Raw2;
+template <> struct Raw2<bf16_t> {
+  uint32_t v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ void load_nt(const bf16_t* p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  }
+  __device__ __forceinline__ float operator[](int i) const { return i ? bf16_hi(v) : bf16_lo(v); }
+};
+template <> struct Raw2<float> {
+  float a, b;
+  __device__ __forceinline__ void load(const float* p) { a = p[0]; b = p[1]; }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    a = __uint_as_float(u.x);
+    b = __uint_as_float(u.y);
+  }
+  __device__ __forceinline__ float operator[](int i) const { return i ? b : a; }
+};
+
 template <class T, int N> struct RawN;
+template <class T> struct RawN<T, 2> : Raw2<T> {};
 template <class T> struct RawN<T, 8> : Raw8<T> {};
 template <class T> struct RawN<T, 4> : Raw4<T> {};
 
@@ -158,6 +181,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 template <class T, int N> struct BufStoreN;
+template <> struct BufStoreN<bf16_t, 2> {
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v) {
+    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v[0], v[1]), r, off, 0, 0);
+  }
+};
+template <> struct BufStoreN<float, 2> {
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = {__float_as_uint(v[0]), __float_as_uint(v[1])};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+  }
+};
 template <> struct BufStoreN<bf16_t, 4> {
   static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

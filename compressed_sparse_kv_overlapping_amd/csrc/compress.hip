@@ -449,21 +449,22 @@ static hipError_t launch_large_t(const void* x, const void* z, const float* bias
 // ---------------------------------------------------------------------------
 // Fused two-scale compressor: one pass over x and z produces the entries of
 // a small block size MS (<= 4, the CSA scale) and of a large block size ML =
-// R * MS (the HCA scale), since both read the same raw rows.
+// R * MS <= 128 (the HCA scale), since both read the same raw rows.
 //
 // Weights share one exp2 per element: with r the maximum of z over the small
 // block being read (per dimension),
 //   small window:  2^(z*log2e - r) * beta_s[p],   beta_s = 2^((b_s - max b_s) log2e)
 //   large window:  2^(z*log2e - r) * beta_l[p],   beta_l = 2^((b_l - max b_l) log2e)
 // (the constant factors cancel in each normalisation).  With ux = u x every
-// accumulation is one FMA.  beta_s (2*MS rows) sits in LDS for the whole
-// block; beta_l (2*ML rows, precomputed into the workspace) is staged in LDS
-// MS positions at a time: the waves of a block stream their large blocks in
-// lockstep, so they need the same beta_l rows at the same time.  A small
-// block's large sums join the running sums of its large block once, scaled
-// by 2^(r - rl) with rl the large block's raise-only reference.  Wave ranges
-// hand their carried halves to the next wave through LDS as in the large
-// compressor.
+// accumulation is one FMA.  A block takes 128 dimensions (2 per lane), so
+// that both weight tables of its dimensions fit LDS whole (beta_l: 2*ML rows,
+// precomputed into the workspace, 128 KB at ML = 128): the 16 waves stream
+// their ranges with no barrier.  A small block's large sums join the running
+// sums of its large block once, scaled by 2^(r - rl) with rl the large
+// block's raise-only reference.  Wave ranges hand their carried halves to the
+// next wave through LDS; the first wave of a block leaves its deferred halves,
+// and the last wave its carried ones, in the workspace for the join kernel.
+
 // One entry from its two half-window sums, each with its own reference
 // (log2 domain): both are brought to the larger reference.
 __device__ __forceinline__ float join_halves(float pS, float pA, float pr, float sS, float sA, float sr) {
@@ -474,12 +475,11 @@ __device__ __forceinline__ float join_halves(float pS, float pA, float pr, float
 __device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_elem(bf16_t* p, float v) { p->u = (uint16_t)f32_to_bf16(v); }
 
-constexpr int kFusedWaves = 4;
-#ifndef CSKV_FUSED_EPW
-#define CSKV_FUSED_EPW 4
-#endif
-constexpr int kFusedEpw = CSKV_FUSED_EPW;     // large entries per wave (wave 0: one less)
-constexpr int kFusedDpl = 4;
+constexpr int kFusedWaves = 16;                // one block of 1024 threads per CU
+constexpr int kFusedDpl = 2;                   // dimensions per lane
+constexpr int kFusedSW = 64 * kFusedDpl;       // dimensions per block
+constexpr int kFusedSlices = kD / kFusedSW;
+constexpr int kFusedMaxML = 128;               // largest large block whose weights fit LDS
 
 // beta[p][d] = 2^((bias[p][d] - max_p bias[p][d]) * log2e): a block takes 64
 // dimensions, its 16 row slices take every 16th row, and the column maxima
@@ -504,26 +504,24 @@ __global__ __launch_bounds__(kBetaDims* kBetaSlices) void beta_table_kernel(
     beta[(int64_t)p * kD + d] = __builtin_amdgcn_exp2f((bias[(int64_t)p * kD + d] - bm) * L2E);
 }
 
-template <class T, int MS, int DPL>
+template <class T, int MS>
 __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
     const T* __restrict__ x, const T* __restrict__ z, const float* __restrict__ bias_s,
     const float* __restrict__ beta_l, int R, int64_t NL, int epw, T* __restrict__ out_s,
     int64_t ld_s, T* __restrict__ out_l, int64_t ld_l, float* __restrict__ bnd) {
-  constexpr int kSlices = kD / (64 * DPL);
-  constexpr int kSW = 64 * DPL;                   // dims of this block's slice
+  constexpr int DPL = kFusedDpl, kSW = kFusedSW;
   const int ML = R * MS;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int blk = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int slice = blk % kSlices;
-  const int64_t group = blk / kSlices;
+  const int slice = blk % kFusedSlices;
+  const int64_t group = blk / kFusedSlices;
   const int dl = lane * DPL;                      // dim within the slice
   const int d0 = slice * kSW + dl;
   const float L2E = 1.4426950408889634f;
   // large entries of this wave: [E0, E1), streamed as large blocks from E0
   const int64_t E0 = (group * kFusedWaves + wave) * (int64_t)epw;
   const int64_t E1 = E0 + epw < NL ? E0 + epw : NL;
-  const int64_t LB0 = E0;                         // first large block streamed
   const int nblocks = epw;                        // large blocks streamed by every wave
   // the first entries of a range wait for the previous range's carried
   // halves: through LDS inside the block, through the workspace (and the
@@ -532,62 +530,46 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
   const int64_t NS = NL * R;                      // small entries
   const int64_t S0 = E0 * R, S1 = E1 * R;         // small entries written by this wave
 
+  // both weight tables of this block's dimensions; after the loop the
+  // large table's space takes the waves' carried halves
+  __shared__ __attribute__((aligned(16))) float bl_lds[2 * kFusedMaxML][kSW];
   __shared__ __attribute__((aligned(16))) float bs_lds[2 * MS][kSW];
-  __shared__ __attribute__((aligned(16))) float bl_lds[2][2 * MS][kSW];
-  __shared__ float xch[kFusedWaves][6][kSW];
-  // second halves of a wave's first small and large entries (all but the
-  // very first range), completed with the previous range's carried halves
-  __shared__ float dfr[kFusedWaves][6][kSW];
+  static_assert(kFusedWaves * 6 <= 2 * kFusedMaxML, "carried halves fit the table's space");
+  float(*xch)[6][kSW] = reinterpret_cast<float(*)[6][kSW]>(&bl_lds[0][0]);
   for (int i = threadIdx.x; i < 2 * MS * kSW; i += 64 * kFusedWaves) {
     const int p = i / kSW, d = i % kSW;
     float bm = bias_s[slice * kSW + d];
     for (int q = 1; q < 2 * MS; ++q) bm = fmaxf(bm, bias_s[(int64_t)q * kD + slice * kSW + d]);
     bs_lds[p][d] = __builtin_amdgcn_exp2f((bias_s[(int64_t)p * kD + slice * kSW + d] - bm) * L2E);
   }
-  // beta_l rows for positions [t, t+MS) of both halves: loaded into
-  // registers one step before they are written to LDS, so that the wait for
-  // them never drains the raw-row loads issued after them
-  constexpr int kBlQuads = 2 * MS * kSW / 4;
-  static_assert(kBlQuads <= 2 * 64 * kFusedWaves, "two quads per thread");
-  // thread's two quads (clamped: surplus threads repeat the last one)
-  const int q0 = (int)threadIdx.x < kBlQuads ? (int)threadIdx.x : kBlQuads - 1;
-  const int q1 = (int)threadIdx.x + 64 * kFusedWaves < kBlQuads ? (int)threadIdx.x + 64 * kFusedWaves
-                                                                 : kBlQuads - 1;
-  auto bl_src = [&](int t, int i) {
-    const int row = (i * 4) / kSW, d = (i * 4) % kSW;
-    const int p = row < MS ? t + row : ML + t + (row - MS);
-    return reinterpret_cast<const float4*>(beta_l + (int64_t)p * kD + slice * kSW + d);
-  };
-  float4 bq0, bq1;
-  auto load_bl = [&](int t) { bq0 = *bl_src(t, q0); bq1 = *bl_src(t, q1); };
-  auto write_bl = [&](int k) {
-    *reinterpret_cast<float4*>(&bl_lds[k][(q0 * 4) / kSW][(q0 * 4) % kSW]) = bq0;
-    *reinterpret_cast<float4*>(&bl_lds[k][(q1 * 4) / kSW][(q1 * 4) % kSW]) = bq1;
-  };
-  load_bl(0);
-  write_bl(0);
+  for (int i = threadIdx.x; i < 2 * ML * kSW / 4; i += 64 * kFusedWaves) {
+    const int p = (4 * i) / kSW, d = (4 * i) % kSW;
+    *reinterpret_cast<float4*>(&bl_lds[p][d]) =
+        *reinterpret_cast<const float4*>(beta_l + (int64_t)p * kD + slice * kSW + d);
+  }
 
   // Small scale: carried first half cS/cA of the next entry with its
   // reference cr (the maximum of the block it came from).  Large scale:
   // reference rl of the current large block (raise-only within the block;
   // both halves of the block use it), running halves lsA/laA, lsB/laB, and
   // the carried first half lcS/lcA of the next large entry with its
-  // reference lcr.
+  // reference lcr.  f*/g*: the deferred second halves of the range's first
+  // small and large entries.
   float cS[DPL], cA[DPL], cr[DPL];
   float rl[DPL], lcS[DPL], lcA[DPL], lcr[DPL];
-  float lsA[DPL], laA[DPL], lsB[DPL], laB[DPL];   // large: halves of the current block
+  float lsA[DPL], laA[DPL], lsB[DPL], laB[DPL];
+  float fS[DPL], fA[DPL], fR[DPL], gS[DPL], gA[DPL], gR[DPL];
 #pragma unroll
   for (int d = 0; d < DPL; ++d) {
     cr[d] = 0.f; cS[d] = cA[d] = 0.f;
     rl[d] = -INFINITY; lcS[d] = lcA[d] = lcr[d] = 0.f;
     lsA[d] = laA[d] = lsB[d] = laB[d] = 0.f;
+    fS[d] = fA[d] = fR[d] = gS[d] = gA[d] = gR[d] = 0.f;
   }
-  const int64_t sbegin = LB0 * R;                            // first small block streamed
-  const int nsteps = nblocks * R;
+  const int64_t sbegin = E0 * R;                             // first small block streamed
   const int64_t sb_last = NS - 1;                            // last small block inside NL large blocks
   auto load_sb = [&](int64_t sb, RawN<T, DPL>* zz, RawN<T, DPL>* xx) {
     if (sb > sb_last) sb = sb_last;
-    if (sb < 0) sb = 0;
 #pragma unroll
     for (int t = 0; t < MS; ++t) {
       const int64_t j = sb * MS + t;
@@ -603,22 +585,18 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
   // Two register slots of raw rows: the step reading one loads the next
   // block into the other.  A wave streams its large blocks in an outer loop
   // and their R (even) small blocks in an inner loop unrolled by two, so that
-  // the slots and the beta_l buffers are fixed per unrolled step and a large
-  // entry closes outside the inner loop.
+  // the slots are fixed per unrolled step and a large entry closes outside
+  // the inner loop.
   RawN<T, DPL> zb[2][MS], xb[2][MS];
-  if (nsteps > 1) load_bl((1 % R) * MS);                     // rows of step 1
   load_sb(sbegin, zb[0], xb[0]);
-  __syncthreads();                                           // bs_lds and bl_lds[0] ready
+  __syncthreads();                                           // weight tables ready
 
-  auto step = [&](const int st, const int kb, const RawN<T, DPL>* zc, const RawN<T, DPL>* xc,
+  // small block j of large block bi (global small block sb); lp = j * MS is
+  // its first position in the large window's first half
+  auto step = [&](const int64_t sb, const int lp, const RawN<T, DPL>* zc, const RawN<T, DPL>* xc,
                   RawN<T, DPL>* zn, RawN<T, DPL>* xn) {
-    const int64_t sb = sbegin + st;                          // global small block (may be < 0)
-    // the next step's beta_l rows go to the other buffer (read by every
-    // wave before the barrier that ended the previous step)
-    if (st + 1 < nsteps) write_bl(kb ^ 1);
-    if (st + 2 < nsteps) load_bl(((st + 2) % R) * MS);
     load_sb(sb + 1, zn, xn);
-    // reference update from the small block maximum
+    // reference from the small block maximum
     float bmx[DPL];
 #pragma unroll
     for (int d = 0; d < DPL; ++d) {
@@ -629,42 +607,34 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
     }
     // This block's sums, all against its maximum bmx: the small halves
     // (sA/aA: first half of entry sb + 1, sB/aB: second half of entry
-    // sb) and the large block's two halves (pA/qA, pB/qB).  ux = u x
-    // turns every accumulation into one FMA.
+    // sb) and the large block's two halves (pA/qA, pB/qB).
     float sA[DPL], aA[DPL], sB[DPL], aB[DPL], pA[DPL], qA[DPL], pB[DPL], qB[DPL];
 #pragma unroll
     for (int t = 0; t < MS; ++t) {
-      float ba[DPL], bb[DPL], la[DPL], lbv[DPL];
-#pragma unroll
-      for (int d = 0; d < DPL; d += 4) {
-        const float4 v0 = *reinterpret_cast<const float4*>(&bs_lds[t][dl + d]);
-        const float4 v1 = *reinterpret_cast<const float4*>(&bs_lds[MS + t][dl + d]);
-        const float4 v2 = *reinterpret_cast<const float4*>(&bl_lds[kb][t][dl + d]);
-        const float4 v3 = *reinterpret_cast<const float4*>(&bl_lds[kb][MS + t][dl + d]);
-        ba[d] = v0.x; ba[d + 1] = v0.y; ba[d + 2] = v0.z; ba[d + 3] = v0.w;
-        bb[d] = v1.x; bb[d + 1] = v1.y; bb[d + 2] = v1.z; bb[d + 3] = v1.w;
-        la[d] = v2.x; la[d + 1] = v2.y; la[d + 2] = v2.z; la[d + 3] = v2.w;
-        lbv[d] = v3.x; lbv[d + 1] = v3.y; lbv[d + 2] = v3.z; lbv[d + 3] = v3.w;
-      }
+      const float2 ba = *reinterpret_cast<const float2*>(&bs_lds[t][dl]);
+      const float2 bb = *reinterpret_cast<const float2*>(&bs_lds[MS + t][dl]);
+      const float2 la = *reinterpret_cast<const float2*>(&bl_lds[lp + t][dl]);
+      const float2 lb = *reinterpret_cast<const float2*>(&bl_lds[ML + lp + t][dl]);
 #pragma unroll
       for (int d = 0; d < DPL; ++d) {
+        const float wa = d ? ba.y : ba.x, wb = d ? bb.y : bb.x;
+        const float va = d ? la.y : la.x, vb = d ? lb.y : lb.x;
         const float u = __builtin_amdgcn_exp2f(fmaf(zc[t][d], L2E, -bmx[d]));
         const float ux = u * xc[t][d];
         if (t == 0) {
-          sA[d] = u * ba[d]; aA[d] = ux * ba[d]; sB[d] = u * bb[d]; aB[d] = ux * bb[d];
-          pA[d] = u * la[d]; qA[d] = ux * la[d]; pB[d] = u * lbv[d]; qB[d] = ux * lbv[d];
+          sA[d] = u * wa; aA[d] = ux * wa; sB[d] = u * wb; aB[d] = ux * wb;
+          pA[d] = u * va; qA[d] = ux * va; pB[d] = u * vb; qB[d] = ux * vb;
         } else {
-          sA[d] = fmaf(u, ba[d], sA[d]);
-          aA[d] = fmaf(ux, ba[d], aA[d]);
-          sB[d] = fmaf(u, bb[d], sB[d]);
-          aB[d] = fmaf(ux, bb[d], aB[d]);
-          pA[d] = fmaf(u, la[d], pA[d]);
-          qA[d] = fmaf(ux, la[d], qA[d]);
-          pB[d] = fmaf(u, lbv[d], pB[d]);
-          qB[d] = fmaf(ux, lbv[d], qB[d]);
+          sA[d] = fmaf(u, wa, sA[d]);
+          aA[d] = fmaf(ux, wa, aA[d]);
+          sB[d] = fmaf(u, wb, sB[d]);
+          aB[d] = fmaf(ux, wb, aB[d]);
+          pA[d] = fmaf(u, va, pA[d]);
+          qA[d] = fmaf(ux, va, qA[d]);
+          pB[d] = fmaf(u, vb, pB[d]);
+          qB[d] = fmaf(ux, vb, qB[d]);
         }
       }
-      asm volatile("" ::: "memory");
     }
     // The large block's reference rl is raise-only within the block (it
     // is -inf before the block's first small block); this block's large sums
@@ -691,71 +661,63 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
       laB[d] = fmaf(G, qB[d], laB[d]);
     }
     // small entry sb: carried first half + this second half
-    {
-      float o[DPL];
-      const bool first = sb == 0;
+    float o[DPL];
+    const bool first = sb == 0;
 #pragma unroll
-      for (int d = 0; d < DPL; ++d) {
-        const float dl = cr[d] - bmx[d];
-        const float g = __builtin_amdgcn_exp2f(-fabsf(dl));
-        const float fc = first ? 0.f : (dl >= 0.f ? 1.f : g);
-        const float fb = (first || dl < 0.f) ? 1.f : g;
-        o[d] = (cA[d] * fc + aB[d] * fb) * __builtin_amdgcn_rcpf(cS[d] * fc + sB[d] * fb);
-      }
-      const bool defer = deferred && sb == S0;            // first half comes from the previous range
-      if (defer) {
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) {
-          dfr[wave][0][dl + d] = sB[d]; dfr[wave][1][dl + d] = aB[d]; dfr[wave][2][dl + d] = bmx[d];
-        }
-      }
-      const uint32_t off = (sb >= S0 && sb < S1 && !defer)
-                               ? (uint32_t)((sb - S0) * ld_s + d0) * sizeof(T) : 0xffffffffu;
-      BufStoreN<T, DPL>::store(rsrc_s, off, o);
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) { cS[d] = sA[d]; cA[d] = aA[d]; cr[d] = bmx[d]; }
+    for (int d = 0; d < DPL; ++d) {
+      const float dl2 = cr[d] - bmx[d];
+      const float g = __builtin_amdgcn_exp2f(-fabsf(dl2));
+      const float fc = first ? 0.f : (dl2 >= 0.f ? 1.f : g);
+      const float fb = (first || dl2 < 0.f) ? 1.f : g;
+      o[d] = (cA[d] * fc + aB[d] * fb) * __builtin_amdgcn_rcpf(cS[d] * fc + sB[d] * fb);
     }
-    __syncthreads();                                         // next beta_l rows staged
+    const bool defer = deferred && sb == S0;                 // first half comes from the previous range
+    if (defer) {
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) { fS[d] = sB[d]; fA[d] = aB[d]; fR[d] = bmx[d]; }
+    }
+    const uint32_t off = (sb >= S0 && sb < S1 && !defer)
+                             ? (uint32_t)((sb - S0) * ld_s + d0) * sizeof(T) : 0xffffffffu;
+    BufStoreN<T, DPL>::store(rsrc_s, off, o);
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) { cS[d] = sA[d]; cA[d] = aA[d]; cr[d] = bmx[d]; }
   };
 
   for (int bi = 0; bi < nblocks; ++bi) {
-    const int64_t lb = LB0 + bi;                             // large block (may be -1)
+    const int64_t lb = E0 + bi;                              // large block
     for (int j = 0; j < R; j += 2) {
-      step(bi * R + j, 0, zb[0], xb[0], zb[1], xb[1]);
-      step(bi * R + j + 1, 1, zb[1], xb[1], zb[0], xb[0]);
+      step(lb * R + j, j * MS, zb[0], xb[0], zb[1], xb[1]);
+      step(lb * R + j + 1, (j + 1) * MS, zb[1], xb[1], zb[0], xb[0]);
     }
     // end of a large block: large entry lb closes
-    {
-      float o[DPL];
-      const bool first = lb == 0;
+    float o[DPL];
+    const bool first = lb == 0;
 #pragma unroll
-      for (int d = 0; d < DPL; ++d) {
-        const float mx = fmaxf(lcr[d], rl[d]);
-        const float fc = first ? 0.f : __builtin_amdgcn_exp2f(lcr[d] - mx);
-        const float fb = __builtin_amdgcn_exp2f(rl[d] - mx);
-        o[d] = (lcA[d] * fc + laB[d] * fb) * __builtin_amdgcn_rcpf(lcS[d] * fc + lsB[d] * fb);
-      }
-      const bool defer = deferred && lb == E0;
-      if (defer) {
+    for (int d = 0; d < DPL; ++d) {
+      const float mx = fmaxf(lcr[d], rl[d]);
+      const float fc = first ? 0.f : __builtin_amdgcn_exp2f(lcr[d] - mx);
+      const float fb = __builtin_amdgcn_exp2f(rl[d] - mx);
+      o[d] = (lcA[d] * fc + laB[d] * fb) * __builtin_amdgcn_rcpf(lcS[d] * fc + lsB[d] * fb);
+    }
+    const bool defer = deferred && lb == E0;
+    if (defer) {
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) {
-          dfr[wave][3][dl + d] = lsB[d]; dfr[wave][4][dl + d] = laB[d]; dfr[wave][5][dl + d] = rl[d];
-        }
-      }
-      const uint32_t off = (lb >= E0 && lb < E1 && !defer)
-                               ? (uint32_t)((lb - E0) * ld_l + d0) * sizeof(T) : 0xffffffffu;
-      BufStoreN<T, DPL>::store(rsrc_l, off, o);
+      for (int d = 0; d < DPL; ++d) { gS[d] = lsB[d]; gA[d] = laB[d]; gR[d] = rl[d]; }
+    }
+    const uint32_t off = (lb >= E0 && lb < E1 && !defer)
+                             ? (uint32_t)((lb - E0) * ld_l + d0) * sizeof(T) : 0xffffffffu;
+    BufStoreN<T, DPL>::store(rsrc_l, off, o);
 #pragma unroll
-      for (int d = 0; d < DPL; ++d) {
-        lcS[d] = lsA[d]; lcA[d] = laA[d]; lcr[d] = rl[d];
-        lsA[d] = 0.f; laA[d] = 0.f; lsB[d] = 0.f; laB[d] = 0.f;
-        rl[d] = -INFINITY;
-      }
+    for (int d = 0; d < DPL; ++d) {
+      lcS[d] = lsA[d]; lcA[d] = laA[d]; lcr[d] = rl[d];
+      lsA[d] = 0.f; laA[d] = 0.f; lsB[d] = 0.f; laB[d] = 0.f;
+      rl[d] = -INFINITY;
     }
   }
   // hand both carried first halves (and the references) to the next wave;
   // the last wave's go to the workspace for the next block's first wave,
   // which leaves its deferred halves there too
+  __syncthreads();                                           // every wave is done with the tables
 #pragma unroll
   for (int d = 0; d < DPL; ++d) {
     xch[wave][0][dl + d] = cS[d];
@@ -779,9 +741,14 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
   }
   if (wave == 0 && group > 0) {
 #pragma unroll
-    for (int d = 0; d < DPL; ++d)
-#pragma unroll
-      for (int f = 0; f < 6; ++f) bg[(6 + f) * kD + d0 + d] = dfr[0][f][dl + d];
+    for (int d = 0; d < DPL; ++d) {
+      bg[6 * kD + d0 + d] = fS[d];
+      bg[7 * kD + d0 + d] = fA[d];
+      bg[8 * kD + d0 + d] = fR[d];
+      bg[9 * kD + d0 + d] = gS[d];
+      bg[10 * kD + d0 + d] = gA[d];
+      bg[11 * kD + d0 + d] = gR[d];
+    }
   }
   __syncthreads();
   if (wave > 0) {
@@ -789,9 +756,9 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
 #pragma unroll
     for (int d = 0; d < DPL; ++d) {
       os[d] = join_halves(xch[wave - 1][0][dl + d], xch[wave - 1][1][dl + d], xch[wave - 1][4][dl + d],
-                          dfr[wave][0][dl + d], dfr[wave][1][dl + d], dfr[wave][2][dl + d]);
+                          fS[d], fA[d], fR[d]);
       ol[d] = join_halves(xch[wave - 1][2][dl + d], xch[wave - 1][3][dl + d], xch[wave - 1][5][dl + d],
-                          dfr[wave][3][dl + d], dfr[wave][4][dl + d], dfr[wave][5][dl + d]);
+                          gS[d], gA[d], gR[d]);
     }
     BufStoreN<T, DPL>::store(rsrc_s, S0 < S1 ? (uint32_t)(d0 * sizeof(T)) : 0xffffffffu, os);
     BufStoreN<T, DPL>::store(rsrc_l, E0 < E1 ? (uint32_t)(d0 * sizeof(T)) : 0xffffffffu, ol);
@@ -824,7 +791,6 @@ template <class T>
 static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens, const float* bias_s,
                                  int ms, void* out_s, int64_t ld_s, const float* bias_l, int ml,
                                  void* out_l, int64_t ld_l, void* ws, hipStream_t stream) {
-  constexpr int kSlices = kD / (64 * kFusedDpl);
   const int64_t NL = T_tokens / ml;
   const int R = ml / ms;
   float* beta_l = (float*)ws;
@@ -833,7 +799,7 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
                      bias_l, 2 * ml, beta_l);
   const T* xp = (const T*)x;
   const T* zp = (const T*)z;
-  int epw = kFusedEpw;
+  int epw = 2;
   int64_t groups = 0;
   auto pick = [&](const void* kern, int msel) {
     // Large entries per wave: the grid runs in rounds of the blocks that fit
@@ -847,20 +813,20 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
           hipGetDevice(&dev) != hipSuccess ||
           hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         nb = 0;
-      slots = nb > 0 && cus > 0 ? nb * cus : 512;
+      slots = nb > 0 && cus > 0 ? nb * cus : 256;
     }
     double best = -1.0;
-    for (int e = 2; e <= 16; ++e) {
+    for (int e = 2; e <= 64; ++e) {
       const int64_t per = (int64_t)kFusedWaves * e;
       const int64_t g = (NL + per - 1) / per;
-      const double rounds = (double)(g * kSlices) / slots;
+      const double rounds = (double)(g * kFusedSlices) / slots;
       const double eff = rounds / std::ceil(rounds) * (double)NL / (double)(g * per);
       if (eff >= best - 1e-9) { best = eff; epw = e; groups = g; }
     }
   };
 #define CSKV_FUSED(MS)                                                                            \
-  pick((const void*)compress_fused_kernel<T, MS, kFusedDpl>, MS);                                 \
-  hipLaunchKernelGGL((compress_fused_kernel<T, MS, kFusedDpl>), dim3((unsigned)(groups * kSlices)), \
+  pick((const void*)compress_fused_kernel<T, MS>, MS);                                            \
+  hipLaunchKernelGGL((compress_fused_kernel<T, MS>), dim3((unsigned)(groups * kFusedSlices)),     \
                      dim3(64 * kFusedWaves), 0, stream, xp, zp, bias_s, beta_l, R, NL, epw,        \
                      (T*)out_s, ld_s, (T*)out_l, ld_l, bnd)
   switch (ms) {
@@ -882,9 +848,10 @@ hipError_t launch_compress_fused(int dt, const void* x, const void* z, int64_t T
                                  hipStream_t stream) {
   const int64_t NL = T_tokens / ml, NSall = T_tokens / ms, NSf = NL * (ml / ms);
   hipError_t e = hipSuccess;
-  if ((ml / ms) % 2 != 0) {
+  if ((ml / ms) % 2 != 0 || ml > kFusedMaxML) {
     // the fused kernel streams an even number of small blocks per large
-    // block; otherwise each scale gets its own streaming kernel
+    // block and holds the large scale's weights in LDS (ml <= 128);
+    // otherwise each scale gets its own streaming kernel
     e = launch_compress(dt, x, z, bias_s, ms, 0, NSall, out_s, ld_s, stream);
     if (e == hipSuccess && NL > 0) e = launch_compress(dt, x, z, bias_l, ml, 0, NL, out_l, ld_l, stream);
     return e;
