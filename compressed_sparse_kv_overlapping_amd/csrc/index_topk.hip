@@ -488,9 +488,9 @@ __device__ uint32_t block_kth_largest(KeyAt key_at, int n, uint32_t kk, uint32_t
   return lo;
 }
 
-// k-th largest of the G group maxima of each query (0 if fewer than k
-// non-empty groups or fewer than k visible entries).  The maxima are read
-// from L2 on every pass; only the histogram lives in LDS.
+// A lower bound of the k-th largest of the G group maxima of each query (0
+// if fewer than k non-empty groups or fewer than k visible entries).  The
+// maxima are read from L2; only the histogram lives in LDS.
 __global__ __launch_bounds__(256) void idx_threshold_kernel(IdxArgs a) {
   __shared__ uint32_t hist[4096], part[8];
   __shared__ uint32_t sh_digit, sh_above;
@@ -510,11 +510,22 @@ __global__ __launch_bounds__(256) void idx_threshold_kernel(IdxArgs a) {
     if (threadIdx.x == 0) a.thr[b] = 0u;
     return;
   }
-  uint32_t above;
-  const uint32_t thr = block_kth_largest<12>(
-      [&](int i, uint32_t& key) { key = gm[i]; return key != 0u; }, a.G, (uint32_t)a.k, lo, hi,
-      hist, part, &sh_digit, &sh_above, &above);
-  if (threadIdx.x == 0) a.thr[b] = thr;
+  // one pass over 4096 bins of the key range: the lower edge of the bin that
+  // holds the k-th largest maximum is at most that maximum, so at least k
+  // groups (hence k entries) still reach it; a bin's width of extra
+  // candidates is all it costs
+  const uint32_t range = hi - lo;
+  const int bits = range ? 32 - __clz((int)range) : 0;     // range < 2^bits
+  const int shift = bits > 12 ? bits - 12 : 0;
+  for (int i = threadIdx.x; i < 4096; i += 256) hist[i] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.G; i += 256) {
+    const uint32_t v = gm[i];
+    if (v != 0u) atomicAdd(&hist[(v - lo) >> shift], 1u);
+  }
+  __syncthreads();
+  find_kth_bin(hist, 4096, (uint32_t)a.k, &sh_digit, &sh_above, part);
+  if (threadIdx.x == 0) a.thr[b] = lo + (sh_digit << shift);
 }
 
 // ----------------------------------------------------------------- final
