@@ -38,6 +38,7 @@ struct IdxArgs {
   const int64_t* q_pos;       // NULL at decode
   int64_t key_bstride;
   int B, N, k, m, GS, G, qpb, tiles_per_wave;
+  int gs_shift;               // GS = 2^gs_shift
   float scale;
   uint32_t* gmax;             // [B][G]
   uint32_t* thr;              // [B]
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
   // every fourth group (or the range's last) the lanes write the 16 bytes of
   // up to four consecutive groups of their query at once
   float held[NQB];
-  const int grp_first = e_w0 / a.GS, grp_last = (e_w1 - 1) / a.GS;
+  const int grp_first = e_w0 >> a.gs_shift, grp_last = (e_w1 - 1) >> a.gs_shift;
   auto tile = [&](const int et, const Frag<T>* kf) {
    if (et < blk_vis) {                                         // skip invisible tiles
     f32x4 S[NQB];
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
     if (MODE == 0) {
       // group boundaries coincide with tile boundaries for GS >= 16
       const int GS = a.GS;
-      if (GS <= 8 || ((et + 16) % GS) == 0) {
+      if (GS <= 8 || ((et + 16) & (GS - 1)) == 0) {
 #pragma unroll
         for (int j = 0; j < NQB; ++j) {
           float v = gm[j];
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
           } else {
             v = fmaxf(v, shfl_xor(v, 16));
             v = fmaxf(v, shfl_xor(v, 32));
-            const int grp = et / GS;
+            const int grp = et >> a.gs_shift;
             if (g == (grp & 3)) held[j] = v;
             if ((grp & 3) == 3 || grp == grp_last) {
               const int gw = (grp & ~3) + g;                   // this lane's group
@@ -360,14 +361,23 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
       __syncthreads();                                         // stage st landed; st - 1 read
       if (st + 1 < nst) issue(st + 1);
       const char* buf = kst[st & 1];
-      for (int t = 0; t < KT::kTiles; ++t) {
-        const int et = e_w0 + (st * KT::kTiles + t) * 16;
-        if (et >= e_w1) break;
-        Frag<T> kf[2];
+      // fragments of the next tile are read from LDS while a tile computes
+      Frag<T> kf[2][2];
+      auto frags = [&](const int t, Frag<T>* f) {
         const char* rowp = buf + (t * 16 + col) * KT::kRow;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) KT::load(kf[ks], rowp, (32 * ks + 8 * g) * (int)sizeof(T), swz);
-        tile(et, kf);
+        for (int ks = 0; ks < 2; ++ks) KT::load(f[ks], rowp, (32 * ks + 8 * g) * (int)sizeof(T), swz);
+      };
+      frags(0, kf[0]);
+      static_assert(KT::kTiles % 2 == 0, "tiles per stage come in pairs");
+      for (int t = 0; t < KT::kTiles; t += 2) {
+        const int et = e_w0 + (st * KT::kTiles + t) * 16;
+        if (et >= e_w1) break;
+        frags(t + 1, kf[1]);
+        tile(et, kf[0]);
+        if (et + 16 >= e_w1) break;
+        if (t + 2 < KT::kTiles) frags(t + 2, kf[0]);
+        tile(et + 16, kf[1]);
       }
     }
   }
@@ -870,6 +880,8 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
   const bool per_seq = p.key_bstride != 0;
   const TopkGeom g = topk_geom(p.B, p.N, p.k, per_seq);
   a.GS = g.GS; a.G = g.G; a.qpb = g.qpb; a.tiles_per_wave = g.tpw;
+  a.gs_shift = 0;
+  while ((1 << a.gs_shift) < g.GS) ++a.gs_shift;             // group sizes are powers of two
   a.chunks = g.chunks; a.region = g.region;
   char* w = (char*)ws;
   a.cand = (uint64_t*)w;            w += (size_t)p.B * g.chunks * g.region * 8;
