@@ -191,3 +191,49 @@ def test_csa_per_sequence_decode():
     same = [b for b in range(B) if np.array_equal(ref_idx[b], idx[b])]
     assert len(same) >= B - 1
     _check_attn(out[same], lse[same], ro[same], rl[same], dt)
+
+
+def test_layer_1m_step_sampled():
+    """The benchmarked step at its full size and launch configuration: both
+    scales compressed from the 1M raw rows into the entry buffers, then the
+    CSA indexer top-1024, CSA attention and HCA attention for 32 queries x
+    128 heads; queries 0 and 31 checked, with every entry they read rebuilt
+    by the oracle from the raw rows."""
+    cfg = wl.CONFIGS["layer_1m"]
+    inp = wl.make_inputs(cfg, seed=0)
+    cskv = _cskv()
+    T, B, H, k, W = cfg.T, cfg.B, cfg.H, cfg.k, cfg.W
+    e4 = torch.empty((T // 4, E), dtype=torch.bfloat16, device="cuda")
+    e128 = torch.empty((T // 128, E), dtype=torch.bfloat16, device="cuda")
+    e4[:, 512:] = dev(inp["rope4"])
+    e128[:, 512:] = dev(inp["rope128"])
+    cskv.compress2(dev(inp["x"]), dev(inp["z"]), dev(inp["b4"]), 4, dev(inp["b128"]), 128,
+                   out_small=e4, out_large=e128)
+    idx = cskv.index_topk(dev(inp["qI"]), dev(inp["kI"]), k)
+    out_c, lse_c = cskv.sparse_attend(dev(inp["q"]), e4, dev(inp["window"]), idx)
+    out_h, lse_h = cskv.hca_attend(dev(inp["q_hca"]), e128)
+    torch.cuda.synchronize()
+    rows = [0, B - 1]
+    # selection
+    s, v = oracle.index_scores(inp["qI"].raw[rows], inp["kI"].raw, wl.DT_BF16)
+    sel = idx.cpu().numpy()[rows]
+    check_selection(sel, s, v, k)
+
+    def entries(m, bias, rope, ids):
+        c = oracle.compress(inp["x"].raw, inp["z"].raw, wl.DT_BF16, bias, m, entry_ids=ids)
+        ent = np.empty((len(ids), E), np.uint16)
+        ent[:, :512] = wl.bf16_bits(c.astype(np.float32))
+        ent[:, 512:] = rope[ids]
+        return ent
+
+    # CSA over each checked query's own selection (entries rebuilt by the oracle)
+    for r, b in enumerate(rows):
+        ids = sel[r].astype(np.int64)
+        ent = entries(4, inp["b4"].raw, inp["rope4"].raw, ids)
+        ro, rl = oracle.csa_attend(inp["q"].raw[[b]], ent, inp["window"].raw, wl.DT_BF16,
+                                   np.arange(k, dtype=np.int32)[None, :])
+        _check_attn(out_c[[b]], lse_c[[b]], ro, rl, wl.DT_BF16)
+    # HCA over all 8,192 large-scale entries
+    ent = entries(128, inp["b128"].raw, inp["rope128"].raw, np.arange(T // 128, dtype=np.int64))
+    ro, rl = oracle.hca_attend(inp["q_hca"].raw[rows], ent, wl.DT_BF16)
+    _check_attn(out_h[rows], lse_h[rows], ro, rl, wl.DT_BF16)
