@@ -125,10 +125,12 @@ def test_compress_1m_tokens_sampled():
 @pytest.mark.parametrize("dt", [wl.DT_F32, wl.DT_BF16])
 @pytest.mark.parametrize("ms,ml,T", [(4, 128, 4096), (4, 128, 4099), (4, 128, 4196), (2, 16, 1000),
                                      (1, 8, 517), (3, 12, 600), (4, 8, 333), (4, 128, 100),
-                                     (4, 64, 64 * 61 + 7), (4, 128, 128 * 40)])
+                                     (4, 64, 64 * 61 + 7), (4, 128, 128 * 40), (4, 256, 256 * 9 + 5),
+                                     (2, 6, 300)])
 def test_compress2_matches_oracle(dt, ms, ml, T):
     """Both scales in one pass equal the oracle at each scale (ragged T,
-    a whole number of blocks of waves or not)."""
+    a whole number of blocks of waves or not; m' > 128 and an odd m'/m take
+    the two single-scale kernels)."""
     cskv = _cskv()
     x, z, _ = _inputs(T, ms, dt, seed=ms * 31 + ml * 7 + T)
     bs = wl.normal(90, T, 5, (2 * ms, D), 0.1)
