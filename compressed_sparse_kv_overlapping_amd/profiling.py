@@ -18,6 +18,10 @@ the copy (known bytes / counted bytes), so the figure is in true bytes.
 ``summarize`` writes profiles/traffic.json (per launch of the benchmark's
 ``compress`` part, keyed by a digest of the kernel sources so that a stale
 figure is never reported) and prints the summary kept in profiles/.
+
+``trace <results.db> <command>`` prints, from a ``rocprofv3 --kernel-trace``
+database, each library kernel's dispatch count and average / min / max
+duration per grid shape, with the profiled command in the header.
 """
 import csv
 import glob
@@ -132,10 +136,33 @@ def summarize(fetch_dir, write_dir, digest=None):
           f"{alg / 1e9:.4f} GB (ratio {total / alg:.3f})")
 
 
+def trace(db, command):
+    import sqlite3
+    con = sqlite3.connect(db)
+    q = ("select s.kernel_name, d.grid_size_x / d.workgroup_size_x, d.grid_size_y, "
+         "d.grid_size_z, d.workgroup_size_x, d.end - d.start from rocpd_kernel_dispatch d "
+         "join rocpd_info_kernel_symbol s on d.kernel_id = s.id")
+    agg = {}
+    for name, gx, gy, gz, wx, dur in con.execute(q):
+        if "cskv" not in name:
+            continue
+        key = (name.replace(".kd", ""), f"{gx}x{gy}x{gz}", wx)
+        agg.setdefault(key, []).append(dur / 1000.0)
+    print(f"# rocprofv3 kernel trace summary\n# command: {command}\n"
+          f"# durations in microseconds (per dispatch)")
+    print(f"{'kernel':78s} {'grid(blocks)':>14s} {'wg':>4s} {'n':>4s} "
+          f"{'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+    for (nm, grid, wx), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{nm[:78]:78s} {grid:>14s} {wx:4d} {len(v):4d} {sum(v) / len(v):10.2f} "
+              f"{min(v):10.2f} {max(v):10.2f}")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 2 and sys.argv[1] == "run":
         run()
     elif len(sys.argv) >= 4 and sys.argv[1] == "summarize":
         summarize(sys.argv[2], sys.argv[3], sys.argv[4] if len(sys.argv) > 4 else None)
+    elif len(sys.argv) == 4 and sys.argv[1] == "trace":
+        trace(sys.argv[2], sys.argv[3])
     else:
         raise SystemExit(__doc__)
