@@ -430,29 +430,47 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
 // bf16 attention, 128 heads per block.
 //
 // A block of 4 waves takes 128 heads of one query and one split of its rows;
-// each wave owns 32 heads (two 16-head MFMA blocks), so every K or V
-// fragment read from LDS feeds two MFMAs.  A wave keeps its output
-// accumulators (256 registers) and the queries of its first head block (72)
-// in registers for the whole split; the queries of its second head block are
-// read from LDS.  One wave per SIMD.
+// each wave owns 32 heads and keeps their queries (144 registers) and their
+// output accumulators (O^T: 512 dims x 32 heads, 256 registers) for the
+// whole split.  One wave per SIMD.  Both products use the 32x32x16 bf16
+// MFMA:
+//   S^T[32 rows, 32 heads]  = K_tile . Q^T        36 k-steps, A = keys (LDS)
+//   O^T[32 dims, 32 heads] += V^T_tile . P^T      16 dim blocks x 2 k-steps,
+//                                                 A = values (LDS, transposed)
+// Lane l of S^T holds head l % 32 and the 16 rows 8 q + 4 (l / 32) + i
+// (register 4 q + i).  Rounded to bf16, registers 8u..8u+7 are the B operand
+// of k-step u of the second product as they stand: slot t there stands for
+// row 16 u + 4 (l / 32) + 8 (t / 4) + t % 4, and the value fragment of the
+// lane reads those same rows (two 4-row transposed reads).
 //
-// Tiles are gathered from HBM straight into LDS (global_load_lds, 16 bytes
-// per lane, no registers), one tile ahead into the other of two buffers.  A
-// tile holds 32 rows x 72 chunks of 16 bytes.  Copy n fills slots
-// [64 n, 64 n + 64): lanes 0..31 take chunk 2n of rows 0..31, lanes 32..63
-// chunk 2n + 1 of the rows rotated by 8, so that chunk c of row r sits in slot
-//   64 (c / 2) + 32 (c % 2) + ((r + 8 (c % 2)) % 32)
-// and every lane copies a single row.  Both LDS read patterns then touch
-// distinct banks (64 banks of 4 bytes, 16 lanes a pass):
-//   logits: 16 rows x one chunk (ds_read_b128): one 256-byte run, or two
-//           128-byte runs that do not alias,
-//   values: 4 rows x two chunks, read transposed (ds_read_b64_tr_b16): runs in
-//           distinct banks; the transposed read hands each lane four
-//           consecutive rows of one value dimension, the A operand of
-//           O^T += V^T P^T.
-// The gather is issued from inline assembly, so the compiler does not see
-// an LDS write in flight; the loop waits for it explicitly before the
-// barrier that opens each tile.
+// The loop is software-pipelined: while the MFMAs of the logits of tile t+1
+// run, the softmax of tile t (VALU work) is issued between them, one short
+// piece per k-step; the weighted sum of tile t follows.  Tiles are gathered
+// from HBM straight into LDS (global_load_lds, 16 bytes per lane, no
+// registers) into three buffers: tile t is read for its values, tile t+1 for
+// its keys, tile t+2 is in flight.
+//
+// Tile layout: 32 rows x 72 chunks of 16 bytes, row-major (1152 bytes a
+// row); chunk c of row r sits in slot c ^ g(r) of the row, with
+//   g(r) = 4 ((r / 2) % 2) + (r / 4) % 4,
+// a permutation inside each aligned group of 8 chunks (128 bytes).  Read
+// patterns (64 banks of 4 bytes; a 16-byte slot covers 4 banks and slot s of
+// row r the bank group (8 r + s) % 16):
+//   keys:   per 16 lanes, 16 rows of one chunk (ds_read_b128): the 8 even
+//           rows take the 8 values of g, the 8 odd rows the same 8 shifted
+//           by 8 groups: every bank once;
+//   values: per 32 lanes, 4 rows 4m..4m+3 of the 4 chunks of a 32-dim block
+//           (ds_read_b64_tr_b16): rows 4m and 4m+2 take opposite halves of
+//           the 8 groups (bit 2 of g differs), 4m+1 and 4m+3 the same shifted
+//           by 8: every bank once.
+// Copy n of a tile fills slots [64 n, 64 n + 64) of the row-major image:
+// lane i takes slot q = 64 n + i, i.e. row q / 72, chunk (q % 72) ^ g(row),
+// so one copy reads at most two rows' contiguous bytes (about 9 cache lines
+// instead of one per lane).  The copies are issued from inline assembly, so
+// the compiler does not see an LDS write in flight; the loop waits for them
+// explicitly before the barrier that opens each tile.  In the pipelined loop
+// a wave issues its 9 copies of tile t+2 spread over the logit steps of tile
+// t+1.
 //
 // Softmax reference: a head's first visible tile sets it (its accumulators
 // are still zero then) and it never moves, so the accumulators are never
@@ -461,15 +479,20 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
 // runs the split again: first for each head's exact maximum, then
 // accumulating against it.
 constexpr int kWideWaves = 4, kWideHeads = 128;
-constexpr int kQPitch = kE + 8;                              // query row pitch in LDS (elements)
-constexpr int kRowBytes = kE * 2, kRowChunks = kE / 8, kTileBytes = kTile * kRowBytes;
-constexpr int kTileLoads = kTile * kRowChunks / 64;          // 64-lane loads per tile (36)
-static_assert(kTileLoads % kWideWaves == 0, "whole loads per wave");
+constexpr int kRowBytes = kE * 2, kTileBytes = kTile * kRowBytes;
+constexpr int kTileLoads = kTile * (kE / 8) / 64;            // 64-lane copies per tile (36)
+constexpr int kQSteps = kE / 16;                             // k-steps of the logits (36)
+constexpr int kVBlocks = kDv / 32;                           // 32-dim blocks of the values (16)
+constexpr int kBufs = 3, kRing = 4;
+constexpr int kQReg = 24;                                    // k-steps whose queries stay in registers
+constexpr int kKDepth = 3, kVDepth = 4;                      // LDS fragment prefetch depths
+constexpr int kCopies = kTileLoads / kWideWaves;             // copies per wave per tile (9)
+static_assert(kTileLoads % kWideWaves == 0, "whole copies per wave");
+static_assert(kCopies * 4 <= kQSteps, "a wave's copies fit between the logit steps");
 
-// byte offset of chunk c of row r in a tile
-__device__ __forceinline__ int tile_off(int r, int c) {
-  return 1024 * (c >> 1) + 512 * (c & 1) + 16 * ((r + 8 * (c & 1)) & 31);
-}
+// slot permutation of row r, and the byte offset of chunk c of row r
+__device__ __forceinline__ int row_swz(int r) { return 4 * ((r >> 1) & 1) + ((r >> 2) & 3); }
+__device__ __forceinline__ int tile_off(int r, int c) { return kRowBytes * r + 16 * (c ^ row_swz(r)); }
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
@@ -479,14 +502,78 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// Logit MFMAs with the accumulator in VGPRs.  The output accumulators take
+// all 256 AGPRs, and the compiler puts every MFMA it emits in one register
+// file, so the logits product is issued here instead; the compiler does not
+// see it as an MFMA, so its hazards are covered by hand:
+//   - a VALU write of an operand needs 2 wait states: each MFMA is preceded
+//     by s_nop 1;
+//   - back-to-back accumulation into the same registers needs none;
+//   - a VALU read of the result needs up to 19 (16-pass XDL): wide_s_done
+//     waits 24 and pins the result after that point.
+__device__ __forceinline__ void mma32_v0(f32x16& c, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a.v), "v"(b.v));
+}
+__device__ __forceinline__ void mma32_v(f32x16& c, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a.v), "v"(b.v));
+}
+__device__ __forceinline__ void wide_s_done(f32x16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
+}
+
 struct WideShared {
-  __attribute__((aligned(16))) char kbuf[2][kTileBytes];
-  // queries of each wave's second head block (the first stays in registers)
-  __attribute__((aligned(16))) bf16_t qs[kWideWaves][16][kQPitch];
-  const char* row_ptr[3][kTile];
-  uint32_t row_mask[3];                                      // bit r: row r of the tile present
-  int flag[2][kWideWaves];
+  __attribute__((aligned(16))) char kbuf[kBufs][kTileBytes];
+  // queries of k-steps kQReg.. of each wave, lane-contiguous (16 bytes a lane)
+  __attribute__((aligned(16))) char qbuf[kWideWaves][kQSteps - kQReg][64 * 16];
+  const char* row_ptr[kRing][kTile];
+  int flag[kWideWaves];
 };
+
+// Lane offsets of the LDS read patterns.  Derived from the lane id where
+// they are used, so nothing lane-dependent stays in a register across the
+// loop.
+__device__ __forceinline__ int wide_lane() {
+  int lid;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
+  return lid;
+}
+// keys: k-step s reads row l % 32, chunk 2 s + l / 32, at k[s % 4] + 128 (s / 4)
+// (slot 2 s ^ (l / 32 ^ g) = 8 (s / 4) + (2 (s % 4) ^ (l / 32 ^ g)))
+struct KeyOffs { int k[4]; };
+__device__ __forceinline__ KeyOffs key_offs() {
+  const int lid = wide_lane();
+  const int r = lid & 31, x = (lid >> 5) ^ row_swz(r);
+  KeyOffs o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o.k[i] = kRowBytes * r + 16 * ((2 * i) ^ x);
+  return o;
+}
+// values: k-step u, read w (rows 16 u + 8 w + 4 (l / 32) + 0..3) of dim
+// block db at v[u][w][db % 2] + 128 (db / 2).  16-lane group G reads dims
+// 16 (G % 2) .. + 15 of the block: lane c of the group row c / 4 of a 4-row
+// run and the 4 dims 4 (c % 4) .. + 3, i.e. half c % 2 of chunk
+// 4 db + y, y = 2 (G % 2) + (c % 4) / 2, in slot 8 (db / 2) + ((4 (db % 2) + y) ^ g).
+struct ValOffs { int v[2][2][2]; };
+__device__ __forceinline__ ValOffs val_offs() {
+  const int lid = wide_lane();
+  const int h = lid >> 5, G = lid >> 4, c = lid & 15;
+  const int y = 2 * (G & 1) + ((c & 3) >> 1);
+  ValOffs o;
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int rr = 16 * u + 8 * w + 4 * h + (c >> 2);
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        o.v[u][w][p] = kRowBytes * rr + 16 * ((4 * p + y) ^ row_swz(rr)) + 8 * (c & 1);
+    }
+  return o;
+}
+// row mask of a tile shifted to the lane's rows: bit 8 q + i is register 4 q + i
+__device__ __forceinline__ uint32_t lane_mask(uint32_t row_mask) {
+  return row_mask >> (4 * (wide_lane() >> 5));
+}
 
 // One block's split.  EXACT = false: the main pass; returns true, without
 // writing anything, when a logit left its head's reference band.  EXACT =
@@ -495,9 +582,7 @@ struct WideShared {
 template <bool EXACT>
 __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   auto& kbuf = sh.kbuf;
-  auto& qs = sh.qs;
   auto& row_ptr = sh.row_ptr;
-  auto& row_mask = sh.row_mask;
   auto& flag = sh.flag;
   // uniform scalars the loop uses, pinned to scalar registers
   const float c_log2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.c)));
@@ -505,46 +590,34 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
-  const int col = lane & 15, g = lane >> 4;
-  int hh[2];
-  bool hok[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    hh[j] = hg * kWideHeads + wave * 32 + j * 16 + col;
-    hok[j] = hh[j] < a.H;
-  }
+  const int hl = lane & 31, lh = lane >> 5;
+  const int head = hg * kWideHeads + wave * 32 + hl;
+  const bool hok = head < a.H;
   const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q);
   const char* ent = reinterpret_cast<const char*>(a.entries);
   const char* win = reinterpret_cast<const char*>(a.window);
   const char* safe_row = reinterpret_cast<const char*>(q + (int64_t)b * a.H * kE);
 
-  // query fragments of head block 0: k-slots (g, t) <-> dim 32 ks + 8g + t
-  Frag<bf16_t> qf[18];
+  // queries, the B operand of the logits: k-step s, lane l holds head l % 32
+  // and dims 16 s + 8 (l / 32) .. + 7.  A head past H reads head 0 and
+  // writes nothing.
+  Frag<bf16_t> qf[kQReg];
   {
-    const bf16_t* qp = q + ((int64_t)b * a.H + (hok[0] ? hh[0] : 0)) * kE + 8 * g;
+    const bf16_t* qp = q + ((int64_t)b * a.H + (hok ? head : 0)) * kE + 8 * lh;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      frag_load(qf[ks], qp + 32 * ks);
-      if (!hok[0]) qf[ks].v = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  // head block 1 to LDS: lane (col, g) copies dims 8g..8g+7 of every 32
-  {
-    const bf16_t* qp = q + ((int64_t)b * a.H + (hok[1] ? hh[1] : 0)) * kE + 8 * g;
-#pragma unroll 6
-    for (int ks = 0; ks < 18; ++ks) {
-      uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * ks);
-      if (!hok[1]) v = make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(&qs[wave][col][32 * ks + 8 * g]) = v;
-    }
+    for (int s = 0; s < kQReg; ++s) frag_load(qf[s], qp + 16 * s);
+#pragma unroll
+    for (int s = kQReg; s < kQSteps; ++s)
+      *reinterpret_cast<uint4*>(&sh.qbuf[wave][s - kQReg][16 * lane]) =
+          *reinterpret_cast<const uint4*>(qp + 16 * s);
   }
 
-  f32x4 O[2][32];
+  f32x16 O[kVBlocks];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int db = 0; db < kVBlocks; ++db)
 #pragma unroll
-    for (int db = 0; db < 32; ++db) O[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
 
   int64_t win_row0 = 0;
   int nwin = a.W;
@@ -559,20 +632,22 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   const int s_end = min(a.nslots, s_begin + a.slots_per_split);
   const int ntiles = s_end > s_begin ? (s_end - s_begin + kTile - 1) / kTile : 0;
 
-  // Row addresses of tile t into ring slot t % 3 (wave 0, one lane per row).
-  // A selected entry comes in as e_sel, loaded a tile ahead by sel_load.
+  // Rows of tile t: every wave works out which rows are present (lane r
+  // for row r) and returns that mask, uniform; wave 0 also writes the row
+  // addresses into ring slot t % kRing for the copies.  A selected entry
+  // comes in as e_sel, loaded a tile ahead by sel_load.
   auto sel_load = [&](int t) {
     int e = -1;
-    if (threadIdx.x < kTile && !a.dense) {
-      const int s = s_begin + t * kTile + threadIdx.x;
+    if (lane < kTile && !a.dense) {
+      const int s = s_begin + t * kTile + lane;
       if (s < s_end && s < a.k) e = a.idx[(int64_t)b * a.k + s];
     }
     return e;
   };
   auto resolve = [&](int t, int e_sel) {
     int ok_lane = 0;
-    if (threadIdx.x < kTile) {
-      const int s = s_begin + t * kTile + threadIdx.x;
+    if (lane < kTile) {
+      const int s = s_begin + t * kTile + lane;
       const char* p = safe_row;
       int ok = 0;
       if (s < s_end) {
@@ -589,225 +664,252 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
           if (ok) p = win + ((int64_t)b * a.win_bstride + r * kE) * 2;
         }
       }
-      row_ptr[t % 3][threadIdx.x] = p;
+      if (wave == 0) row_ptr[t % kRing][lane] = p;
       ok_lane = ok;
     }
-    if (threadIdx.x < 64) {                                  // wave 0: bit r = row r present
-      const uint64_t m = __ballot(threadIdx.x < kTile && ok_lane);
-      if (threadIdx.x == 0) row_mask[t % 3] = (uint32_t)m;
-    }
+    return (uint32_t)__ballot(lane < kTile && ok_lane);     // bit r: row r present
   };
-  // gather tile t into buffer k: copy n (64 lanes x 16 bytes) fills LDS bytes
-  // [1024 n, 1024 n + 1024) of the buffer with chunks 2n (lanes 0..31) and
-  // 2n + 1 (lanes 32..63); a lane's copies all come from one row
+  // Copy i of this wave for tile t (copy n = wave + 4 i of the tile): this
+  // lane fills slot q = 64 n + lane of the row-major image, chunk
+  // (q % 72) ^ g of row q / 72.
+  auto copy_row = [&](int t, int i) {
+    const int q = 64 * (wave + kWideWaves * i) + lane;
+    return row_ptr[t % kRing][q / (kE / 8)];
+  };
+  auto copy_off = [&](int i) {
+    const int q = 64 * (wave + kWideWaves * i) + lane;
+    const int r = q / (kE / 8), j = q - (kE / 8) * r;
+    return 16 * (j ^ row_swz(r));
+  };
+  auto copy_src = [&](int t, int i) { return copy_row(t, i) + copy_off(i); };
+  auto copy_issue = [&](const char* src, int k, int i) {
+    const unsigned base = lds_offset(kbuf[k]) + 1024 * (wave + kWideWaves * i);
+    dma16(src, (unsigned)__builtin_amdgcn_readfirstlane(base));
+  };
+  // gather tile t into buffer k at once
   auto issue = [&](int t, int k) {
-    const unsigned base = lds_offset(kbuf[k]);
-    const int par = lane >> 5;
-    const int r = ((lane & 31) - 8 * par) & 31;
-    const char* rowp = row_ptr[t % 3][r] + 16 * par;
+    const char* src[kCopies];
 #pragma unroll
-    for (int i = 0; i < kTileLoads / kWideWaves; ++i) {
-      const int n = wave + i * kWideWaves;
-      dma16(rowp + 32 * n, (unsigned)__builtin_amdgcn_readfirstlane(base + 1024 * n));
-    }
+    for (int i = 0; i < kCopies; ++i) src[i] = copy_src(t, i);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) copy_issue(src[i], k, i);
   };
 
-  // Lane offsets of the LDS read patterns, derived from the lane id each
-  // time a tile starts: nothing lane-dependent stays in a register across
-  // the loop.
-  struct LaneOffs {
-    int k0, k1;        // logit rows col and 16 + col at chunk g (+ 2048 per 32-dim step)
-    int v0, v1;        // value rows 4g + col/4 and 16 + that (+ 1024 per 16-dim block)
-    int qoff;          // second head block's queries in LDS
-    int g4;            // 4 g
-  };
-  auto lane_offs = [&]() {
-    int lid;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
-    const int c = lid & 15, gg = lid >> 4;
-    LaneOffs o;
-    o.k0 = tile_off(c, gg);
-    o.k1 = tile_off(16 + c, gg);
-    const int vr = 4 * gg + (c >> 2), vc = (c & 3) >> 1;     // chunk 2 db + vc, half c & 1
-    o.v0 = tile_off(vr, vc) + ((c & 1) << 3);
-    o.v1 = tile_off(16 + vr, vc) + ((c & 1) << 3);
-    o.qoff = (int)lds_offset(&qs[wave][c][8 * gg]);
-    o.g4 = 4 * gg;
-    return o;
-  };
-
-  int flagged_here = 0;
-  // logits S^T[row, head] of one tile: rows 0..15 in S0, 16..31 in S1
-  auto qk_tile = [&](const char* kb, const LaneOffs& L, f32x4* S0, f32x4* S1) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) { S0[j] = f32x4{0.f, 0.f, 0.f, 0.f}; S1[j] = S0[j]; }
-    // fragments of step ks: rows col and 16 + col at chunk 4 ks + g, and the
-    // second head block's queries; double-buffered one step ahead
-    Frag<bf16_t> A0[2], A1[2], Q1[2];
-    auto kfrag = [&](int ks, int u) {
-      const uint4 x0 = *reinterpret_cast<const uint4*>(kb + L.k0 + 2048 * ks);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(kb + L.k1 + 2048 * ks);
-      const u32x4 y = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          (const __attribute__((address_space(3))) char*)(uintptr_t)(L.qoff + 64 * ks));
-      A0[u].v = u32x4{x0.x, x0.y, x0.z, x0.w};
-      A1[u].v = u32x4{x1.x, x1.y, x1.z, x1.w};
-      Q1[u].v = y;
+  // logits S^T of one tile; piece(s) is issued after the MFMA of k-step s
+  auto qk = [&](const char* kb, f32x16& S, auto&& piece) {
+    const KeyOffs L = key_offs();
+    const char* qb = &sh.qbuf[wave][0][16 * wide_lane()];
+    Frag<bf16_t> K[kKDepth], Q[kKDepth];
+    auto kload = [&](int s) {
+      const int off = L.k[s & 3] + 128 * (s >> 2);
+      K[s % kKDepth].v = *reinterpret_cast<const u32x4*>(kb + off);
+      if (s >= kQReg) Q[s % kKDepth].v = *reinterpret_cast<const u32x4*>(qb + 1024 * (s - kQReg));
     };
-    kfrag(0, 0);
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const int u = ks & 1;
-      if (ks + 1 < 18) kfrag(ks + 1, u ^ 1);
-      fence_sched();
-      mma16(S0[0], A0[u], qf[ks]);
-      mma16(S1[0], A1[u], qf[ks]);
-      mma16(S0[1], A0[u], Q1[u]);
-      mma16(S1[1], A1[u], Q1[u]);
+    for (int s = 0; s < kKDepth - 1; ++s) kload(s);
+#pragma unroll
+    for (int s = 0; s < kQSteps; ++s) {
+      if (s + kKDepth - 1 < kQSteps) kload(s + kKDepth - 1);
+      if (s == 0) mma32_v0(S, K[0], qf[0]);
+      else mma32_v(S, K[s % kKDepth], s < kQReg ? qf[s] : Q[s % kKDepth]);
+      piece(s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wide_s_done(S);
+  };
+  // O^T += V^T P^T for one tile
+  auto pv = [&](const char* vb, const Frag<bf16_t>* P) {
+    const ValOffs L = val_offs();
+    Frag<bf16_t> V[kVDepth];
+    // MFMA j: k-step u = j / 16, dim block db = j % 16
+    auto vload = [&](int j) {
+      const int u = j >> 4, db = j & 15;
+      const uint2 x = lds_read_tr(vb + L.v[u][0][db & 1] + 128 * (db >> 1));
+      const uint2 y = lds_read_tr(vb + L.v[u][1][db & 1] + 128 * (db >> 1));
+      V[j % kVDepth].v = u32x4{x.x, x.y, y.x, y.y};
+    };
+#pragma unroll
+    for (int j = 0; j < kVDepth - 1; ++j) vload(j);
+#pragma unroll
+    for (int j = 0; j < 2 * kVBlocks; ++j) {
+      if (j + kVDepth - 1 < 2 * kVBlocks) vload(j + kVDepth - 1);
+      mma32(O[j & 15], V[j % kVDepth], P[j >> 4]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // masked, scaled logits of one head block (log2 units) and their tile max
-  auto tile_logits = [&](int t, const LaneOffs& L, const f32x4& s0, const f32x4& s1, float* sv) {
-    const uint32_t m = row_mask[t % 3] >> L.g4;               // rows 4g + i and 16 + 4g + i
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = i < 4 ? s0[i] : s1[i - 4];
-      const int bit = i < 4 ? i : 12 + i;
-      sv[i] = ((m >> bit) & 1u) ? x * c_log2 : -INFINITY;
-      tmax = fmaxf(tmax, sv[i]);
-    }
-    return max_xor32(max_xor16(tmax));
+
+  // Softmax of one tile in pieces (piece s runs after logit k-step s of the
+  // next tile): masked, scaled logits; the tile maximum of the head; the
+  // reference (check: the main pass, which sets references and flags logits
+  // past the band); the weights, their sum and their bf16 B operands.
+  struct Soft {
+    float sv[16];
+    float mx, m_use, psum;
+    int flagged;
+    Frag<bf16_t> P[2];
   };
-  // one tile of the accumulation (check: the main pass, which sets the
-  // references and flags logits past the band)
-  auto tile_body = [&](int t, const char* kb, bool check) {
-    const LaneOffs L = lane_offs();
-    f32x4 S0[2], S1[2];
-    qk_tile(kb, L, S0, S1);
-    Frag<bf16_t> pf[2];
+  auto soft_piece = [&](int s, const f32x16& S, uint32_t mask, Soft& st, bool check) {
+    if (s < 4) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float sv[8];
-      const float tmax = tile_logits(t, L, S0[j], S1[j], sv);
+      for (int i = 4 * s; i < 4 * s + 4; ++i) {
+        const int bit = 8 * (i >> 2) + (i & 3);
+        const uint32_t m = (uint32_t)((int32_t)(mask << (31 - bit)) >> 31);  // all ones: row present
+        st.sv[i] = __uint_as_float((__float_as_uint(S[i] * c_log2) & m) | (0xff800000u & ~m));
+      }
+    } else if (s == 4) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, st.sv[i]);
+      st.mx = m;
+    } else if (s == 5) {
+      st.mx = max_xor32(st.mx);
+    } else if (s == 6) {
       if (check) {
-        if (m_ref[j] == -INFINITY) m_ref[j] = tmax;
-        else if (tmax > m_ref[j] + kRefBand) flagged_here = 1;
+        const bool first = (m_ref == -INFINITY);
+        st.flagged |= (!first && st.mx > m_ref + kRefBand) ? 1 : 0;
+        m_ref = first ? st.mx : m_ref;
       }
-      const float m_use = (m_ref[j] == -INFINITY) ? 0.f : m_ref[j];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sv[i] = __builtin_amdgcn_exp2f(sv[i] - m_use);
-        psum += sv[i];
+      st.m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      st.psum = 0.f;
+    } else if (s >= 7 && s < 23) {
+      const int i = s - 7;
+      st.sv[i] = __builtin_amdgcn_exp2f(st.sv[i] - st.m_use);
+      st.psum += st.sv[i];
+      if (i & 1) {
+        const int k = i >> 1;                                // pair k: slot pair of P[k / 4]
+        st.P[k >> 2].v[k & 3] = pack_bf16x2(st.sv[i - 1], st.sv[i]);
       }
-      l_run[j] += psum;
-      p_frag(pf[j], sv);
-    }
-    // O^T[d, head] += V^T[d, rows] . P^T[rows, head]; value fragments of
-    // 16-dim block db (chunks 2 db, 2 db + 1) run three blocks ahead
-    Frag<bf16_t> VF[4];
-    auto vfrag = [&](int db) {
-      const uint2 v0 = lds_read_tr(kb + L.v0 + 1024 * db), v1 = lds_read_tr(kb + L.v1 + 1024 * db);
-      VF[db & 3].v = u32x4{v0.x, v0.y, v1.x, v1.y};
-    };
-    vfrag(0);
-    vfrag(1);
-    vfrag(2);
-#pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      if (db + 3 < 32) vfrag(db + 3);
-      fence_sched();
-#pragma unroll
-      for (int j = 0; j < 2; ++j) mma16(O[j][db], VF[db & 3], pf[j]);
+    } else if (s == 23) {
+      l_run += st.psum;
     }
   };
-  auto any_flag = [&](int t) {
+  auto soft_all = [&](const f32x16& S, uint32_t mask, Soft& st, bool check) {
+#pragma unroll
+    for (int s = 0; s < 24; ++s) soft_piece(s, S, mask, st, check);
+  };
+  auto any_flag = [&]() {
     int any = 0;
 #pragma unroll
-    for (int w = 0; w < kWideWaves; ++w) any |= flag[t & 1][w];
+    for (int w = 0; w < kWideWaves; ++w) any |= flag[w];
     return any != 0;
   };
 
-  // prologue: rows of tiles 0 and 1, selection of tile 2, tile 0 in flight
-  int e_next = -1;
-  if (ntiles > 0) resolve(0, sel_load(0));
-  if (ntiles > 1) resolve(1, sel_load(1));
-  if (ntiles > 2) e_next = sel_load(2);
-  __syncthreads();                                           // rows and queries in LDS
-  if (ntiles > 0) issue(0, 0);
-
   if constexpr (!EXACT) {
-    bool redo = false;
+    // prologue: rows of tiles 0..2, selection of tile 3, tile 0 landed and
+    // its logits done, tile 1 in flight
+    // every ring slot the loop reads holds valid row addresses: slots of
+    // tiles past the split resolve to the safe row.  mk[i]: row mask of tile
+    // t + i.
+    uint32_t mk[4];
+    mk[0] = resolve(0, sel_load(0));
+    mk[1] = resolve(1, sel_load(1));
+    mk[2] = resolve(2, sel_load(2));
+    int e_next = sel_load(3);
+    __syncthreads();                                         // rows in LDS
+    f32x16 S;
+    if (ntiles > 0) {
+      issue(0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();                                       // tile 0 landed
+      if (ntiles > 1) issue(1, 1);
+      qk(kbuf[0], S, [](int) {});
+    }
+    // A logit past its band sets the wave's flag; the split then runs to the
+    // end and the block redoes it (the accumulated values are dropped).
+    Soft st;
+    st.flagged = 0;
     for (int t = 0; t < ntiles; ++t) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();                                       // tile t landed; tile t-1 fully read
-      if (t > 0 && any_flag(t - 1)) { redo = true; break; }  // block-uniform
-      // every load but the gather is issued first: a wait for it would
-      // otherwise drain the gather too
-      if (t + 2 < ntiles) resolve(t + 2, e_next);
-      if (t + 3 < ntiles) e_next = sel_load(t + 3);
-      if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
-      tile_body(t, kbuf[t & 1], true);
-      const int wave_flag = __any(flagged_here);             // any head of this wave
-      if (lane == 0) flag[t & 1][wave] = wave_flag;
+      __syncthreads();                                       // tile t+1 landed; tile t-1 fully read
+      const uint32_t mt = lane_mask(mk[0]);
+      if (t + 1 < ntiles) {
+        // every load but the gather is issued first: a wait for it would
+        // otherwise drain the gather too
+        mk[3] = resolve(t + 3, e_next);
+        e_next = sel_load(t + 4);
+        // copies of tile t+2 between the logit steps (row address read two
+        // steps ahead); past the last tile the ring holds the safe row, read
+        // into the free buffer
+        const int kn = (t + 2) % kBufs;
+        const char* rp = nullptr;
+        f32x16 Sn;
+        qk(kbuf[(t + 1) % kBufs], Sn, [&](int s) {
+          soft_piece(s, S, mt, st, true);
+          if ((s & 3) == 0 && (s >> 2) < kCopies) rp = copy_row(t + 2, s >> 2);
+          if ((s & 3) == 2 && (s >> 2) < kCopies) copy_issue(rp + copy_off(s >> 2), kn, s >> 2);
+        });
+        S = Sn;
+      } else {
+        soft_all(S, mt, st, true);
+      }
+      pv(kbuf[t % kBufs], st.P);
+      mk[0] = mk[1];
+      mk[1] = mk[2];
+      mk[2] = mk[3];
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0) flag[wave] = __any(st.flagged);
     __syncthreads();
-    if (!redo && ntiles > 0) redo = any_flag(ntiles - 1);
+    const bool redo = ntiles > 0 && any_flag();
     if (redo) return true;
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     auto load_tile = [&](int t) {
       __syncthreads();                                       // buffer and ring free
-      resolve(t, sel_load(t));
+      const uint32_t m = resolve(t, sel_load(t));
       __syncthreads();
       issue(t, 0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      return m;
     };
-    float mx[2] = {-INFINITY, -INFINITY};
+    float mx = -INFINITY;
     for (int t = 0; t < ntiles; ++t) {
-      load_tile(t);
-      const LaneOffs L = lane_offs();
-      f32x4 S0[2], S1[2];
-      qk_tile(kbuf[0], L, S0, S1);
+      const uint32_t mt = lane_mask(load_tile(t));
+      f32x16 S;
+      qk(kbuf[0], S, [](int) {});
+      Soft st;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float sv[8];
-        mx[j] = fmaxf(mx[j], tile_logits(t, L, S0[j], S1[j], sv));
-      }
+      for (int s = 0; s < 6; ++s) soft_piece(s, S, mt, st, false);
+      mx = fmaxf(mx, st.mx);
     }
-    m_ref[0] = mx[0];
-    m_ref[1] = mx[1];
+    m_ref = mx;
     for (int t = 0; t < ntiles; ++t) {
-      load_tile(t);
-      tile_body(t, kbuf[0], false);
+      const uint32_t mt = lane_mask(load_tile(t));
+      f32x16 S;
+      qk(kbuf[0], S, [](int) {});
+      Soft st;
+      st.flagged = 0;
+      soft_all(S, mt, st, false);
+      pv(kbuf[0], st.P);
     }
   }
 
   const float LN2 = 0.6931471805599453f;
+  const float l = sum_xor32(l_run);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse2 = l > 0.f ? m_ref + __log2f(l) : -INFINITY;
+  if (!hok) return false;
+  // lane l holds head l % 32, dims 32 db + 8 q + 4 (l / 32) + 0..3 in
+  // registers 4 q .. 4 q + 3 of block db
+  if (a.nsplit == 1) {
+    bf16_t* o = reinterpret_cast<bf16_t*>(a.out) + ((int64_t)b * a.H + head) * kDv + 4 * lh;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float l = sum_xor32(sum_xor16(l_run[j]));
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse2 = l > 0.f ? m_ref[j] + __log2f(l) : -INFINITY;
-    if (!hok[j]) continue;
-    const int h = hh[j];
-    if (a.nsplit == 1) {
-      bf16_t* o = reinterpret_cast<bf16_t*>(a.out) + ((int64_t)b * a.H + h) * kDv;
+    for (int db = 0; db < kVBlocks; ++db)
 #pragma unroll
-      for (int db = 0; db < 32; ++db)
-        store_out4<bf16_t>(o + 16 * db + 4 * g, O[j][db][0] * inv, O[j][db][1] * inv,
-                           O[j][db][2] * inv, O[j][db][3] * inv);
-      if (a.lse && g == 0) a.lse[(int64_t)b * a.H + h] = lse2 * LN2;
-    } else {
-      float* o = a.o_part + (((int64_t)b * a.H + h) * a.nsplit + split) * kDv;
+      for (int qq = 0; qq < 4; ++qq)
+        store_out4<bf16_t>(o + 32 * db + 8 * qq, O[db][4 * qq] * inv, O[db][4 * qq + 1] * inv,
+                           O[db][4 * qq + 2] * inv, O[db][4 * qq + 3] * inv);
+    if (a.lse && lh == 0) a.lse[(int64_t)b * a.H + head] = lse2 * LN2;
+  } else {
+    float* o = a.o_part + (((int64_t)b * a.H + head) * a.nsplit + split) * kDv + 4 * lh;
 #pragma unroll
-      for (int db = 0; db < 32; ++db)
-        store_out4<float>(o + 16 * db + 4 * g, O[j][db][0] * inv, O[j][db][1] * inv,
-                          O[j][db][2] * inv, O[j][db][3] * inv);
-      if (g == 0) a.lse_part[((int64_t)b * a.H + h) * a.nsplit + split] = lse2 * LN2;
-    }
+    for (int db = 0; db < kVBlocks; ++db)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        store_out4<float>(o + 32 * db + 8 * qq, O[db][4 * qq] * inv, O[db][4 * qq + 1] * inv,
+                          O[db][4 * qq + 2] * inv, O[db][4 * qq + 3] * inv);
+    if (lh == 0) a.lse_part[((int64_t)b * a.H + head) * a.nsplit + split] = lse2 * LN2;
   }
   return false;
 }
