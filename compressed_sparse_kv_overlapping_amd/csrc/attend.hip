@@ -484,8 +484,7 @@ constexpr int kTileLoads = kTile * (kE / 8) / 64;            // 64-lane copies p
 constexpr int kQSteps = kE / 16;                             // k-steps of the logits (36)
 constexpr int kVBlocks = kDv / 32;                           // 32-dim blocks of the values (16)
 constexpr int kBufs = 3, kRing = 4;
-constexpr int kQReg = 24;                                    // k-steps whose queries stay in registers
-constexpr int kKDepth = 3, kVDepth = 4;                      // LDS fragment prefetch depths
+constexpr int kKDepth = 4, kVDepth = 4;                      // LDS fragment prefetch depths
 constexpr int kCopies = kTileLoads / kWideWaves;             // copies per wave per tile (9)
 static_assert(kTileLoads % kWideWaves == 0, "whole copies per wave");
 static_assert(kCopies * 4 <= kQSteps, "a wave's copies fit between the logit steps");
@@ -523,8 +522,6 @@ __device__ __forceinline__ void wide_s_done(f32x16& c) {
 
 struct WideShared {
   __attribute__((aligned(16))) char kbuf[kBufs][kTileBytes];
-  // queries of k-steps kQReg.. of each wave, lane-contiguous (16 bytes a lane)
-  __attribute__((aligned(16))) char qbuf[kWideWaves][kQSteps - kQReg][64 * 16];
   const char* row_ptr[kRing][kTile];
   int flag[kWideWaves];
 };
@@ -601,15 +598,11 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   // queries, the B operand of the logits: k-step s, lane l holds head l % 32
   // and dims 16 s + 8 (l / 32) .. + 7.  A head past H reads head 0 and
   // writes nothing.
-  Frag<bf16_t> qf[kQReg];
+  Frag<bf16_t> qf[kQSteps];
   {
     const bf16_t* qp = q + ((int64_t)b * a.H + (hok ? head : 0)) * kE + 8 * lh;
 #pragma unroll
-    for (int s = 0; s < kQReg; ++s) frag_load(qf[s], qp + 16 * s);
-#pragma unroll
-    for (int s = kQReg; s < kQSteps; ++s)
-      *reinterpret_cast<uint4*>(&sh.qbuf[wave][s - kQReg][16 * lane]) =
-          *reinterpret_cast<const uint4*>(qp + 16 * s);
+    for (int s = 0; s < kQSteps; ++s) frag_load(qf[s], qp + 16 * s);
   }
 
   f32x16 O[kVBlocks];
@@ -698,12 +691,10 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   // logits S^T of one tile; piece(s) is issued after the MFMA of k-step s
   auto qk = [&](const char* kb, f32x16& S, auto&& piece) {
     const KeyOffs L = key_offs();
-    const char* qb = &sh.qbuf[wave][0][16 * wide_lane()];
-    Frag<bf16_t> K[kKDepth], Q[kKDepth];
+    Frag<bf16_t> K[kKDepth];
     auto kload = [&](int s) {
       const int off = L.k[s & 3] + 128 * (s >> 2);
       K[s % kKDepth].v = *reinterpret_cast<const u32x4*>(kb + off);
-      if (s >= kQReg) Q[s % kKDepth].v = *reinterpret_cast<const u32x4*>(qb + 1024 * (s - kQReg));
     };
 #pragma unroll
     for (int s = 0; s < kKDepth - 1; ++s) kload(s);
@@ -711,7 +702,7 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     for (int s = 0; s < kQSteps; ++s) {
       if (s + kKDepth - 1 < kQSteps) kload(s + kKDepth - 1);
       if (s == 0) mma32_v0(S, K[0], qf[0]);
-      else mma32_v(S, K[s % kKDepth], s < kQReg ? qf[s] : Q[s % kKDepth]);
+      else mma32_v(S, K[s % kKDepth], qf[s]);
       piece(s);
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -102,6 +102,37 @@ def test_sparse_attend_special_cases():
     np.testing.assert_allclose(lse.cpu().numpy(), np.log(N), rtol=1e-5)
 
 
+@pytest.mark.parametrize("N", [300, 8192])
+def test_logits_past_reference_band(N):
+    """Rows of tile 0 have small logits, and one row in every later tile a
+    logit about 200 log2-units higher: past the 64-unit band that a split
+    accumulates against after its first tile, so the split holding tile 0
+    (two or more tiles here) redoes its rows exactly, while later splits set
+    their reference from a large logit.  HCA and sparse attention must still
+    match the oracle."""
+    dt, B, H = wl.DT_BF16, 2, 128
+    rng = np.random.default_rng(N)
+    qf = 0.5 + 0.01 * rng.standard_normal((B, H, E))
+    ef = 0.1 * rng.standard_normal((N, E))
+    big = np.arange(32 + 5, N, 32)
+    ef[big] = 0.5 + 0.01 * rng.standard_normal((len(big), E))
+    q, ent = wl.encode(qf, dt).raw, wl.encode(ef, dt).raw
+    out, lse = _cskv().hca_attend(dev(q), dev(ent))
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q, ent, dt)
+    _check_attn(out, lse, ro, rl, dt)
+    # the same rows as a selection (entries in index order), plus a window
+    # of small rows
+    W = 128
+    win = wl.encode(0.1 * rng.standard_normal((W, E)), dt).raw
+    k = min(N, 1024)
+    idx = np.tile(np.arange(k, dtype=np.int32), (B, 1))
+    out, lse = _cskv().sparse_attend(dev(q), dev(ent), dev(win), torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend(q, ent, win, dt, idx)
+    _check_attn(out, lse, ro, rl, dt)
+
+
 def test_merge_of_split_partials():
     """cskv_merge combines oracle partials over a row partition into the
     oracle's unsplit result."""
