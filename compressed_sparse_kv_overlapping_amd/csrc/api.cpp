@@ -171,8 +171,11 @@ size_t cskv_attend_workspace_size(int64_t B, int32_t H, int64_t rows_per_query) 
 
 static int check_attend(const char* fn, const void* q, const void* entries, const void* window,
                         int64_t B, int32_t H, int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
-                        int64_t win_bstride, int64_t win_rows, cskv_dtype dt, const void* out) {
+                        int64_t win_bstride, int64_t win_rows, cskv_dtype dt, const void* out,
+                        float scale) {
   if (!q || !entries || !out) return fail(CSKV_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (!(scale >= 0.f) || scale > 3.0e38f)
+    return fail(CSKV_ERR_INVALID_ARG, "%s: scale must be non-negative and finite", fn);
   if (W > 0 && !window) return fail(CSKV_ERR_INVALID_ARG, "%s: W=%d without a window", fn, W);
   if (B < 1 || H < 1 || N < 0 || W < 0 || k < 0 || ent_bstride < 0 || win_bstride < 0 ||
       win_rows < 0)
@@ -195,7 +198,7 @@ int cskv_sparse_attend(const void* q, const void* entries, const void* window, c
                        int64_t win_pos0, float scale, cskv_dtype dt, void* out, float* lse,
                        void* workspace, size_t ws_bytes, void* stream) {
   int st = check_attend("cskv_sparse_attend", q, entries, window, B, H, N, W, k, ent_bstride,
-                        win_bstride, win_rows, dt, out);
+                        win_bstride, win_rows, dt, out, scale);
   if (st) return st;
   if (k > 0 && !idx) return fail(CSKV_ERR_INVALID_ARG, "cskv_sparse_attend: null idx");
   if (!q_pos && W > win_rows)
@@ -226,7 +229,7 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
                       idx_scale, idx_dt, idx_out);
   if (st) return st;
   st = check_attend("cskv_csa_attend", q, entries, window, B, H, N, W, k, ent_bstride, win_bstride,
-                    win_rows, dt, out);
+                    win_rows, dt, out, scale);
   if (st) return st;
   if (!q_pos && W > win_rows)
     return fail(CSKV_ERR_INVALID_ARG, "cskv_csa_attend: W=%d > window rows %lld", W,
@@ -254,7 +257,7 @@ int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, in
                     int64_t ent_bstride, float scale, cskv_dtype dt, void* out, float* lse,
                     void* workspace, size_t ws_bytes, void* stream) {
   int st = check_attend("cskv_hca_attend", q, entries, nullptr, B, H, N, 0, 0, ent_bstride, 0, 0,
-                        dt, out);
+                        dt, out, scale);
   if (st) return st;
   const size_t need = cskv::attend_partial_bytes((int)dt, B, H, N);
   if (need && (!workspace || ws_bytes < need || !aligned16(workspace)))

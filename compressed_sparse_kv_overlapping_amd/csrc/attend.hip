@@ -496,8 +496,11 @@ __device__ __forceinline__ int tile_off(int r, int c) { return kRowBytes * r + 1
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
 
-__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
-  const v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)p);
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+
+// transposed 4 x b16 read at LDS byte offset off
+__device__ __forceinline__ uint2 lds_read_tr_at(unsigned off) {
+  const v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(uintptr_t)off);
   return __builtin_bit_cast(uint2, r);
 }
 
@@ -567,9 +570,11 @@ __device__ __forceinline__ ValOffs val_offs() {
     }
   return o;
 }
-// row mask of a tile shifted to the lane's rows: bit 8 q + i is register 4 q + i
-__device__ __forceinline__ uint32_t lane_mask(uint32_t row_mask) {
-  return row_mask >> (4 * (wide_lane() >> 5));
+// x in the lanes of m, y in the others (one v_cndmask on a scalar lane mask)
+__device__ __forceinline__ float sel_lanes(float x, float y, uint64_t m) {
+  float r;
+  asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(y), "v"(x), "s"(m));
+  return r;
 }
 
 // One block's split.  EXACT = false: the main pass; returns true, without
@@ -583,6 +588,8 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   auto& flag = sh.flag;
   // uniform scalars the loop uses, pinned to scalar registers
   const float c_log2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.c)));
+  const float ninf = -INFINITY;
+  const hw_bf16x2_t ones_bf16x2 = __builtin_bit_cast(hw_bf16x2_t, 0x3f803f80u);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -690,11 +697,18 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
 
   // logits S^T of one tile; piece(s) is issued after the MFMA of k-step s
   auto qk = [&](const char* kb, f32x16& S, auto&& piece) {
+    // per-lane read addresses of this buffer, pinned so that every read is
+    // one of them plus an immediate offset
     const KeyOffs L = key_offs();
+    unsigned kp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kp[i] = lds_offset(kb) + L.k[i];
+      asm volatile("" : "+v"(kp[i]));
+    }
     Frag<bf16_t> K[kKDepth];
     auto kload = [&](int s) {
-      const int off = L.k[s & 3] + 128 * (s >> 2);
-      K[s % kKDepth].v = *reinterpret_cast<const u32x4*>(kb + off);
+      K[s % kKDepth].v = *reinterpret_cast<const lds_u32x4_t*>((uintptr_t)(kp[s & 3] + 128 * (s >> 2)));
     };
 #pragma unroll
     for (int s = 0; s < kKDepth - 1; ++s) kload(s);
@@ -709,14 +723,24 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     wide_s_done(S);
   };
   // O^T += V^T P^T for one tile
-  auto pv = [&](const char* vb, const Frag<bf16_t>* P) {
+  auto pv = [&](const char* vb, const Frag<bf16_t>* P, auto&& piece) {
     const ValOffs L = val_offs();
+    unsigned vp[2][2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          vp[u][w][q] = lds_offset(vb) + L.v[u][w][q];
+          asm volatile("" : "+v"(vp[u][w][q]));
+        }
     Frag<bf16_t> V[kVDepth];
     // MFMA j: k-step u = j / 16, dim block db = j % 16
     auto vload = [&](int j) {
       const int u = j >> 4, db = j & 15;
-      const uint2 x = lds_read_tr(vb + L.v[u][0][db & 1] + 128 * (db >> 1));
-      const uint2 y = lds_read_tr(vb + L.v[u][1][db & 1] + 128 * (db >> 1));
+      const uint2 x = lds_read_tr_at(vp[u][0][db & 1] + 128 * (db >> 1));
+      const uint2 y = lds_read_tr_at(vp[u][1][db & 1] + 128 * (db >> 1));
       V[j % kVDepth].v = u32x4{x.x, x.y, y.x, y.y};
     };
 #pragma unroll
@@ -725,6 +749,7 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     for (int j = 0; j < 2 * kVBlocks; ++j) {
       if (j + kVDepth - 1 < 2 * kVBlocks) vload(j + kVDepth - 1);
       mma32(O[j & 15], V[j % kVDepth], P[j >> 4]);
+      piece(j);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -739,13 +764,20 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     int flagged;
     Frag<bf16_t> P[2];
   };
+  // mask: the tile's row mask (uniform).  Logits stay unscaled until the
+  // exponent: c >= 0, so the head's maximum of c l is c times its maximum of
+  // l, and exp2(c l - m) is one FMA and the exponential.  The weights' sum is
+  // taken over their bf16 values, the ones the weighted sum uses.
   auto soft_piece = [&](int s, const f32x16& S, uint32_t mask, Soft& st, bool check) {
     if (s < 4) {
 #pragma unroll
       for (int i = 4 * s; i < 4 * s + 4; ++i) {
-        const int bit = 8 * (i >> 2) + (i & 3);
-        const uint32_t m = (uint32_t)((int32_t)(mask << (31 - bit)) >> 31);  // all ones: row present
-        st.sv[i] = __uint_as_float((__float_as_uint(S[i] * c_log2) & m) | (0xff800000u & ~m));
+        // register i holds row 8 (i / 4) + 4 (l / 32) + i % 4: lanes 0..31
+        // take bit b of the mask, lanes 32..63 bit b + 4
+        const int b = 8 * (i >> 2) + (i & 3);
+        const uint64_t lo = (mask >> b) & 1u ? 0xffffffffull : 0ull;
+        const uint64_t hi = (mask >> (b + 4)) & 1u ? 0xffffffff00000000ull : 0ull;
+        st.sv[i] = sel_lanes(S[i], ninf, lo | hi);
       }
     } else if (s == 4) {
       float m = -INFINITY;
@@ -753,22 +785,25 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
       for (int i = 0; i < 16; ++i) m = fmaxf(m, st.sv[i]);
       st.mx = m;
     } else if (s == 5) {
-      st.mx = max_xor32(st.mx);
+      const float m = max_xor32(st.mx);
+      st.mx = m == -INFINITY ? m : m * c_log2;               // the head's tile maximum of c l
     } else if (s == 6) {
       if (check) {
         const bool first = (m_ref == -INFINITY);
         st.flagged |= (!first && st.mx > m_ref + kRefBand) ? 1 : 0;
         m_ref = first ? st.mx : m_ref;
       }
-      st.m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      st.m_use = (m_ref == -INFINITY) ? 0.f : -m_ref;        // negated reference
       st.psum = 0.f;
     } else if (s >= 7 && s < 23) {
       const int i = s - 7;
-      st.sv[i] = __builtin_amdgcn_exp2f(st.sv[i] - st.m_use);
-      st.psum += st.sv[i];
+      st.sv[i] = __builtin_amdgcn_exp2f(fmaf(st.sv[i], c_log2, st.m_use));
       if (i & 1) {
         const int k = i >> 1;                                // pair k: slot pair of P[k / 4]
-        st.P[k >> 2].v[k & 3] = pack_bf16x2(st.sv[i - 1], st.sv[i]);
+        const uint32_t pk = pack_bf16x2(st.sv[i - 1], st.sv[i]);
+        st.P[k >> 2].v[k & 3] = pk;
+        st.psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(hw_bf16x2_t, pk), ones_bf16x2,
+                                                  st.psum, false);
       }
     } else if (s == 23) {
       l_run += st.psum;
@@ -811,21 +846,25 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     st.flagged = 0;
     for (int t = 0; t < ntiles; ++t) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // the selection loaded last tile is settled here, where nothing is in
+      // flight: its use below then waits for no copy of this tile
+      asm volatile("" : "+v"(e_next));
       __syncthreads();                                       // tile t+1 landed; tile t-1 fully read
-      const uint32_t mt = lane_mask(mk[0]);
+      const uint32_t mt = mk[0];
       if (t + 1 < ntiles) {
-        // every load but the gather is issued first: a wait for it would
-        // otherwise drain the gather too
-        mk[3] = resolve(t + 3, e_next);
-        e_next = sel_load(t + 4);
-        // copies of tile t+2 between the logit steps (row address read two
-        // steps ahead); past the last tile the ring holds the safe row, read
-        // into the free buffer
+        // Between the logit steps: the copies of tile t+2 (row address read
+        // two steps ahead; past the last tile the ring holds the safe row,
+        // read into the free buffer).  The rows of tile t+3 and the
+        // selection of tile t+4 follow between the weighted-sum steps.
         const int kn = (t + 2) % kBufs;
         const char* rp = nullptr;
+        // a fresh copy of the logits: the softmax below is then not merged
+        // with the last tile's and hoisted ahead of the MFMAs
+        uint32_t mtp = mt;
+        asm volatile("" : "+v"(S));
         f32x16 Sn;
         qk(kbuf[(t + 1) % kBufs], Sn, [&](int s) {
-          soft_piece(s, S, mt, st, true);
+          soft_piece(s, S, mtp, st, true);
           if ((s & 3) == 0 && (s >> 2) < kCopies) rp = copy_row(t + 2, s >> 2);
           if ((s & 3) == 2 && (s >> 2) < kCopies) copy_issue(rp + copy_off(s >> 2), kn, s >> 2);
         });
@@ -833,7 +872,12 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
       } else {
         soft_all(S, mt, st, true);
       }
-      pv(kbuf[t % kBufs], st.P);
+      pv(kbuf[t % kBufs], st.P, [&](int j) {
+        if (j == 8) {
+          mk[3] = resolve(t + 3, e_next);
+          e_next = sel_load(t + 4);
+        }
+      });
       mk[0] = mk[1];
       mk[1] = mk[2];
       mk[2] = mk[3];
@@ -856,7 +900,7 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     };
     float mx = -INFINITY;
     for (int t = 0; t < ntiles; ++t) {
-      const uint32_t mt = lane_mask(load_tile(t));
+      const uint32_t mt = load_tile(t);
       f32x16 S;
       qk(kbuf[0], S, [](int) {});
       Soft st;
@@ -866,13 +910,13 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     }
     m_ref = mx;
     for (int t = 0; t < ntiles; ++t) {
-      const uint32_t mt = lane_mask(load_tile(t));
+      const uint32_t mt = load_tile(t);
       f32x16 S;
       qk(kbuf[0], S, [](int) {});
       Soft st;
       st.flagged = 0;
       soft_all(S, mt, st, false);
-      pv(kbuf[0], st.P);
+      pv(kbuf[0], st.P, [](int) {});
     }
   }
 
@@ -994,7 +1038,10 @@ static hipError_t launch_attend_t(const AttendParams& p, void* ws, hipStream_t s
   a.win_rows = p.win_rows; a.dense = p.dense;
   a.N = p.N; a.B = (int)p.B; a.H = p.H; a.W = p.dense ? 0 : p.W; a.k = p.dense ? 0 : p.k;
   a.nslots = (int)(p.dense ? p.N : (int64_t)p.k + p.W);
-  a.c = p.scale * 1.4426950408889634f;
+  // scale >= 0 (checked by the caller).  Scale 0 (uniform weights) runs as
+  // the smallest normal scale: the logits are then indistinguishable from 0,
+  // and a missing row (logit -inf) still gets weight 0 rather than NaN.
+  a.c = p.scale > 0.f ? p.scale * 1.4426950408889634f : 1.17549435e-38f;
   a.out = p.out; a.lse = p.lse;
   const int S = attend_splits(p.dt, p.B, p.H, a.nslots);
   const int64_t tiles = (a.nslots + kTile - 1) / kTile;

@@ -157,8 +157,9 @@ int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t 
  * One softmax covers the selected entries and the window together.
  *   idx [B][k] int32 (-1 = no entry; any order); q, entries, window, out in dt
  *   (F32 or BF16); workspace: cskv_attend_workspace_size(...) bytes.
+ * scale must be >= 0 and finite (0 gives uniform weights over the rows).
  * Errors: INVALID_ARG (null pointers, sizes < 0, window positions outside the
- * buffer); UNSUPPORTED (dt not F32/BF16); WORKSPACE.
+ * buffer, scale < 0 or not finite); UNSUPPORTED (dt not F32/BF16); WORKSPACE.
  */
 size_t cskv_attend_workspace_size(int64_t B, int32_t H, int64_t rows_per_query);
 int cskv_sparse_attend(const void* q, const void* entries, const void* window, const int32_t* idx,
@@ -184,7 +185,8 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
  * HCA ("Frontier Techniques", 2.2; "DeepSeek V4 comprimeix el context",
  * section "HCA: un resum global 128 vegades mes curt"): every query attends
  * densely over all N entries, no selection and no window.  Same formulas as
- * cskv_sparse_attend with rows = entries[b*ent_bstride + i*576], i < N.
+ * cskv_sparse_attend with rows = entries[b*ent_bstride + i*576], i < N, and
+ * the same conditions on scale and errors.
  */
 size_t cskv_hca_workspace_size(int64_t B, int32_t H, int64_t N);
 int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, int64_t N,

@@ -102,10 +102,14 @@ def test_attend_errors(lib):
     assert call(idx=NULL) == INVALID
     assert call(ws=NULL) == WORKSPACE
     assert call(w=NULL) == INVALID
+    assert call(sc=-0.5) == INVALID                                   # negative scale
+    assert call(sc=float("inf")) == INVALID
+    assert call(sc=float("nan")) == INVALID
     h = lib.cskv_hca_attend
     hws = lib.cskv_hca_workspace_size(32, 128, 8192)
     assert h(P, P, 32, 128, 8192, 0, 1.0, 1, P, P, NULL, hws, NULL) == WORKSPACE
     assert h(P, P, 32, 128, 8192, 0, 1.0, 2, P, P, P, hws, NULL) == UNSUPPORTED
+    assert h(P, P, 32, 128, 8192, 0, -1.0, 1, P, P, P, hws, NULL) == INVALID
     m = lib.cskv_merge
     assert m(P, P, 2, 4, 0, P, P, 1, NULL) == INVALID
     assert m(P, P, 2, 4, 3, P, P, 2, NULL) == UNSUPPORTED
