@@ -11,11 +11,12 @@
 // generation must remember").  All heads read the same rows.
 //
 // Kernel shape: a block handles one query, a group of heads and one split of
-// that query's rows.  Rows arrive in tiles of 32: the block gathers them into
-// LDS twice, row-major (K, for the logits) and transposed (V^T, for the
-// weighted sum).  Each wave owns HB blocks of 16 heads (16x16x32 bf16 MFMA,
-// or 16x16x4 fp32) and keeps their queries and output accumulators in
-// registers.  Per tile:
+// that query's rows, in tiles of 32 rows.  Two kernels: attend_wide_kernel
+// (bf16, 128 heads per block, described at its section below) and
+// attend_kernel (fp32, 16 heads per block), which gathers each tile into LDS
+// twice, row-major (K, for the logits) and transposed (V^T, for the weighted
+// sum), with 16x16x4 fp32 MFMA; each wave keeps its heads' queries and
+// output accumulators in registers.  Per tile:
 //   S^T[rows, heads] = K_tile . Q^T            (MFMA, A = K from LDS)
 //   online softmax per head (exp2 domain)
 //   O^T[d, heads]   += V^T_tile . P^T           (MFMA, A = V^T from LDS)
