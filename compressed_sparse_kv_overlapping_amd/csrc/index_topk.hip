@@ -395,6 +395,7 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
 
 // Exclusive prefix sum over the block (256 threads): wave scans, then the
 // wave totals.  *total receives the block sum.  part[] holds 4 values.
+template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* part, uint32_t* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint32_t incl = x;
@@ -407,7 +408,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* part, 
   __syncthreads();
   uint32_t base = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     const uint32_t p = part[i];
     base += i < w ? p : 0u;
     tot += p;
@@ -417,17 +418,18 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* part, 
   return base + incl - x;
 }
 
-// Bin of hist[nbins] (nbins a multiple of 256, 256 threads) that holds the
-// kk-th largest counted key: thread t owns the t-th group of nbins/256 bins
+// Bin of hist[nbins] (nbins a multiple of NT, NT threads) that holds the
+// kk-th largest counted key: thread t owns the t-th group of nbins/NT bins
 // from the top.  *sh_digit gets the bin, *sh_above the keys in higher bins.
+template <int NT>
 __device__ void find_kth_bin(const uint32_t* hist, int nbins, uint32_t kk, uint32_t* sh_digit,
                              uint32_t* sh_above, uint32_t* part) {
   const int t = threadIdx.x;
-  const int per = nbins / 256;
+  const int per = nbins / NT;
   uint32_t local = 0;
   for (int i = 0; i < per; ++i) local += hist[nbins - 1 - (t * per + i)];
   uint32_t tot;
-  const uint32_t before = block_excl_scan(local, part, &tot);
+  const uint32_t before = block_excl_scan<NT>(local, part, &tot);
   if (before < kk && kk <= before + local) {
     uint32_t cum = before;
     for (int i = 0; i < per; ++i) {
@@ -443,7 +445,9 @@ __device__ void find_kth_bin(const uint32_t* hist, int nbins, uint32_t kk, uint3
   __syncthreads();
 }
 
-// Block min and max of the valid keys (256 threads; part[] holds 8 values).
+// Block min and max of the valid keys (NT threads; part[] holds NT / 32
+// values).
+template <int NT>
 __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, uint32_t* part, uint32_t* out_mn,
                                              uint32_t* out_mx) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -452,10 +456,15 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, uint32_t*
     mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
   }
-  if (lane == 0) { part[w] = mn; part[4 + w] = mx; }
+  if (lane == 0) { part[w] = mn; part[NT / 64 + w] = mx; }
   __syncthreads();
-  mn = min(min(part[0], part[1]), min(part[2], part[3]));
-  mx = max(max(part[4], part[5]), max(part[6], part[7]));
+  mn = part[0];
+  mx = part[NT / 64];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) {
+    mn = min(mn, part[i]);
+    mx = max(mx, part[NT / 64 + i]);
+  }
   __syncthreads();
   *out_mn = mn;
   *out_mx = mx;
@@ -467,7 +476,7 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, uint32_t*
 // high bits still fall into distinct bins (few colliding LDS atomics) and a
 // range of 2^r takes ceil(r / BB) passes.  *above_out: valid keys greater
 // than the result.
-template <int BB, class KeyAt>
+template <int BB, int NT, class KeyAt>
 __device__ uint32_t block_kth_largest(KeyAt key_at, int n, uint32_t kk, uint32_t lo, uint32_t hi,
                                       uint32_t* hist, uint32_t* part, uint32_t* sh_digit,
                                       uint32_t* sh_above, uint32_t* above_out) {
@@ -477,14 +486,14 @@ __device__ uint32_t block_kth_largest(KeyAt key_at, int n, uint32_t kk, uint32_t
     if (range == 0) break;
     const int bits = 32 - __clz((int)range);              // range < 2^bits
     const int shift = bits > BB ? bits - BB : 0;
-    for (int i = threadIdx.x; i < (1 << BB); i += 256) hist[i] = 0;
+    for (int i = threadIdx.x; i < (1 << BB); i += NT) hist[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += 256) {
+    for (int i = threadIdx.x; i < n; i += NT) {
       uint32_t key;
       if (key_at(i, key) && key >= lo && key <= hi) atomicAdd(&hist[(key - lo) >> shift], 1u);
     }
     __syncthreads();
-    find_kth_bin(hist, 1 << BB, kk, sh_digit, sh_above, part);
+    find_kth_bin<NT>(hist, 1 << BB, kk, sh_digit, sh_above, part);
     const uint32_t bin = *sh_digit;
     kk -= *sh_above;
     above_total += *sh_above;
@@ -501,20 +510,21 @@ __device__ uint32_t block_kth_largest(KeyAt key_at, int n, uint32_t kk, uint32_t
 // A lower bound of the k-th largest of the G group maxima of each query (0
 // if fewer than k non-empty groups or fewer than k visible entries).  The
 // maxima are read from L2; only the histogram lives in LDS.
-__global__ __launch_bounds__(256) void idx_threshold_kernel(IdxArgs a) {
-  __shared__ uint32_t hist[4096], part[8];
+template <int NT>
+__global__ __launch_bounds__(NT) void idx_threshold_kernel(IdxArgs a) {
+  __shared__ uint32_t hist[4096], part[NT / 32];
   __shared__ uint32_t sh_digit, sh_above;
   const int b = blockIdx.x;
   const uint32_t* gm = a.gmax + (int64_t)b * a.G;
   uint32_t ne = 0, mn = 0xffffffffu, mx = 0u;
-  for (int i = threadIdx.x; i < a.G; i += 256) {
+  for (int i = threadIdx.x; i < a.G; i += NT) {
     const uint32_t v = gm[i];
     if (v != 0u) { ++ne; mn = min(mn, v); mx = max(mx, v); }
   }
   uint32_t nonempty;
-  block_excl_scan(ne, part, &nonempty);
+  block_excl_scan<NT>(ne, part, &nonempty);
   uint32_t lo, hi;
-  block_minmax(mn, mx, part, &lo, &hi);
+  block_minmax<NT>(mn, mx, part, &lo, &hi);
   const int nv = n_visible(a, b);
   if (nv <= a.k || nonempty < (uint32_t)a.k) {
     if (threadIdx.x == 0) a.thr[b] = 0u;
@@ -527,20 +537,19 @@ __global__ __launch_bounds__(256) void idx_threshold_kernel(IdxArgs a) {
   const uint32_t range = hi - lo;
   const int bits = range ? 32 - __clz((int)range) : 0;     // range < 2^bits
   const int shift = bits > 12 ? bits - 12 : 0;
-  for (int i = threadIdx.x; i < 4096; i += 256) hist[i] = 0;
+  for (int i = threadIdx.x; i < 4096; i += NT) hist[i] = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < a.G; i += 256) {
+  for (int i = threadIdx.x; i < a.G; i += NT) {
     const uint32_t v = gm[i];
     if (v != 0u) atomicAdd(&hist[(v - lo) >> shift], 1u);
   }
   __syncthreads();
-  find_kth_bin(hist, 4096, (uint32_t)a.k, &sh_digit, &sh_above, part);
+  find_kth_bin<NT>(hist, 4096, (uint32_t)a.k, &sh_digit, &sh_above, part);
   if (threadIdx.x == 0) a.thr[b] = lo + (sh_digit << shift);
 }
 
 // ----------------------------------------------------------------- final
 
-constexpr int kFinalThreads = 256;
 
 // 64-bit composite of the scored entry e: score key high, ~e low (so that
 // larger composite = higher score, then lower index).
@@ -581,15 +590,15 @@ template <> __device__ __forceinline__ float dot64<e4m3_t>(const e4m3_t* q, cons
 constexpr int kMaxChunks = 2048;
 constexpr int kFinalBB = 11;                 // histogram of 2^11 bins
 constexpr int kMem = 512;                    // bin members ranked exactly
-template <class T>
-__global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
+template <class T, int NT>
+__global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
   // candidates (list) or, on overflow, the k selected indices
   __shared__ union { uint64_t cand[kCap]; int32_t sel[kMaxK]; } cs;
   // the histogram, then the members of the k-th bin, then the chunks' output
   // offsets
   __shared__ union { uint32_t hist[1 << kFinalBB]; uint64_t mem[kMem]; uint16_t csel[kMaxChunks]; } hs;
   __shared__ uint16_t coff[kMaxChunks + 1];                  // list offset of each chunk
-  __shared__ uint32_t part[8];
+  __shared__ uint32_t part[NT / 32];
   __shared__ uint32_t sh_digit, sh_above, sh_nsel, sh_over;
   __shared__ uint64_t sh_thr;
   uint64_t* cand = cs.cand;
@@ -600,14 +609,14 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
   const int nv = n_visible(a, b);
   int32_t* out = a.out + (int64_t)b * a.k;
   if (nv <= a.k) {
-    for (int j = t; j < a.k; j += kFinalThreads) out[j] = j < nv ? j : -1;
+    for (int j = t; j < a.k; j += NT) out[j] = j < nv ? j : -1;
     return;
   }
   // gather: thread t owns chunks [c0, c1); a full region or more than kCap
   // candidates in total means overflow
   if (t == 0) sh_over = 0;
   const bool listed = a.chunks <= kMaxChunks;               // else: streaming path
-  const int cpt = (a.chunks + kFinalThreads - 1) / kFinalThreads;
+  const int cpt = (a.chunks + NT - 1) / NT;
   const int c0 = listed ? min(a.chunks, t * cpt) : 0, c1 = listed ? min(a.chunks, c0 + cpt) : 0;
   uint32_t mine = 0;
   bool full = !listed;
@@ -619,7 +628,7 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
   __syncthreads();
   if (full) sh_over = 1;
   uint32_t total;
-  const uint32_t base = block_excl_scan(mine, part, &total);
+  const uint32_t base = block_excl_scan<NT>(mine, part, &total);
   const bool overflow = sh_over != 0 || total > (uint32_t)kCap;
   if (!overflow) {
     // chunk offsets in the list, then a copy spread over the whole block:
@@ -632,7 +641,7 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
     }
     if (t == 0) coff[a.chunks] = (uint16_t)total;
     __syncthreads();
-    for (uint32_t j = t; j < total; j += kFinalThreads) {
+    for (uint32_t j = t; j < total; j += NT) {
       int lo = 0, hi = a.chunks;                             // coff[lo] <= j < coff[hi]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -650,34 +659,34 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
   uint64_t prefix = 0;
   if (!overflow) {
     uint32_t mn = 0xffffffffu, mx = 0u;
-    for (int j = t; j < nc; j += kFinalThreads) {
+    for (int j = t; j < nc; j += NT) {
       const uint32_t h = (uint32_t)(cand[j] >> 32);
       mn = min(mn, h);
       mx = max(mx, h);
     }
     uint32_t lo, hi;
-    block_minmax(mn, mx, part, &lo, &hi);
+    block_minmax<NT>(mn, mx, part, &lo, &hi);
     const uint32_t range = hi - lo;
     const int bits = range ? 32 - __clz((int)range) : 0;   // range < 2^bits
     const int shift = bits > kFinalBB ? bits - kFinalBB : 0;
-    for (int i = t; i < (1 << kFinalBB); i += kFinalThreads) hist[i] = 0;
+    for (int i = t; i < (1 << kFinalBB); i += NT) hist[i] = 0;
     if (t == 0) { sh_nsel = 0; sh_thr = 0; }
     __syncthreads();
-    for (int j = t; j < nc; j += kFinalThreads)
+    for (int j = t; j < nc; j += NT)
       atomicAdd(&hist[((uint32_t)(cand[j] >> 32) - lo) >> shift], 1u);
     __syncthreads();
-    find_kth_bin(hist, 1 << kFinalBB, (uint32_t)a.k, &sh_digit, &sh_above, part);
+    find_kth_bin<NT>(hist, 1 << kFinalBB, (uint32_t)a.k, &sh_digit, &sh_above, part);
     const uint32_t bin = sh_digit, kk = (uint32_t)a.k - sh_above, nbin = hist[bin];
     __syncthreads();                                         // hist is read; mem reuses it
     if (nbin <= (uint32_t)kMem) {
       // the bin's members; the one with exactly kk - 1 larger members is
       // the k-th largest overall (composites are distinct)
-      for (int j = t; j < nc; j += kFinalThreads) {
+      for (int j = t; j < nc; j += NT) {
         const uint64_t v = cand[j];
         if ((((uint32_t)(v >> 32) - lo) >> shift) == bin) hs.mem[atomicAdd(&sh_nsel, 1u)] = v;
       }
       __syncthreads();
-      for (uint32_t i = t; i < nbin; i += kFinalThreads) {
+      for (uint32_t i = t; i < nbin; i += NT) {
         const uint64_t v = hs.mem[i];
         uint32_t r = 0;
         for (uint32_t j = 0; j < nbin; ++j) r += hs.mem[j] > v;
@@ -689,21 +698,21 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
       // a crowded bin: the score word by further passes, then the index
       // word among the candidates tied on that score
       uint32_t above;
-      const uint32_t th = block_kth_largest<kFinalBB>(
+      const uint32_t th = block_kth_largest<kFinalBB, NT>(
           [&](int j, uint32_t& key) { key = (uint32_t)(cand[j] >> 32); return true; }, nc,
           (uint32_t)a.k, lo, hi, hist, part, &sh_digit, &sh_above, &above);
       const uint32_t kt = (uint32_t)a.k - above;             // to take among score th
       mn = 0xffffffffu;
       mx = 0u;
-      for (int j = t; j < nc; j += kFinalThreads) {
+      for (int j = t; j < nc; j += NT) {
         const uint64_t v = cand[j];
         if ((uint32_t)(v >> 32) == th) {
           mn = min(mn, (uint32_t)v);
           mx = max(mx, (uint32_t)v);
         }
       }
-      block_minmax(mn, mx, part, &lo, &hi);
-      const uint32_t tl = block_kth_largest<kFinalBB>(
+      block_minmax<NT>(mn, mx, part, &lo, &hi);
+      const uint32_t tl = block_kth_largest<kFinalBB, NT>(
           [&](int j, uint32_t& key) {
             const uint64_t v = cand[j];
             key = (uint32_t)v;
@@ -723,15 +732,15 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
       const int bits = (p % 3 == 2) ? 10 : 11;
       const int shift = 64 - 32 * (p / 3) - (p % 3 == 0 ? 11 : (p % 3 == 1 ? 22 : 32));
       const uint32_t nb = 1u << bits;
-      for (int i = t; i < (int)nb; i += kFinalThreads) hist[i] = 0;
+      for (int i = t; i < (int)nb; i += NT) hist[i] = 0;
       __syncthreads();
-      for (int e = t; e < nv; e += kFinalThreads) {
+      for (int e = t; e < nv; e += NT) {
         const float s = dot64<T>(qrow, kb + (int64_t)e * kI) * a.scale;
         const uint64_t v = composite(score_key(s), e);
         if ((v & mask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & (nb - 1)], 1u);
       }
       __syncthreads();
-      find_kth_bin(hist, (int)nb, kk, &sh_digit, &sh_above, part);
+      find_kth_bin<NT>(hist, (int)nb, kk, &sh_digit, &sh_above, part);
       kk -= sh_above;
       const uint32_t bucket = hist[sh_digit];
       prefix |= (uint64_t)sh_digit << shift;
@@ -755,14 +764,14 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
       mine_sel += m;
     }
     uint32_t nsel;
-    uint32_t ob = block_excl_scan(mine_sel, part, &nsel);
+    uint32_t ob = block_excl_scan<NT>(mine_sel, part, &nsel);
     for (int c = c0; c < c1; ++c) {
       const uint32_t m = hs.csel[c];
       hs.csel[c] = (uint16_t)ob;
       ob += m;
     }
     __syncthreads();
-    for (uint32_t j = t; j < total; j += kFinalThreads) {
+    for (uint32_t j = t; j < total; j += NT) {
       const uint64_t v = cand[j];
       if (v < thr) continue;
       int lo = 0, hi = a.chunks;                             // chunk of slot j
@@ -778,13 +787,13 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
       const uint32_t o = hs.csel[lo] + rank;
       if (o < (uint32_t)a.k) out[o] = (int32_t)(0xffffffffu - (uint32_t)v);
     }
-    for (int j = (int)nsel + t; j < a.k; j += kFinalThreads) out[j] = -1;
+    for (int j = (int)nsel + t; j < a.k; j += NT) out[j] = -1;
     return;
   }
   // overflow: collect the selected indices by streaming, then sort them
   if (t == 0) sh_nsel = 0;
   __syncthreads();
-  for (int e = t; e < nv; e += kFinalThreads) {
+  for (int e = t; e < nv; e += NT) {
     const float s = dot64<T>(qrow, kb + (int64_t)e * kI) * a.scale;
     if (composite(score_key(s), e) >= thr) {
       const uint32_t at = atomicAdd(&sh_nsel, 1u);
@@ -794,11 +803,11 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
   __syncthreads();
   int n2 = 1;
   while (n2 < a.k) n2 <<= 1;
-  for (int j = a.k + t; j < n2; j += kFinalThreads) sel[j] = 0x7fffffff;
+  for (int j = a.k + t; j < n2; j += NT) sel[j] = 0x7fffffff;
   __syncthreads();
   for (int size = 2; size <= n2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = t; i < n2 / 2; i += kFinalThreads) {
+      for (int i = t; i < n2 / 2; i += NT) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
         const bool up = (lo & size) == 0;
@@ -808,7 +817,7 @@ __global__ __launch_bounds__(kFinalThreads) void idx_final_kernel(IdxArgs a) {
       __syncthreads();
     }
   }
-  for (int j = t; j < a.k; j += kFinalThreads) out[j] = sel[j];
+  for (int j = t; j < a.k; j += NT) out[j] = sel[j];
 }
 
 // ------------------------------------------------------------------ host
@@ -869,6 +878,9 @@ size_t topk_workspace_bytes(int64_t B, int64_t N, int k) {
   return bytes + 256;
 }
 
+// below this many queries the per-query kernels take 1024 threads a block
+constexpr int64_t kWideBelow = 256;
+
 int topk_max_k() { return kMaxK; }
 int64_t topk_max_entries() { return (int64_t)kMaxGroups * 64; }
 
@@ -897,12 +909,19 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
   else if (nqb == 1) CSKV_SCORE(1, MODE, 1);                                   \
   else if (nqb == 2) CSKV_SCORE(2, MODE, 1);                                   \
   else CSKV_SCORE(4, MODE, 1)
+  // one block per query for the threshold and the final selection: 1024
+  // threads when there are fewer queries than compute units (decode), so
+  // that each query's serial steps run on a whole compute unit; 256 threads
+  // otherwise (two blocks per compute unit)
+  const bool wide = p.B < kWideBelow;
   CSKV_SCORE_PASS(0);
-  hipLaunchKernelGGL(idx_threshold_kernel, dim3((unsigned)p.B), dim3(256), 0, stream, a);
+  if (wide) hipLaunchKernelGGL(idx_threshold_kernel<1024>, dim3((unsigned)p.B), dim3(1024), 0, stream, a);
+  else hipLaunchKernelGGL(idx_threshold_kernel<256>, dim3((unsigned)p.B), dim3(256), 0, stream, a);
   CSKV_SCORE_PASS(1);
 #undef CSKV_SCORE_PASS
 #undef CSKV_SCORE
-  hipLaunchKernelGGL(idx_final_kernel<T>, dim3((unsigned)p.B), dim3(kFinalThreads), 0, stream, a);
+  if (wide) hipLaunchKernelGGL((idx_final_kernel<T, 1024>), dim3((unsigned)p.B), dim3(1024), 0, stream, a);
+  else hipLaunchKernelGGL((idx_final_kernel<T, 256>), dim3((unsigned)p.B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
