@@ -835,10 +835,17 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     __syncthreads();                                         // rows in LDS
     f32x16 S;
     if (ntiles > 0) {
+      // tiles 0 and 1 in flight together; at most the kCopies copies of
+      // tile 1 may still be outstanding once tile 0 has landed
       issue(0, 0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (ntiles > 1) {
+        issue(1, 1);
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      static_assert(kCopies == 9, "the wait above counts one tile's copies");
       __syncthreads();                                       // tile 0 landed
-      if (ntiles > 1) issue(1, 1);
       qk(kbuf[0], S, [](int) {});
     }
     // A logit past its band sets the wave's flag; the split then runs to the
@@ -967,7 +974,9 @@ __global__ __launch_bounds__(64 * kWideWaves) void attend_wide_kernel(AttnArgs a
 }
 
 // One wave per (query, head): lse = ln sum_s exp(lse_s); out = sum_s
-// exp(lse_s - lse) o_s.  Splits are combined in index order.
+// exp(lse_s - lse) o_s.  Lane l takes the lse of splits l, l + 64, ...; the
+// partial rows are loaded eight splits at a time and accumulated in split
+// order, so the result does not depend on timing.
 template <class T>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
                                                     const float* __restrict__ lse_part, int64_t BH,
@@ -978,18 +987,37 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   if (bh >= BH) return;
   const float* lp = lse_part + bh * S;
   float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, lp[s]);
+  for (int s = lane; s < S; s += 64) mx = fmaxf(mx, lp[s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (mx != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float w = __expf(lp[s] - mx);
-      tot += w;
-      float v[8];
-      Row8<float>::load(o_part + (bh * S + s) * kDv + lane * 8, v);
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const int n = min(64, S - s0);
+      const float wl = lane < n ? __expf(lp[s0 + lane] - mx) : 0.f;   // weight of split s0 + lane
+      tot += wl;
+      for (int j = 0; j < n; j += 8) {
+        float v[8][8];
+        float w[8];
 #pragma unroll
-      for (int d = 0; d < 8; ++d) acc[d] = fmaf(w, v[d], acc[d]);
+        for (int u = 0; u < 8; ++u) {
+          w[u] = __shfl(wl, j + u, 64);
+          if (j + u < n) {
+            Row8<float>::load(o_part + (bh * S + s0 + j + u) * kDv + lane * 8, v[u]);
+          } else {
+#pragma unroll
+            for (int d = 0; d < 8; ++d) v[u][d] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int d = 0; d < 8; ++d) acc[d] = fmaf(w[u], v[u][d], acc[d]);
+      }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
