@@ -52,7 +52,8 @@ def lib():
         L.cskv_oracle_topk.argtypes = [vp, vp, i64, i64, i32, vp]
         L.cskv_oracle_csa_attend.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, vp,
                                              i64, i64, i64, i64, vp, i64, dbl, vp, vp]
-        L.cskv_oracle_hca_attend.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, dbl, vp, vp]
+        L.cskv_oracle_hca_attend.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, vp, i32, dbl,
+                                             vp, vp]
         L.cskv_oracle_max_threads.restype = i32
         _lib = L
     return _lib
@@ -158,14 +159,19 @@ def csa_attend(q, entries, window, dt, idx, scale=1.0, q_pos=None, win_pos0=0, W
     return out, lse
 
 
-def hca_attend(q, entries, dt, scale=1.0, per_seq=False, Dv=D):
-    """Dense attention over all entries.  Returns (out [B, H, Dv], lse [B, H])."""
+def hca_attend(q, entries, dt, scale=1.0, per_seq=False, Dv=D, q_pos=None, m=None):
+    """Dense attention over the entries each query sees: all of them at
+    decode (q_pos None); at a prefill chunk, entries i with (i+1)*m <=
+    q_pos[b] + 1.  Returns (out [B, H, Dv], lse [B, H])."""
     q, entries = _c(q), _c(entries)
     B, H, Ee = q.shape
     N = entries.shape[-2]
+    qp = None if q_pos is None else np.ascontiguousarray(q_pos, dtype=np.int64)
     out = np.empty((B, H, Dv), dtype=np.float64)
     lse = np.empty((B, H), dtype=np.float64)
     _check(lib().cskv_oracle_hca_attend(_p(q), _p(entries), dt, B, H, Ee, Dv, N,
-                                        N * Ee if per_seq else 0, float(scale), _p(out), _p(lse)),
+                                        N * Ee if per_seq else 0, _p(qp),
+                                        int(m) if m is not None else 0, float(scale), _p(out),
+                                        _p(lse)),
            "hca_attend")
     return out, lse

@@ -274,23 +274,33 @@ int cskv_oracle_csa_attend(const void* q, const void* entries, const void* windo
   return 0;
 }
 
-/* HCA: every query attends densely over all N entries; no window. */
+/* HCA: every query attends densely over the entries it can see; no window.
+ * Decode (q_pos == NULL): all N entries.  Prefill chunk: the query at
+ * position q_pos[b] sees entry i iff (i+1)*m <= q_pos[b] + 1, the same
+ * causal rule as the indexer's (an entry exists once its block of m tokens
+ * is complete), i.e. entries 0 .. min(N, (q_pos[b]+1)/m) - 1. */
 int cskv_oracle_hca_attend(const void* q, const void* entries, int dt, int64_t B, int64_t H,
-                           int64_t E, int64_t Dv, int64_t N, int64_t ent_bstride, double scale,
-                           double* out, double* lse) {
+                           int64_t E, int64_t Dv, int64_t N, int64_t ent_bstride,
+                           const int64_t* q_pos, int m, double scale, double* out, double* lse) {
   if (!q || !entries || !out || !lse || B < 0 || H <= 0 || E <= 0 || Dv <= 0 || Dv > E ||
       N < 0 || !dt_ok(dt))
     return -1;
+  if (q_pos && m <= 0) return -1;
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
   for (int64_t b = 0; b < B; ++b) {
     for (int64_t h = 0; h < H; ++h) {
-      const void** buf = (const void**)malloc(sizeof(void*) * (N > 0 ? N : 1));
-      int64_t* off = (int64_t*)malloc(sizeof(int64_t) * (N > 0 ? N : 1));
-      for (int64_t i = 0; i < N; ++i) {
+      int64_t n = N;
+      if (q_pos) {
+        const int64_t vis = q_pos[b] + 1 < 0 ? 0 : (q_pos[b] + 1) / m;
+        n = vis < N ? vis : N;
+      }
+      const void** buf = (const void**)malloc(sizeof(void*) * (n > 0 ? n : 1));
+      int64_t* off = (int64_t*)malloc(sizeof(int64_t) * (n > 0 ? n : 1));
+      for (int64_t i = 0; i < n; ++i) {
         buf[i] = entries;
         off[i] = b * ent_bstride + i * E;
       }
-      attend_rows(q, (b * H + h) * E, dt, buf, off, N, E, Dv, scale, out + (b * H + h) * Dv,
+      attend_rows(q, (b * H + h) * E, dt, buf, off, n, E, Dv, scale, out + (b * H + h) * Dv,
                   lse + b * H + h);
       free(buf);
       free(off);

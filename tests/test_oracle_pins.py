@@ -402,6 +402,39 @@ def test_hca_equals_csa_with_all_entries_and_no_window():
         np.testing.assert_allclose(o1[b], ro, rtol=1e-12, atol=1e-14)
 
 
+def test_hca_prefill_causal_visibility():
+    """HCA at a prefill chunk: the query at position pos sees entries i with
+    (i+1)m <= pos+1.  Pins: no visible entry gives a zero output and lse
+    -inf; otherwise the result equals the NumPy formulation over the first
+    min(N, (pos+1)//m) entries; with every entry visible it is the decode
+    result itself; one more block of m positions adds exactly one entry."""
+    m, N, Dv = 4, 40, 8
+    pos = np.array([2, 3, 57, 60, 61, N * m - 1, 10**6], dtype=np.int64)
+    q, ent, _ = _rand_attn(19, B=len(pos), N=N)
+    out, lse = oracle.hca_attend(q, ent, F32, Dv=Dv, q_pos=pos, m=m)
+    full, lfull = oracle.hca_attend(q, ent, F32, Dv=Dv)
+    nvis = [min(N, (int(p) + 1) // m) for p in pos]
+    assert nvis == [0, 1, 14, 15, 15, N, N]
+    for b, n in enumerate(nvis):
+        if n == 0:
+            assert (out[b] == 0).all() and np.isneginf(lse[b]).all()
+            continue
+        ro, rl = numpy_ref.attend(q[b].astype(float), ent[:n].astype(float), Dv)
+        np.testing.assert_allclose(out[b], ro, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[b], rl, rtol=1e-13)
+        if n == N:
+            np.testing.assert_array_equal(out[b], full[b])
+            np.testing.assert_array_equal(lse[b], lfull[b])
+    # the same query at positions 57 and 61 (one block later): exactly
+    # entry 14 more
+    oa, _ = oracle.hca_attend(q[2:3], ent, F32, Dv=Dv, q_pos=np.array([57]), m=m)
+    ob, _ = oracle.hca_attend(q[2:3], ent, F32, Dv=Dv, q_pos=np.array([61]), m=m)
+    o15, _ = oracle.hca_attend(q[2:3], ent[:15], F32, Dv=Dv)
+    np.testing.assert_array_equal(oa, out[2:3])
+    np.testing.assert_array_equal(ob, o15)
+    assert not np.allclose(oa, ob)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 7, 40])
 def test_split_merge_formula_recovers_unsplit(splits):
     """lse-weighted merge of partial attentions over a partition of the rows
