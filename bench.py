@@ -186,6 +186,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args, cskv, wl, dev, torch, np)
+        torch.cuda.empty_cache()
+        result["hca_prefill"] = bench_hca_prefill(args, cskv, wl, dev, torch, np)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, inp, cfg, ms_step, np)
     print(json.dumps(result), flush=True)
@@ -242,6 +244,41 @@ def bench_prefill(args, cskv, wl, dev, torch, np):
         "attention_roofline": {"bound": "mfma", "achieved": round(att_flops / (t_att * 1e-3) / 1e12, 1),
                                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                "frac": round(att_flops / (t_att * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+    }
+
+
+def bench_hca_prefill(args, cskv, wl, dev, torch, np):
+    """HCA at the same prefill chunk: 4,096 causal queries at positions
+    1,044,480..1,048,575 attend densely over the 8,192 m'=128 entries they
+    see ((i+1)*128 <= pos+1: 8,160..8,192 of them)."""
+    cfg = wl.CONFIGS["hca_prefill"]
+    inp = wl.make_inputs(cfg, seed=args.seed)
+    B, H, N, m = cfg.B, cfg.H, cfg.N_hca, cfg.m_hca
+    q, ent = dev(inp["q_hca"]), dev(inp["entries_hca"])
+    qp = torch.from_numpy(inp["q_pos"]).cuda()
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, cskv.hca_workspace_size(B, H, N)), dtype=torch.uint8, device="cuda")
+    run = lambda: cskv.hca_attend(q, ent, q_pos=qp, m=m, out=out, lse=lse, workspace=ws)
+    for _ in range(2):
+        run()
+    steps = max(3, args.steps // 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / steps
+    n_vis = np.minimum((inp["q_pos"] + 1) // m, N)
+    flops = 2 * H * int(n_vis.sum()) * (E + D)
+    return {
+        "workload": "hca_prefill", "queries": B, "entries": N, "ms": round(t, 4),
+        "entries_attended_per_s": round(int(n_vis.sum()) / (t * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(flops / (t * 1e-3) / 1e12, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
 
 

@@ -48,8 +48,8 @@ _SIGS = {
                          _i64, _i64, _vp, _i64, _f32, _f32, ctypes.c_int, ctypes.c_int, _vp, _vp,
                          _vp, _vp, _sz, _vp], ctypes.c_int),
     "cskv_hca_workspace_size": ([_i64, _i32, _i64], _sz),
-    "cskv_hca_attend": ([_vp, _vp, _i64, _i32, _i64, _i64, _f32, ctypes.c_int, _vp, _vp, _vp, _sz,
-                         _vp], ctypes.c_int),
+    "cskv_hca_attend": ([_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, ctypes.c_int, _vp, _vp,
+                         _vp, _sz, _vp], ctypes.c_int),
     "cskv_merge": ([_vp, _vp, _i64, _i32, _i32, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
@@ -244,10 +244,14 @@ def hca_workspace_size(B, H, N):
     return library().cskv_hca_workspace_size(B, H, N)
 
 
-def hca_attend(q, entries, scale=1.0, per_seq=False, out=None, lse=None, workspace=None,
-               stream=None):
-    """HCA: dense attention of q [B, H, 576] over all entries [N, 576]."""
-    _dev(q, entries, out, lse)
+def hca_attend(q, entries, scale=1.0, per_seq=False, q_pos=None, m=None, out=None, lse=None,
+               workspace=None, stream=None):
+    """HCA: dense attention of q [B, H, 576] over the entries [N, 576] each
+    query sees: all of them (q_pos None), or at a prefill chunk those with
+    (i+1)*m <= q_pos[b] + 1 (q_pos [B] int64 on the device)."""
+    _dev(q, entries, q_pos, out, lse)
+    if q_pos is not None and m is None:
+        raise ValueError("hca_attend: q_pos needs the block size m")
     B, H = q.shape[0], q.shape[1]
     N = entries.shape[-2]
     if out is None:
@@ -257,8 +261,8 @@ def hca_attend(q, entries, scale=1.0, per_seq=False, out=None, lse=None, workspa
     if workspace is None:
         workspace = _workspace(hca_workspace_size(B, H, N), q.device)
     _call("cskv_hca_attend", _ptr(q), _ptr(entries), B, H, N, N * E if per_seq else 0,
-          float(scale), _dt(q), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
-          _stream(stream))
+          _ptr(q_pos), int(m) if q_pos is not None else 0, float(scale), _dt(q), _ptr(out),
+          _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
     return out, lse
 
 

@@ -209,7 +209,7 @@ int cskv_sparse_attend(const void* q, const void* entries, const void* window, c
     return fail(CSKV_ERR_WORKSPACE, "cskv_sparse_attend: workspace %zu bytes, need %zu", ws_bytes,
                 need);
   cskv::AttendParams p{(int)dt, q, entries, window, idx, q_pos, B, N, ent_bstride, win_bstride,
-                       win_pos0, win_rows, H, W, k, scale, out, lse, 0};
+                       win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), "cskv_sparse_attend");
 }
 
@@ -243,7 +243,7 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
   hipError_t e = cskv::launch_topk(tp, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "cskv_csa_attend (top-k)");
   cskv::AttendParams ap{(int)dt, q, entries, window, idx_out, q_pos, B, N, ent_bstride,
-                        win_bstride, win_pos0, win_rows, H, W, k, scale, out, lse, 0};
+                        win_bstride, win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0};
   return hip_status(cskv::launch_attend(ap, (char*)workspace + topk_bytes, (hipStream_t)stream),
                     "cskv_csa_attend (attention)");
 }
@@ -254,16 +254,18 @@ size_t cskv_hca_workspace_size(int64_t B, int32_t H, int64_t N) {
 }
 
 int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, int64_t N,
-                    int64_t ent_bstride, float scale, cskv_dtype dt, void* out, float* lse,
-                    void* workspace, size_t ws_bytes, void* stream) {
+                    int64_t ent_bstride, const int64_t* q_pos, int32_t m, float scale,
+                    cskv_dtype dt, void* out, float* lse, void* workspace, size_t ws_bytes,
+                    void* stream) {
   int st = check_attend("cskv_hca_attend", q, entries, nullptr, B, H, N, 0, 0, ent_bstride, 0, 0,
                         dt, out, scale);
   if (st) return st;
+  if (q_pos && m < 1) return fail(CSKV_ERR_INVALID_ARG, "cskv_hca_attend: m=%d with q_pos", m);
   const size_t need = cskv::attend_partial_bytes((int)dt, B, H, N);
   if (need && (!workspace || ws_bytes < need || !aligned16(workspace)))
     return fail(CSKV_ERR_WORKSPACE, "cskv_hca_attend: workspace %zu bytes, need %zu", ws_bytes, need);
-  cskv::AttendParams p{(int)dt, q, entries, nullptr, nullptr, nullptr, B, N, ent_bstride, 0, 0, 0,
-                       H, 0, 0, scale, out, lse, 1};
+  cskv::AttendParams p{(int)dt, q, entries, nullptr, nullptr, q_pos, B, N, ent_bstride, 0, 0, 0,
+                       H, 0, 0, scale, out, lse, 1, q_pos ? m : 0};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), "cskv_hca_attend");
 }
 

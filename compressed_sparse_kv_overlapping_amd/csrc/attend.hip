@@ -56,6 +56,7 @@ struct AttnArgs {
   const int64_t* q_pos;      // NULL: decode window
   int64_t ent_bstride, win_bstride, win_pos0, win_rows, N;
   int dense;                 // 1: all N entries, no window (HCA)
+  int hm;                    // dense with q_pos: entry i visible iff (i+1)*hm <= q_pos[b]+1
   int B, H, W, k, nslots, slots_per_split, nsplit;
   float c;                   // scale * log2(e)
   void* out;                 // [B][H][512] when nsplit == 1
@@ -63,6 +64,16 @@ struct AttnArgs {
   float* o_part;             // [B][H][nsplit][512]
   float* lse_part;           // [B][H][nsplit]
 };
+
+// End of a split's rows: in dense mode at a prefill chunk, the entries the
+// query at q_pos[b] sees (i with (i+1)*hm <= q_pos[b]+1) end the range, so
+// tiles past them are not visited at all.
+__device__ __forceinline__ int dense_end(const AttnArgs& a, int b, int s_begin, int s_end) {
+  if (!a.dense || a.hm <= 0 || !a.q_pos) return s_end;
+  const int64_t p1 = a.q_pos[b] + 1;
+  const int64_t vis = p1 > 0 ? p1 / a.hm : 0;
+  return vis < s_end ? (vis > s_begin ? (int)vis : s_begin) : s_end;
+}
 
 // Keeps the scheduler from hoisting every LDS fragment load of an unrolled
 // loop to its top (which would need more registers than a wave has).
@@ -214,7 +225,7 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
     win_row0 = lo - a.win_pos0;
   }
   const int s_begin = split * a.slots_per_split;
-  const int s_end = min(a.nslots, s_begin + a.slots_per_split);
+  const int s_end = dense_end(a, b, s_begin, min(a.nslots, s_begin + a.slots_per_split));
 
   // Software pipeline: while tile i is multiplied out of LDS, the rows of
   // tile i+1 are already in flight into registers (their addresses were
@@ -630,7 +641,7 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     win_row0 = lo - a.win_pos0;
   }
   const int s_begin = split * a.slots_per_split;
-  const int s_end = min(a.nslots, s_begin + a.slots_per_split);
+  const int s_end = dense_end(a, b, s_begin, min(a.nslots, s_begin + a.slots_per_split));
   const int ntiles = s_end > s_begin ? (s_end - s_begin + kTile - 1) / kTile : 0;
 
   // Rows of tile t: every wave works out which rows are present (lane r
@@ -1064,7 +1075,7 @@ static hipError_t launch_attend_t(const AttendParams& p, void* ws, hipStream_t s
   AttnArgs a;
   a.q = p.q; a.entries = p.entries; a.window = p.window; a.idx = p.idx; a.q_pos = p.q_pos;
   a.ent_bstride = p.ent_bstride; a.win_bstride = p.win_bstride; a.win_pos0 = p.win_pos0;
-  a.win_rows = p.win_rows; a.dense = p.dense;
+  a.win_rows = p.win_rows; a.dense = p.dense; a.hm = p.hm;
   a.N = p.N; a.B = (int)p.B; a.H = p.H; a.W = p.dense ? 0 : p.W; a.k = p.dense ? 0 : p.k;
   a.nslots = (int)(p.dense ? p.N : (int64_t)p.k + p.W);
   // scale >= 0 (checked by the caller).  Scale 0 (uniform weights) runs as

@@ -29,6 +29,7 @@ struct AttendParams {
   void* out;                 // [B][H][512]
   float* lse;                // [B][H] or NULL
   int dense;                 // 1: rows = all N entries, no window
+  int hm;                    // dense with q_pos: entry i visible iff (i+1)*hm <= q_pos[b]+1
 };
 
 int attend_splits(int dt, int64_t B, int H, int64_t nslots);

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CSKV_VERSION 10000
+#define CSKV_VERSION 10100                  /* major*10000 + minor*100: 1.1 (cskv_hca_attend takes q_pos, m) */
 
 typedef enum cskv_dtype {
   CSKV_F32 = 0,       /* IEEE binary32 */
@@ -184,14 +184,20 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
 /*
  * HCA ("Frontier Techniques", 2.2; "DeepSeek V4 comprimeix el context",
  * section "HCA: un resum global 128 vegades mes curt"): every query attends
- * densely over all N entries, no selection and no window.  Same formulas as
- * cskv_sparse_attend with rows = entries[b*ent_bstride + i*576], i < N, and
- * the same conditions on scale and errors.
+ * densely over the entries it sees, no selection and no window.  Same
+ * formulas as cskv_sparse_attend with rows = entries[b*ent_bstride + i*576]:
+ *   q_pos == NULL (decode): i < N;
+ *   q_pos != NULL (a prefill chunk, positions q_pos[b]): i < N with
+ *   (i+1)*m <= q_pos[b] + 1, the causal rule of the indexer (an entry
+ *   exists once its block of m tokens is complete).  A query that sees no
+ *   entry gets a zero output and lse = -inf.
+ * Errors as cskv_sparse_attend, plus INVALID_ARG for m < 1 with q_pos.
  */
 size_t cskv_hca_workspace_size(int64_t B, int32_t H, int64_t N);
 int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, int64_t N,
-                    int64_t ent_bstride, float scale, cskv_dtype dt, void* out, float* lse,
-                    void* workspace, size_t ws_bytes, void* stream);
+                    int64_t ent_bstride, const int64_t* q_pos, int32_t m, float scale,
+                    cskv_dtype dt, void* out, float* lse, void* workspace, size_t ws_bytes,
+                    void* stream);
 
 /*
  * Merge of split-KV partial results: for each (b, h) with S partial results

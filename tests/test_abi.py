@@ -35,7 +35,7 @@ def test_header_functions_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cskv_version() == 10000
+    assert lib.cskv_version() == 10100
     assert lib.cskv_status_string(OK) == b"ok"
     for code in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.cskv_status_string(code) not in (b"ok", b"unknown status")
@@ -107,9 +107,10 @@ def test_attend_errors(lib):
     assert call(sc=float("nan")) == INVALID
     h = lib.cskv_hca_attend
     hws = lib.cskv_hca_workspace_size(32, 128, 8192)
-    assert h(P, P, 32, 128, 8192, 0, 1.0, 1, P, P, NULL, hws, NULL) == WORKSPACE
-    assert h(P, P, 32, 128, 8192, 0, 1.0, 2, P, P, P, hws, NULL) == UNSUPPORTED
-    assert h(P, P, 32, 128, 8192, 0, -1.0, 1, P, P, P, hws, NULL) == INVALID
+    assert h(P, P, 32, 128, 8192, 0, NULL, 0, 1.0, 1, P, P, NULL, hws, NULL) == WORKSPACE
+    assert h(P, P, 32, 128, 8192, 0, NULL, 0, 1.0, 2, P, P, P, hws, NULL) == UNSUPPORTED
+    assert h(P, P, 32, 128, 8192, 0, NULL, 0, -1.0, 1, P, P, P, hws, NULL) == INVALID
+    assert h(P, P, 32, 128, 8192, 0, P, 0, 1.0, 1, P, P, P, hws, NULL) == INVALID  # q_pos, m < 1
     m = lib.cskv_merge
     assert m(P, P, 2, 4, 0, P, P, 1, NULL) == INVALID
     assert m(P, P, 2, 4, 3, P, P, 2, NULL) == UNSUPPORTED

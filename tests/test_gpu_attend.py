@@ -61,6 +61,37 @@ def test_hca_per_sequence_caches():
 
 
 @pytest.mark.parametrize("dt", [wl.DT_F32, wl.DT_BF16])
+def test_hca_prefill_matches_oracle(dt):
+    """HCA at a prefill chunk: the query at position pos attends over entries
+    i with (i+1)m <= pos+1; positions from none visible through one, part
+    and all to past the end."""
+    B, H, N, m = 7, 128 if dt == wl.DT_BF16 else 16, 300, 128
+    pos = np.array([0, 126, 127, 37 * m + 5, 150 * m - 1, N * m - 1, 10**7], dtype=np.int64)
+    q = _rand(99, 0, 1, (B, H, E), dt, 1 / 24)
+    ent = _rand(99, 0, 2, (N, E), dt)
+    out, lse = _cskv().hca_attend(dev(q), dev(ent), q_pos=torch.from_numpy(pos).cuda(), m=m)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q, ent, dt, q_pos=pos, m=m)
+    assert np.isneginf(rl[:2]).all() and (host_f64(out)[:2] == 0).all()
+    assert np.isneginf(lse[:2].cpu().numpy()).all()
+    _check_attn(out[2:], lse[2:], ro[2:], rl[2:], dt)
+
+
+def test_hca_prefill_chunk_sampled():
+    """4,096 queries at positions 1,044,480..1,048,575 over 8,192 m'=128
+    entries (8,160..8,192 visible); the first and last query checked."""
+    cfg = wl.CONFIGS["hca_prefill"]
+    inp = wl.make_inputs(cfg, seed=0)
+    qp = torch.from_numpy(inp["q_pos"]).cuda()
+    out, lse = _cskv().hca_attend(dev(inp["q_hca"]), dev(inp["entries_hca"]), q_pos=qp, m=cfg.m_hca)
+    torch.cuda.synchronize()
+    rows = [0, cfg.B - 1]
+    ro, rl = oracle.hca_attend(inp["q_hca"].raw[rows], inp["entries_hca"].raw, wl.DT_BF16,
+                               q_pos=inp["q_pos"][rows], m=cfg.m_hca)
+    _check_attn(out[rows], lse[rows], ro, rl, wl.DT_BF16)
+
+
+@pytest.mark.parametrize("dt", [wl.DT_F32, wl.DT_BF16])
 def test_sparse_attend_given_selection(dt):
     """Attention over a given index list (with -1 holes, unsorted) plus the window."""
     B, H, N, W, k = 3, 128 if dt == wl.DT_BF16 else 16, 5000, 128, 200

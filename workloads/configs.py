@@ -62,6 +62,9 @@ CONFIGS = {
     "csa_prefill": Config("csa_prefill", 3, DT_BF16, DT_E4M3, B=4096, H=128, k=1024, W=128,
                           N_csa=262144, prefill_pos0=1044480, parts=("csa",),
                           notes="4,096 causal queries at positions 1,044,480..1,048,575; 262,144 entries; fp8 e4m3 indexer"),
+    "hca_prefill": Config("hca_prefill", 5, DT_BF16, DT_BF16, B=4096, H=128, N_hca=8192,
+                          prefill_pos0=1044480, parts=("hca",),
+                          notes="4,096 causal queries at positions 1,044,480..1,048,575 over 8,192 m'=128 entries, bf16"),
     "layer_1m": Config("layer_1m", 4, DT_BF16, DT_BF16, B=32, H=128, k=1024, W=128,
                        T=1 << 20, N_csa=262144, N_hca=8192,
                        parts=("compress", "csa", "hca"),
@@ -122,4 +125,6 @@ def make_inputs(cfg, seed=0, per_seq=False, with_compress_source=True):
             out["entries_hca"] = encode(_n(cfg, seed, "entries_hca", bshape(cfg.N_hca, E)), dt)
         qname = "q_hca" if "csa" in cfg.parts else "q"
         out["q_hca"] = encode(_n(cfg, seed, qname, (cfg.B, cfg.H, E), qstd), dt)
+        if cfg.prefill_pos0 >= 0:
+            out["q_pos"] = np.arange(cfg.prefill_pos0, cfg.prefill_pos0 + cfg.B, dtype=np.int64)
     return out
