@@ -186,27 +186,37 @@ int cskv_oracle_topk(const double* scores, const uint8_t* visible, int64_t B, in
 /* ---- attention [P1 2.1, 2.2; P4 "CSA: ...", "HCA: ..."] ------------------- */
 
 /* Softmax attention of one query head over an explicit list of rows:
- * l_r = scale * sum_{e<E} q[e] * row_r[e]; p = softmax(l); o[d] = sum_r p_r
- * row_r[d] for d < Dv; lse = ln sum_r exp(l_r). */
+ * l_r = scale * sum_{e<E} q[e] * row_r[e]; o[d] = sum_r p_r row_r[d] for
+ * d < Dv; lse = ln(sum_r exp(l_r) + exp(sink)).  The attention sink
+ * ("DeepSeek V4 comprimeix el context", section "CSA: buscar primer i
+ * atendre despres": learned logits that absorb attention mass) is one more
+ * softmax term with logit `sink` and a zero value: p_r = exp(l_r) /
+ * (sum_r' exp(l_r') + exp(sink)).  sink = -inf: no sink. */
 static void attend_rows(const void* q, int64_t q_off, int dt, const void* const* row_buf,
                         const int64_t* row_off, int64_t n_rows, int64_t E, int64_t Dv,
-                        double scale, double* out, double* lse) {
+                        double scale, double sink, double* out, double* lse) {
   double* l = (double*)malloc(sizeof(double) * (n_rows > 0 ? n_rows : 1));
-  double mx = -INFINITY;
+  double mx = sink;
   for (int64_t r = 0; r < n_rows; ++r) {
     double acc = 0.0;
     for (int64_t e = 0; e < E; ++e) acc += ld(q, q_off + e, dt) * ld(row_buf[r], row_off[r] + e, dt);
     l[r] = scale * acc;
     if (l[r] > mx) mx = l[r];
   }
-  double den = 0.0;
+  if (mx == -INFINITY) {                       /* no rows and no sink */
+    for (int64_t d = 0; d < Dv; ++d) out[d] = 0.0;
+    *lse = -INFINITY;
+    free(l);
+    return;
+  }
+  double den = sink == -INFINITY ? 0.0 : exp(sink - mx);
   for (int64_t r = 0; r < n_rows; ++r) { l[r] = exp(l[r] - mx); den += l[r]; }
   for (int64_t d = 0; d < Dv; ++d) {
     double acc = 0.0;
     for (int64_t r = 0; r < n_rows; ++r) acc += l[r] * ld(row_buf[r], row_off[r] + d, dt);
-    out[d] = n_rows ? acc / den : 0.0;
+    out[d] = acc / den;
   }
-  *lse = n_rows ? mx + log(den) : -INFINITY;
+  *lse = mx + log(den);
   free(l);
 }
 
@@ -220,7 +230,8 @@ int cskv_oracle_csa_attend(const void* q, const void* entries, const void* windo
                            int64_t B, int64_t H, int64_t E, int64_t Dv, int64_t N, int64_t W,
                            const int32_t* idx, int64_t k, int64_t ent_bstride,
                            int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
-                           int64_t win_pos0, double scale, double* out, double* lse) {
+                           int64_t win_pos0, double scale, const double* sink, double* out,
+                           double* lse) {
   if (!q || !entries || !idx || !out || !lse || B < 0 || H <= 0 || E <= 0 || Dv <= 0 ||
       Dv > E || N < 0 || W < 0 || k <= 0 || !dt_ok(dt))
     return -1;
@@ -265,8 +276,8 @@ int cskv_oracle_csa_attend(const void* q, const void* entries, const void* windo
           ++n;
         }
       }
-      attend_rows(q, (b * H + h) * E, dt, buf, off, n, E, Dv, scale, out + (b * H + h) * Dv,
-                  lse + b * H + h);
+      attend_rows(q, (b * H + h) * E, dt, buf, off, n, E, Dv, scale, sink ? sink[h] : -INFINITY,
+                  out + (b * H + h) * Dv, lse + b * H + h);
       free(buf);
       free(off);
     }
@@ -281,7 +292,8 @@ int cskv_oracle_csa_attend(const void* q, const void* entries, const void* windo
  * is complete), i.e. entries 0 .. min(N, (q_pos[b]+1)/m) - 1. */
 int cskv_oracle_hca_attend(const void* q, const void* entries, int dt, int64_t B, int64_t H,
                            int64_t E, int64_t Dv, int64_t N, int64_t ent_bstride,
-                           const int64_t* q_pos, int m, double scale, double* out, double* lse) {
+                           const int64_t* q_pos, int m, double scale, const double* sink,
+                           double* out, double* lse) {
   if (!q || !entries || !out || !lse || B < 0 || H <= 0 || E <= 0 || Dv <= 0 || Dv > E ||
       N < 0 || !dt_ok(dt))
     return -1;
@@ -300,8 +312,8 @@ int cskv_oracle_hca_attend(const void* q, const void* entries, int dt, int64_t B
         buf[i] = entries;
         off[i] = b * ent_bstride + i * E;
       }
-      attend_rows(q, (b * H + h) * E, dt, buf, off, n, E, Dv, scale, out + (b * H + h) * Dv,
-                  lse + b * H + h);
+      attend_rows(q, (b * H + h) * E, dt, buf, off, n, E, Dv, scale, sink ? sink[h] : -INFINITY,
+                  out + (b * H + h) * Dv, lse + b * H + h);
       free(buf);
       free(off);
     }

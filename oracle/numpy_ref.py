@@ -43,10 +43,15 @@ def topk(scores, visible, k):
     return out
 
 
-def attend(qv, rows, Dv=512, scale=1.0):
-    """qv [H, E], rows [n, E] -> (out [H, Dv], lse [H])."""
+def attend(qv, rows, Dv=512, scale=1.0, sink=None):
+    """qv [H, E], rows [n, E] -> (out [H, Dv], lse [H]).  sink [H]: one more
+    softmax column per head with that logit and a zero value."""
     logits = scale * (qv @ rows.T)
+    values = rows[:, :Dv]
+    if sink is not None:
+        logits = np.concatenate([logits, np.asarray(sink, dtype=np.float64)[:, None]], axis=1)
+        values = np.concatenate([values, np.zeros((1, Dv))], axis=0)
     mx = logits.max(axis=1, keepdims=True)
     p = np.exp(logits - mx)
     den = p.sum(axis=1, keepdims=True)
-    return (p / den) @ rows[:, :Dv], (mx + np.log(den))[:, 0]
+    return (p / den) @ values, (mx + np.log(den))[:, 0]

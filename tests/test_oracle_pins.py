@@ -435,6 +435,52 @@ def test_hca_prefill_causal_visibility():
     assert not np.allclose(oa, ob)
 
 
+def test_attention_sink():
+    """Attention-sink logits: one more softmax term per head with a zero
+    value.  Pins: a sink of -inf is no sink; with all logits 0 (q = 0) the
+    output is the rows' mean times n / (n + e^s) and lse = ln(n + e^s); a
+    sink far above every logit takes all the mass (output -> 0, lse -> s);
+    both HCA and CSA equal the NumPy formulation with a virtual zero row;
+    the lse-weighted merge of sink-free partials plus the sink term in the
+    denominator equals the unsplit result with the sink."""
+    q, ent, win = _rand_attn(20, H=3)
+    N, Dv = ent.shape[0], 8
+    sink = np.array([0.3, -1.5, 2.0])
+    o0, l0 = oracle.hca_attend(q, ent, F32, Dv=Dv)
+    oi, li = oracle.hca_attend(q, ent, F32, Dv=Dv, sink=np.full(3, -np.inf))
+    np.testing.assert_array_equal(o0, oi)
+    np.testing.assert_array_equal(l0, li)
+    zq = np.zeros_like(q)
+    oz, lz = oracle.hca_attend(zq, ent, F32, Dv=Dv, sink=sink)
+    mean = ent[:, :Dv].astype(np.float64).mean(0)
+    for h in range(3):
+        np.testing.assert_allclose(oz[0, h], mean * N / (N + np.exp(sink[h])), rtol=1e-12)
+        np.testing.assert_allclose(lz[0, h], np.log(N + np.exp(sink[h])), rtol=1e-13)
+    big = np.full(3, 300.0)
+    ob, lb = oracle.hca_attend(q, ent, F32, Dv=Dv, sink=big)
+    assert np.abs(ob).max() < 1e-90
+    np.testing.assert_allclose(lb, 300.0, rtol=1e-15)
+    os_, ls = oracle.hca_attend(q, ent, F32, Dv=Dv, sink=sink)
+    idx = np.array([[3, 9, -1, 20], [0, 1, 2, 3]], dtype=np.int32)
+    oc, lc = oracle.csa_attend(q, ent, win, F32, idx, Dv=Dv, sink=sink)
+    for b in range(2):
+        ro, rl = numpy_ref.attend(q[b].astype(float), ent.astype(float), Dv, sink=sink)
+        np.testing.assert_allclose(os_[b], ro, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(ls[b], rl, rtol=1e-13)
+        sel = [i for i in idx[b] if i >= 0]
+        rows = np.concatenate([ent[sel], win]).astype(float)
+        ro, rl = numpy_ref.attend(q[b].astype(float), rows, Dv, sink=sink)
+        np.testing.assert_allclose(oc[b], ro, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lc[b], rl, rtol=1e-13)
+    parts = np.array_split(np.arange(N), 5)
+    po, pl = zip(*[oracle.hca_attend(q, ent[p], F32, Dv=Dv) for p in parts])
+    pl = np.stack(pl)                                                 # [S, B, H]
+    L = np.log(np.exp(pl).sum(0) + np.exp(sink))
+    mo = sum(np.exp(pl[s] - L)[..., None] * po[s] for s in range(5))
+    np.testing.assert_allclose(L, ls, rtol=1e-12)
+    np.testing.assert_allclose(mo, os_, rtol=1e-11, atol=1e-13)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 7, 40])
 def test_split_merge_formula_recovers_unsplit(splits):
     """lse-weighted merge of partial attentions over a partition of the rows
