@@ -42,15 +42,16 @@ _SIGS = {
                          _vp, _sz, _vp], ctypes.c_int),
     "cskv_attend_workspace_size": ([_i64, _i32, _i64], _sz),
     "cskv_sparse_attend": ([_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i64, _i64, _i64,
-                            _vp, _i64, _f32, ctypes.c_int, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+                            _vp, _i64, _f32, _vp, ctypes.c_int, _vp, _vp, _vp, _sz, _vp],
+                           ctypes.c_int),
     "cskv_csa_workspace_size": ([_i64, _i32, _i64, _i32, _i32], _sz),
     "cskv_csa_attend": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i32, _i64, _i64,
-                         _i64, _i64, _vp, _i64, _f32, _f32, ctypes.c_int, ctypes.c_int, _vp, _vp,
-                         _vp, _vp, _sz, _vp], ctypes.c_int),
+                         _i64, _i64, _vp, _i64, _f32, _vp, _f32, ctypes.c_int, ctypes.c_int, _vp,
+                         _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "cskv_hca_workspace_size": ([_i64, _i32, _i64], _sz),
-    "cskv_hca_attend": ([_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, ctypes.c_int, _vp, _vp,
-                         _vp, _sz, _vp], ctypes.c_int),
-    "cskv_merge": ([_vp, _vp, _i64, _i32, _i32, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
+    "cskv_hca_attend": ([_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, _vp, ctypes.c_int, _vp,
+                         _vp, _vp, _sz, _vp], ctypes.c_int),
+    "cskv_merge": ([_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -89,6 +90,16 @@ def _dev(*ts):
                 raise ValueError("cskv tensors must live in GPU memory")
             if not t.is_contiguous():
                 raise ValueError("cskv tensors must be contiguous")
+
+
+def _sink(sink, H):
+    """Per-head attention-sink logits: None, or fp32 [H] on the device."""
+    if sink is None:
+        return None
+    _dev(sink)
+    if sink.dtype != torch.float32 or sink.shape != (H,):
+        raise ValueError(f"sink must be fp32 [{H}]")
+    return _ptr(sink)
 
 
 def _stream(stream):
@@ -187,8 +198,9 @@ def attend_workspace_size(B, H, rows_per_query):
 
 
 def sparse_attend(q, entries, window, idx, q_pos=None, win_pos0=0, W=None, scale=1.0,
-                  per_seq=False, out=None, lse=None, workspace=None, stream=None):
-    """Attention of q [B, H, 576] over entries[idx] plus the raw window."""
+                  per_seq=False, out=None, lse=None, workspace=None, stream=None, sink=None):
+    """Attention of q [B, H, 576] over entries[idx] plus the raw window;
+    sink: per-head attention-sink logits, fp32 [H] (None: no sink)."""
     _dev(q, entries, window, idx, q_pos, out, lse)
     B, H = q.shape[0], q.shape[1]
     N = entries.shape[-2]
@@ -204,8 +216,8 @@ def sparse_attend(q, entries, window, idx, q_pos=None, win_pos0=0, W=None, scale
         workspace = _workspace(attend_workspace_size(B, H, k + W), q.device)
     _call("cskv_sparse_attend", _ptr(q), _ptr(entries), _ptr(window), _ptr(idx), B, H, N, W, k,
           N * E if per_seq else 0, win_rows * E if per_seq else 0, win_rows, _ptr(q_pos),
-          int(win_pos0), float(scale), _dt(q), _ptr(out), _ptr(lse), _ptr(workspace),
-          workspace.numel(), _stream(stream))
+          int(win_pos0), float(scale), _sink(sink, H), _dt(q), _ptr(out), _ptr(lse),
+          _ptr(workspace), workspace.numel(), _stream(stream))
     return out, lse
 
 
@@ -215,7 +227,7 @@ def csa_workspace_size(B, H, N, W, k):
 
 def csa_attend(q, q_idx, entries, idx_keys, window, k, m=4, q_pos=None, win_pos0=0, W=None,
                scale=1.0, idx_scale=1.0, per_seq=False, out=None, lse=None, idx_out=None,
-               workspace=None, stream=None):
+               workspace=None, stream=None, sink=None):
     """CSA: indexer top-k then attention over the selection plus the window.
     Returns (out [B, H, 512], lse [B, H], idx [B, k])."""
     _dev(q, q_idx, entries, idx_keys, window, q_pos, out, lse, idx_out)
@@ -235,7 +247,8 @@ def csa_attend(q, q_idx, entries, idx_keys, window, k, m=4, q_pos=None, win_pos0
     _call("cskv_csa_attend", _ptr(q), _ptr(q_idx), _ptr(entries), _ptr(idx_keys), _ptr(window),
           B, H, N, W, k, m, N * E if per_seq else 0, N * I if per_seq else 0,
           win_rows * E if per_seq else 0, win_rows, _ptr(q_pos), int(win_pos0), float(scale),
-          float(idx_scale), _dt(q), _dt(q_idx), _ptr(out), _ptr(lse), _ptr(idx_out),
+          _sink(sink, H), float(idx_scale), _dt(q), _dt(q_idx), _ptr(out), _ptr(lse),
+          _ptr(idx_out),
           _ptr(workspace), workspace.numel(), _stream(stream))
     return out, lse, idx_out
 
@@ -245,7 +258,7 @@ def hca_workspace_size(B, H, N):
 
 
 def hca_attend(q, entries, scale=1.0, per_seq=False, q_pos=None, m=None, out=None, lse=None,
-               workspace=None, stream=None):
+               workspace=None, stream=None, sink=None):
     """HCA: dense attention of q [B, H, 576] over the entries [N, 576] each
     query sees: all of them (q_pos None), or at a prefill chunk those with
     (i+1)*m <= q_pos[b] + 1 (q_pos [B] int64 on the device)."""
@@ -261,12 +274,12 @@ def hca_attend(q, entries, scale=1.0, per_seq=False, q_pos=None, m=None, out=Non
     if workspace is None:
         workspace = _workspace(hca_workspace_size(B, H, N), q.device)
     _call("cskv_hca_attend", _ptr(q), _ptr(entries), B, H, N, N * E if per_seq else 0,
-          _ptr(q_pos), int(m) if q_pos is not None else 0, float(scale), _dt(q), _ptr(out),
-          _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
+          _ptr(q_pos), int(m) if q_pos is not None else 0, float(scale), _sink(sink, H), _dt(q),
+          _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
     return out, lse
 
 
-def merge(o_part, lse_part, dtype=torch.bfloat16, out=None, lse=None, stream=None):
+def merge(o_part, lse_part, dtype=torch.bfloat16, out=None, lse=None, stream=None, sink=None):
     """Merge split partials o_part [B, H, S, 512] fp32, lse_part [B, H, S]."""
     _dev(o_part, lse_part, out, lse)
     B, H, S = lse_part.shape
@@ -274,6 +287,6 @@ def merge(o_part, lse_part, dtype=torch.bfloat16, out=None, lse=None, stream=Non
         out = torch.empty((B, H, D), dtype=dtype, device=o_part.device)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=o_part.device)
-    _call("cskv_merge", _ptr(o_part), _ptr(lse_part), B, H, S, _ptr(out), _ptr(lse), _dt(out),
-          _stream(stream))
+    _call("cskv_merge", _ptr(o_part), _ptr(lse_part), B, H, S, _sink(sink, H), _ptr(out),
+          _ptr(lse), _dt(out), _stream(stream))
     return out, lse

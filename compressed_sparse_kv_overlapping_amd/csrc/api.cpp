@@ -195,8 +195,8 @@ static int check_attend(const char* fn, const void* q, const void* entries, cons
 int cskv_sparse_attend(const void* q, const void* entries, const void* window, const int32_t* idx,
                        int64_t B, int32_t H, int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
                        int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
-                       int64_t win_pos0, float scale, cskv_dtype dt, void* out, float* lse,
-                       void* workspace, size_t ws_bytes, void* stream) {
+                       int64_t win_pos0, float scale, const float* sink, cskv_dtype dt, void* out,
+                       float* lse, void* workspace, size_t ws_bytes, void* stream) {
   int st = check_attend("cskv_sparse_attend", q, entries, window, B, H, N, W, k, ent_bstride,
                         win_bstride, win_rows, dt, out, scale);
   if (st) return st;
@@ -209,7 +209,7 @@ int cskv_sparse_attend(const void* q, const void* entries, const void* window, c
     return fail(CSKV_ERR_WORKSPACE, "cskv_sparse_attend: workspace %zu bytes, need %zu", ws_bytes,
                 need);
   cskv::AttendParams p{(int)dt, q, entries, window, idx, q_pos, B, N, ent_bstride, win_bstride,
-                       win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0};
+                       win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0, sink};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), "cskv_sparse_attend");
 }
 
@@ -223,7 +223,8 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
                     const void* window, int64_t B, int32_t H, int64_t N, int32_t W, int32_t k,
                     int32_t m, int64_t ent_bstride, int64_t key_bstride, int64_t win_bstride,
                     int64_t win_rows, const int64_t* q_pos, int64_t win_pos0, float scale,
-                    float idx_scale, cskv_dtype dt, cskv_dtype idx_dt, void* out, float* lse,
+                    const float* sink, float idx_scale, cskv_dtype dt, cskv_dtype idx_dt,
+                    void* out, float* lse,
                     int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
   int st = check_topk("cskv_csa_attend", q_idx, idx_keys, B, N, k, key_bstride, q_pos, m,
                       idx_scale, idx_dt, idx_out);
@@ -243,7 +244,7 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
   hipError_t e = cskv::launch_topk(tp, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "cskv_csa_attend (top-k)");
   cskv::AttendParams ap{(int)dt, q, entries, window, idx_out, q_pos, B, N, ent_bstride,
-                        win_bstride, win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0};
+                        win_bstride, win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0, sink};
   return hip_status(cskv::launch_attend(ap, (char*)workspace + topk_bytes, (hipStream_t)stream),
                     "cskv_csa_attend (attention)");
 }
@@ -255,8 +256,8 @@ size_t cskv_hca_workspace_size(int64_t B, int32_t H, int64_t N) {
 
 int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, int64_t N,
                     int64_t ent_bstride, const int64_t* q_pos, int32_t m, float scale,
-                    cskv_dtype dt, void* out, float* lse, void* workspace, size_t ws_bytes,
-                    void* stream) {
+                    const float* sink, cskv_dtype dt, void* out, float* lse, void* workspace,
+                    size_t ws_bytes, void* stream) {
   int st = check_attend("cskv_hca_attend", q, entries, nullptr, B, H, N, 0, 0, ent_bstride, 0, 0,
                         dt, out, scale);
   if (st) return st;
@@ -265,12 +266,12 @@ int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, in
   if (need && (!workspace || ws_bytes < need || !aligned16(workspace)))
     return fail(CSKV_ERR_WORKSPACE, "cskv_hca_attend: workspace %zu bytes, need %zu", ws_bytes, need);
   cskv::AttendParams p{(int)dt, q, entries, nullptr, nullptr, q_pos, B, N, ent_bstride, 0, 0, 0,
-                       H, 0, 0, scale, out, lse, 1, q_pos ? m : 0};
+                       H, 0, 0, scale, out, lse, 1, q_pos ? m : 0, sink};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), "cskv_hca_attend");
 }
 
 int cskv_merge(const float* o_part, const float* lse_part, int64_t B, int32_t H, int32_t S,
-               void* out, float* lse, cskv_dtype dt, void* stream) {
+               const float* sink, void* out, float* lse, cskv_dtype dt, void* stream) {
   if (!o_part || !lse_part || !out) return fail(CSKV_ERR_INVALID_ARG, "cskv_merge: null pointer");
   if (B < 1 || H < 1 || S < 1) return fail(CSKV_ERR_INVALID_ARG, "cskv_merge: B=%lld H=%d S=%d",
                                            (long long)B, H, S);
@@ -278,7 +279,7 @@ int cskv_merge(const float* o_part, const float* lse_part, int64_t B, int32_t H,
     return fail(CSKV_ERR_UNSUPPORTED, "cskv_merge: dtype %d (F32 or BF16)", (int)dt);
   if (!aligned16(o_part) || !aligned16(out))
     return fail(CSKV_ERR_INVALID_ARG, "cskv_merge: tensors must be 16-byte aligned");
-  return hip_status(cskv::launch_merge((int)dt, o_part, lse_part, B * H, S, out, lse,
+  return hip_status(cskv::launch_merge((int)dt, o_part, lse_part, B * H, S, sink, H, out, lse,
                                        (hipStream_t)stream),
                     "cskv_merge");
 }

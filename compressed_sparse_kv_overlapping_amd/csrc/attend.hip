@@ -57,6 +57,7 @@ struct AttnArgs {
   int64_t ent_bstride, win_bstride, win_pos0, win_rows, N;
   int dense;                 // 1: all N entries, no window (HCA)
   int hm;                    // dense with q_pos: entry i visible iff (i+1)*hm <= q_pos[b]+1
+  const float* sink;         // [H] attention-sink logits (nullable), applied where splits end
   int B, H, W, k, nslots, slots_per_split, nsplit;
   float c;                   // scale * log2(e)
   void* out;                 // [B][H][512] when nsplit == 1
@@ -64,6 +65,23 @@ struct AttnArgs {
   float* o_part;             // [B][H][nsplit][512]
   float* lse_part;           // [B][H][nsplit]
 };
+
+// Final normalisation of one head.  l: the sum of its weights relative to
+// the reference m2 (log2 units); s2: its attention-sink logit in log2 units
+// (-inf: no sink), one more softmax term with a zero value.  *scale
+// multiplies the accumulators; *lse2 is log2 of the whole denominator.
+__device__ __forceinline__ void head_norm(float l, float m2, float s2, float* scale, float* lse2) {
+  if (s2 == -INFINITY) {
+    *scale = l > 0.f ? 1.f / l : 0.f;
+    *lse2 = l > 0.f ? m2 + __log2f(l) : -INFINITY;
+    return;
+  }
+  const float M = l > 0.f ? fmaxf(m2, s2) : s2;
+  const float w = l > 0.f ? __builtin_amdgcn_exp2f(m2 - M) : 0.f;
+  const float den = l * w + __builtin_amdgcn_exp2f(s2 - M);
+  *scale = w / den;
+  *lse2 = M + __log2f(den);
+}
 
 // End of a split's rows: in dense mode at a prefill chunk, the entries the
 // query at q_pos[b] sees (i with (i+1)*hm <= q_pos[b]+1) end the range, so
@@ -412,8 +430,12 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
     float l = l_run[j];
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse2 = l > 0.f ? m_run[j] + __log2f(l) : -INFINITY;
+    // the sink joins where the splits end: here with one split, else in
+    // the merge
+    const float s2 = (a.sink && a.nsplit == 1) ? a.sink[hok[j] ? hh[j] : 0] * 1.4426950408889634f
+                                               : -INFINITY;
+    float inv, lse2;
+    head_norm(l, m_run[j], s2, &inv, &lse2);
     if (!hok[j]) continue;
     const int h = hh[j];
     if (a.nsplit == 1) {
@@ -941,8 +963,12 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
 
   const float LN2 = 0.6931471805599453f;
   const float l = sum_xor32(l_run);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const float lse2 = l > 0.f ? m_ref + __log2f(l) : -INFINITY;
+  // the sink joins where the splits end: here with one split, else in the
+  // merge
+  const float s2 = (a.sink && a.nsplit == 1) ? a.sink[hok ? head : 0] * 1.4426950408889634f
+                                             : -INFINITY;
+  float inv, lse2;
+  head_norm(l, m_ref, s2, &inv, &lse2);
   if (!hok) return false;
   // lane l holds head l % 32, dims 32 db + 8 q + 4 (l / 32) + 0..3 in
   // registers 4 q .. 4 q + 3 of block db
@@ -984,14 +1010,16 @@ __global__ __launch_bounds__(64 * kWideWaves) void attend_wide_kernel(AttnArgs a
   }
 }
 
-// One wave per (query, head): lse = ln sum_s exp(lse_s); out = sum_s
-// exp(lse_s - lse) o_s.  Lane l takes the lse of splits l, l + 64, ...; the
-// partial rows are loaded eight splits at a time and accumulated in split
-// order, so the result does not depend on timing.
+// One wave per (query, head): lse = ln(sum_s exp(lse_s) + exp(sink_h));
+// out = sum_s exp(lse_s - lse) o_s (the partials carry no sink; sink may be
+// NULL).  Lane l takes the lse of splits l, l + 64, ...; the partial rows
+// are loaded eight splits at a time and accumulated in split order, so the
+// result does not depend on timing.
 template <class T>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
                                                     const float* __restrict__ lse_part, int64_t BH,
-                                                    int S, T* __restrict__ out,
+                                                    int S, const float* __restrict__ sink, int H,
+                                                    T* __restrict__ out,
                                                     float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1001,6 +1029,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   for (int s = lane; s < S; s += 64) mx = fmaxf(mx, lp[s]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  const float sk = sink ? sink[bh % H] : -INFINITY;
+  mx = fmaxf(mx, sk);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (mx != -INFINITY) {
@@ -1029,6 +1059,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+    if (sk != -INFINITY) tot += __expf(sk - mx);
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
@@ -1075,7 +1106,7 @@ static hipError_t launch_attend_t(const AttendParams& p, void* ws, hipStream_t s
   AttnArgs a;
   a.q = p.q; a.entries = p.entries; a.window = p.window; a.idx = p.idx; a.q_pos = p.q_pos;
   a.ent_bstride = p.ent_bstride; a.win_bstride = p.win_bstride; a.win_pos0 = p.win_pos0;
-  a.win_rows = p.win_rows; a.dense = p.dense; a.hm = p.hm;
+  a.win_rows = p.win_rows; a.dense = p.dense; a.hm = p.hm; a.sink = p.sink;
   a.N = p.N; a.B = (int)p.B; a.H = p.H; a.W = p.dense ? 0 : p.W; a.k = p.dense ? 0 : p.k;
   a.nslots = (int)(p.dense ? p.N : (int64_t)p.k + p.W);
   // scale >= 0 (checked by the caller).  Scale 0 (uniform weights) runs as
@@ -1099,7 +1130,7 @@ static hipError_t launch_attend_t(const AttendParams& p, void* ws, hipStream_t s
   if (e != hipSuccess || S == 1) return e;
   const int64_t BH = p.B * p.H;
   hipLaunchKernelGGL(merge_kernel<T>, dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, stream,
-                     a.o_part, a.lse_part, BH, S, (T*)p.out, p.lse);
+                     a.o_part, a.lse_part, BH, S, p.sink, p.H, (T*)p.out, p.lse);
   return hipGetLastError();
 }
 
@@ -1109,13 +1140,13 @@ hipError_t launch_attend(const AttendParams& p, void* ws, hipStream_t stream) {
 }
 
 hipError_t launch_merge(int dt, const float* o_part, const float* lse_part, int64_t BH, int S,
-                        void* out, float* lse, hipStream_t stream) {
+                        const float* sink, int H, void* out, float* lse, hipStream_t stream) {
   if (dt == 0)
     hipLaunchKernelGGL(merge_kernel<float>, dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, stream,
-                       o_part, lse_part, BH, S, (float*)out, lse);
+                       o_part, lse_part, BH, S, sink, H, (float*)out, lse);
   else
     hipLaunchKernelGGL(merge_kernel<bf16_t>, dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, stream,
-                       o_part, lse_part, BH, S, (bf16_t*)out, lse);
+                       o_part, lse_part, BH, S, sink, H, (bf16_t*)out, lse);
   return hipGetLastError();
 }
 

@@ -30,13 +30,14 @@ struct AttendParams {
   float* lse;                // [B][H] or NULL
   int dense;                 // 1: rows = all N entries, no window
   int hm;                    // dense with q_pos: entry i visible iff (i+1)*hm <= q_pos[b]+1
+  const float* sink;         // [H] attention-sink logits, or NULL
 };
 
 int attend_splits(int dt, int64_t B, int H, int64_t nslots);
 size_t attend_partial_bytes(int dt, int64_t B, int H, int64_t nslots);
 hipError_t launch_attend(const AttendParams& p, void* ws, hipStream_t stream);
 hipError_t launch_merge(int dt, const float* o_part, const float* lse_part, int64_t BH, int S,
-                        void* out, float* lse, hipStream_t stream);
+                        const float* sink, int H, void* out, float* lse, hipStream_t stream);
 
 struct TopkParams {
   int dt;                    // 0 fp32, 1 bf16, 2 fp8 e4m3

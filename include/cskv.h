@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CSKV_VERSION 10100                  /* major*10000 + minor*100: 1.1 (cskv_hca_attend takes q_pos, m) */
+#define CSKV_VERSION 10200 /* major*10000 + minor*100: 1.2 (HCA q_pos/m; attention-sink logits) */
 
 typedef enum cskv_dtype {
   CSKV_F32 = 0,       /* IEEE binary32 */
@@ -152,9 +152,13 @@ int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t 
  * max(0, q_pos[b]-W+1) .. q_pos[b], where row 0 of the window buffer holds
  * position win_pos0 (the buffer has win_rows rows).  For every head h:
  *   l_r = scale * sum_{e<576} q[b][h][e] * row_r[e],
- *   out[b][h][d] = sum_r softmax(l)_r * row_r[d]  (d < 512),
- *   lse[b][h] = ln sum_r exp(l_r)   (lse may be NULL).
+ *   out[b][h][d] = sum_r exp(l_r) * row_r[d] / Z  (d < 512),
+ *   lse[b][h] = ln Z,  Z = sum_r exp(l_r) + exp(sink[h])   (lse may be NULL).
  * One softmax covers the selected entries and the window together.
+ * sink [H] fp32 (nullable: no sink term) holds per-head attention-sink
+ * logits ("DeepSeek V4 comprimeix el context", section "CSA: buscar primer i
+ * atendre despres": learned logits that absorb attention mass), in the
+ * units of l; a query with no rows then gets out = 0 and lse = sink[h].
  *   idx [B][k] int32 (-1 = no entry; any order); q, entries, window, out in dt
  *   (F32 or BF16); workspace: cskv_attend_workspace_size(...) bytes.
  * scale must be >= 0 and finite (0 gives uniform weights over the rows).
@@ -165,8 +169,8 @@ size_t cskv_attend_workspace_size(int64_t B, int32_t H, int64_t rows_per_query);
 int cskv_sparse_attend(const void* q, const void* entries, const void* window, const int32_t* idx,
                        int64_t B, int32_t H, int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
                        int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
-                       int64_t win_pos0, float scale, cskv_dtype dt, void* out, float* lse,
-                       void* workspace, size_t ws_bytes, void* stream);
+                       int64_t win_pos0, float scale, const float* sink, cskv_dtype dt, void* out,
+                       float* lse, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * CSA: cskv_index_topk followed by cskv_sparse_attend, on one stream, with
@@ -178,7 +182,8 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
                     const void* window, int64_t B, int32_t H, int64_t N, int32_t W, int32_t k,
                     int32_t m, int64_t ent_bstride, int64_t key_bstride, int64_t win_bstride,
                     int64_t win_rows, const int64_t* q_pos, int64_t win_pos0, float scale,
-                    float idx_scale, cskv_dtype dt, cskv_dtype idx_dt, void* out, float* lse,
+                    const float* sink, float idx_scale, cskv_dtype dt, cskv_dtype idx_dt,
+                    void* out, float* lse,
                     int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -196,18 +201,19 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
 size_t cskv_hca_workspace_size(int64_t B, int32_t H, int64_t N);
 int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, int64_t N,
                     int64_t ent_bstride, const int64_t* q_pos, int32_t m, float scale,
-                    cskv_dtype dt, void* out, float* lse, void* workspace, size_t ws_bytes,
-                    void* stream);
+                    const float* sink, cskv_dtype dt, void* out, float* lse, void* workspace,
+                    size_t ws_bytes, void* stream);
 
 /*
  * Merge of split-KV partial results: for each (b, h) with S partial results
- * o_part[b][h][s][512] (fp32, each normalised over its own rows) and
- * lse_part[b][h][s]:  lse = ln sum_s exp(lse_s),  out = sum_s exp(lse_s - lse)
- * * o_s.  A split with no rows has lse_s = -inf and contributes nothing.
+ * o_part[b][h][s][512] (fp32, each normalised over its own rows, no sink)
+ * and lse_part[b][h][s]:  lse = ln(sum_s exp(lse_s) + exp(sink[h])),
+ * out = sum_s exp(lse_s - lse) * o_s.  A split with no rows has lse_s = -inf
+ * and contributes nothing; sink (nullable) as in cskv_sparse_attend.
  * out [B][H][512] in dt; lse may be NULL.
  */
 int cskv_merge(const float* o_part, const float* lse_part, int64_t B, int32_t H, int32_t S,
-               void* out, float* lse, cskv_dtype dt, void* stream);
+               const float* sink, void* out, float* lse, cskv_dtype dt, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ def test_header_functions_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cskv_version() == 10100
+    assert lib.cskv_version() == 10200
     assert lib.cskv_status_string(OK) == b"ok"
     for code in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.cskv_status_string(code) not in (b"ok", b"unknown status")
@@ -91,7 +91,7 @@ def test_attend_errors(lib):
     ws = lib.cskv_attend_workspace_size(8, 128, 1152)
     assert ws > 0
     args = dict(q=P, e=P, w=P, idx=P, B=8, H=128, N=16384, W=128, k=1024, eb=0, wb=0, wr=128,
-                qp=NULL, wp0=0, sc=1.0, dt=1, out=P, lse=P, ws=P, wsb=ws, st=NULL)
+                qp=NULL, wp0=0, sc=1.0, sink=NULL, dt=1, out=P, lse=P, ws=P, wsb=ws, st=NULL)
 
     def call(**kw):
         a = dict(args, **kw)
@@ -107,21 +107,21 @@ def test_attend_errors(lib):
     assert call(sc=float("nan")) == INVALID
     h = lib.cskv_hca_attend
     hws = lib.cskv_hca_workspace_size(32, 128, 8192)
-    assert h(P, P, 32, 128, 8192, 0, NULL, 0, 1.0, 1, P, P, NULL, hws, NULL) == WORKSPACE
-    assert h(P, P, 32, 128, 8192, 0, NULL, 0, 1.0, 2, P, P, P, hws, NULL) == UNSUPPORTED
-    assert h(P, P, 32, 128, 8192, 0, NULL, 0, -1.0, 1, P, P, P, hws, NULL) == INVALID
-    assert h(P, P, 32, 128, 8192, 0, P, 0, 1.0, 1, P, P, P, hws, NULL) == INVALID  # q_pos, m < 1
+    assert h(P, P, 32, 128, 8192, 0, NULL, 0, 1.0, NULL, 1, P, P, NULL, hws, NULL) == WORKSPACE
+    assert h(P, P, 32, 128, 8192, 0, NULL, 0, 1.0, NULL, 2, P, P, P, hws, NULL) == UNSUPPORTED
+    assert h(P, P, 32, 128, 8192, 0, NULL, 0, -1.0, NULL, 1, P, P, P, hws, NULL) == INVALID
+    assert h(P, P, 32, 128, 8192, 0, P, 0, 1.0, NULL, 1, P, P, P, hws, NULL) == INVALID  # m < 1
     m = lib.cskv_merge
-    assert m(P, P, 2, 4, 0, P, P, 1, NULL) == INVALID
-    assert m(P, P, 2, 4, 3, P, P, 2, NULL) == UNSUPPORTED
+    assert m(P, P, 2, 4, 0, NULL, P, P, 1, NULL) == INVALID
+    assert m(P, P, 2, 4, 3, NULL, P, P, 2, NULL) == UNSUPPORTED
 
 
 def test_csa_workspace_covers_parts(lib):
     B, H, N, W, k = 32, 128, 262144, 128, 1024
     total = lib.cskv_csa_workspace_size(B, H, N, W, k)
     assert total >= lib.cskv_index_topk_workspace_size(B, N, k) + lib.cskv_attend_workspace_size(B, H, k + W)
-    assert lib.cskv_csa_attend(P, P, P, P, P, B, H, N, W, k, 4, 0, 0, 0, W, NULL, 0, 1.0, 1.0, 1, 1,
-                               P, P, P, P, total - 1, NULL) == WORKSPACE
+    assert lib.cskv_csa_attend(P, P, P, P, P, B, H, N, W, k, 4, 0, 0, 0, W, NULL, 0, 1.0, NULL, 1.0,
+                               1, 1, P, P, P, P, total - 1, NULL) == WORKSPACE
 
 
 def test_binding_refuses_missing_library(monkeypatch, tmp_path):

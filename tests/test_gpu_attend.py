@@ -164,6 +164,59 @@ def test_logits_past_reference_band(N):
     _check_attn(out, lse, ro, rl, dt)
 
 
+@pytest.mark.parametrize("dt", [wl.DT_F32, wl.DT_BF16])
+def test_attention_sink(dt):
+    """Per-head attention-sink logits: split paths (the merge adds the sink)
+    and single-split paths (the attention kernel adds it), HCA decode and
+    prefill, sparse attention, and a query with no rows (output 0, lse =
+    sink)."""
+    cskv = _cskv()
+    H = 128 if dt == wl.DT_BF16 else 16
+    rng = np.random.default_rng(5)
+    sink_h = rng.uniform(-2.0, 4.0, H)
+    sink = torch.from_numpy(sink_h.astype(np.float32)).cuda()
+    # HCA decode, several splits
+    B, N = 3, 1000
+    q = _rand(101, 0, 1, (B, H, E), dt, 1 / 24)
+    ent = _rand(101, 0, 2, (N, E), dt)
+    out, lse = cskv.hca_attend(dev(q), dev(ent), sink=sink)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q, ent, dt, sink=sink_h)
+    _check_attn(out, lse, ro, rl, dt)
+    # one split per query (300 queries), at prefill positions
+    B2, N2, m = 300, 96, 128
+    q2 = _rand(101, 0, 3, (B2, H, E), dt, 1 / 24)
+    ent2 = _rand(101, 0, 4, (N2, E), dt)
+    pos = (np.arange(B2, dtype=np.int64) * 41) % (N2 * m + 200)
+    out, lse = cskv.hca_attend(dev(q2), dev(ent2), q_pos=torch.from_numpy(pos).cuda(), m=m,
+                               sink=sink)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q2, ent2, dt, q_pos=pos, m=m, sink=sink_h)
+    _check_attn(out, lse, ro, rl, dt)
+    none = np.nonzero((pos + 1) // m == 0)[0]
+    assert len(none) > 0
+    assert (host_f64(out)[none] == 0).all()
+    np.testing.assert_allclose(lse.cpu().numpy()[none], np.tile(sink_h, (len(none), 1)), rtol=1e-6)
+    # sparse attention over a selection plus the window; query 2 has no rows
+    Bs, Ns, W, k = 3, 5000, 128, 200
+    qs = _rand(101, 0, 5, (Bs, H, E), dt, 1 / 24)
+    ents = _rand(101, 0, 6, (Ns, E), dt)
+    win = _rand(101, 0, 7, (W, E), dt)
+    idx = np.stack([rng.choice(Ns, k, replace=False) for _ in range(Bs)]).astype(np.int32)
+    idx[1, 10:50] = -1
+    out, lse = cskv.sparse_attend(dev(qs), dev(ents), dev(win), torch.from_numpy(idx).cuda(),
+                                  sink=sink)
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend(qs, ents, win, dt, idx, sink=sink_h)
+    _check_attn(out, lse, ro, rl, dt)
+    idx0 = np.full((Bs, 4), -1, np.int32)
+    out, lse = cskv.sparse_attend(dev(qs), dev(ents), dev(win), torch.from_numpy(idx0).cuda(), W=0,
+                                  sink=sink)
+    torch.cuda.synchronize()
+    assert (host_f64(out) == 0).all()
+    np.testing.assert_allclose(lse.cpu().numpy(), np.tile(sink_h, (Bs, 1)), rtol=1e-6)
+
+
 def test_merge_of_split_partials():
     """cskv_merge combines oracle partials over a row partition into the
     oracle's unsplit result."""
@@ -185,6 +238,14 @@ def test_merge_of_split_partials():
     out, lse = _cskv().merge(o_part, l_part, dtype=torch.float32)
     torch.cuda.synchronize()
     ro, rl = oracle.hca_attend(q, ent, wl.DT_F32)
+    assert rowwise_err(host_f64(out), ro) <= 1e-5
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=1e-5)
+    # the same partials with a per-head sink in the merge's denominator
+    sink_h = np.linspace(-1.0, 3.0, H)
+    out, lse = _cskv().merge(o_part, l_part, dtype=torch.float32,
+                             sink=torch.from_numpy(sink_h.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q, ent, wl.DT_F32, sink=sink_h)
     assert rowwise_err(host_f64(out), ro) <= 1e-5
     np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=1e-5)
 
