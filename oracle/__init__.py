@@ -20,7 +20,7 @@ _SRC = os.path.join(_HERE, "cskv_oracle.c")
 _LIB = os.path.join(_HERE, "libcskv_oracle.so")
 _lib = None
 
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, F64 = 0, 1, 2, 3
 D, R, E, I = 512, 64, 576, 64
 
 
@@ -45,6 +45,11 @@ def lib():
         L.cskv_oracle_e4m3_value.restype = dbl
         L.cskv_oracle_bf16_value.argtypes = [ctypes.c_uint16]
         L.cskv_oracle_bf16_value.restype = dbl
+        L.cskv_oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.cskv_oracle_e2m1_value.restype = dbl
+        L.cskv_oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        L.cskv_oracle_e8m0_value.restype = dbl
+        L.cskv_oracle_mxfp4_decode.argtypes = [vp, vp, i64, vp]
         L.cskv_oracle_num_entries.argtypes = [i64, i32]
         L.cskv_oracle_num_entries.restype = i64
         L.cskv_oracle_compress.argtypes = [vp, vp, i32, vp, i64, i64, i32, vp, i64, vp]
@@ -125,6 +130,36 @@ def index_scores(qI, kI, dt, scale=1.0, q_pos=None, m=4, per_seq=False):
     _check(lib().cskv_oracle_index_scores(_p(qI), _p(kI), dt, B, N, Id, float(scale), kstride,
                                           _p(qp), m, _p(s), _p(v)), "index_scores")
     return s, v
+
+
+def e2m1_value(code):
+    return lib().cskv_oracle_e2m1_value(code)
+
+
+def e8m0_value(x):
+    return lib().cskv_oracle_e8m0_value(x)
+
+
+def mxfp4_decode(codes, scales):
+    """MXFP4 rows of 64 elements -> float64 [rows, 64] (codes uint8
+    [rows, 32], scales uint8 [rows, 2]; leading dimensions are kept)."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    lead = codes.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    if codes.shape[-1] != 32 or scales.shape != lead + (2,):
+        raise ValueError("mxfp4 rows: codes [..., 32] and scales [..., 2]")
+    out = np.empty(lead + (64,), dtype=np.float64)
+    _check(lib().cskv_oracle_mxfp4_decode(_p(codes), _p(scales), rows, _p(out)), "mxfp4_decode")
+    return out
+
+
+def index_scores_mxfp4(q_codes, q_scales, k_codes, k_scales, scale=1.0, q_pos=None, m=4,
+                       per_seq=False):
+    """Indexer scores of MXFP4 queries and keys: the rows are decoded exactly,
+    then scored like any other input."""
+    return index_scores(mxfp4_decode(q_codes, q_scales), mxfp4_decode(k_codes, k_scales), F64,
+                        scale, q_pos=q_pos, m=m, per_seq=per_seq)
 
 
 def topk(scores, visible, k):

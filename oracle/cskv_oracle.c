@@ -48,6 +48,7 @@
 #define ORC_F32 0
 #define ORC_BF16 1
 #define ORC_E4M3 2
+#define ORC_F64 3   /* values already decoded (MXFP4 rows, see below) */
 
 /* ---- decoding of stored inputs (fp32, bf16, OCP fp8 e4m3fn) ------------- */
 
@@ -73,15 +74,48 @@ double cskv_oracle_bf16_value(uint16_t bits) {
   return (double)f;
 }
 
+/* ---- MXFP4 [P1 "QAT": the indexer's QK path runs in FP4 (MXFP4)].  The
+ * pages name the format only; its definition is the OCP Microscaling
+ * Formats (MX) specification v1.0: a block of 32 FP4 E2M1 elements shares
+ * one E8M0 scale, and element i of a block is worth scale * P_i.
+ *
+ * E2M1: 1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit, no
+ * infinities or NaN; exponent 0 is subnormal (m * 0.5); largest value 6. */
+double cskv_oracle_e2m1_value(uint8_t code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -v : v;
+}
+
+/* E8M0: an unsigned biased exponent X (bias 127) and no mantissa: 2^(X-127);
+ * X = 255 is NaN. */
+double cskv_oracle_e8m0_value(uint8_t x) { return x == 255 ? NAN : ldexp(1.0, (int)x - 127); }
+
+/* Rows of 64 elements in two MX blocks: codes [rows][32], element 2j in the
+ * low nibble of byte j and element 2j+1 in its high nibble; scales
+ * [rows][2], scale b covering elements 32b .. 32b+31.  out [rows][64]. */
+int cskv_oracle_mxfp4_decode(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                             double* out) {
+  if (!codes || !scales || !out || rows < 0) return -1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int i = 0; i < 64; ++i) {
+      const uint8_t byte = codes[r * 32 + i / 2];
+      const uint8_t code = (i & 1) ? (byte >> 4) : (byte & 15);
+      out[r * 64 + i] = cskv_oracle_e8m0_value(scales[r * 2 + i / 32]) * cskv_oracle_e2m1_value(code);
+    }
+  return 0;
+}
+
 static double ld(const void* buf, int64_t i, int dt) {
   switch (dt) {
     case ORC_F32: return (double)((const float*)buf)[i];
     case ORC_BF16: return cskv_oracle_bf16_value(((const uint16_t*)buf)[i]);
+    case ORC_F64: return ((const double*)buf)[i];
     default: return cskv_oracle_e4m3_value(((const uint8_t*)buf)[i]);
   }
 }
 
-static int dt_ok(int dt) { return dt == ORC_F32 || dt == ORC_BF16 || dt == ORC_E4M3; }
+static int dt_ok(int dt) { return dt == ORC_F32 || dt == ORC_BF16 || dt == ORC_E4M3 || dt == ORC_F64; }
 
 /* ---- compression [P4 "DeepSeek comprimeix la dimensio temporal",
  *      "Finestres solapades ..."; P1 2.1 and 2.2] ------------------------- */

@@ -101,6 +101,92 @@ def test_e4m3_roundtrip_of_the_input_encoder():
     assert np.abs(dec).max() == pytest.approx(np.abs(a).max(), rel=1e-6)
 
 
+def test_mxfp4_decode_matches_ocp_tables():
+    g = _gold("worked_examples.json")["mxfp4"]
+    for code, val in g["e2m1"].items():
+        v = oracle.e2m1_value(int(code, 16))
+        assert v == val and math.copysign(1, v) == math.copysign(1, val), code
+    for x, val in g["e8m0"].items():
+        assert oracle.e8m0_value(int(x)) == val, x
+    for x in g["e8m0_nan"]:
+        assert math.isnan(oracle.e8m0_value(x))
+
+
+def _one_hot_mxfp4(i, code, s0, s1):
+    codes = np.zeros((1, 32), np.uint8)
+    codes[0, i // 2] = code << (4 * (i % 2))
+    return codes, np.array([[s0, s1]], np.uint8)
+
+
+def test_mxfp4_element_placement():
+    """Element i sits in nibble i % 2 of byte i // 2 and takes the scale of
+    block i // 32: a single non-zero code lands at i with that block's
+    power of two, nowhere else."""
+    for i in range(64):
+        for code, val in ((0x2, 1.0), (0xF, -6.0), (0x1, 0.5)):
+            c, sc = _one_hot_mxfp4(i, code, 120, 131)
+            row = oracle.mxfp4_decode(c, sc)[0]
+            want = np.zeros(64)
+            want[i] = val * 2.0 ** ((120 if i < 32 else 131) - 127)
+            assert np.array_equal(row, want), (i, code)
+
+
+def _unpack_codes(codes):
+    return np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[:-1] + (64,))
+
+
+def test_mxfp4_scores_reduce_to_the_f32_path():
+    """With unit scales (X = 127) MXFP4 scores equal the fp32 scores of the
+    E2M1 table values; other scales multiply each block's share of the dot
+    product by 2^(Xq + Xk - 254)."""
+    table = np.array([_gold("worked_examples.json")["mxfp4"]["e2m1"]["0x%x" % c] for c in range(16)])
+    rng = np.random.default_rng(41)
+    B, N = 3, 50
+    qc = rng.integers(0, 256, (B, 32), dtype=np.uint8)
+    kc = rng.integers(0, 256, (N, 32), dtype=np.uint8)
+    ones_q, ones_k = np.full((B, 2), 127, np.uint8), np.full((N, 2), 127, np.uint8)
+    s, v = oracle.index_scores_mxfp4(qc, ones_q, kc, ones_k, 0.75)
+    qf = table[_unpack_codes(qc)].astype(np.float32)
+    kf = table[_unpack_codes(kc)].astype(np.float32)
+    s32, v32 = oracle.index_scores(qf, kf, F32, 0.75)
+    assert np.array_equal(s, s32) and np.array_equal(v, v32)
+    # per-block scale: blocks scored on their own with unit scales
+    xq = rng.integers(120, 135, (B, 2)).astype(np.uint8)
+    xk = rng.integers(120, 135, (N, 2)).astype(np.uint8)
+    sx, _ = oracle.index_scores_mxfp4(qc, xq, kc, xk, 1.0)
+    part = []
+    for blk in range(2):
+        keep = np.zeros(64, bool)
+        keep[32 * blk:32 * blk + 32] = True
+        sb, _ = oracle.index_scores((qf * keep).astype(np.float32), kf, F32, 1.0)
+        f = 2.0 ** (xq[:, blk, None].astype(float) + xk[None, :, blk].astype(float) - 254)
+        part.append(sb * f)
+    assert np.array_equal(sx, part[0] + part[1])
+
+
+def test_mxfp4_encoder_roundtrip():
+    """The input encoder keeps values that MXFP4 holds exactly, and rounds
+    others to the nearest value on their block's grid."""
+    rng = np.random.default_rng(5)
+    table = np.array([oracle.e2m1_value(c) for c in range(16)])
+    # exact: table values times a block power of two, each block reaching 4 or 6
+    c = rng.integers(0, 16, (20, 64))
+    c[:, 0], c[:, 32] = 6, 15
+    e = rng.integers(-10, 10, (20, 2))
+    a = table[c] * np.repeat(2.0 ** e, 32, axis=1)
+    codes, scales = wl.mxfp4_encode(a)
+    assert np.array_equal(oracle.mxfp4_decode(codes, scales), a)
+    # general values: nearest grid point of the chosen block scale
+    a = rng.standard_normal((200, 64)) * 3
+    codes, scales = wl.mxfp4_encode(a)
+    dec = oracle.mxfp4_decode(codes, scales)
+    unit = np.repeat(np.array([[oracle.e8m0_value(x) for x in r] for r in scales]), 32, axis=1)
+    grid = table[None, None, :] * unit[..., None]
+    best = np.abs(a[..., None] - grid).min(axis=-1)
+    assert np.allclose(np.abs(a - dec), best, rtol=0, atol=1e-12)
+    assert (np.abs(dec) <= 6 * unit).all()
+
+
 def test_bf16_decode():
     g = _gold("worked_examples.json")["bf16"]
     for code, val in g["codes"].items():

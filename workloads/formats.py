@@ -1,4 +1,5 @@
-"""Storage formats of the inputs: bf16 (round to nearest even) and OCP fp8 e4m3.
+"""Storage formats of the inputs: bf16 (round to nearest even), OCP fp8 e4m3
+and OCP MXFP4 (32-element blocks of FP4 E2M1 sharing an E8M0 scale).
 
 These are input-preparation encoders only.  The oracle and the GPU library
 each decode the stored bytes with their own code.
@@ -64,3 +65,37 @@ def e4m3_encode(a, scale):
     # -0 is stored as +0 so that equal values have equal codes
     code = np.where(code == 0x80, np.uint8(0), code).astype(np.uint8)
     return code
+
+
+# Non-negative FP4 E2M1 values by code 0..7 (exponent bias 1, one mantissa
+# bit, code 1 subnormal).
+_E2M1_POS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mxfp4_encode(a):
+    """Quantise rows of 64 values to MXFP4: codes uint8 [..., 32] (element 2j
+    in the low nibble of byte j) and E8M0 scales uint8 [..., 2], one per
+    32-element block.  The scale exponent is floor(log2(amax)) - 2 (the
+    largest E2M1 exponent), so the block's largest value lands in [4, 8)
+    before rounding; elements round to the nearest E2M1 value, ties to the
+    even code, saturating at 6.  All-zero blocks get scale 2^0."""
+    v = np.asarray(a, dtype=np.float64)
+    if v.shape[-1] != 64:
+        raise ValueError("mxfp4 rows have 64 elements")
+    lead = v.shape[:-1]
+    blk = v.reshape(lead + (2, 32))
+    amax = np.abs(blk).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        ex = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0)
+    ex = np.clip(ex, -127, 127).astype(np.int64)
+    scales = (ex + 127).astype(np.uint8)
+    mag = np.minimum(np.abs(blk) / np.ldexp(1.0, ex)[..., None], 6.0)
+    hi = np.minimum(np.searchsorted(_E2M1_POS, mag, side="left"), 7)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = mag - _E2M1_POS[lo], _E2M1_POS[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where((blk < 0) & (code != 0), code | np.uint8(8), code).astype(np.uint8)
+    code = code.reshape(lead + (64,))
+    packed = (code[..., 0::2] | (code[..., 1::2] << np.uint8(4))).astype(np.uint8)
+    return np.ascontiguousarray(packed), np.ascontiguousarray(scales)
