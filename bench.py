@@ -188,6 +188,8 @@ def main():
         result["prefill"] = bench_prefill(args, cskv, wl, dev, torch, np)
         torch.cuda.empty_cache()
         result["hca_prefill"] = bench_hca_prefill(args, cskv, wl, dev, torch, np)
+        result["mxfp4_topk"] = bench_mxfp4_topk(args, cskv, wl, inp, cfg, torch, np,
+                                                part_ms["csa_topk"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, inp, cfg, ms_step, np)
     print(json.dumps(result), flush=True)
@@ -279,6 +281,38 @@ def bench_hca_prefill(args, cskv, wl, dev, torch, np):
         "roofline": {"bound": "mfma", "achieved": round(flops / (t * 1e-3) / 1e12, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+    }
+
+
+def bench_mxfp4_topk(args, cskv, wl, inp, cfg, torch, np, bf16_ms):
+    """The decode step's indexer selection with MXFP4 queries and keys: the
+    same draws as the bf16 indexer inputs, quantised per 32-element block
+    (34 bytes per key instead of 128)."""
+    B, N, k = cfg.B, cfg.N_csa, cfg.k
+    qc, qs = wl.mxfp4_encode(wl.bf16_bits_to_f32(inp["qI"].raw))
+    kc, ks = wl.mxfp4_encode(wl.bf16_bits_to_f32(inp["kI"].raw))
+    qc, qs, kc, ks = (torch.from_numpy(a).cuda() for a in (qc, qs, kc, ks))
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(cskv.index_topk_workspace_size(B, N, k), dtype=torch.uint8, device="cuda")
+    run = lambda: cskv.index_topk_mxfp4(qc, qs, kc, ks, k, idx_out=idx, workspace=ws)
+    for _ in range(3):
+        run()
+    steps = max(20, args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / steps
+    nbytes = N * 34 + B * 34 + B * k * 4
+    return {
+        "workload": "layer_1m decode indexer, MXFP4", "queries": B, "entries": N, "k": k,
+        "ms": round(t, 4), "bf16_ms": bf16_ms,
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (t * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
 
 

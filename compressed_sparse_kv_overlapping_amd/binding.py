@@ -40,6 +40,8 @@ _SIGS = {
     "cskv_index_topk_workspace_size": ([_i64, _i64, _i32], _sz),
     "cskv_index_topk": ([_vp, _vp, _i64, _i64, _i32, _i64, _vp, _i32, _f32, ctypes.c_int, _vp,
                          _vp, _sz, _vp], ctypes.c_int),
+    "cskv_index_topk_mxfp4": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _vp, _i32, _f32, _vp,
+                               _vp, _sz, _vp], ctypes.c_int),
     "cskv_attend_workspace_size": ([_i64, _i32, _i64], _sz),
     "cskv_sparse_attend": ([_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i64, _i64, _i64,
                             _vp, _i64, _f32, _vp, ctypes.c_int, _vp, _vp, _vp, _sz, _vp],
@@ -188,6 +190,27 @@ def index_topk(q_idx, idx_keys, k, q_pos=None, m=4, idx_scale=1.0, per_seq=False
     _call("cskv_index_topk", _ptr(q_idx), _ptr(idx_keys), B, N, k, N * I if per_seq else 0,
           _ptr(q_pos), m, float(idx_scale), _dt(q_idx), _ptr(idx_out), _ptr(workspace),
           workspace.numel(), _stream(stream))
+    return idx_out
+
+
+def index_topk_mxfp4(q_codes, q_scales, key_codes, key_scales, k, q_pos=None, m=4, idx_scale=1.0,
+                     per_seq=False, idx_out=None, workspace=None, stream=None):
+    """index_topk over MXFP4 rows: codes uint8 [B, 32] / [N, 32] (or
+    [B, N, 32] per sequence), E8M0 scales uint8 [B, 2] / [N, 2] (or
+    [B, N, 2])."""
+    _dev(q_codes, q_scales, key_codes, key_scales, q_pos, idx_out)
+    for t in (q_codes, q_scales, key_codes, key_scales):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("MXFP4 codes and scales are contiguous uint8 tensors")
+    B, N = q_codes.shape[0], key_codes.shape[-2]
+    if idx_out is None:
+        idx_out = torch.empty((B, k), dtype=torch.int32, device=q_codes.device)
+    ws = index_topk_workspace_size(B, N, k)
+    if workspace is None:
+        workspace = _workspace(ws, q_codes.device)
+    _call("cskv_index_topk_mxfp4", _ptr(q_codes), _ptr(q_scales), _ptr(key_codes), _ptr(key_scales),
+          B, N, k, N if per_seq else 0, _ptr(q_pos), m, float(idx_scale), _ptr(idx_out),
+          _ptr(workspace), workspace.numel(), _stream(stream))
     return idx_out
 
 

@@ -161,6 +161,28 @@ int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t 
   return hip_status(cskv::launch_topk(p, workspace, (hipStream_t)stream), "cskv_index_topk");
 }
 
+int cskv_index_topk_mxfp4(const void* q_codes, const uint8_t* q_scales, const void* key_codes,
+                          const uint8_t* key_scales, int64_t B, int64_t N, int32_t k,
+                          int64_t key_bstride, const int64_t* q_pos, int32_t m, float idx_scale,
+                          int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "cskv_index_topk_mxfp4";
+  if (!q_scales || !key_scales) return fail(CSKV_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (key_bstride < 0 || key_bstride > ((int64_t)1 << 40))
+    return fail(CSKV_ERR_INVALID_ARG, "%s: key_bstride=%lld", fn, (long long)key_bstride);
+  // rows are 64 elements: the element stride the shared checks expect
+  int st = check_topk(fn, q_codes, key_codes, B, N, k, key_bstride * 64, q_pos, m, idx_scale,
+                      CSKV_BF16, idx_out);
+  if (st) return st;
+  if ((reinterpret_cast<uintptr_t>(q_scales) | reinterpret_cast<uintptr_t>(key_scales)) & 1u)
+    return fail(CSKV_ERR_INVALID_ARG, "%s: scale arrays must be 2-byte aligned", fn);
+  const size_t need = cskv::topk_workspace_bytes(B, N, k);
+  if (!workspace || ws_bytes < need || !aligned16(workspace))
+    return fail(CSKV_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  cskv::TopkParams p{3, q_codes, key_codes, q_pos, key_bstride * 64, B, N, k, m, idx_scale, idx_out,
+                     q_scales, key_scales};
+  return hip_status(cskv::launch_topk(p, workspace, (hipStream_t)stream), fn);
+}
+
 size_t cskv_attend_workspace_size(int64_t B, int32_t H, int64_t rows_per_query) {
   if (B < 1 || H < 1 || rows_per_query < 0) return 0;
   // the larger of the fp32 and bf16 layouts, so one size serves both

@@ -34,7 +34,9 @@ constexpr int kMaxGroups = 16384;
 
 struct IdxArgs {
   const void* q;              // [B][64]
-  const void* keys;           // [N][64] (+ b * key_bstride)
+  const void* keys;           // [N][64] (+ b * key_bstride elements)
+  const uint8_t* qsc;         // MXFP4 only: E8M0 scales [B][2]
+  const uint8_t* ksc;         // MXFP4 only: E8M0 scales [N][2] (+ b * key_bstride / 32)
   const int64_t* q_pos;       // NULL at decode
   int64_t key_bstride;
   int B, N, k, m, GS, G, qpb, tiles_per_wave;
@@ -58,6 +60,97 @@ template <class T> struct KeyFrag;
 template <> struct KeyFrag<bf16_t> { static constexpr int bytes = 2; };
 template <> struct KeyFrag<float> { static constexpr int bytes = 4; };
 template <> struct KeyFrag<e4m3_t> { static constexpr int bytes = 1; };
+
+// MXFP4 rows (OCP Microscaling v1.0; the format named for the indexer's QK
+// path in "Frontier Techniques: NTK RoPE, CSA+HCA, QAT, MTP", QAT): 64 E2M1
+// codes in 32 bytes, element 2j in the low nibble of byte j, and two E8M0
+// scales per row (elements 0..31, 32..63) in a separate byte array.
+struct fp4x2_t { uint8_t u; };
+template <> struct Frag<fp4x2_t> { uint32_t v; uint32_t s; };  // 8 codes; block scale as fp32 bits
+
+// Bytes of a 64-element row, and the fragment type the MFMA consumes.
+// MXFP4 is decoded to bf16, which is exact: an E2M1 value times a power of
+// two has at most two significant bits (within bf16's exponent range).
+template <class T> struct Elem {
+  static constexpr int kRowBytes = 64 * (int)sizeof(T);
+  using QF = Frag<T>;
+};
+template <> struct Elem<fp4x2_t> {
+  static constexpr int kRowBytes = 32;
+  using QF = Frag<bf16_t>;
+};
+
+// E8M0 scale X as the fp32 2^(X-127): X = 0 is the subnormal 2^-127 and
+// X = 255 (NaN in E8M0) a NaN, so that the value is right whether the
+// conversion reads the whole fp32 or only its exponent field.
+__device__ __forceinline__ uint32_t e8m0_f32_bits(uint32_t x) {
+  return x == 0u ? 0x00400000u : (x == 255u ? 0x7fc00000u : x << 23);
+}
+
+// 8 E2M1 codes times their block scale, as 8 bf16 (gfx950 converts two
+// codes per instruction).  Queries and keys go through the same conversion,
+// so the pairing of slots in a dot product never depends on which nibble a
+// converted pair puts first.
+__device__ __forceinline__ void fp4_decode(Frag<bf16_t>& d, const Frag<fp4x2_t>& f) {
+  const float sc = __uint_as_float(f.s);
+  const hw_bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.v, sc, 0);
+  const hw_bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.v, sc, 1);
+  const hw_bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.v, sc, 2);
+  const hw_bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.v, sc, 3);
+  d.v = u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+              __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+}
+
+// Key fragments as the MFMA takes them (a copy, or the MXFP4 decode).
+template <class T>
+__device__ __forceinline__ void key_decode(typename Elem<T>::QF* d, const Frag<T>* k) {
+  d[0] = k[0];
+  d[1] = k[1];
+}
+template <>
+__device__ __forceinline__ void key_decode<fp4x2_t>(Frag<bf16_t>* d, const Frag<fp4x2_t>* k) {
+  fp4_decode(d[0], k[0]);
+  fp4_decode(d[1], k[1]);
+}
+
+// Both k-step fragments (dims 0..31 and 32..63, slots 8g..8g+7) of row r,
+// from global memory: kb = the rows' first byte, sb = their scales (MXFP4).
+template <class T>
+__device__ __forceinline__ void key_frags(Frag<T>* f, const char* kb, const uint8_t* sb, int64_t r,
+                                          int g) {
+  const T* p = reinterpret_cast<const T*>(kb + r * Elem<T>::kRowBytes);
+  frag_load(f[0], p + 8 * g);
+  frag_load(f[1], p + 32 + 8 * g);
+}
+template <>
+__device__ __forceinline__ void key_frags<fp4x2_t>(Frag<fp4x2_t>* f, const char* kb, const uint8_t* sb,
+                                                   int64_t r, int g) {
+  const char* p = kb + r * 32;
+  f[0].v = *reinterpret_cast<const uint32_t*>(p + 4 * g);
+  f[1].v = *reinterpret_cast<const uint32_t*>(p + 16 + 4 * g);
+  const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sb + 2 * r);
+  f[0].s = e8m0_f32_bits(s2 & 255u);
+  f[1].s = e8m0_f32_bits(s2 >> 8);
+}
+
+// The block scales of row r for fragments whose codes came from LDS.
+template <class T>
+__device__ __forceinline__ void key_scales(Frag<T>* f, const uint8_t* sb, int64_t r) {}
+template <>
+__device__ __forceinline__ void key_scales<fp4x2_t>(Frag<fp4x2_t>* f, const uint8_t* sb, int64_t r) {
+  const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sb + 2 * r);
+  f[0].s = e8m0_f32_bits(s2 & 255u);
+  f[1].s = e8m0_f32_bits(s2 >> 8);
+}
+
+// Query row r's fragments, decoded once per kernel.
+template <class T>
+__device__ __forceinline__ void query_frags(typename Elem<T>::QF* f, const IdxArgs& a, int64_t r,
+                                            int g) {
+  Frag<T> raw[2];
+  key_frags<T>(raw, reinterpret_cast<const char*>(a.q), a.qsc, r, g);
+  key_decode<T>(f, raw);
+}
 
 // Maximum of two scores in one instruction: the median of (a, b, +inf),
 // which skips the quieting of signalling NaNs that the compiler puts before
@@ -100,15 +193,21 @@ __device__ float raw_threshold(float t, float scale) {
 // chunk c ^ swz(r).  16 consecutive rows then put a lane group's fragment
 // reads on distinct banks (rows per 256 bytes: 4 fp8, 2 bf16, 1 fp32).
 template <class T> struct KeyTiles {
-  static constexpr int kRow = 64 * (int)sizeof(T);
+  static constexpr int kRow = Elem<T>::kRowBytes;
   static constexpr int kChunks = kRow / 16;
   static constexpr int kRowsPer256 = 256 / kRow;
   static constexpr int kStage = 16384;
   static constexpr int kTiles = kStage / (16 * kRow);        // 16-row tiles per stage
   static __device__ __forceinline__ int swz(int r) { return (r / kRowsPer256) % kChunks; }
+  // byte offset of the fragment of k-step ks, lane group g, in a row
+  static __device__ __forceinline__ int frag_off(int ks, int g) { return (32 * ks + 8 * g) * kRow / 64; }
   // the 8-element fragment at byte offset off of a staged row
   static __device__ __forceinline__ void load(Frag<T>& f, const char* row, int off, int sw);
 };
+template <> __device__ __forceinline__ void KeyTiles<fp4x2_t>::load(Frag<fp4x2_t>& f, const char* row,
+                                                                    int off, int sw) {
+  f.v = *reinterpret_cast<const uint32_t*>(row + 16 * ((off >> 4) ^ sw) + (off & 15));
+}
 template <> __device__ __forceinline__ void KeyTiles<e4m3_t>::load(Frag<e4m3_t>& f, const char* row,
                                                                    int off, int sw) {
   f.v = *reinterpret_cast<const uint64_t*>(row + 16 * ((off >> 4) ^ sw) + (off & 15));
@@ -149,11 +248,13 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
   }
   const int col = lane & 15, g = lane >> 4;
   const int q0 = blockIdx.y * a.qpb + qw * 16 * NQB;
-  const T* qbase = reinterpret_cast<const T*>(a.q);
-  const T* kbase = reinterpret_cast<const T*>(a.keys) + (int64_t)q0 * a.key_bstride;
+  // per-sequence keys: key_bstride elements per query (a multiple of 64)
+  const int64_t krow0 = (int64_t)q0 * (a.key_bstride / kI);
+  const char* kbase = reinterpret_cast<const char*>(a.keys) + krow0 * Elem<T>::kRowBytes;
+  const uint8_t* sbase = a.ksc ? a.ksc + 2 * krow0 : nullptr;
 
   // this lane's queries (one per 16-column block) and their query fragments
-  Frag<T> qf[NQB][2];
+  typename Elem<T>::QF qf[NQB][2];
   int qb[NQB], nvis[NQB];
   float tscore[NQB], traw[NQB];
   int blk_vis = 0, min_vis = 0x7fffffff;
@@ -165,14 +266,12 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
     nvis[j] = ok ? n_visible(a, q0 + c) : 0;
     blk_vis = max(blk_vis, nvis[j]);
     min_vis = min(min_vis, ok ? nvis[j] : 0x7fffffff);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (ok) {
-        frag_load(qf[j][ks], qbase + (int64_t)(q0 + c) * kI + 32 * ks + 8 * g);
-      } else {
-        Frag<T> z{};
-        qf[j][ks] = z;
-      }
+    if (ok) {
+      query_frags<T>(qf[j], a, q0 + c, g);
+    } else {
+      typename Elem<T>::QF z{};
+      qf[j][0] = z;
+      qf[j][1] = z;
     }
     tscore[j] = -INFINITY;                                       // threshold 0: take all
     if (MODE == 1 && ok && a.thr[q0 + c] != 0u) tscore[j] = key_score(a.thr[q0 + c]);
@@ -204,12 +303,14 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
   const int grp_first = e_w0 >> a.gs_shift, grp_last = (e_w1 - 1) >> a.gs_shift;
   auto tile = [&](const int et, const Frag<T>* kf) {
    if (et < blk_vis) {                                         // skip invisible tiles
+    typename Elem<T>::QF kd[2];
+    key_decode<T>(kd, kf);
     f32x4 S[NQB];
 #pragma unroll
     for (int j = 0; j < NQB; ++j) {
       S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16(S[j], kf[0], qf[j][0]);
-      mma16(S[j], kf[1], qf[j][1]);
+      mma16(S[j], kd[0], qf[j][0]);
+      mma16(S[j], kd[1], qf[j][1]);
     }
     // S[j][i]: query qb[j], entry et + 4g + i
     if (et + 16 <= min_vis) {
@@ -304,14 +405,12 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
     Frag<T> kr[PF][2];
     auto load_tile = [&](const int et, Frag<T>* kf) {
       const int er = et + col;                                 // A row of this lane
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (et < e_w1 && et < blk_vis && er < a.N) {
-          frag_load(kf[ks], kbase + (int64_t)er * kI + 32 * ks + 8 * g);
-        } else {
-          Frag<T> z{};
-          kf[ks] = z;
-        }
+      if (et < e_w1 && et < blk_vis && er < a.N) {
+        key_frags<T>(kf, kbase, sbase, er, g);
+      } else {
+        Frag<T> z{};
+        kf[0] = z;
+        kf[1] = z;
       }
     };
 #pragma unroll
@@ -366,7 +465,9 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
       auto frags = [&](const int t, Frag<T>* f) {
         const char* rowp = buf + (t * 16 + col) * KT::kRow;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) KT::load(f[ks], rowp, (32 * ks + 8 * g) * (int)sizeof(T), swz);
+        for (int ks = 0; ks < 2; ++ks) KT::load(f[ks], rowp, KT::frag_off(ks, g), swz);
+        const int row = e_w0 + (st * KT::kTiles + t) * 16 + col;   // as staged (clamped)
+        key_scales<T>(f, sbase, row < a.N ? row : a.N - 1);
       };
       frags(0, kf[0]);
       static_assert(KT::kTiles % 2 == 0, "tiles per stage come in pairs");
@@ -559,6 +660,12 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, int e) {
 
 template <class T>
 __device__ __forceinline__ float dot64(const T* qrow, const T* krow);
+// Raw score of query b and entry e (key rows of query b when per sequence).
+template <class T>
+__device__ __forceinline__ float entry_dot(const IdxArgs& a, int b, int e) {
+  const T* kb = reinterpret_cast<const T*>(a.keys) + (int64_t)b * a.key_bstride;
+  return dot64<T>(reinterpret_cast<const T*>(a.q) + (int64_t)b * kI, kb + (int64_t)e * kI);
+}
 template <> __device__ __forceinline__ float dot64<float>(const float* q, const float* k) {
   float s = 0.f;
   for (int r = 0; r < kI; ++r) s = fmaf(q[r], k[r], s);
@@ -574,6 +681,32 @@ template <> __device__ __forceinline__ float dot64<e4m3_t>(const e4m3_t* q, cons
   float s = 0.f;
   for (int r = 0; r < kI; ++r)
     s = fmaf(__builtin_amdgcn_cvt_f32_fp8((int)q[r].u, 0), __builtin_amdgcn_cvt_f32_fp8((int)k[r].u, 0), s);
+  return s;
+}
+template <>
+__device__ __forceinline__ float entry_dot<fp4x2_t>(const IdxArgs& a, int b, int e) {
+  const int64_t kr = (int64_t)b * (a.key_bstride / kI) + e;
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(a.q) + (int64_t)b * 32);
+  const uint32_t* k = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(a.keys) + kr * 32);
+  float s = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const float sq = __uint_as_float(e8m0_f32_bits(a.qsc[(int64_t)b * 2 + blk]));
+    const float sk = __uint_as_float(e8m0_f32_bits(a.ksc[kr * 2 + blk]));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t qw = q[4 * blk + w], kw = k[4 * blk + w];
+#define CSKV_FP4_PAIR(SEL)                                                          \
+      {                                                                             \
+        const hw_f32x2_t qv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw, sq, SEL);    \
+        const hw_f32x2_t kv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(kw, sk, SEL);    \
+        s = fmaf(qv[0], kv[0], s);                                                  \
+        s = fmaf(qv[1], kv[1], s);                                                  \
+      }
+      CSKV_FP4_PAIR(0) CSKV_FP4_PAIR(1) CSKV_FP4_PAIR(2) CSKV_FP4_PAIR(3)
+#undef CSKV_FP4_PAIR
+    }
+  }
   return s;
 }
 
@@ -651,8 +784,6 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
     }
   }
   const int nc = overflow ? 0 : (int)total;
-  const T* kb = reinterpret_cast<const T*>(a.keys) + (int64_t)b * a.key_bstride;
-  const T* qrow = reinterpret_cast<const T*>(a.q) + (int64_t)b * kI;
   __syncthreads();
 
   // the k-th largest composite
@@ -735,7 +866,7 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
       for (int i = t; i < (int)nb; i += NT) hist[i] = 0;
       __syncthreads();
       for (int e = t; e < nv; e += NT) {
-        const float s = dot64<T>(qrow, kb + (int64_t)e * kI) * a.scale;
+        const float s = entry_dot<T>(a, b, e) * a.scale;
         const uint64_t v = composite(score_key(s), e);
         if ((v & mask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & (nb - 1)], 1u);
       }
@@ -794,7 +925,7 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
   if (t == 0) sh_nsel = 0;
   __syncthreads();
   for (int e = t; e < nv; e += NT) {
-    const float s = dot64<T>(qrow, kb + (int64_t)e * kI) * a.scale;
+    const float s = entry_dot<T>(a, b, e) * a.scale;
     if (composite(score_key(s), e) >= thr) {
       const uint32_t at = atomicAdd(&sh_nsel, 1u);
       if (at < (uint32_t)kMaxK) sel[at] = e;
@@ -888,6 +1019,7 @@ template <class T>
 static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t stream) {
   IdxArgs a;
   a.q = p.q; a.keys = p.keys; a.q_pos = p.q_pos; a.key_bstride = p.key_bstride;
+  a.qsc = p.qsc; a.ksc = p.ksc;
   a.B = (int)p.B; a.N = (int)p.N; a.k = p.k; a.m = p.m; a.scale = p.scale; a.out = p.out;
   const bool per_seq = p.key_bstride != 0;
   const TopkGeom g = topk_geom(p.B, p.N, p.k, per_seq);
@@ -928,6 +1060,7 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
 hipError_t launch_topk(const TopkParams& p, void* ws, hipStream_t stream) {
   if (p.dt == 0) return launch_topk_t<float>(p, ws, stream);
   if (p.dt == 1) return launch_topk_t<bf16_t>(p, ws, stream);
+  if (p.dt == 3) return launch_topk_t<fp4x2_t>(p, ws, stream);
   return launch_topk_t<e4m3_t>(p, ws, stream);
 }
 

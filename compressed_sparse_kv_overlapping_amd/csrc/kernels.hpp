@@ -40,14 +40,16 @@ hipError_t launch_merge(int dt, const float* o_part, const float* lse_part, int6
                         const float* sink, int H, void* out, float* lse, hipStream_t stream);
 
 struct TopkParams {
-  int dt;                    // 0 fp32, 1 bf16, 2 fp8 e4m3
+  int dt;                    // 0 fp32, 1 bf16, 2 fp8 e4m3, 3 MXFP4
   const void* q;             // [B][64]
-  const void* keys;          // [N][64] (+ b * key_bstride)
+  const void* keys;          // [N][64] (+ b * key_bstride elements)
   const int64_t* q_pos;      // NULL at decode
   int64_t key_bstride, B, N;
   int k, m;
   float scale;
   int32_t* out;              // [B][k]
+  const uint8_t* qsc = nullptr;   // MXFP4: E8M0 scales of the queries [B][2]
+  const uint8_t* ksc = nullptr;   // MXFP4: E8M0 scales of the keys [N][2]
 };
 
 int topk_max_k();

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CSKV_VERSION 10200 /* major*10000 + minor*100: 1.2 (HCA q_pos/m; attention-sink logits) */
+#define CSKV_VERSION 10300 /* major*10000 + minor*100: 1.3 (MXFP4 indexer) */
 
 typedef enum cskv_dtype {
   CSKV_F32 = 0,       /* IEEE binary32 */
@@ -139,6 +139,32 @@ int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t 
                     int64_t key_bstride, const int64_t* q_pos, int32_t m, float idx_scale,
                     cskv_dtype idx_dt, int32_t* idx_out, void* workspace, size_t ws_bytes,
                     void* stream);
+
+/*
+ * Indexer scoring and top-k selection over MXFP4 queries and keys ("Frontier
+ * Techniques: NTK RoPE, CSA+HCA, QAT, MTP", QAT: the indexer's QK path runs
+ * in FP4, MXFP4).  Same selection as cskv_index_topk; only the storage of
+ * q_idx and idx_keys differs.  MXFP4 is the OCP Microscaling v1.0 format: a
+ * block of 32 FP4 E2M1 elements shares one E8M0 scale 2^(X-127), and each
+ * element is worth scale * E2M1 value.
+ *   q_codes [B][32] and key_codes [N][32] bytes (per query if key_bstride > 0):
+ *     the 64 E2M1 codes of a row, element 2j in the low nibble of byte j and
+ *     element 2j+1 in the high nibble.  16-byte aligned.
+ *   q_scales [B][2] and key_scales [N][2] bytes: E8M0 scales of elements
+ *     0..31 and 32..63 of each row.  2-byte aligned.
+ *   key_bstride: rows (not elements) between the key sets of consecutive
+ *     queries, 0 for keys shared by all queries.
+ *   s[b][i] = idx_scale * sum_r q[b][r] * key[i][r] over the decoded values,
+ *   accumulated in fp32; it is exact while every product and partial sum is
+ *   an fp32 normal number (as for fp32 inputs).  Scale bytes 0 and 255 decode
+ *   to 2^-127 and NaN; rows with NaN scores have no defined rank.
+ *   workspace: at least cskv_index_topk_workspace_size(B, N, k) bytes.
+ * Errors: as cskv_index_topk, and INVALID_ARG for null or odd scale pointers.
+ */
+int cskv_index_topk_mxfp4(const void* q_codes, const uint8_t* q_scales, const void* key_codes,
+                          const uint8_t* key_scales, int64_t B, int64_t N, int32_t k,
+                          int64_t key_bstride, const int64_t* q_pos, int32_t m, float idx_scale,
+                          int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Sparse attention over selected entries plus the raw window ("Frontier

@@ -27,7 +27,7 @@ def declared():
 
 def test_header_functions_are_exported(lib):
     names = declared()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), f"{n} declared in cskv.h but not exported"
     from compressed_sparse_kv_overlapping_amd import binding
@@ -35,7 +35,7 @@ def test_header_functions_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cskv_version() == 10200
+    assert lib.cskv_version() == 10300
     assert lib.cskv_status_string(OK) == b"ok"
     for code in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.cskv_status_string(code) not in (b"ok", b"unknown status")
@@ -84,6 +84,23 @@ def test_index_topk_errors(lib):
     assert f(P, P, 8, 16384, 64, 0, NULL, 4, 1.0, 1, P, NULL, ws, NULL) == WORKSPACE
     assert f(P, P, 8, 16384, 64, 0, NULL, 4, 1.0, 1, P, P, 16, NULL) == WORKSPACE
     assert f(NULL, P, 8, 16384, 64, 0, NULL, 4, 1.0, 1, P, P, ws, NULL) == INVALID
+
+
+def test_index_topk_mxfp4_errors(lib):
+    f = lib.cskv_index_topk_mxfp4
+    ws = lib.cskv_index_topk_workspace_size(8, 16384, 1024)
+    S = P  # scale arrays: any even address (no call reaches a kernel)
+
+    def call(q=P, qs=S, kc=P, ks=S, B=8, N=16384, k=64, kb=0, qp=NULL, m=4, sc=1.0, out=P, w=P,
+             wsb=ws):
+        return f(q, qs, kc, ks, B, N, k, kb, qp, m, sc, out, w, wsb, NULL)
+    assert call(qs=NULL) == INVALID and call(ks=NULL) == INVALID       # scales
+    assert call(q=NULL) == INVALID and call(out=NULL) == INVALID
+    assert call(k=0) == INVALID and call(k=4097) == UNSUPPORTED
+    assert call(kb=-1) == INVALID                                      # stride in rows
+    assert call(qp=P, m=0) == INVALID and call(sc=0.0) == INVALID
+    assert call(N=1 << 21) == UNSUPPORTED
+    assert call(w=NULL) == WORKSPACE and call(wsb=16) == WORKSPACE
 
 
 def test_attend_errors(lib):

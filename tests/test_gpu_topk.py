@@ -156,3 +156,101 @@ def test_topk_prefill_workload_sampled():
     rows = np.unique(np.concatenate([[0, 1, cfg.B - 1], np.linspace(0, cfg.B - 1, 29).astype(int)]))
     s, v = oracle.index_scores(qI.raw[rows], kI.raw, wl.DT_E4M3, scale, q_pos=inp["q_pos"][rows], m=4)
     check_selection(idx[rows], s, v, cfg.k)
+
+
+# ------------------------------------------------------------------ MXFP4
+
+def _run_mx(qc, qs, kc, ks, k, scale=1.0, q_pos=None, m=4, per_seq=False):
+    cskv = _cskv()
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    qp = None if q_pos is None else up(np.asarray(q_pos, np.int64))
+    idx = cskv.index_topk_mxfp4(up(qc), up(qs), up(kc), up(ks), k, q_pos=qp, m=m, idx_scale=scale,
+                                per_seq=per_seq)
+    torch.cuda.synchronize()
+    s, v = oracle.index_scores_mxfp4(qc, qs, kc, ks, scale, q_pos=q_pos, m=m, per_seq=per_seq)
+    return idx.cpu().numpy(), s, v
+
+
+def _exact(idx, s, v, k):
+    """MXFP4 scores are exact in fp32 here (few significant bits, a narrow
+    scale range, a power-of-two idx_scale): the selection must be the
+    oracle's, ties broken by index."""
+    check_selection(idx, s, v, k)
+    ref = oracle.topk(s, v, k)
+    for b in range(idx.shape[0]):
+        want = np.sort(ref[b][ref[b] >= 0])
+        np.testing.assert_array_equal(idx[b, :len(want)], want)
+
+
+@pytest.mark.parametrize("B,N,k", [(1, 1024, 64), (32, 16384, 1024), (3, 5000, 100), (40, 3001, 17),
+                                   (5, 777, 1), (2, 100, 128)])
+def test_topk_mxfp4_matches_oracle(B, N, k):
+    qc, qs = wl.mxfp4_encode(wl.normal(95, N, 1, (B, 64)))
+    kc, ks = wl.mxfp4_encode(wl.normal(95, N, 2, (N, 64)))
+    idx, s, v = _run_mx(qc, qs, kc, ks, k, scale=0.5)
+    _exact(idx, s, v, k)
+
+
+def test_topk_mxfp4_many_queries_causal():
+    """1,536 queries (key tiles staged through LDS, shared by four query
+    sets) with a causal mask, and a non-power-of-two idx_scale."""
+    B, N, k, m = 1536, 6000, 256, 4
+    qc, qs = wl.mxfp4_encode(wl.normal(96, 0, 1, (B, 64)))
+    kc, ks = wl.mxfp4_encode(wl.normal(96, 0, 2, (N, 64)))
+    pos = np.random.default_rng(4).integers(0, N * m, B)
+    pos[:4] = [0, 3, 4, N * m - 1]
+    idx, s, v = _run_mx(qc, qs, kc, ks, k, scale=1.0, q_pos=pos, m=m)
+    _exact(idx, s, v, k)
+    idx, s, v = _run_mx(qc, qs, kc, ks, k, scale=0.37)
+    check_selection(idx, s, v, k)
+
+
+def test_topk_mxfp4_per_sequence_keys():
+    B, N, k = 6, 9000, 256
+    qc, qs = wl.mxfp4_encode(wl.normal(97, 0, 1, (B, 64)))
+    kc, ks = wl.mxfp4_encode(wl.normal(97, 0, 2, (B, N, 64)))
+    idx, s, v = _run_mx(qc, qs, kc, ks, k, per_seq=True)
+    _exact(idx, s, v, k)
+
+
+def test_topk_mxfp4_all_equal_scores_take_lowest_indices():
+    """Identical keys: every score ties, the candidate list overflows and the
+    streaming path (scores recomputed from the codes) must keep 0..k-1."""
+    B, N, k = 3, 30000, 50
+    qc, qs = wl.mxfp4_encode(wl.normal(98, 0, 1, (B, 64)))
+    kc, ks = wl.mxfp4_encode(np.tile(wl.normal(98, 0, 2, (1, 64)), (N, 1)))
+    idx, s, v = _run_mx(qc, qs, kc, ks, k)
+    np.testing.assert_array_equal(idx, np.tile(np.arange(k, dtype=np.int32), (B, 1)))
+    assert (s == s[:, :1]).all()
+
+
+def test_topk_mxfp4_scale_bytes_across_the_range():
+    """Row scales from 2^-125 to 2^73 (one per row, so each score is exact),
+    and rows at byte 0 (2^-127) holding elements of magnitude >= 2, which
+    decode to fp32 normals; with query scales of 2^103 those rows score
+    well inside fp32 and must rank exactly."""
+    rng = np.random.default_rng(8)
+    B, N, k = 4, 4000, 300
+    kc = rng.integers(0, 256, (N, 32), dtype=np.uint8)
+    ks = np.repeat(rng.integers(2, 201, (N, 1)), 2, axis=1).astype(np.uint8)
+    big = np.array([4, 5, 6, 7, 12, 13, 14, 15], np.uint8)     # |E2M1| >= 2
+    c = rng.choice(big, (50, 64))
+    kc[:50] = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    ks[:50] = 0
+    qc = rng.integers(0, 256, (B, 32), dtype=np.uint8)
+    qs = np.full((B, 2), 127, np.uint8)
+    idx, s, v = _run_mx(qc, qs, kc, ks, k)
+    _exact(idx, s, v, k)
+    qs[:] = 230
+    idx, s, v = _run_mx(qc, qs, kc[:50].copy(), ks[:50].copy(), 20)
+    _exact(idx, s, v, 20)
+
+
+def test_topk_mxfp4_decode_workload():
+    """The 1M-token decode shape: 32 queries over 262,144 entries, top-1024,
+    with the bf16 workload's draws quantised to MXFP4; every query checked."""
+    cfg = wl.CONFIGS["layer_1m"]
+    qc, qs = wl.mxfp4_encode(wl.normal(cfg.config_id, 0, 8, (cfg.B, 64)))
+    kc, ks = wl.mxfp4_encode(wl.normal(cfg.config_id, 0, 9, (cfg.N_csa, 64)))
+    idx, s, v = _run_mx(qc, qs, kc, ks, cfg.k)
+    _exact(idx, s, v, cfg.k)
