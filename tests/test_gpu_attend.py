@@ -360,3 +360,23 @@ def test_layer_1m_step_sampled():
     ent = entries(128, inp["b128"].raw, inp["rope128"].raw, np.arange(T // 128, dtype=np.int64))
     ro, rl = oracle.hca_attend(inp["q_hca"].raw[rows], ent, wl.DT_BF16)
     _check_attn(out_h[rows], lse_h[rows], ro, rl, wl.DT_BF16)
+
+
+def test_index_reuse_across_layers():
+    """A later layer reuses an earlier layer's selection: the indices that
+    cskv_csa_attend returns for layer 1 drive cskv_sparse_attend over layer
+    2's own queries, entries and window, which must equal the oracle's
+    attention over that same selection."""
+    cfg = wl.CONFIGS["csa_decode"]
+    l1 = wl.make_inputs(cfg, seed=0)
+    l2 = wl.make_inputs(cfg, seed=1)
+    cskv = _cskv()
+    _, _, idx = cskv.csa_attend(dev(l1["q"]), dev(l1["qI"]), dev(l1["entries"]), dev(l1["kI"]),
+                                dev(l1["window"]), cfg.k)
+    out, lse = cskv.sparse_attend(dev(l2["q"]), dev(l2["entries"]), dev(l2["window"]), idx)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    s, v = oracle.index_scores(l1["qI"].raw, l1["kI"].raw, cfg.idx_dt)
+    check_selection(idx, s, v, cfg.k)
+    ro, rl = oracle.csa_attend(l2["q"].raw, l2["entries"].raw, l2["window"].raw, cfg.dt, idx)
+    _check_attn(out, lse, ro, rl, cfg.dt)
