@@ -317,58 +317,77 @@ def bench_mxfp4_topk(args, cskv, wl, inp, cfg, torch, np, bf16_ms):
 
 
 def cpu_baseline(args, inp, cfg, gpu_ms, np):
-    """The oracle (plain fp64 C, OpenMP over independent outputs) on a bounded
-    sample of the same step, extrapolated to a whole step."""
+    """The oracle (plain fp64 C, OpenMP over independent outputs) on the same
+    step: a small calibration sample predicts the whole step's time, then the
+    largest fraction of the step that fits --cpu-seconds (the whole step when
+    it fits) is run and timed, and scaled to a whole step.  Attention runs
+    over the oracle's own compressed entries."""
     import oracle
     import workloads as wl
     threads = oracle.max_threads()
     T, B, H, k = cfg.T, cfg.B, cfg.H, cfg.k
     N4, N128 = T // 4, T // 128
     rng = np.random.default_rng(0)
-    budget = args.cpu_seconds
-    # compress: a sample of entries at each scale
-    n4, n128 = 4096, 64
-    t = time.perf_counter()
-    oracle.compress(inp["x"].raw, inp["z"].raw, wl.DT_BF16, inp["b4"].raw, 4,
-                    entry_ids=rng.choice(N4, n4, replace=False))
-    t_c4 = (time.perf_counter() - t) * N4 / n4
-    t = time.perf_counter()
-    oracle.compress(inp["x"].raw, inp["z"].raw, wl.DT_BF16, inp["b128"].raw, 128,
-                    entry_ids=rng.choice(N128, n128, replace=False))
-    t_c128 = (time.perf_counter() - t) * N128 / n128
-    # CSA and HCA: one query with all its heads (the oracle's cost does not
-    # depend on the entry values, so the content dims are a constant here)
-    ent = np.empty((N4, E), np.uint16)
-    ent[:, :D] = 0x3f80
-    ent[:, D:] = inp["rope4"].raw
-    t = time.perf_counter()
-    s, v = oracle.index_scores(inp["qI"].raw[:1], inp["kI"].raw, wl.DT_BF16)
-    sel = oracle.topk(s, v, k)
-    t_sel = (time.perf_counter() - t) * B
-    t = time.perf_counter()
-    oracle.csa_attend(inp["q"].raw[:1], ent, inp["window"].raw, wl.DT_BF16, sel)
-    t_csa = (time.perf_counter() - t) * B
-    ent128 = np.empty((N128, E), np.uint16)
-    ent128[:, :D] = 0x3f80
-    ent128[:, D:] = inp["rope128"].raw
-    nh = 16
-    t = time.perf_counter()
-    oracle.hca_attend(inp["q_hca"].raw[:1, :nh], ent128, wl.DT_BF16)
-    t_hca = (time.perf_counter() - t) * B * H / nh
-    step_s = t_c4 + t_c128 + t_sel + t_csa + t_hca
+
+    def ids(n, total):
+        return np.arange(total) if n >= total else np.sort(rng.choice(total, n, replace=False))
+
+    def entries(ids_, m, bias):
+        return oracle.compress(inp["x"].raw, inp["z"].raw, wl.DT_BF16, bias, m, entry_ids=ids_)
+
+    def run(f):
+        """Times of each part on fraction f of the step, scaled to the step."""
+        n4, n128 = max(64, int(N4 * f)), max(4, int(N128 * f))
+        nq, nh = max(1, int(round(B * f))), max(8, int(H * f)) if f < 1 else H
+        i4, i128 = ids(n4, N4), ids(n128, N128)
+        t = time.perf_counter()
+        c4 = entries(i4, 4, inp["b4"].raw)
+        t_c4 = (time.perf_counter() - t) * N4 / len(i4)
+        t = time.perf_counter()
+        c128 = entries(i128, 128, inp["b128"].raw)
+        t_c128 = (time.perf_counter() - t) * N128 / len(i128)
+        # entries for attention: the computed ones where sampled, the rest a
+        # constant (the oracle's attention cost does not depend on values)
+        ent = np.full((N4, E), 0x3f80, np.uint16)
+        ent[i4, :D] = wl.bf16_bits(c4.astype(np.float32))
+        ent[:, D:] = inp["rope4"].raw
+        ent128 = np.full((N128, E), 0x3f80, np.uint16)
+        ent128[i128, :D] = wl.bf16_bits(c128.astype(np.float32))
+        ent128[:, D:] = inp["rope128"].raw
+        t = time.perf_counter()
+        sc, vis = oracle.index_scores(inp["qI"].raw[:nq], inp["kI"].raw, wl.DT_BF16)
+        sel = oracle.topk(sc, vis, k)
+        t_sel = (time.perf_counter() - t) * B / nq
+        t = time.perf_counter()
+        oracle.csa_attend(inp["q"].raw[:nq], ent, inp["window"].raw, wl.DT_BF16, sel)
+        t_csa = (time.perf_counter() - t) * B / nq
+        t = time.perf_counter()
+        oracle.hca_attend(inp["q_hca"].raw[:nq, :nh], ent128, wl.DT_BF16)
+        t_hca = (time.perf_counter() - t) * B * H / (nq * nh)
+        return (t_c4, t_c128, t_sel, t_csa, t_hca), (n4, n128, nq, nh)
+
+    est, _ = run(1.0 / 64)
+    frac = min(1.0, args.cpu_seconds / max(sum(est), 1e-9))
+    t0 = time.perf_counter()
+    parts, (n4, n128, nq, nh) = run(frac)
+    sample_s = time.perf_counter() - t0
+    t_c4, t_c128, t_sel, t_csa, t_hca = parts
+    step_s = sum(parts)
     pairs = B * k + B * N128
+    whole = n4 >= N4 and n128 >= N128 and nq >= B and nh >= H
     return {
         "value": round(pairs / step_s, 2), "unit": "entries/s", "cores": threads, "kind": "oracle",
-        "sample": (f"compress {n4} of {N4} m=4 entries and {n128} of {N128} m'=128 entries; "
-                   f"indexer+top-k and CSA attention for 1 of {B} queries (all {H} heads); HCA for "
-                   f"1 query x {nh} of {H} heads; each part scaled to the full step"),
+        "sample": ("the whole step" if whole else
+                   f"compress {n4} of {N4} m=4 entries and {n128} of {N128} m'=128 entries; "
+                   f"indexer+top-k and CSA attention for {nq} of {B} queries (all {H} heads); "
+                   f"HCA for {nq} queries x {nh} of {H} heads; each part scaled to the full step")
+                  + f" ({sample_s:.1f} s of oracle time, after a 1/64 calibration sample)",
         "step_s_extrapolated": round(step_s, 2),
         "parts_s": {"compress_m4": round(t_c4, 2), "compress_m128": round(t_c128, 2),
                     "csa_topk": round(t_sel, 2), "csa_attend": round(t_csa, 2),
                     "hca_attend": round(t_hca, 2)},
         "gpu_speedup": round(step_s / (gpu_ms * 1e-3), 1),
     }
-
 
 if __name__ == "__main__":
     main()
