@@ -49,7 +49,7 @@ def lib():
         L.cskv_oracle_e2m1_value.restype = dbl
         L.cskv_oracle_e8m0_value.argtypes = [ctypes.c_uint8]
         L.cskv_oracle_e8m0_value.restype = dbl
-        L.cskv_oracle_mxfp4_decode.argtypes = [vp, vp, i64, vp]
+        L.cskv_oracle_mxfp4_decode.argtypes = [vp, vp, i64, i32, vp]
         L.cskv_oracle_num_entries.argtypes = [i64, i32]
         L.cskv_oracle_num_entries.restype = i64
         L.cskv_oracle_compress.argtypes = [vp, vp, i32, vp, i64, i64, i32, vp, i64, vp]
@@ -141,16 +141,19 @@ def e8m0_value(x):
 
 
 def mxfp4_decode(codes, scales):
-    """MXFP4 rows of 64 elements -> float64 [rows, 64] (codes uint8
-    [rows, 32], scales uint8 [rows, 2]; leading dimensions are kept)."""
+    """MXFP4 rows of C elements (C a multiple of 32) -> float64 [..., C]
+    (codes uint8 [..., C/2], scales uint8 [..., C/32]; leading dimensions
+    are kept)."""
     codes = _c(codes, np.uint8)
     scales = _c(scales, np.uint8)
     lead = codes.shape[:-1]
     rows = int(np.prod(lead)) if lead else 1
-    if codes.shape[-1] != 32 or scales.shape != lead + (2,):
-        raise ValueError("mxfp4 rows: codes [..., 32] and scales [..., 2]")
-    out = np.empty(lead + (64,), dtype=np.float64)
-    _check(lib().cskv_oracle_mxfp4_decode(_p(codes), _p(scales), rows, _p(out)), "mxfp4_decode")
+    cols = 2 * codes.shape[-1]
+    if cols % 32 or scales.shape != lead + (cols // 32,):
+        raise ValueError("mxfp4 rows: codes [..., C/2] and scales [..., C/32], C % 32 == 0")
+    out = np.empty(lead + (cols,), dtype=np.float64)
+    _check(lib().cskv_oracle_mxfp4_decode(_p(codes), _p(scales), rows, cols, _p(out)),
+           "mxfp4_decode")
     return out
 
 
@@ -194,6 +197,19 @@ def csa_attend(q, entries, window, dt, idx, scale=1.0, q_pos=None, win_pos0=0, W
                                         float(scale), _p(_c(sink, np.float64)), _p(out), _p(lse)),
            "csa_attend")
     return out, lse
+
+
+def csa_attend_mxfp4(q, ent_codes, ent_scales, window, idx, **kw):
+    """csa_attend with MXFP4 entries (codes [.., N, 288], scales [.., N, 18])
+    and bf16 queries and window rows: every input is decoded exactly, then
+    attended in fp64."""
+    win = None if window is None else decode(window, BF16)
+    return csa_attend(decode(q, BF16), mxfp4_decode(ent_codes, ent_scales), win, F64, idx, **kw)
+
+
+def hca_attend_mxfp4(q, ent_codes, ent_scales, **kw):
+    """hca_attend with MXFP4 entries and bf16 queries."""
+    return hca_attend(decode(q, BF16), mxfp4_decode(ent_codes, ent_scales), F64, **kw)
 
 
 def hca_attend(q, entries, dt, scale=1.0, per_seq=False, Dv=D, q_pos=None, m=None, sink=None):

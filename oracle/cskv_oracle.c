@@ -91,17 +91,19 @@ double cskv_oracle_e2m1_value(uint8_t code) {
  * X = 255 is NaN. */
 double cskv_oracle_e8m0_value(uint8_t x) { return x == 255 ? NAN : ldexp(1.0, (int)x - 127); }
 
-/* Rows of 64 elements in two MX blocks: codes [rows][32], element 2j in the
- * low nibble of byte j and element 2j+1 in its high nibble; scales
- * [rows][2], scale b covering elements 32b .. 32b+31.  out [rows][64]. */
-int cskv_oracle_mxfp4_decode(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+/* Rows of `cols` elements (a multiple of 32) in cols/32 MX blocks: codes
+ * [rows][cols/2], element 2j in the low nibble of byte j and element 2j+1 in
+ * its high nibble; scales [rows][cols/32], scale b covering elements
+ * 32b .. 32b+31.  out [rows][cols]. */
+int cskv_oracle_mxfp4_decode(const uint8_t* codes, const uint8_t* scales, int64_t rows, int cols,
                              double* out) {
-  if (!codes || !scales || !out || rows < 0) return -1;
+  if (!codes || !scales || !out || rows < 0 || cols <= 0 || cols % 32) return -1;
   for (int64_t r = 0; r < rows; ++r)
-    for (int i = 0; i < 64; ++i) {
-      const uint8_t byte = codes[r * 32 + i / 2];
+    for (int i = 0; i < cols; ++i) {
+      const uint8_t byte = codes[r * (cols / 2) + i / 2];
       const uint8_t code = (i & 1) ? (byte >> 4) : (byte & 15);
-      out[r * 64 + i] = cskv_oracle_e8m0_value(scales[r * 2 + i / 32]) * cskv_oracle_e2m1_value(code);
+      out[r * cols + i] =
+          cskv_oracle_e8m0_value(scales[r * (cols / 32) + i / 32]) * cskv_oracle_e2m1_value(code);
     }
   return 0;
 }

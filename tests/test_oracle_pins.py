@@ -131,6 +131,45 @@ def test_mxfp4_element_placement():
             assert np.array_equal(row, want), (i, code)
 
 
+def test_mxfp4_element_placement_in_entry_rows():
+    """576-element entry rows (18 blocks): element i sits in nibble i % 2 of
+    byte i // 2 with the scale of block i // 32, each block its own power."""
+    rng = np.random.default_rng(9)
+    xs = rng.integers(100, 150, 18).astype(np.uint8)
+    for i in list(range(0, 576, 7)) + [31, 32, 63, 64, 543, 544, 575]:
+        codes = np.zeros((1, 288), np.uint8)
+        codes[0, i // 2] = 0x5 << (4 * (i % 2))                 # 3.0
+        row = oracle.mxfp4_decode(codes, xs[None])[0]
+        want = np.zeros(576)
+        want[i] = 3.0 * 2.0 ** (int(xs[i // 32]) - 127)
+        assert np.array_equal(row, want), i
+
+
+def test_decoded_inputs_attend_like_stored_ones():
+    """The fp64 input path (used for MXFP4 entries, decoded first) gives the
+    bf16 path's results exactly on the decoded values, and MXFP4 entries
+    holding bf16-exact values attend like those bf16 rows."""
+    rng = np.random.default_rng(12)
+    B, H, N, W, k = 2, 3, 40, 5, 7
+    q = wl.bf16_bits(rng.standard_normal((B, H, 576)).astype(np.float32) / 24)
+    vals = rng.integers(-6, 7, (N, 576)).astype(np.float64) * 0.5     # on the E2M1 grid
+    vals[np.abs(vals) == 2.5] = 2.0
+    ent = wl.bf16_bits(vals.astype(np.float32))
+    win = wl.bf16_bits(rng.standard_normal((W, 576)).astype(np.float32))
+    idx = np.sort(rng.choice(N, (B, k)), axis=1).astype(np.int32)
+    o1, l1 = oracle.csa_attend(q, ent, win, BF16, idx)
+    o2, l2 = oracle.csa_attend(oracle.decode(q, BF16), oracle.decode(ent, BF16),
+                               oracle.decode(win, BF16), oracle.F64, idx)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    codes, scales = wl.mxfp4_encode(vals)
+    assert np.array_equal(oracle.mxfp4_decode(codes, scales), vals)
+    o3, l3 = oracle.csa_attend_mxfp4(q, codes, scales, win, idx)
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+    h1, hl1 = oracle.hca_attend(q, ent, BF16)
+    h3, hl3 = oracle.hca_attend_mxfp4(q, codes, scales)
+    assert np.array_equal(h1, h3) and np.array_equal(hl1, hl3)
+
+
 def _unpack_codes(codes):
     return np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[:-1] + (64,))
 

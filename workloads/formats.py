@@ -73,17 +73,18 @@ _E2M1_POS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
 def mxfp4_encode(a):
-    """Quantise rows of 64 values to MXFP4: codes uint8 [..., 32] (element 2j
-    in the low nibble of byte j) and E8M0 scales uint8 [..., 2], one per
-    32-element block.  The scale exponent is floor(log2(amax)) - 2 (the
+    """Quantise rows of C values (C a multiple of 32) to MXFP4: codes uint8
+    [..., C/2] (element 2j in the low nibble of byte j) and E8M0 scales uint8
+    [..., C/32], one per 32-element block.  The scale exponent is floor(log2(amax)) - 2 (the
     largest E2M1 exponent), so the block's largest value lands in [4, 8)
     before rounding; elements round to the nearest E2M1 value, ties to the
     even code, saturating at 6.  All-zero blocks get scale 2^0."""
     v = np.asarray(a, dtype=np.float64)
-    if v.shape[-1] != 64:
-        raise ValueError("mxfp4 rows have 64 elements")
+    C = v.shape[-1]
+    if C % 32:
+        raise ValueError("mxfp4 rows are whole 32-element blocks")
     lead = v.shape[:-1]
-    blk = v.reshape(lead + (2, 32))
+    blk = v.reshape(lead + (C // 32, 32))
     amax = np.abs(blk).max(axis=-1)
     with np.errstate(divide="ignore"):
         ex = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0)
@@ -96,6 +97,6 @@ def mxfp4_encode(a):
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
     code = np.where((blk < 0) & (code != 0), code | np.uint8(8), code).astype(np.uint8)
-    code = code.reshape(lead + (64,))
+    code = code.reshape(lead + (C,))
     packed = (code[..., 0::2] | (code[..., 1::2] << np.uint8(4))).astype(np.uint8)
     return np.ascontiguousarray(packed), np.ascontiguousarray(scales)
