@@ -190,6 +190,8 @@ def main():
         result["hca_prefill"] = bench_hca_prefill(args, cskv, wl, dev, torch, np)
         result["mxfp4_topk"] = bench_mxfp4_topk(args, cskv, wl, inp, cfg, torch, np,
                                                 part_ms["csa_topk"])
+        result["mxfp4_attend"] = bench_mxfp4_attend(args, cskv, inp, cfg, dev, torch, np,
+                                                    part_ms)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, inp, cfg, ms_step, np)
     print(json.dumps(result), flush=True)
@@ -314,6 +316,54 @@ def bench_mxfp4_topk(args, cskv, wl, inp, cfg, torch, np, bf16_ms):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+
+
+def bench_mxfp4_attend(args, cskv, inp, cfg, dev, torch, np, part_ms):
+    """The decode step's two attentions over MXFP4 entries (306 bytes a row
+    instead of 1,152): CSA over 1,024 selected of 262,144 entries plus the
+    128 window rows, and HCA over 8,192 entries, 32 queries x 128 heads.
+    The codes are uniform random bytes and the scales 2^-2..2^0 (the
+    kernels' time does not depend on the values); the selection is a random
+    sorted one per query."""
+    B, H, k, W = cfg.B, cfg.H, cfg.k, cfg.W
+    rng = np.random.default_rng(5)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    c4 = up(rng.integers(0, 256, (cfg.N_csa, E // 2), dtype=np.uint8))
+    s4 = up(rng.integers(125, 128, (cfg.N_csa, E // 32), dtype=np.uint8))
+    c128 = up(rng.integers(0, 256, (cfg.N_hca, E // 2), dtype=np.uint8))
+    s128 = up(rng.integers(125, 128, (cfg.N_hca, E // 32), dtype=np.uint8))
+    idx = up(np.sort(np.stack([rng.choice(cfg.N_csa, k, replace=False) for _ in range(B)]),
+                     axis=1).astype(np.int32))
+    q, qh, win = dev(inp["q"]), dev(inp["q_hca"]), dev(inp["window"])
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(cskv.attend_workspace_size(B, H, k + W), cskv.hca_workspace_size(B, H, cfg.N_hca)),
+                     dtype=torch.uint8, device="cuda")
+    runs = {
+        "csa_attend": lambda: cskv.sparse_attend_mxfp4(q, c4, s4, win, idx, out=out, lse=lse,
+                                                       workspace=ws),
+        "hca_attend": lambda: cskv.hca_attend_mxfp4(qh, c128, s128, out=out, lse=lse, workspace=ws),
+    }
+    res = {"workload": "layer_1m decode attention, MXFP4 entries", "queries": B, "heads": H}
+    for name, run in runs.items():
+        for _ in range(3):
+            run()
+        steps = max(20, args.steps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / steps
+        rows = k + W if name == "csa_attend" else cfg.N_hca
+        flops = 2 * B * H * rows * (E + D)
+        res[name] = {"ms": round(t, 4), "bf16_entries_ms": round(part_ms[name], 4),
+                     "roofline": {"bound": "mfma", "achieved": round(flops / (t * 1e-3) / 1e12, 1),
+                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(flops / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
+    return res
 
 
 def cpu_baseline(args, inp, cfg, gpu_ms, np):

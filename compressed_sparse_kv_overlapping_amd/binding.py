@@ -53,6 +53,10 @@ _SIGS = {
     "cskv_hca_workspace_size": ([_i64, _i32, _i64], _sz),
     "cskv_hca_attend": ([_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, _vp, ctypes.c_int, _vp,
                          _vp, _vp, _sz, _vp], ctypes.c_int),
+    "cskv_sparse_attend_mxfp4": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i64, _i64,
+                                  _i64, _vp, _i64, _f32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "cskv_hca_attend_mxfp4": ([_vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, _vp, _vp, _vp,
+                               _vp, _sz, _vp], ctypes.c_int),
     "cskv_merge": ([_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
@@ -299,6 +303,62 @@ def hca_attend(q, entries, scale=1.0, per_seq=False, q_pos=None, m=None, out=Non
     _call("cskv_hca_attend", _ptr(q), _ptr(entries), B, H, N, N * E if per_seq else 0,
           _ptr(q_pos), int(m) if q_pos is not None else 0, float(scale), _sink(sink, H), _dt(q),
           _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
+    return out, lse
+
+
+def _mx_entries(codes, scales):
+    for t in (codes, scales):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("MXFP4 entry codes and scales are contiguous uint8 tensors")
+    if codes.shape[-1] != E // 2 or scales.shape[-1] != E // 32 or codes.shape[:-1] != scales.shape[:-1]:
+        raise ValueError(f"MXFP4 entries: codes [..., {E // 2}] and scales [..., {E // 32}]")
+    return codes.shape[-2]
+
+
+def sparse_attend_mxfp4(q, ent_codes, ent_scales, window, idx, q_pos=None, win_pos0=0, W=None,
+                        scale=1.0, per_seq=False, out=None, lse=None, workspace=None, stream=None,
+                        sink=None):
+    """sparse_attend over MXFP4 entries: codes uint8 [N, 288] and E8M0
+    scales uint8 [N, 18] (with a leading batch dimension per sequence); q,
+    window and out are bf16."""
+    _dev(q, ent_codes, ent_scales, window, idx, q_pos, out, lse)
+    N = _mx_entries(ent_codes, ent_scales)
+    B, H = q.shape[0], q.shape[1]
+    k = idx.shape[1]
+    win_rows = 0 if window is None else window.shape[-2]
+    if W is None:
+        W = win_rows
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _workspace(attend_workspace_size(B, H, k + W), q.device)
+    _call("cskv_sparse_attend_mxfp4", _ptr(q), _ptr(ent_codes), _ptr(ent_scales), _ptr(window),
+          _ptr(idx), B, H, N, W, k, N if per_seq else 0, win_rows * E if per_seq else 0, win_rows,
+          _ptr(q_pos), int(win_pos0), float(scale), _sink(sink, H), _ptr(out), _ptr(lse),
+          _ptr(workspace), workspace.numel(), _stream(stream))
+    return out, lse
+
+
+def hca_attend_mxfp4(q, ent_codes, ent_scales, scale=1.0, per_seq=False, q_pos=None, m=None,
+                     out=None, lse=None, workspace=None, stream=None, sink=None):
+    """hca_attend over MXFP4 entries (codes [N, 288], scales [N, 18])."""
+    _dev(q, ent_codes, ent_scales, q_pos, out, lse)
+    if q_pos is not None and m is None:
+        raise ValueError("hca_attend_mxfp4: q_pos needs the block size m")
+    N = _mx_entries(ent_codes, ent_scales)
+    B, H = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((B, H, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _workspace(hca_workspace_size(B, H, N), q.device)
+    _call("cskv_hca_attend_mxfp4", _ptr(q), _ptr(ent_codes), _ptr(ent_scales), B, H, N,
+          N if per_seq else 0, _ptr(q_pos), int(m) if q_pos is not None else 0, float(scale),
+          _sink(sink, H), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+          _stream(stream))
     return out, lse
 
 

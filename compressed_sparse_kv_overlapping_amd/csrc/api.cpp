@@ -185,10 +185,13 @@ int cskv_index_topk_mxfp4(const void* q_codes, const uint8_t* q_scales, const vo
 
 size_t cskv_attend_workspace_size(int64_t B, int32_t H, int64_t rows_per_query) {
   if (B < 1 || H < 1 || rows_per_query < 0) return 0;
-  // the larger of the fp32 and bf16 layouts, so one size serves both
+  // the largest of the fp32, bf16 and MXFP4-entry layouts, so one size
+  // serves them all
   size_t a = cskv::attend_partial_bytes(0, B, H, rows_per_query);
   size_t b = cskv::attend_partial_bytes(1, B, H, rows_per_query);
-  return a > b ? a : b;
+  size_t c = cskv::attend_partial_bytes(2, B, H, rows_per_query);
+  a = a > b ? a : b;
+  return a > c ? a : c;
 }
 
 static int check_attend(const char* fn, const void* q, const void* entries, const void* window,
@@ -290,6 +293,60 @@ int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, in
   cskv::AttendParams p{(int)dt, q, entries, nullptr, nullptr, q_pos, B, N, ent_bstride, 0, 0, 0,
                        H, 0, 0, scale, out, lse, 1, q_pos ? m : 0, sink};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), "cskv_hca_attend");
+}
+
+// MXFP4 entries: the codes and scales of row i of sequence b start at
+// (b * ent_bstride + i) * 288 and * 18 bytes; the kernels take element
+// offsets, 576 per row.
+static int check_mxfp4_entries(const char* fn, const void* codes, const uint8_t* scales,
+                               int64_t ent_bstride) {
+  if (!codes || !scales) return fail(CSKV_ERR_INVALID_ARG, "%s: null entry pointer", fn);
+  if (ent_bstride < 0 || ent_bstride > ((int64_t)1 << 40))
+    return fail(CSKV_ERR_INVALID_ARG, "%s: ent_bstride=%lld", fn, (long long)ent_bstride);
+  if (!aligned16(codes)) return fail(CSKV_ERR_INVALID_ARG, "%s: entry codes must be 16-byte aligned", fn);
+  return CSKV_OK;
+}
+
+int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
+                             const void* window, const int32_t* idx, int64_t B, int32_t H,
+                             int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
+                             int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
+                             int64_t win_pos0, float scale, const float* sink, void* out,
+                             float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "cskv_sparse_attend_mxfp4";
+  int st = check_mxfp4_entries(fn, ent_codes, ent_scales, ent_bstride);
+  if (st) return st;
+  st = check_attend(fn, q, ent_codes, window, B, H, N, W, k, ent_bstride * 576, win_bstride,
+                    win_rows, CSKV_BF16, out, scale);
+  if (st) return st;
+  if (k > 0 && !idx) return fail(CSKV_ERR_INVALID_ARG, "%s: null idx", fn);
+  if (!q_pos && W > win_rows)
+    return fail(CSKV_ERR_INVALID_ARG, "%s: W=%d > window rows %lld", fn, W, (long long)win_rows);
+  const size_t need = cskv::attend_partial_bytes(2, B, H, (int64_t)k + W);
+  if (need && (!workspace || ws_bytes < need || !aligned16(workspace)))
+    return fail(CSKV_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  cskv::AttendParams p{2, q, ent_codes, window, idx, q_pos, B, N, ent_bstride * 576, win_bstride,
+                       win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0, sink, ent_scales};
+  return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), fn);
+}
+
+int cskv_hca_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
+                          int64_t B, int32_t H, int64_t N, int64_t ent_bstride,
+                          const int64_t* q_pos, int32_t m, float scale, const float* sink,
+                          void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "cskv_hca_attend_mxfp4";
+  int st = check_mxfp4_entries(fn, ent_codes, ent_scales, ent_bstride);
+  if (st) return st;
+  st = check_attend(fn, q, ent_codes, nullptr, B, H, N, 0, 0, ent_bstride * 576, 0, 0, CSKV_BF16,
+                    out, scale);
+  if (st) return st;
+  if (q_pos && m < 1) return fail(CSKV_ERR_INVALID_ARG, "%s: m=%d with q_pos", fn, m);
+  const size_t need = cskv::attend_partial_bytes(2, B, H, N);
+  if (need && (!workspace || ws_bytes < need || !aligned16(workspace)))
+    return fail(CSKV_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  cskv::AttendParams p{2, q, ent_codes, nullptr, nullptr, q_pos, B, N, ent_bstride * 576, 0, 0, 0,
+                       H, 0, 0, scale, out, lse, 1, q_pos ? m : 0, sink, ent_scales};
+  return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), fn);
 }
 
 int cskv_merge(const float* o_part, const float* lse_part, int64_t B, int32_t H, int32_t S,

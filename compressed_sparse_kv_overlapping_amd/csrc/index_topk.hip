@@ -23,6 +23,7 @@
 //     score ties), the query is resolved by a self-contained streaming radix
 //     select over all its entries instead.
 #include "common.hpp"
+#include "fp4.hpp"
 #include "kernels.hpp"
 
 namespace cskv {
@@ -80,25 +81,12 @@ template <> struct Elem<fp4x2_t> {
   using QF = Frag<bf16_t>;
 };
 
-// E8M0 scale X as the fp32 2^(X-127): X = 0 is the subnormal 2^-127 and
-// X = 255 (NaN in E8M0) a NaN, so that the value is right whether the
-// conversion reads the whole fp32 or only its exponent field.
-__device__ __forceinline__ uint32_t e8m0_f32_bits(uint32_t x) {
-  return x == 0u ? 0x00400000u : (x == 255u ? 0x7fc00000u : x << 23);
-}
-
 // 8 E2M1 codes times their block scale, as 8 bf16 (gfx950 converts two
 // codes per instruction).  Queries and keys go through the same conversion,
 // so the pairing of slots in a dot product never depends on which nibble a
 // converted pair puts first.
 __device__ __forceinline__ void fp4_decode(Frag<bf16_t>& d, const Frag<fp4x2_t>& f) {
-  const float sc = __uint_as_float(f.s);
-  const hw_bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.v, sc, 0);
-  const hw_bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.v, sc, 1);
-  const hw_bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.v, sc, 2);
-  const hw_bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.v, sc, 3);
-  d.v = u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-              __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+  d.v = fp4x8_to_bf16(f.v, __uint_as_float(f.s));
 }
 
 // Key fragments as the MFMA takes them (a copy, or the MXFP4 decode).

@@ -17,7 +17,7 @@ hipError_t launch_compress_fused(int dt, const void* x, const void* z, int64_t T
 size_t compress_fused_workspace_bytes(int64_t T_tokens, int ml);
 
 struct AttendParams {
-  int dt;                    // 0 fp32, 1 bf16
+  int dt;                    // 0 fp32, 1 bf16, 2 bf16 with MXFP4 entries
   const void* q;             // [B][H][576]
   const void* entries;       // [N][576] (+ b * ent_bstride)
   const void* window;        // rows of 576 (+ b * win_bstride)
@@ -31,6 +31,7 @@ struct AttendParams {
   int dense;                 // 1: rows = all N entries, no window
   int hm;                    // dense with q_pos: entry i visible iff (i+1)*hm <= q_pos[b]+1
   const float* sink;         // [H] attention-sink logits, or NULL
+  const uint8_t* ent_scales = nullptr;   // dt 2: MXFP4 entries, E8M0 scales [N][18]
 };
 
 int attend_splits(int dt, int64_t B, int H, int64_t nslots);

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CSKV_VERSION 10300 /* major*10000 + minor*100: 1.3 (MXFP4 indexer) */
+#define CSKV_VERSION 10400 /* major*10000 + minor*100: 1.4 (MXFP4 indexer and entries) */
 
 typedef enum cskv_dtype {
   CSKV_F32 = 0,       /* IEEE binary32 */
@@ -229,6 +229,35 @@ int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, in
                     int64_t ent_bstride, const int64_t* q_pos, int32_t m, float scale,
                     const float* sink, cskv_dtype dt, void* out, float* lse, void* workspace,
                     size_t ws_bytes, void* stream);
+
+/*
+ * CSA sparse attention and HCA dense attention over MXFP4 entries
+ * ("Compressed attention · CSA / HCA và hai trục nén", section 3: the V4.1
+ * KV cache is FP4 with block scales).  Same results as cskv_sparse_attend
+ * and cskv_hca_attend in BF16 (queries, window rows and outputs are bf16)
+ * with each compressed entry given as an MXFP4 row instead: 576 elements
+ * in 18 blocks of 32 (OCP Microscaling v1.0: FP4 E2M1 elements, one E8M0
+ * scale 2^(X-127) per block).
+ *   ent_codes [N][288] bytes: element 2j of a row in the low nibble of byte
+ *     j, element 2j+1 in the high nibble.  16-byte aligned.
+ *   ent_scales [N][18] bytes: the scale of elements 32b .. 32b+31.
+ *   ent_bstride: rows (not elements) between the entry sets of consecutive
+ *     queries, 0 for one shared context.  Other arguments, the workspace
+ *     (cskv_attend_workspace_size / cskv_hca_workspace_size) and the errors
+ *     are those of cskv_sparse_attend / cskv_hca_attend.
+ * The entries decode to bf16 exactly while every decoded value lies in
+ * bf16's normal range (scale bytes 2..252 with any code, at least).
+ */
+int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
+                             const void* window, const int32_t* idx, int64_t B, int32_t H,
+                             int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
+                             int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
+                             int64_t win_pos0, float scale, const float* sink, void* out,
+                             float* lse, void* workspace, size_t ws_bytes, void* stream);
+int cskv_hca_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
+                          int64_t B, int32_t H, int64_t N, int64_t ent_bstride,
+                          const int64_t* q_pos, int32_t m, float scale, const float* sink,
+                          void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Merge of split-KV partial results: for each (b, h) with S partial results

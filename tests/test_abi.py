@@ -27,7 +27,7 @@ def declared():
 
 def test_header_functions_are_exported(lib):
     names = declared()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), f"{n} declared in cskv.h but not exported"
     from compressed_sparse_kv_overlapping_amd import binding
@@ -35,7 +35,7 @@ def test_header_functions_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cskv_version() == 10300
+    assert lib.cskv_version() == 10400
     assert lib.cskv_status_string(OK) == b"ok"
     for code in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.cskv_status_string(code) not in (b"ok", b"unknown status")
@@ -101,6 +101,23 @@ def test_index_topk_mxfp4_errors(lib):
     assert call(qp=P, m=0) == INVALID and call(sc=0.0) == INVALID
     assert call(N=1 << 21) == UNSUPPORTED
     assert call(w=NULL) == WORKSPACE and call(wsb=16) == WORKSPACE
+
+
+def test_attend_mxfp4_errors(lib):
+    s, h = lib.cskv_sparse_attend_mxfp4, lib.cskv_hca_attend_mxfp4
+    ws = lib.cskv_attend_workspace_size(8, 128, 1152)
+
+    def sp(q=P, c=P, sc=P, w=P, idx=P, B=8, H=128, N=16384, W=128, k=1024, eb=0, wr=128, wsb=ws):
+        return s(q, c, sc, w, idx, B, H, N, W, k, eb, 0, wr, NULL, 0, 1.0, NULL, P, P, P, wsb, NULL)
+    assert sp(sc=NULL) == INVALID and sp(c=NULL) == INVALID and sp(q=NULL) == INVALID
+    assert sp(idx=NULL) == INVALID and sp(W=200) == INVALID and sp(eb=-1) == INVALID
+    assert sp(B=0) == INVALID and sp(wsb=16) == WORKSPACE
+    hws = lib.cskv_hca_workspace_size(8, 128, 8192)
+
+    def hc(c=P, sc=P, B=8, N=8192, eb=0, qp=NULL, m=0, wsb=hws):
+        return h(P, c, sc, B, 128, N, eb, qp, m, 1.0, NULL, P, P, P, wsb, NULL)
+    assert hc(sc=NULL) == INVALID and hc(c=NULL) == INVALID and hc(eb=-3) == INVALID
+    assert hc(qp=P, m=0) == INVALID and hc(wsb=16) == WORKSPACE
 
 
 def test_attend_errors(lib):

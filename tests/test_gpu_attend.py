@@ -380,3 +380,98 @@ def test_index_reuse_across_layers():
     check_selection(idx, s, v, cfg.k)
     ro, rl = oracle.csa_attend(l2["q"].raw, l2["entries"].raw, l2["window"].raw, cfg.dt, idx)
     _check_attn(out, lse, ro, rl, cfg.dt)
+
+
+# ------------------------------------------------------- MXFP4 entries
+
+def _mx_entries(cfg_id, seed, shape):
+    """Entries drawn ~N(0,1) in fp32 and quantised to MXFP4 (codes, scales)."""
+    return wl.mxfp4_encode(wl.normal(cfg_id, seed, 2, shape))
+
+
+def _up(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.mark.parametrize("B,H,N,W,k", [(2, 128, 5000, 128, 1024), (3, 80, 700, 16, 37),
+                                       (1, 16, 40, 0, 40), (4, 128, 300, 5, 1)])
+def test_sparse_attend_mxfp4_matches_oracle(B, H, N, W, k):
+    """CSA over MXFP4 entries plus bf16 window rows; some selections hold -1
+    (no row)."""
+    rng = np.random.default_rng(B * 1000 + k)
+    q = _rand(97, N, 1, (B, H, E), wl.DT_BF16, 1 / 24)
+    codes, scales = _mx_entries(97, N, (N, E))
+    win = _rand(97, N, 3, (max(W, 1), E), wl.DT_BF16)
+    idx = np.stack([np.sort(rng.choice(N, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    idx[0, -1] = -1
+    out, lse = _cskv().sparse_attend_mxfp4(dev(q), _up(codes), _up(scales), dev(win), _up(idx), W=W)
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend_mxfp4(q, codes, scales, win, idx, W=W)
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+
+
+def test_sparse_attend_mxfp4_prefill_and_sink():
+    """Prefill queries with per-query causal windows, per-sequence entries,
+    and attention-sink logits."""
+    rng = np.random.default_rng(3)
+    B, H, N, W, k = 3, 128, 900, 128, 64
+    q = _rand(98, 0, 1, (B, H, E), wl.DT_BF16, 1 / 24)
+    codes, scales = _mx_entries(98, 0, (B, N, E))
+    pos0, rows = 1000, 300
+    win = _rand(98, 0, 3, (B, rows, E), wl.DT_BF16)
+    qp = np.array([pos0 + W - 1, pos0 + 200, pos0 + rows - 1], np.int64)   # windows inside the rows
+    idx = np.stack([np.sort(rng.choice(N, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    sink = rng.standard_normal(H) * 2
+    out, lse = _cskv().sparse_attend_mxfp4(dev(q), _up(codes), _up(scales), dev(win), _up(idx),
+                                           q_pos=_up(qp), win_pos0=pos0, W=W, per_seq=True,
+                                           sink=torch.from_numpy(sink).float().cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend_mxfp4(q, codes, scales, win, idx, q_pos=qp, win_pos0=pos0, W=W,
+                                     per_seq=True, sink=sink.astype(np.float32).astype(np.float64))
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+
+
+@pytest.mark.parametrize("B,H,N", [(2, 128, 1000), (3, 48, 33), (1, 16, 1)])
+def test_hca_attend_mxfp4_matches_oracle(B, H, N):
+    q = _rand(99, N, 1, (B, H, E), wl.DT_BF16, 1 / 24)
+    codes, scales = _mx_entries(99, N, (N, E))
+    out, lse = _cskv().hca_attend_mxfp4(dev(q), _up(codes), _up(scales))
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend_mxfp4(q, codes, scales)
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+
+
+def test_hca_attend_mxfp4_prefill():
+    B, H, N, m = 4, 128, 600, 128
+    q = _rand(100, 0, 1, (B, H, E), wl.DT_BF16, 1 / 24)
+    codes, scales = _mx_entries(100, 0, (N, E))
+    qp = np.array([0, 127, 50000, N * m + 9], np.int64)          # none, one, part, all visible
+    out, lse = _cskv().hca_attend_mxfp4(dev(q), _up(codes), _up(scales), q_pos=_up(qp), m=m)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend_mxfp4(q, codes, scales, q_pos=qp, m=m)
+    assert np.isneginf(rl[:1]).all() and (host_f64(out)[:1] == 0).all()
+    assert np.isneginf(lse[:1].cpu().numpy()).all()
+    _check_attn(out[1:], lse[1:], ro[1:], rl[1:], wl.DT_BF16)
+
+
+def test_attend_mxfp4_decode_workload_sampled():
+    """The 1M-token decode shapes with MXFP4 entries: HCA over 8,192 entries
+    and CSA over 1,024 selected of 262,144 plus 128 window rows, 32 queries x
+    128 heads, checked on sampled queries."""
+    cfg = wl.CONFIGS["layer_1m"]
+    B, H, k, W = cfg.B, cfg.H, cfg.k, cfg.W
+    rng = np.random.default_rng(11)
+    q = _rand(cfg.config_id, 0, 1, (B, H, E), wl.DT_BF16, 1 / 24)
+    c128, s128 = _mx_entries(cfg.config_id, 1, (cfg.N_hca, E))
+    out, lse = _cskv().hca_attend_mxfp4(dev(q), _up(c128), _up(s128))
+    c4, s4 = _mx_entries(cfg.config_id, 2, (cfg.N_csa, E))
+    win = _rand(cfg.config_id, 0, 3, (W, E), wl.DT_BF16)
+    idx = np.stack([np.sort(rng.choice(cfg.N_csa, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    o2, l2 = _cskv().sparse_attend_mxfp4(dev(q), _up(c4), _up(s4), dev(win), _up(idx))
+    torch.cuda.synchronize()
+    rows = np.array([0, 13, B - 1])
+    sel = torch.from_numpy(rows).cuda()
+    ro, rl = oracle.hca_attend_mxfp4(q[rows], c128, s128)
+    _check_attn(out[sel], lse[sel], ro, rl, wl.DT_BF16)
+    ro, rl = oracle.csa_attend_mxfp4(q[rows], c4, s4, win, idx[rows])
+    _check_attn(o2[sel], l2[sel], ro, rl, wl.DT_BF16)
