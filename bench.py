@@ -322,6 +322,7 @@ def bench_mxfp4_attend(args, cskv, inp, cfg, dev, torch, np, part_ms):
     """The decode step's two attentions over MXFP4 entries (306 bytes a row
     instead of 1,152): CSA over 1,024 selected of 262,144 entries plus the
     128 window rows, and HCA over 8,192 entries, 32 queries x 128 heads.
+    Each call includes the decode of the rows it reads to bf16.
     The codes are uniform random bytes and the scales 2^-2..2^0 (the
     kernels' time does not depend on the values); the selection is a random
     sorted one per query."""
@@ -337,7 +338,9 @@ def bench_mxfp4_attend(args, cskv, inp, cfg, dev, torch, np, part_ms):
     q, qh, win = dev(inp["q"]), dev(inp["q_hca"]), dev(inp["window"])
     out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(cskv.attend_workspace_size(B, H, k + W), cskv.hca_workspace_size(B, H, cfg.N_hca)),
+    lib = cskv.binding.library()
+    ws = torch.empty(max(lib.cskv_sparse_attend_mxfp4_workspace_size(B, H, W, k),
+                         lib.cskv_hca_attend_mxfp4_workspace_size(B, H, cfg.N_hca, 0)),
                      dtype=torch.uint8, device="cuda")
     runs = {
         "csa_attend": lambda: cskv.sparse_attend_mxfp4(q, c4, s4, win, idx, out=out, lse=lse,

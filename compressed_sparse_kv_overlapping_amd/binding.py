@@ -53,6 +53,8 @@ _SIGS = {
     "cskv_hca_workspace_size": ([_i64, _i32, _i64], _sz),
     "cskv_hca_attend": ([_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, _vp, ctypes.c_int, _vp,
                          _vp, _vp, _sz, _vp], ctypes.c_int),
+    "cskv_sparse_attend_mxfp4_workspace_size": ([_i64, _i32, _i32, _i32], _sz),
+    "cskv_hca_attend_mxfp4_workspace_size": ([_i64, _i32, _i64, _i32], _sz),
     "cskv_sparse_attend_mxfp4": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i64, _i64,
                                   _i64, _vp, _i64, _f32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "cskv_hca_attend_mxfp4": ([_vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, _vp, _vp, _vp,
@@ -333,7 +335,8 @@ def sparse_attend_mxfp4(q, ent_codes, ent_scales, window, idx, q_pos=None, win_p
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = _workspace(attend_workspace_size(B, H, k + W), q.device)
+        workspace = _workspace(library().cskv_sparse_attend_mxfp4_workspace_size(B, H, W, k),
+                               q.device)
     _call("cskv_sparse_attend_mxfp4", _ptr(q), _ptr(ent_codes), _ptr(ent_scales), _ptr(window),
           _ptr(idx), B, H, N, W, k, N if per_seq else 0, win_rows * E if per_seq else 0, win_rows,
           _ptr(q_pos), int(win_pos0), float(scale), _sink(sink, H), _ptr(out), _ptr(lse),
@@ -354,7 +357,8 @@ def hca_attend_mxfp4(q, ent_codes, ent_scales, scale=1.0, per_seq=False, q_pos=N
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = _workspace(hca_workspace_size(B, H, N), q.device)
+        workspace = _workspace(library().cskv_hca_attend_mxfp4_workspace_size(B, H, N, int(per_seq)),
+                               q.device)
     _call("cskv_hca_attend_mxfp4", _ptr(q), _ptr(ent_codes), _ptr(ent_scales), B, H, N,
           N if per_seq else 0, _ptr(q_pos), int(m) if q_pos is not None else 0, float(scale),
           _sink(sink, H), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),

@@ -185,13 +185,10 @@ int cskv_index_topk_mxfp4(const void* q_codes, const uint8_t* q_scales, const vo
 
 size_t cskv_attend_workspace_size(int64_t B, int32_t H, int64_t rows_per_query) {
   if (B < 1 || H < 1 || rows_per_query < 0) return 0;
-  // the largest of the fp32, bf16 and MXFP4-entry layouts, so one size
-  // serves them all
+  // the larger of the fp32 and bf16 layouts, so one size serves both
   size_t a = cskv::attend_partial_bytes(0, B, H, rows_per_query);
   size_t b = cskv::attend_partial_bytes(1, B, H, rows_per_query);
-  size_t c = cskv::attend_partial_bytes(2, B, H, rows_per_query);
-  a = a > b ? a : b;
-  return a > c ? a : c;
+  return a > b ? a : b;
 }
 
 static int check_attend(const char* fn, const void* q, const void* entries, const void* window,
@@ -296,8 +293,11 @@ int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, in
 }
 
 // MXFP4 entries: the codes and scales of row i of sequence b start at
-// (b * ent_bstride + i) * 288 and * 18 bytes; the kernels take element
-// offsets, 576 per row.
+// (b * ent_bstride + i) * 288 and * 18 bytes.  The rows an attention call
+// reads are first decoded to bf16 rows in the workspace (each row once: the
+// selected rows of every query, or all rows for dense attention), then the
+// bf16 attention kernels run on them.  Workspace: [partials][bf16 rows][row
+// table].
 static int check_mxfp4_entries(const char* fn, const void* codes, const uint8_t* scales,
                                int64_t ent_bstride) {
   if (!codes || !scales) return fail(CSKV_ERR_INVALID_ARG, "%s: null entry pointer", fn);
@@ -305,6 +305,20 @@ static int check_mxfp4_entries(const char* fn, const void* codes, const uint8_t*
     return fail(CSKV_ERR_INVALID_ARG, "%s: ent_bstride=%lld", fn, (long long)ent_bstride);
   if (!aligned16(codes)) return fail(CSKV_ERR_INVALID_ARG, "%s: entry codes must be 16-byte aligned", fn);
   return CSKV_OK;
+}
+
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t cskv_sparse_attend_mxfp4_workspace_size(int64_t B, int32_t H, int32_t W, int32_t k) {
+  if (B < 1 || H < 1 || W < 0 || k < 0) return 0;
+  return round256(cskv::attend_partial_bytes(1, B, H, (int64_t)k + W)) +
+         round256((size_t)B * k * 576 * 2) + round256((size_t)B * k * 4);
+}
+
+size_t cskv_hca_attend_mxfp4_workspace_size(int64_t B, int32_t H, int64_t N, int32_t per_sequence) {
+  if (B < 1 || H < 1 || N < 0) return 0;
+  return round256(cskv::attend_partial_bytes(1, B, H, N)) +
+         round256((size_t)(per_sequence ? B : 1) * N * 576 * 2);
 }
 
 int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
@@ -322,11 +336,17 @@ int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t
   if (k > 0 && !idx) return fail(CSKV_ERR_INVALID_ARG, "%s: null idx", fn);
   if (!q_pos && W > win_rows)
     return fail(CSKV_ERR_INVALID_ARG, "%s: W=%d > window rows %lld", fn, W, (long long)win_rows);
-  const size_t need = cskv::attend_partial_bytes(2, B, H, (int64_t)k + W);
-  if (need && (!workspace || ws_bytes < need || !aligned16(workspace)))
+  const size_t need = cskv_sparse_attend_mxfp4_workspace_size(B, H, W, k);
+  if (!workspace || ws_bytes < need || !aligned16(workspace))
     return fail(CSKV_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
-  cskv::AttendParams p{2, q, ent_codes, window, idx, q_pos, B, N, ent_bstride * 576, win_bstride,
-                       win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0, sink, ent_scales};
+  char* w = (char*)workspace;
+  char* rows = w + round256(cskv::attend_partial_bytes(1, B, H, (int64_t)k + W));
+  int32_t* sel = (int32_t*)(rows + round256((size_t)B * k * 576 * 2));
+  hipError_t e = cskv::launch_mx_rows((const uint8_t*)ent_codes, ent_scales, idx, B * k, k, N,
+                                      ent_bstride, rows, sel, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  cskv::AttendParams p{1, q, rows, window, sel, q_pos, B, k, (int64_t)k * 576, win_bstride,
+                       win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0, sink};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), fn);
 }
 
@@ -341,11 +361,17 @@ int cskv_hca_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* e
                     out, scale);
   if (st) return st;
   if (q_pos && m < 1) return fail(CSKV_ERR_INVALID_ARG, "%s: m=%d with q_pos", fn, m);
-  const size_t need = cskv::attend_partial_bytes(2, B, H, N);
-  if (need && (!workspace || ws_bytes < need || !aligned16(workspace)))
+  const bool per_seq = ent_bstride > 0;
+  const size_t need = cskv_hca_attend_mxfp4_workspace_size(B, H, N, per_seq);
+  if (!workspace || ws_bytes < need || !aligned16(workspace))
     return fail(CSKV_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
-  cskv::AttendParams p{2, q, ent_codes, nullptr, nullptr, q_pos, B, N, ent_bstride * 576, 0, 0, 0,
-                       H, 0, 0, scale, out, lse, 1, q_pos ? m : 0, sink, ent_scales};
+  char* rows = (char*)workspace + round256(cskv::attend_partial_bytes(1, B, H, N));
+  hipError_t e = cskv::launch_mx_rows((const uint8_t*)ent_codes, ent_scales, nullptr,
+                                      (per_seq ? B : 1) * N, 0, N, ent_bstride, rows, nullptr,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  cskv::AttendParams p{1, q, rows, nullptr, nullptr, q_pos, B, N, per_seq ? N * 576 : 0, 0, 0, 0,
+                       H, 0, 0, scale, out, lse, 1, q_pos ? m : 0, sink};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), fn);
 }
 

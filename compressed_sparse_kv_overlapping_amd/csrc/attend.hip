@@ -57,7 +57,6 @@ struct AttnArgs {
   const int64_t* q_pos;      // NULL: decode window
   int64_t ent_bstride, win_bstride, win_pos0, win_rows, N;
   int dense;                 // 1: all N entries, no window (HCA)
-  const uint8_t* ent_scales;  // MXFP4 entries: E8M0 scales, one per 32 elements (else NULL)
   int hm;                    // dense with q_pos: entry i visible iff (i+1)*hm <= q_pos[b]+1
   const float* sink;         // [H] attention-sink logits (nullable), applied where splits end
   int B, H, W, k, nslots, slots_per_split, nsplit;
@@ -183,12 +182,7 @@ __device__ __forceinline__ int srow(int g, int i) { return 16 * (i >> 2) + 4 * g
 
 // HB = head blocks of 16 per wave.  With HB = 2 every K and V^T fragment read
 // from LDS feeds two MFMAs, which halves the LDS traffic per flop.
-//
-// FP4E: the compressed entries are MXFP4 (T = bf16 for the queries, the
-// window rows and the output): an entry row is 288 code bytes plus 18 scale
-// bytes, and each 8-element chunk is decoded to bf16 in registers on its way
-// into LDS, so the products run on the same bf16 tiles.
-template <class T, int HB, bool FP4E = false>
+template <class T, int HB>
 __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a) {
   typedef AttnCfg<T> C;
   constexpr int MN = 16, NW = C::NW, NT = 64 * NW;
@@ -213,15 +207,6 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
   const T* q = reinterpret_cast<const T*>(a.q);
   const T* ent = reinterpret_cast<const T*>(a.entries);
   const T* win = reinterpret_cast<const T*>(a.window);
-  // MXFP4 entries: the 8-element chunk at element offset e (a multiple of 8)
-  auto fp4_chunk = [&](Chunk8<T>& c, int64_t e) {
-    if constexpr (FP4E) {
-      const uint8_t* codes = reinterpret_cast<const uint8_t*>(a.entries);
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + (e >> 1));
-      const u32x4 d = fp4x8_to_bf16(w, __uint_as_float(e8m0_f32_bits(a.ent_scales[e >> 5])));
-      c.v = make_uint4(d[0], d[1], d[2], d[3]);
-    }
-  };
 
   // query fragments of this lane's heads: k-slots (g, t) <-> dim 32*ks + 8g + t
   Frag<T> qf[HB][NKS];
@@ -302,12 +287,8 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
         const int r = 4 * qd + i;
         if (task < kVTasks && row_ok[slot][r]) {
           const int64_t off = row_off[slot][r];
-          if (FP4E && off >= 0) {
-            fp4_chunk(pv[u][i], off + cc * 8);
-          } else {
-            const T* src = off >= 0 ? ent + off : win + (-1 - off);
-            pv[u][i].load(src + cc * 8);
-          }
+          const T* src = off >= 0 ? ent + off : win + (-1 - off);
+          pv[u][i].load(src + cc * 8);
         } else {
           pv[u][i].zero();
         }
@@ -319,12 +300,8 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
       const int r = (task >> 3) & (kTile - 1), cc = kDv / 8 + (task & 7);
       if (task < kRTasks && row_ok[slot][r]) {
         const int64_t off = row_off[slot][r];
-        if (FP4E && off >= 0) {
-          fp4_chunk(pr[u], off + cc * 8);
-        } else {
-          const T* src = off >= 0 ? ent + off : win + (-1 - off);
-          pr[u].load(src + cc * 8);
-        }
+        const T* src = off >= 0 ? ent + off : win + (-1 - off);
+        pr[u].load(src + cc * 8);
       } else {
         pr[u].zero();
       }
@@ -1094,10 +1071,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
 
 // ------------------------------------------------------------------ host
 
-// dt: 0 fp32, 1 bf16, 2 bf16 with MXFP4 entries (the generic kernel, HB = 1)
 int attend_heads_per_block(int dt, int H) {
   (void)H;
-  return dt == 0 ? 16 * AttnCfg<float>::NW : dt == 2 ? 16 * AttnCfg<bf16_t>::NW : kWideHeads;
+  return dt == 0 ? 16 * AttnCfg<float>::NW : kWideHeads;
 }
 
 int attend_splits(int dt, int64_t B, int H, int64_t nslots) {
@@ -1105,7 +1081,7 @@ int attend_splits(int dt, int64_t B, int H, int64_t nslots) {
   const int64_t blocks = B * ((H + hpb - 1) / hpb);
   const int64_t tiles = (nslots + kTile - 1) / kTile;
   if (tiles == 0) return 1;
-  // about one round of resident blocks (the bf16 kernels hold one block per
+  // about one round of resident blocks (the bf16 kernel holds one block per
   // compute unit): more splits than that only add partial outputs
   const int64_t target = dt == 0 ? 512 : 256;
   int64_t s = (target + blocks - 1) / blocks;
@@ -1132,7 +1108,6 @@ static hipError_t launch_attend_t(const AttendParams& p, void* ws, hipStream_t s
   a.q = p.q; a.entries = p.entries; a.window = p.window; a.idx = p.idx; a.q_pos = p.q_pos;
   a.ent_bstride = p.ent_bstride; a.win_bstride = p.win_bstride; a.win_pos0 = p.win_pos0;
   a.win_rows = p.win_rows; a.dense = p.dense; a.hm = p.hm; a.sink = p.sink;
-  a.ent_scales = p.ent_scales;
   a.N = p.N; a.B = (int)p.B; a.H = p.H; a.W = p.dense ? 0 : p.W; a.k = p.dense ? 0 : p.k;
   a.nslots = (int)(p.dense ? p.N : (int64_t)p.k + p.W);
   // scale >= 0 (checked by the caller).  Scale 0 (uniform weights) runs as
@@ -1148,18 +1123,57 @@ static hipError_t launch_attend_t(const AttendParams& p, void* ws, hipStream_t s
   a.lse_part = a.o_part + (size_t)p.B * p.H * S * kDv;
   const int hpb = attend_heads_per_block(p.dt, p.H);
   dim3 grid(S, (p.H + hpb - 1) / hpb, (unsigned)p.B);
-  if constexpr (sizeof(T) == 2) {
-    if (p.dt == 2)
-      hipLaunchKernelGGL((attend_kernel<bf16_t, 1, true>), grid, dim3(64 * C::NW), 0, stream, a);
-    else
-      hipLaunchKernelGGL(attend_wide_kernel, grid, dim3(64 * kWideWaves), 0, stream, a);
-  } else
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL(attend_wide_kernel, grid, dim3(64 * kWideWaves), 0, stream, a);
+  else
     hipLaunchKernelGGL((attend_kernel<T, 1>), grid, dim3(64 * C::NW), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t BH = p.B * p.H;
   hipLaunchKernelGGL(merge_kernel<T>, dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, stream,
                      a.o_part, a.lse_part, BH, S, p.sink, p.H, (T*)p.out, p.lse);
+  return hipGetLastError();
+}
+
+// MXFP4 entry rows -> bf16 rows for the attention kernels, one 8-element
+// chunk (a 32-bit code word and its block's scale) per thread, 72 per row.
+// Dense (idx == NULL): output row r = b * N + i is entry i of sequence b
+// (ent_bstride rows apart; one sequence when it is 0).  Gathered: output row
+// r = b * k + j is entry idx[b][j] of sequence b, and idx_out[r] = j, or -1
+// with a zero row where the selection holds no entry.
+__global__ __launch_bounds__(256) void mx_rows_kernel(const uint8_t* codes, const uint8_t* scales,
+                                                      const int32_t* idx, int64_t rows, int k,
+                                                      int64_t N, int64_t ent_bstride,
+                                                      bf16_t* out, int32_t* idx_out) {
+  constexpr int kChunks = kE / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows * kChunks) return;
+  const int64_t r = t / kChunks;
+  const int c = (int)(t - r * kChunks);
+  int64_t src = -1;
+  if (!idx) {
+    src = (r / N) * ent_bstride + r % N;
+  } else {
+    const int64_t b = r / k;
+    const int e = idx[r];
+    if (e >= 0 && e < N) src = b * ent_bstride + e;
+    if (c == 0) idx_out[r] = src >= 0 ? (int32_t)(r - b * k) : -1;
+  }
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (src >= 0) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + src * (kE / 2) + 4 * c);
+    v = fp4x8_to_bf16(w, __uint_as_float(e8m0_f32_bits(scales[src * (kE / 32) + c / 4])));
+  }
+  *reinterpret_cast<u32x4*>(out + r * kE + 8 * c) = v;
+}
+
+hipError_t launch_mx_rows(const uint8_t* codes, const uint8_t* scales, const int32_t* idx,
+                          int64_t rows, int k, int64_t N, int64_t ent_bstride, void* out,
+                          int32_t* idx_out, hipStream_t stream) {
+  const int64_t threads = rows * (kE / 8);
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(mx_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     codes, scales, idx, rows, k, N, ent_bstride, (bf16_t*)out, idx_out);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ hipError_t launch_compress_fused(int dt, const void* x, const void* z, int64_t T
 size_t compress_fused_workspace_bytes(int64_t T_tokens, int ml);
 
 struct AttendParams {
-  int dt;                    // 0 fp32, 1 bf16, 2 bf16 with MXFP4 entries
+  int dt;                    // 0 fp32, 1 bf16
   const void* q;             // [B][H][576]
   const void* entries;       // [N][576] (+ b * ent_bstride)
   const void* window;        // rows of 576 (+ b * win_bstride)
@@ -31,12 +31,17 @@ struct AttendParams {
   int dense;                 // 1: rows = all N entries, no window
   int hm;                    // dense with q_pos: entry i visible iff (i+1)*hm <= q_pos[b]+1
   const float* sink;         // [H] attention-sink logits, or NULL
-  const uint8_t* ent_scales = nullptr;   // dt 2: MXFP4 entries, E8M0 scales [N][18]
 };
 
 int attend_splits(int dt, int64_t B, int H, int64_t nslots);
 size_t attend_partial_bytes(int dt, int64_t B, int H, int64_t nslots);
 hipError_t launch_attend(const AttendParams& p, void* ws, hipStream_t stream);
+// MXFP4 entry rows (codes [.][288], E8M0 scales [.][18]) decoded to bf16
+// rows of 576: dense (idx NULL) rows b * N + i, or gathered rows b * k + j
+// with idx_out[b][j] = j or -1.
+hipError_t launch_mx_rows(const uint8_t* codes, const uint8_t* scales, const int32_t* idx,
+                          int64_t rows, int k, int64_t N, int64_t ent_bstride, void* out,
+                          int32_t* idx_out, hipStream_t stream);
 hipError_t launch_merge(int dt, const float* o_part, const float* lse_part, int64_t BH, int S,
                         const float* sink, int H, void* out, float* lse, hipStream_t stream);
 

@@ -242,12 +242,17 @@ int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, in
  *     j, element 2j+1 in the high nibble.  16-byte aligned.
  *   ent_scales [N][18] bytes: the scale of elements 32b .. 32b+31.
  *   ent_bstride: rows (not elements) between the entry sets of consecutive
- *     queries, 0 for one shared context.  Other arguments, the workspace
- *     (cskv_attend_workspace_size / cskv_hca_workspace_size) and the errors
+ *     queries, 0 for one shared context.  Other arguments and the errors
  *     are those of cskv_sparse_attend / cskv_hca_attend.
+ *   workspace: at least cskv_sparse_attend_mxfp4_workspace_size(B, H, W, k)
+ *     or cskv_hca_attend_mxfp4_workspace_size(B, H, N, ent_bstride > 0)
+ *     bytes.  The rows a call reads (each query's selected entries, or all
+ *     N entries of each context) are decoded into it as bf16 first.
  * The entries decode to bf16 exactly while every decoded value lies in
  * bf16's normal range (scale bytes 2..252 with any code, at least).
  */
+size_t cskv_sparse_attend_mxfp4_workspace_size(int64_t B, int32_t H, int32_t W, int32_t k);
+size_t cskv_hca_attend_mxfp4_workspace_size(int64_t B, int32_t H, int64_t N, int32_t per_sequence);
 int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
                              const void* window, const int32_t* idx, int64_t B, int32_t H,
                              int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
