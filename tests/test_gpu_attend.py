@@ -475,3 +475,26 @@ def test_attend_mxfp4_decode_workload_sampled():
     _check_attn(out[sel], lse[sel], ro, rl, wl.DT_BF16)
     ro, rl = oracle.csa_attend_mxfp4(q[rows], c4, s4, win, idx[rows])
     _check_attn(o2[sel], l2[sel], ro, rl, wl.DT_BF16)
+
+
+def test_attend_mxfp4_per_sequence_hca_and_window_only():
+    """HCA over per-sequence MXFP4 entries with sinks, and CSA with an empty
+    selection (the window rows alone)."""
+    rng = np.random.default_rng(21)
+    B, H, N, W = 3, 128, 500, 128
+    q = _rand(101, 0, 1, (B, H, E), wl.DT_BF16, 1 / 24)
+    codes, scales = _mx_entries(101, 0, (B, N, E))
+    sink = rng.standard_normal(H)
+    out, lse = _cskv().hca_attend_mxfp4(dev(q), _up(codes), _up(scales), per_seq=True,
+                                        sink=torch.from_numpy(sink).float().cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend_mxfp4(q, codes, scales, per_seq=True,
+                                     sink=sink.astype(np.float32).astype(np.float64))
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+    win = _rand(101, 0, 3, (W, E), wl.DT_BF16)
+    idx = np.zeros((B, 0), np.int32)
+    out, lse = _cskv().sparse_attend_mxfp4(dev(q), _up(codes[0]), _up(scales[0]), dev(win), _up(idx))
+    torch.cuda.synchronize()
+    # the oracle takes k >= 1: one empty slot (-1) is the same window-only attention
+    ro, rl = oracle.csa_attend_mxfp4(q, codes[0], scales[0], win, np.full((B, 1), -1, np.int32))
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
