@@ -34,7 +34,7 @@ D, R, E, I = 512, 64, 576, 64
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
@@ -132,6 +132,13 @@ def main():
     ms_step = start.elapsed_time(stop) / args.steps
     part_ms = {p: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
                for j, p in enumerate(parts)}
+    # per-step latency: first launch to last completion of each step
+    lat = np.array([e[0].elapsed_time(e[-1]) for e in evs])
+    latency = {"p50": round(float(np.percentile(lat, 50)), 4),
+               "p95": round(float(np.percentile(lat, 95)), 4),
+               "p99": round(float(np.percentile(lat, 99)), 4), "samples": int(len(lat)),
+               "parts_p50": {p: round(float(np.percentile([e[j].elapsed_time(e[j + 1]) for e in evs], 50)), 4)
+                             for j, p in enumerate(parts)}}
 
     pairs = B * k + B * N128
     value = pairs / (ms_step * 1e-3)
@@ -176,6 +183,10 @@ def main():
                    "queries": B, "heads": H, "top_k": k, "window": W,
                    "pairs_per_step": pairs, "kv": "shared context"},
         "roofline": roofline,
+        "latency_ms": latency,
+        "cache_bytes": cache_accounting(T, W, k),
+        "run": {"device": torch.cuda.get_device_name(0), "hip": torch.version.hip, "streams": 1,
+                "queries": B, "context_tokens": T},
         "compressor_GBps": round(comp_bytes / (comp_ms * 1e-3) / 1e9, 1),
         "attention_GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
         "decode_only_entries_per_s": round(pairs / (attn_ms * 1e-3), 1),
@@ -195,6 +206,24 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, inp, cfg, ms_step, np)
     print(json.dumps(result), flush=True)
+
+
+def cache_accounting(T, W, k):
+    """Cache bytes of one layer by kind at T raw tokens, and their slope in
+    bytes per raw token: the raw window is a constant, the compressed
+    entries and indexer keys grow with T (bf16 storage, and MXFP4 with its
+    scale bytes counted apart)."""
+    n4, n128 = T // 4, T // 128
+    bf16 = {"raw_window": W * E * 2, "csa_entries": n4 * E * 2, "hca_entries": n128 * E * 2,
+            "indexer_keys": n4 * I * 2}
+    mx = {"raw_window": W * E * 2, "csa_entries": n4 * E // 2, "hca_entries": n128 * E // 2,
+          "indexer_keys": n4 * I // 2,
+          "scales": n4 * E // 32 + n128 * E // 32 + n4 * I // 32}
+    slope = lambda d: {kk: round((v - (W * E * 2 if kk == "raw_window" else 0)) / T, 4)
+                       for kk, v in d.items()}
+    return {"tokens": T, "selected_per_query": k,
+            "bf16": {"bytes": bf16, "total": sum(bf16.values()), "per_token": slope(bf16)},
+            "mxfp4": {"bytes": mx, "total": sum(mx.values()), "per_token": slope(mx)}}
 
 
 def bench_prefill(args, cskv, wl, dev, torch, np):
