@@ -8,7 +8,8 @@
  *   "MLA compresses what generation must remember": 512-dim shared latent plus
  *   a decoupled 64-dim RoPE key),
  *   "Compressed attention - CSA / HCA" (sections 1-4: token-axis compression,
- *   recent window plus compressed history, cache budgeting).
+ *   recent window plus compressed history, cache budgeting, the FP4 KV cache
+ *   with block scales).
  *
  * Data layout (row-major, element counts; D = 512, R = 64, E = D + R = 576):
  *   raw_kv, score_logits [T][512]   raw shared-KV rows and compressor logits
@@ -21,6 +22,10 @@
  *   out                  [B][H][512] attention output;  lse [B][H] fp32
  *   idx_out              [B][k]     int32 selected entries: valid indices in
  *                                    ascending order, then -1 padding
+ * MXFP4 storage (the *_mxfp4 calls; OCP Microscaling v1.0, 32 FP4 E2M1
+ * elements per E8M0 scale): a row of C elements is C/2 code bytes (element
+ * 2j in the low nibble of byte j) plus C/32 scale bytes in a separate array;
+ *   entry codes / scales [N][288] / [N][18];  key codes / scales [N][32] / [N][2].
  * Per-query caches: *_bstride gives the element offset between the caches of
  * consecutive queries (0 = one cache shared by all queries).
  *
@@ -37,7 +42,8 @@
  *    CSKV_ERR_UNSUPPORTED; there is no fallback path.
  *  - Results are deterministic for fixed shapes (fixed split counts and merge
  *    order; the selected set is fully ordered by score then index).
- *  - Tensors must be 16-byte aligned.
+ *  - Tensors must be 16-byte aligned (MXFP4 scale arrays: 1-byte entry
+ *    scales, 2-byte aligned key scales).
  */
 #ifndef CSKV_H
 #define CSKV_H
