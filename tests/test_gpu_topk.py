@@ -254,3 +254,17 @@ def test_topk_mxfp4_decode_workload():
     kc, ks = wl.mxfp4_encode(wl.normal(cfg.config_id, 0, 9, (cfg.N_csa, 64)))
     idx, s, v = _run_mx(qc, qs, kc, ks, cfg.k)
     _exact(idx, s, v, cfg.k)
+
+
+def test_topk_maximum_sizes():
+    """The largest selection the kernels take: k = 4096 over 1,048,576
+    entries (16,384 groups of 64), bf16 and MXFP4 keys."""
+    B, N, k = 2, 1 << 20, 4096
+    q = wl.normal(102, 0, 1, (B, 64))
+    kk = wl.normal(102, 0, 2, (N, 64))
+    idx, s, v = _run(wl.bf16_bits(q), wl.bf16_bits(kk), wl.DT_BF16, k)
+    check_selection(idx, s, v, k)
+    qc, qs = wl.mxfp4_encode(q)
+    kc, ks = wl.mxfp4_encode(kk)
+    idx, s, v = _run_mx(qc, qs, kc, ks, k)
+    _exact(idx, s, v, k)
