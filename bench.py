@@ -203,9 +203,66 @@ def main():
                                                 part_ms["csa_topk"])
         result["mxfp4_attend"] = bench_mxfp4_attend(args, cskv, inp, cfg, dev, torch, np,
                                                     part_ms)
+        torch.cuda.empty_cache()
+        result["per_sequence"] = bench_per_sequence(args, cskv, inp, cfg, dev, torch)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, inp, cfg, ms_step, np)
     print(json.dumps(result), flush=True)
+
+
+def bench_per_sequence(args, cskv, inp, cfg, dev, torch):
+    """The decode attention in per-sequence mode: each of the 32 queries has
+    its own 1M-token caches (262,144 CSA entries and indexer keys, 8,192 HCA
+    entries, its own window), the serving reading of a decode batch.  The
+    caches are random bf16 drawn on the device (9.7 GB of CSA entries; the
+    kernels' time does not depend on the values).  Each query scans its own
+    keys and reads its own HCA entries, so this regime is HBM-bound."""
+    B, H, k, W, N4, N128 = cfg.B, cfg.H, cfg.k, cfg.W, cfg.N_csa, cfg.N_hca
+    g = torch.Generator(device="cuda").manual_seed(args.seed + 7)
+
+    def rnd(*shape):
+        t = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        for i in range(shape[0]):
+            t[i] = torch.randn(shape[1:], generator=g, device="cuda").to(torch.bfloat16)
+        return t
+    ent4, keys, ent128, win = rnd(B, N4, E), rnd(B, N4, I), rnd(B, N128, E), rnd(B, W, E)
+    qI, q, qh = dev(inp["qI"]), dev(inp["q"]), dev(inp["q_hca"])
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws_t = torch.empty(cskv.index_topk_workspace_size(B, N4, k), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(max(cskv.attend_workspace_size(B, H, k + W), cskv.hca_workspace_size(B, H, N128)),
+                       dtype=torch.uint8, device="cuda")
+    runs = {
+        "csa_topk": lambda: cskv.index_topk(qI, keys, k, per_seq=True, idx_out=idx, workspace=ws_t),
+        "csa_attend": lambda: cskv.sparse_attend(q, ent4, win, idx, per_seq=True, out=out, lse=lse,
+                                                 workspace=ws_a),
+        "hca_attend": lambda: cskv.hca_attend(qh, ent128, per_seq=True, out=out, lse=lse,
+                                              workspace=ws_a),
+    }
+    alg = {"csa_topk": B * N4 * I * 2 + B * I * 2 + B * k * 4,
+           "csa_attend": B * (k + W) * E * 2 + B * H * E * 2 + B * H * D * 2,
+           "hca_attend": B * N128 * E * 2 + B * H * E * 2 + B * H * D * 2}
+    res = {"workload": "layer_1m decode, per-sequence caches", "queries": B}
+    for name, run in runs.items():
+        for _ in range(3):
+            run()
+        steps = max(20, args.steps // 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / steps
+        gbs = alg[name] / (t * 1e-3) / 1e9
+        res[name] = {"ms": round(t, 4), "alg_bytes": alg[name],
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    del ent4, keys, ent128, win
+    return res
 
 
 def cache_accounting(T, W, k):
