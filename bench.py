@@ -231,7 +231,8 @@ def bench_per_sequence(args, cskv, inp, cfg, dev, torch):
     idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
     out = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    ws_t = torch.empty(cskv.index_topk_workspace_size(B, N4, k), dtype=torch.uint8, device="cuda")
+    ws_t = torch.empty(cskv.index_topk_workspace_size(B, N4, k, per_seq=True), dtype=torch.uint8,
+                       device="cuda")
     ws_a = torch.empty(max(cskv.attend_workspace_size(B, H, k + W), cskv.hca_workspace_size(B, H, N128)),
                        dtype=torch.uint8, device="cuda")
     runs = {

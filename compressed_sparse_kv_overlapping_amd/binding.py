@@ -42,6 +42,7 @@ _SIGS = {
                          _vp, _sz, _vp], ctypes.c_int),
     "cskv_index_topk_mxfp4": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _vp, _i32, _f32, _vp,
                                _vp, _sz, _vp], ctypes.c_int),
+    "cskv_index_topk_per_seq_workspace_size": ([_i64, _i64, _i32], _sz),
     "cskv_attend_workspace_size": ([_i64, _i32, _i64], _sz),
     "cskv_sparse_attend": ([_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i64, _i64, _i64,
                             _vp, _i64, _f32, _vp, ctypes.c_int, _vp, _vp, _vp, _sz, _vp],
@@ -178,7 +179,11 @@ def compress2(x, z, bias_small, m_small, bias_large, m_large, out_small=None, ou
 
 # -------------------------------------------------------------- indexer/top-k
 
-def index_topk_workspace_size(B, N, k):
+def index_topk_workspace_size(B, N, k, per_seq=False):
+    """Workspace bytes of index_topk; with per_seq, the size with which
+    per-query keys are read once."""
+    if per_seq:
+        return library().cskv_index_topk_per_seq_workspace_size(B, N, k)
     return library().cskv_index_topk_workspace_size(B, N, k)
 
 
@@ -190,7 +195,7 @@ def index_topk(q_idx, idx_keys, k, q_pos=None, m=4, idx_scale=1.0, per_seq=False
     B, N = q_idx.shape[0], idx_keys.shape[-2]
     if idx_out is None:
         idx_out = torch.empty((B, k), dtype=torch.int32, device=q_idx.device)
-    ws = index_topk_workspace_size(B, N, k)
+    ws = index_topk_workspace_size(B, N, k, per_seq)
     if workspace is None:
         workspace = _workspace(ws, q_idx.device)
     _call("cskv_index_topk", _ptr(q_idx), _ptr(idx_keys), B, N, k, N * I if per_seq else 0,
@@ -211,7 +216,7 @@ def index_topk_mxfp4(q_codes, q_scales, key_codes, key_scales, k, q_pos=None, m=
     B, N = q_codes.shape[0], key_codes.shape[-2]
     if idx_out is None:
         idx_out = torch.empty((B, k), dtype=torch.int32, device=q_codes.device)
-    ws = index_topk_workspace_size(B, N, k)
+    ws = index_topk_workspace_size(B, N, k, per_seq)
     if workspace is None:
         workspace = _workspace(ws, q_codes.device)
     _call("cskv_index_topk_mxfp4", _ptr(q_codes), _ptr(q_scales), _ptr(key_codes), _ptr(key_scales),

@@ -124,6 +124,11 @@ size_t cskv_index_topk_workspace_size(int64_t B, int64_t N, int32_t k) {
   return cskv::topk_workspace_bytes(B, N, k);
 }
 
+size_t cskv_index_topk_per_seq_workspace_size(int64_t B, int64_t N, int32_t k) {
+  if (B < 1 || N < 1 || k < 1) return 0;
+  return cskv::topk_workspace_bytes(B, N, k) + cskv::topk_stored_score_bytes(B, N);
+}
+
 static int check_topk(const char* fn, const void* q_idx, const void* idx_keys, int64_t B, int64_t N,
                       int32_t k, int64_t key_bstride, const int64_t* q_pos, int32_t m,
                       float idx_scale, cskv_dtype idx_dt, const int32_t* idx_out) {
@@ -158,6 +163,7 @@ int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t 
   if (!workspace || ws_bytes < need || !aligned16(workspace))
     return fail(CSKV_ERR_WORKSPACE, "cskv_index_topk: workspace %zu bytes, need %zu", ws_bytes, need);
   cskv::TopkParams p{(int)idx_dt, q_idx, idx_keys, q_pos, key_bstride, B, N, k, m, idx_scale, idx_out};
+  p.ws_bytes = ws_bytes;
   return hip_status(cskv::launch_topk(p, workspace, (hipStream_t)stream), "cskv_index_topk");
 }
 
@@ -180,6 +186,7 @@ int cskv_index_topk_mxfp4(const void* q_codes, const uint8_t* q_scales, const vo
     return fail(CSKV_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   cskv::TopkParams p{3, q_codes, key_codes, q_pos, key_bstride * 64, B, N, k, m, idx_scale, idx_out,
                      q_scales, key_scales};
+  p.ws_bytes = ws_bytes;
   return hip_status(cskv::launch_topk(p, workspace, (hipStream_t)stream), fn);
 }
 

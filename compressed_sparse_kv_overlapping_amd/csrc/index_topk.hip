@@ -49,6 +49,8 @@ struct IdxArgs {
   uint64_t* cand;             // [B][chunks][region] candidate regions
   int32_t* out;               // [B][k]
   int chunks, region;         // score-pass chunks; slots per (query, chunk)
+  float* sraw;                // per-sequence keys: raw scores [B][Np] kept between the passes, or NULL
+  int64_t np;                 // row pitch of sraw (N rounded up to 16)
 };
 
 __device__ __forceinline__ int n_visible(const IdxArgs& a, int b) {
@@ -301,6 +303,8 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
       mma16(S[j], kd[1], qf[j][1]);
     }
     // S[j][i]: query qb[j], entry et + 4g + i
+    if (MODE == 0 && NQB == 1 && a.sraw && qb[0] >= 0)         // one query per block
+      *reinterpret_cast<f32x4*>(a.sraw + (int64_t)qb[0] * a.np + et + 4 * g) = S[0];
     if (et + 16 <= min_vis) {
       if (MODE == 0) {
 #pragma unroll
@@ -478,6 +482,33 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
       if ((WQ == 4 || c < a.qpb) && q < a.B) a.cnt[(int64_t)q * a.chunks + blockIdx.x] = lcnt[c];
     }
   }
+}
+
+// Collect pass from kept scores (per-sequence keys): the same candidates as
+// the MODE 1 score pass, read from the raw scores the group-maximum pass
+// stored instead of recomputed from the keys, so every key is read once.
+// Block (chunk c, query b) covers the entries the score pass gave chunk c.
+__global__ __launch_bounds__(256) void idx_collect_kept_kernel(IdxArgs a) {
+  __shared__ uint32_t lcnt;
+  const int b = blockIdx.y, c = blockIdx.x;
+  if (threadIdx.x == 0) lcnt = 0;
+  __syncthreads();
+  const int e0 = c * a.tiles_per_wave * 16 * 4;
+  const int e1 = min(e0 + a.tiles_per_wave * 16 * 4, n_visible(a, b));
+  const float tscore = a.thr[b] != 0u ? key_score(a.thr[b]) : -INFINITY;
+  const float traw = raw_threshold(tscore, a.scale);
+  const float* sr = a.sraw + (int64_t)b * a.np;
+  for (int e = e0 + threadIdx.x; e < e1; e += 256) {
+    const float v = sr[e];
+    if (v >= traw) {
+      const uint32_t slot = atomicAdd(&lcnt, 1u);
+      if (slot < (uint32_t)a.region)
+        a.cand[((int64_t)b * a.chunks + c) * a.region + slot] =
+            ((uint64_t)score_key(v * a.scale) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.cnt[(int64_t)b * a.chunks + c] = lcnt;
 }
 
 // ------------------------------------------------- block-wide radix helpers
@@ -997,6 +1028,10 @@ size_t topk_workspace_bytes(int64_t B, int64_t N, int k) {
   return bytes + 256;
 }
 
+size_t topk_stored_score_bytes(int64_t B, int64_t N) {
+  return (size_t)B * ((N + 15) / 16 * 16) * 4 + 256;
+}
+
 // below this many queries the per-query kernels take 1024 threads a block
 constexpr int64_t kWideBelow = 256;
 
@@ -1020,6 +1055,12 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
   a.gmax = (uint32_t*)w;            w += (size_t)p.B * a.G * 4;
   a.thr = (uint32_t*)w;             w += (size_t)p.B * 4;
   a.cnt = (uint32_t*)w;
+  // per-sequence keys with room in the workspace: keep the raw scores
+  const size_t base = topk_workspace_bytes(p.B, p.N, p.k);
+  a.sraw = nullptr;
+  a.np = (p.N + 15) / 16 * 16;
+  if (per_seq && p.ws_bytes >= base + topk_stored_score_bytes(p.B, p.N))
+    a.sraw = (float*)((char*)ws + (base + 255) / 256 * 256);
   const int nqb = g.nqb, qblocks = g.qblocks, chunks = g.chunks;
   dim3 grid(chunks, qblocks);
 #define CSKV_SCORE(NQB, MODE, WQ) \
@@ -1037,7 +1078,10 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
   CSKV_SCORE_PASS(0);
   if (wide) hipLaunchKernelGGL(idx_threshold_kernel<1024>, dim3((unsigned)p.B), dim3(1024), 0, stream, a);
   else hipLaunchKernelGGL(idx_threshold_kernel<256>, dim3((unsigned)p.B), dim3(256), 0, stream, a);
-  CSKV_SCORE_PASS(1);
+  if (a.sraw)
+    hipLaunchKernelGGL(idx_collect_kept_kernel, grid, dim3(256), 0, stream, a);
+  else
+    CSKV_SCORE_PASS(1);
 #undef CSKV_SCORE_PASS
 #undef CSKV_SCORE
   if (wide) hipLaunchKernelGGL((idx_final_kernel<T, 1024>), dim3((unsigned)p.B), dim3(1024), 0, stream, a);

@@ -56,11 +56,14 @@ struct TopkParams {
   int32_t* out;              // [B][k]
   const uint8_t* qsc = nullptr;   // MXFP4: E8M0 scales of the queries [B][2]
   const uint8_t* ksc = nullptr;   // MXFP4: E8M0 scales of the keys [N][2]
+  size_t ws_bytes = 0;            // workspace size (per-sequence keys: room to keep the scores)
 };
 
 int topk_max_k();
 int64_t topk_max_entries();
 size_t topk_workspace_bytes(int64_t B, int64_t N, int k);
+// extra workspace with which per-sequence selections read every key once
+size_t topk_stored_score_bytes(int64_t B, int64_t N);
 hipError_t launch_topk(const TopkParams& p, void* ws, hipStream_t stream);
 
 }  // namespace cskv

@@ -136,11 +136,16 @@ int cskv_compress2(const void* raw_kv, const void* score_logits, int64_t T,
  * followed by -1 padding.
  *   q_idx [B][64], idx_keys [N][64] (per query if key_bstride > 0), both in
  *   idx_dt (F32, BF16 or FP8_E4M3; for FP8 pass idx_scale = scale_q*scale_k).
- *   workspace: at least cskv_index_topk_workspace_size(B, N, k) bytes.
+ *   workspace: at least cskv_index_topk_workspace_size(B, N, k) bytes.  With
+ *     per-query keys (key_bstride > 0), a workspace of at least
+ *     cskv_index_topk_per_seq_workspace_size(B, N, k) bytes also keeps the
+ *     raw scores between the selection's two passes, so that every key is
+ *     read from memory once instead of twice (same result).
  * Errors: INVALID_ARG (null pointers, B < 1, N < 1, k < 1, m < 1 with q_pos);
  * UNSUPPORTED (k > 4096); WORKSPACE.
  */
 size_t cskv_index_topk_workspace_size(int64_t B, int64_t N, int32_t k);
+size_t cskv_index_topk_per_seq_workspace_size(int64_t B, int64_t N, int32_t k);
 int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t N, int32_t k,
                     int64_t key_bstride, const int64_t* q_pos, int32_t m, float idx_scale,
                     cskv_dtype idx_dt, int32_t* idx_out, void* workspace, size_t ws_bytes,
@@ -164,7 +169,8 @@ int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t 
  *   accumulated in fp32; it is exact while every product and partial sum is
  *   an fp32 normal number (as for fp32 inputs).  Scale bytes 0 and 255 decode
  *   to 2^-127 and NaN; rows with NaN scores have no defined rank.
- *   workspace: at least cskv_index_topk_workspace_size(B, N, k) bytes.
+ *   workspace: as cskv_index_topk (per-query keys read once with
+ *   cskv_index_topk_per_seq_workspace_size(B, N, k) bytes).
  * Errors: as cskv_index_topk, and INVALID_ARG for null or odd scale pointers.
  */
 int cskv_index_topk_mxfp4(const void* q_codes, const uint8_t* q_scales, const void* key_codes,

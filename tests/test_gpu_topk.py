@@ -268,3 +268,26 @@ def test_topk_maximum_sizes():
     kc, ks = wl.mxfp4_encode(kk)
     idx, s, v = _run_mx(qc, qs, kc, ks, k)
     _exact(idx, s, v, k)
+
+
+def test_topk_per_sequence_keys_read_once_or_twice():
+    """Per-query keys with and without room to keep the scores between the
+    passes (each key read once, or twice): the same selection, the
+    oracle's, including causal queries that see part of their keys."""
+    cskv = _cskv()
+    B, N, k, m = 5, 20000, 300, 4
+    q = wl.normal(103, 0, 1, (B, 64))
+    kk = wl.normal(103, 0, 2, (B, N, 64))
+    qI, kI = dev(wl.bf16_bits(q)), dev(wl.bf16_bits(kk))
+    pos = np.array([0, 1500, 40000, 79999, 123456], np.int64)
+    qp = torch.from_numpy(pos).cuda()
+    small = torch.empty(cskv.index_topk_workspace_size(B, N, k), dtype=torch.uint8, device="cuda")
+    big = torch.empty(cskv.index_topk_workspace_size(B, N, k, per_seq=True), dtype=torch.uint8,
+                      device="cuda")
+    assert big.numel() > small.numel()
+    a = cskv.index_topk(qI, kI, k, q_pos=qp, m=m, per_seq=True, workspace=small).cpu().numpy()
+    b = cskv.index_topk(qI, kI, k, q_pos=qp, m=m, per_seq=True, workspace=big).cpu().numpy()
+    np.testing.assert_array_equal(a, b)
+    s, v = oracle.index_scores(wl.bf16_bits(q), wl.bf16_bits(kk), wl.DT_BF16, q_pos=pos, m=m,
+                               per_seq=True)
+    check_selection(b, s, v, k)
