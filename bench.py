@@ -508,10 +508,13 @@ def cpu_baseline(args, inp, cfg, gpu_ms, np):
 
     est, _ = run(1.0 / 64)
     frac = min(1.0, args.cpu_seconds / max(sum(est), 1e-9))
-    # the whole step when it fits, repeated while the budget allows (at most 3 times)
-    reps = max(1, min(3, int(args.cpu_seconds / max(sum(est), 1e-9)))) if frac >= 1.0 else 1
+    # the whole step when it fits, repeated while the budget allows (at most 3 runs)
     t0 = time.perf_counter()
-    runs = [run(frac) for _ in range(reps)]
+    runs = [run(frac)]
+    while (frac >= 1.0 and len(runs) < 3 and
+           (time.perf_counter() - t0) * (len(runs) + 1) / len(runs) <= args.cpu_seconds):
+        runs.append(run(frac))
+    reps = len(runs)
     sample_s = time.perf_counter() - t0
     (n4, n128, nq, nh) = runs[0][1]
     parts = tuple(float(np.mean([r[0][i] for r in runs])) for i in range(5))
