@@ -36,7 +36,12 @@
  *    entry i for a query at position pos: (i+1)m <= pos+1;
  *  - top-k order: score descending, then index ascending; -1 padding;
  *  - CSA attention: one joint softmax over selected entries and window rows;
- *    logits use all 576 dims, values are dims 0..511.
+ *    logits use all 576 dims, values are dims 0..511;
+ *  - attention-sink logits: one more softmax term per head with a zero value;
+ *  - MXFP4 (named by [P1] for the indexer's QK path and, as FP4 with block
+ *    scales, by "Compressed attention - CSA / HCA" section 3 for the V4.1 KV
+ *    cache): the OCP Microscaling v1.0 format, element 2j in the low nibble
+ *    of byte j, one E8M0 scale per 32 elements in a separate array.
  *
  * All functions return 0 on success and a negative value on bad arguments.
  */
