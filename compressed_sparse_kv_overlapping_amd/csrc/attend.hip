@@ -1089,6 +1089,21 @@ int attend_splits(int dt, int64_t B, int H, int64_t nslots) {
   if (s > cap) s = cap;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
+  // bf16 with a full round of blocks: fewer splits can be cheaper.  Each
+  // split adds a partial output (written, then read by the merge) that costs
+  // about 1.1 tiles of the wide kernel, so take the split count in
+  // [s/2, s] with the least tiles-per-split + 1.1 * splits (measured: 36
+  // tiles over 32 queries run in 45.5 us as 6 splits of 6 tiles against
+  // 48.5 us as 8 splits of up to 5; 256 tiles keep 8 splits).
+  if (dt == 1 && blocks * s >= 256 && s > 1) {
+    int64_t best = s, best_cost = -1;
+    for (int64_t c = (s + 1) / 2; c <= s; ++c) {
+      const int64_t per_c = (tiles + c - 1) / c;
+      const int64_t cost = 10 * per_c + 11 * c;
+      if (best_cost < 0 || cost < best_cost) { best = c; best_cost = cost; }
+    }
+    s = best;
+  }
   // equal whole tiles per split; drop splits that would be empty
   const int64_t per = (tiles + s - 1) / s;
   return (int)((tiles + per - 1) / per);
