@@ -3,12 +3,12 @@
 Two passes of the same program, one counter each (the counters do not fit
 one pass):
 
-    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/traffic_fetch -o p -- \\
+    rocprofv3 --pmc FETCH_SIZE -f csv -d <fetch_dir> -o p -- \\
         python -m compressed_sparse_kv_overlapping_amd.profiling run
-    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/traffic_write -o p -- \\
+    rocprofv3 --pmc WRITE_SIZE -f csv -d <write_dir> -o p -- \\
         python -m compressed_sparse_kv_overlapping_amd.profiling run
     python -m compressed_sparse_kv_overlapping_amd.profiling summarize \\
-        gpurun_out/traffic_fetch gpurun_out/traffic_write
+        <fetch_dir> <write_dir>
 
 ``run`` launches a plain device copy of a known size (the runtime's
 copy-buffer kernel, through torch's copy_)
@@ -123,12 +123,12 @@ def summarize(fetch_dir, write_dir, digest=None):
         json.dump(out, fh, indent=1)
     print("# HBM traffic of the two-scale compressor, 1M tokens x 512 dims bf16, m=4 and m'=128")
     print("# commands:")
-    print("#   rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/traffic_fetch -o p -- "
+    fd, wd = os.path.normpath(fetch_dir), os.path.normpath(write_dir)
+    print(f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d {fd} -o p -- "
           "python -m compressed_sparse_kv_overlapping_amd.profiling run")
-    print("#   rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/traffic_write -o p -- "
+    print(f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d {wd} -o p -- "
           "python -m compressed_sparse_kv_overlapping_amd.profiling run")
-    print("#   python -m compressed_sparse_kv_overlapping_amd.profiling summarize "
-          "gpurun_out/traffic_fetch gpurun_out/traffic_write")
+    print(f"#   python -m compressed_sparse_kv_overlapping_amd.profiling summarize {fd} {wd}")
     print(f"# calibration: a {COPY_BYTES >> 20} MiB device copy reads FETCH_SIZE {copy_f:.0f} KiB "
           f"and WRITE_SIZE {copy_w:.0f} KiB per dispatch -> scale {f_scale:.4f} (fetch), "
           f"{w_scale:.4f} (write)")
