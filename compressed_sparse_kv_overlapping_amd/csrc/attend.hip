@@ -757,9 +757,18 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     }
     wide_s_done(S);
   };
-  // O^T += V^T P^T for one tile
+  // O^T += V^T P^T for one tile.  The lane's V^T read offsets within a tile
+  // are the same for every tile: computed once, pinned so that they are not
+  // recomputed in the loop (33 fewer VALU instructions per tile).
+  ValOffs L0 = val_offs();
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) asm volatile("" : "+v"(L0.v[u][w][q]));
   auto pv = [&](const char* vb, const Frag<bf16_t>* P, auto&& piece) {
-    const ValOffs L = val_offs();
+    const ValOffs& L = L0;
     unsigned vp[2][2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
