@@ -731,10 +731,14 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   };
 
   // logits S^T of one tile; piece(s) is issued after the MFMA of k-step s
+  // the lane's K read offsets within a tile, computed once per split
+  KeyOffs LK = key_offs();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(LK.k[i]));
   auto qk = [&](const char* kb, f32x16& S, auto&& piece) {
     // per-lane read addresses of this buffer, pinned so that every read is
     // one of them plus an immediate offset
-    const KeyOffs L = key_offs();
+    const KeyOffs& L = LK;
     unsigned kp[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
