@@ -71,7 +71,7 @@ def main():
 
     import compressed_sparse_kv_overlapping_amd as cskv
     import workloads as wl
-    from tests.helpers import dev
+    from workloads.device import dev
 
     torch.cuda.set_device(0)
     cfg = wl.CONFIGS["layer_1m"]

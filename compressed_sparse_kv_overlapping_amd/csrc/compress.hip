@@ -738,20 +738,18 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
   const T* zp = (const T*)z;
   int epw = 2;
   int64_t groups = 0;
-  auto pick = [&](const void* kern, int msel) {
+  auto pick = [&](const void* kern) {
     // Large entries per wave: the grid runs in rounds of the blocks that fit
     // on the chip at once; take the epw (at least 2) that fills its last
     // round best, the largest of equals (fewest block boundaries to join).
-    static int slots_by_ms[5] = {0, 0, 0, 0, 0};
-    int& slots = slots_by_ms[msel];
-    if (slots == 0) {
-      int nb = 0, dev = 0, cus = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 64 * kFusedWaves, 0) != hipSuccess ||
-          hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        nb = 0;
-      slots = nb > 0 && cus > 0 ? nb * cus : 256;
-    }
+    // The resident block count is queried on every call, for the current
+    // device (host-side queries, no device work, nothing kept between calls).
+    int nb = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 64 * kFusedWaves, 0) != hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      nb = 0;
+    const int slots = nb > 0 && cus > 0 ? nb * cus : 256;
     double best = -1.0;
     for (int e = 2; e <= 64; ++e) {
       const int64_t per = (int64_t)kFusedWaves * e;
@@ -762,7 +760,7 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
     }
   };
 #define CSKV_FUSED(MS)                                                                            \
-  pick((const void*)compress_fused_kernel<T, MS>, MS);                                            \
+  pick((const void*)compress_fused_kernel<T, MS>);                                            \
   hipLaunchKernelGGL((compress_fused_kernel<T, MS>), dim3((unsigned)(groups * kFusedSlices)),     \
                      dim3(64 * kFusedWaves), 0, stream, xp, zp, bias_s, beta_l, R, NL, epw,        \
                      (T*)out_s, ld_s, (T*)out_l, ld_l, bnd)

@@ -4,19 +4,9 @@ import numpy as np
 import torch
 
 import workloads as wl
+from workloads.device import dev  # noqa: F401  (re-exported for the tests)
 
 TOL = {wl.DT_F32: 1e-4, wl.DT_BF16: 2e-2}
-
-
-def dev(t, device="cuda"):
-    """Upload a stored input (workloads.Tensor or raw numpy) as a torch tensor
-    of the matching dtype."""
-    raw, dt = (t.raw, t.dt) if isinstance(t, wl.Tensor) else (t, None)
-    if raw.dtype == np.uint16:
-        return torch.from_numpy(raw.view(np.int16)).to(device).view(torch.bfloat16)
-    if raw.dtype == np.uint8:
-        return torch.from_numpy(raw).to(device).view(torch.float8_e4m3fn)
-    return torch.from_numpy(np.ascontiguousarray(raw)).to(device)
 
 
 def host_f64(t):

@@ -153,7 +153,7 @@ def test_topk_prefill_workload_sampled():
     cskv = _cskv()
     qp = torch.from_numpy(inp["q_pos"]).cuda()
     idx = cskv.index_topk(dev(qI), dev(kI), cfg.k, q_pos=qp, m=4, idx_scale=scale).cpu().numpy()
-    rows = np.unique(np.concatenate([[0, 1, cfg.B - 1], np.linspace(0, cfg.B - 1, 29).astype(int)]))
+    rows = np.unique(np.concatenate([[0, 1, cfg.B - 1], np.linspace(0, cfg.B - 1, 64).round().astype(int)]))
     s, v = oracle.index_scores(qI.raw[rows], kI.raw, wl.DT_E4M3, scale, q_pos=inp["q_pos"][rows], m=4)
     check_selection(idx[rows], s, v, cfg.k)
 
