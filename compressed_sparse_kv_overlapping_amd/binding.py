@@ -245,8 +245,9 @@ def index_topk(q_idx, idx_keys, k, q_pos=None, m=4, idx_scale=1.0, per_seq=False
     N = idx_keys.shape[-2]
     _need(q_pos, "q_pos", torch.int64, (B,))
     _need(idx_out, "idx_out", torch.int32, (B, k))
+    # the per-sequence size (keys read once) is optional: the base size is the minimum
+    _need_ws(workspace, index_topk_workspace_size(B, N, k))
     ws = index_topk_workspace_size(B, N, k, per_seq)
-    _need_ws(workspace, ws)
     _dev(q_idx, idx_keys, q_pos, idx_out)
     if idx_out is None:
         idx_out = torch.empty((B, k), dtype=torch.int32, device=q_idx.device)
@@ -271,8 +272,8 @@ def index_topk_mxfp4(q_codes, q_scales, key_codes, key_scales, k, q_pos=None, m=
     _need(key_scales, "key_scales", torch.uint8, (B, N, I // 32) if per_seq else (N, I // 32))
     _need(q_pos, "q_pos", torch.int64, (B,))
     _need(idx_out, "idx_out", torch.int32, (B, k))
+    _need_ws(workspace, index_topk_workspace_size(B, N, k))
     ws = index_topk_workspace_size(B, N, k, per_seq)
-    _need_ws(workspace, ws)
     _dev(q_codes, q_scales, key_codes, key_scales, q_pos, idx_out)
     if idx_out is None:
         idx_out = torch.empty((B, k), dtype=torch.int32, device=q_codes.device)
