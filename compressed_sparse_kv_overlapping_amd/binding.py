@@ -46,6 +46,9 @@ _SIGS = {
     "cskv_index_topk_mxfp4": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _i64, _vp, _i32, _f32, _vp,
                                _vp, _sz, _vp], ctypes.c_int),
     "cskv_index_topk_per_seq_workspace_size": ([_i64, _i64, _i32], _sz),
+    "cskv_index_topk_noalloc_max_bytes": ([], _sz),
+    "cskv_index_topk_noalloc": ([_vp, _vp, _i64, _i64, _i32, _i64, _vp, _i32, _f32, ctypes.c_int,
+                                 _vp, _vp], ctypes.c_int),
     "cskv_attend_workspace_size": ([_i64, _i32, _i64], _sz),
     "cskv_sparse_attend": ([_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i64, _i64, _i64,
                             _vp, _i64, _f32, _vp, ctypes.c_int, _vp, _vp, _vp, _sz, _vp],
@@ -256,6 +259,25 @@ def index_topk(q_idx, idx_keys, k, q_pos=None, m=4, idx_scale=1.0, per_seq=False
     _call("cskv_index_topk", _ptr(q_idx), _ptr(idx_keys), B, N, k, N * I if per_seq else 0,
           _ptr(q_pos), m, float(idx_scale), _dt(q_idx), _ptr(idx_out), _ptr(workspace),
           workspace.numel(), _stream(stream))
+    return idx_out
+
+
+def index_topk_noalloc(q_idx, idx_keys, k, q_pos=None, m=4, idx_scale=1.0, per_seq=False,
+                       idx_out=None, stream=None):
+    """index_topk through the allocation-free entry point: the library's own
+    fixed scratch array replaces the workspace (calls on one GPU must not
+    overlap).  With idx_out given, nothing is allocated here either."""
+    _need(q_idx, "q_idx", _IDX_DT, (None, I))
+    B = q_idx.shape[0]
+    _kv(idx_keys, "idx_keys", per_seq, B, I, q_idx.dtype)
+    N = idx_keys.shape[-2]
+    _need(q_pos, "q_pos", torch.int64, (B,))
+    _need(idx_out, "idx_out", torch.int32, (B, k))
+    _dev(q_idx, idx_keys, q_pos, idx_out)
+    if idx_out is None:
+        idx_out = torch.empty((B, k), dtype=torch.int32, device=q_idx.device)
+    _call("cskv_index_topk_noalloc", _ptr(q_idx), _ptr(idx_keys), B, N, k, N * I if per_seq else 0,
+          _ptr(q_pos), m, float(idx_scale), _dt(q_idx), _ptr(idx_out), _stream(stream))
     return idx_out
 
 

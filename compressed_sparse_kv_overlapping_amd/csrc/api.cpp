@@ -167,6 +167,29 @@ int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t 
   return hip_status(cskv::launch_topk(p, workspace, (hipStream_t)stream), "cskv_index_topk");
 }
 
+size_t cskv_index_topk_noalloc_max_bytes(void) { return cskv::noalloc_scratch_bytes(); }
+
+int cskv_index_topk_noalloc(const void* q_idx, const void* idx_keys, int64_t B, int64_t N, int32_t k,
+                            int64_t key_bstride, const int64_t* q_pos, int32_t m, float idx_scale,
+                            cskv_dtype idx_dt, int32_t* idx_out, void* stream) {
+  const char* fn = "cskv_index_topk_noalloc";
+  int st = check_topk(fn, q_idx, idx_keys, B, N, k, key_bstride, q_pos, m, idx_scale, idx_dt,
+                      idx_out);
+  if (st) return st;
+  const size_t need = cskv::topk_workspace_bytes(B, N, k);
+  const size_t have = cskv::noalloc_scratch_bytes();
+  if (need > have)
+    return fail(CSKV_ERR_UNSUPPORTED,
+                "%s: this selection needs %zu bytes of scratch; the allocation-free call has %zu "
+                "(use cskv_index_topk with a workspace)", fn, need, have);
+  void* ws = nullptr;
+  hipError_t e = cskv::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "cskv_index_topk_noalloc (scratch address)");
+  cskv::TopkParams p{(int)idx_dt, q_idx, idx_keys, q_pos, key_bstride, B, N, k, m, idx_scale, idx_out};
+  p.ws_bytes = have;
+  return hip_status(cskv::launch_topk(p, ws, (hipStream_t)stream), fn);
+}
+
 int cskv_index_topk_mxfp4(const void* q_codes, const uint8_t* q_scales, const void* key_codes,
                           const uint8_t* key_scales, int64_t B, int64_t N, int32_t k,
                           int64_t key_bstride, const int64_t* q_pos, int32_t m, float idx_scale,

@@ -66,4 +66,9 @@ size_t topk_workspace_bytes(int64_t B, int64_t N, int k);
 size_t topk_stored_score_bytes(int64_t B, int64_t N);
 hipError_t launch_topk(const TopkParams& p, void* ws, hipStream_t stream);
 
+// The allocation-free calls' scratch: its size, and its device address on
+// the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace cskv

@@ -32,7 +32,9 @@
  * Conventions
  *  - Every pointer argument except `stream` is device memory (or host-pinned
  *    memory the GPU can read), owned by the caller; the library allocates and
- *    frees nothing and keeps no state between calls.
+ *    frees nothing and keeps no state between calls (the one exception is
+ *    the allocation-free selection call, which uses a fixed scratch array of
+ *    the library's on each GPU).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream) and never synchronize the device.
  *  - All arguments are validated before anything is launched: on error
@@ -150,6 +152,29 @@ int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t 
                     int64_t key_bstride, const int64_t* q_pos, int32_t m, float idx_scale,
                     cskv_dtype idx_dt, int32_t* idx_out, void* workspace, size_t ws_bytes,
                     void* stream);
+
+/*
+ * cskv_index_topk without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops and harnesses
+ * that forbid allocation.  The same selection as cskv_index_topk (the same
+ * kernels; bit-identical idx_out), with its scratch in a fixed device array
+ * of cskv_index_topk_noalloc_max_bytes() bytes (32 MiB) that the library
+ * holds on every GPU it runs on until the process ends.  Nothing is
+ * allocated or freed by the call.
+ *   Selections whose cskv_index_topk_workspace_size(B, N, k) (or, with
+ *   per-query keys, less than the per-sequence size: the two-read path)
+ *   exceeds that size are rejected with CSKV_ERR_UNSUPPORTED.  Up to 1M
+ *   entries at k = 1024 fit for a few dozen queries.
+ *   Every call on a GPU uses that GPU's one scratch array: calls that
+ *   overlap on one GPU (different streams, or threads) race and must be
+ *   serialised by the caller.  Every scratch byte a call reads it first
+ *   writes, so nothing carries over from the previous call.
+ * Arguments and the other errors are those of cskv_index_topk.
+ */
+size_t cskv_index_topk_noalloc_max_bytes(void);
+int cskv_index_topk_noalloc(const void* q_idx, const void* idx_keys, int64_t B, int64_t N, int32_t k,
+                            int64_t key_bstride, const int64_t* q_pos, int32_t m, float idx_scale,
+                            cskv_dtype idx_dt, int32_t* idx_out, void* stream);
 
 /*
  * Indexer scoring and top-k selection over MXFP4 queries and keys ("Frontier

@@ -27,7 +27,7 @@ def declared():
 
 def test_header_functions_are_exported(lib):
     names = declared()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), f"{n} declared in cskv.h but not exported"
     from compressed_sparse_kv_overlapping_amd import binding
@@ -84,6 +84,23 @@ def test_index_topk_errors(lib):
     assert f(P, P, 8, 16384, 64, 0, NULL, 4, 1.0, 1, P, NULL, ws, NULL) == WORKSPACE
     assert f(P, P, 8, 16384, 64, 0, NULL, 4, 1.0, 1, P, P, 16, NULL) == WORKSPACE
     assert f(NULL, P, 8, 16384, 64, 0, NULL, 4, 1.0, 1, P, P, ws, NULL) == INVALID
+
+
+def test_index_topk_noalloc_errors(lib):
+    """The allocation-free selection rejects bad arguments, and selections
+    whose scratch exceeds its fixed array, before touching the device."""
+    f = lib.cskv_index_topk_noalloc
+    cap = lib.cskv_index_topk_noalloc_max_bytes()
+    assert cap == 32 << 20
+    assert lib.cskv_index_topk_workspace_size(32, 1 << 18, 1024) <= cap       # 1M-token decode fits
+    assert lib.cskv_index_topk_workspace_size(4096, 1 << 18, 1024) > cap
+    assert f(P, P, 4096, 1 << 18, 1024, 0, NULL, 4, 1.0, 2, P, NULL) == UNSUPPORTED
+    assert b"scratch" in lib.cskv_last_error()
+    assert f(P, P, 8, 16384, 0, 0, NULL, 4, 1.0, 1, P, NULL) == INVALID       # k < 1
+    assert f(P, P, 8, 16384, 4097, 0, NULL, 4, 1.0, 1, P, NULL) == UNSUPPORTED  # k > 4096
+    assert f(NULL, P, 8, 16384, 64, 0, NULL, 4, 1.0, 1, P, NULL) == INVALID
+    assert f(P, P, 8, 16384, 64, 0, NULL, 4, 1.0, 1, NULL, NULL) == INVALID
+    assert f(P, P, 8, 16384, 64, 0, P, 0, 1.0, 1, P, NULL) == INVALID        # m with q_pos
 
 
 def test_index_topk_mxfp4_errors(lib):
