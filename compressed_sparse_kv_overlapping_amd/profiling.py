@@ -19,6 +19,11 @@ the copy (known bytes / counted bytes), so the figure is in true bytes.
 ``compress`` part, keyed by a digest of the kernel sources so that a stale
 figure is never reported) and prints the summary kept in profiles/.
 
+``indexer`` runs the selection at the prefill-chunk and decode shapes (the
+program profiled for the indexer's SQ counters and kernel trace), and
+``sq <pmc_dir> <title> <command>`` prints every counter of a --pmc run per
+kernel.
+
 ``trace <results.db> <command>`` prints, from a ``rocprofv3 --kernel-trace``
 database, each library kernel's dispatch count and average / min / max
 duration per grid shape, with the profiled command in the header.
@@ -72,6 +77,56 @@ def run():
         cskv.compress2(x, z, b4, 4, b128, 128, out_small=e4, out_large=e128, workspace=ws)
     torch.cuda.synchronize()
     print(json.dumps({"source_digest": source_digest(), "copy_bytes": COPY_BYTES}), flush=True)
+
+
+def indexer():
+    """The selection at the prefill chunk (4,096 causal queries over 262,144
+    fp8 keys, top-1024) and at the 1M-token decode (32 queries over 262,144
+    bf16 keys), three launches each, on random device inputs (the kernels'
+    work does not depend on the values beyond the candidate counts, which
+    random scores keep near their typical 1.2k per query)."""
+    import torch
+    import compressed_sparse_kv_overlapping_amd as cskv
+    g = torch.Generator(device="cuda").manual_seed(0)
+    N, k = 1 << 18, 1024
+    for B, dt, causal in ((4096, torch.float8_e4m3fn, True), (32, torch.bfloat16, False)):
+        q = torch.randn(B, 64, device="cuda", generator=g).to(dt)
+        keys = torch.randn(N, 64, device="cuda", generator=g).to(dt)
+        qp = (torch.arange(B, device="cuda", dtype=torch.int64) + (N * 4 - B)) if causal else None
+        out = torch.empty(B, k, dtype=torch.int32, device="cuda")
+        ws = torch.empty(cskv.index_topk_workspace_size(B, N, k), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            cskv.index_topk(q, keys, k, q_pos=qp, m=4, idx_out=out, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            cskv.index_topk(q, keys, k, q_pos=qp, m=4, idx_out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"queries": B, "entries": N, "k": k, "dtype": str(dt),
+                          "ms_per_selection": round(e0.elapsed_time(e1) / 5, 4)}), flush=True)
+
+
+def sq_summary(directory, title, command):
+    """Per-kernel averages of every counter in a rocprofv3 --pmc directory."""
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    acc = {}
+    grid = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                key = r["Kernel_Name"]
+                acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                grid[key] = (r.get("Grid_Size", ""), r.get("Workgroup_Size", ""))
+    print(f"# {title}\n# command: {command}\n# per dispatch, averaged over the dispatches of each kernel")
+    for key in sorted(acc):
+        g, w = grid[key]
+        print(f"\n{key}  (grid {g}, workgroup {w})")
+        for c, v in sorted(acc[key].items()):
+            print(f"  {c:28s} {sum(v) / len(v):16.1f}")
 
 
 def _per_kernel(directory, counter):
@@ -164,6 +219,10 @@ if __name__ == "__main__":
         run()
     elif len(sys.argv) >= 4 and sys.argv[1] == "summarize":
         summarize(sys.argv[2], sys.argv[3], sys.argv[4] if len(sys.argv) > 4 else None)
+    elif len(sys.argv) == 2 and sys.argv[1] == "indexer":
+        indexer()
+    elif len(sys.argv) == 5 and sys.argv[1] == "sq":
+        sq_summary(sys.argv[2], sys.argv[3], sys.argv[4])
     elif len(sys.argv) == 4 and sys.argv[1] == "trace":
         trace(sys.argv[2], sys.argv[3])
     else:
