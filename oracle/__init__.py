@@ -56,9 +56,9 @@ def lib():
         L.cskv_oracle_index_scores.argtypes = [vp, vp, i32, i64, i64, i64, dbl, i64, vp, i32, vp, vp]
         L.cskv_oracle_topk.argtypes = [vp, vp, i64, i64, i32, vp]
         L.cskv_oracle_csa_attend.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, vp,
-                                             i64, i64, i64, i64, vp, i64, dbl, vp, vp, vp]
+                                             i64, i64, i64, i64, vp, i64, dbl, vp, dbl, vp, vp]
         L.cskv_oracle_hca_attend.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, vp, i32, dbl,
-                                             vp, vp, vp]
+                                             vp, dbl, vp, vp]
         L.cskv_oracle_max_threads.restype = i32
         _lib = L
     return _lib
@@ -175,9 +175,11 @@ def topk(scores, visible, k):
 
 
 def csa_attend(q, entries, window, dt, idx, scale=1.0, q_pos=None, win_pos0=0, W=None,
-               per_seq=False, Dv=D, sink=None):
+               per_seq=False, Dv=D, sink=None, norm_eps=None):
     """CSA attention over selected entries plus the raw window; sink: per-head
-    attention-sink logits [H] (None: no sink).
+    attention-sink logits [H] (None: no sink); norm_eps: normalise the
+    queries and the selected entries to unit RMS with this epsilon (None: no
+    normalisation; window rows are never normalised).
     Returns (out float64 [B, H, Dv], lse float64 [B, H])."""
     q, entries, window = _c(q), _c(entries), _c(window)
     idx = _c(idx, np.int32)
@@ -194,7 +196,8 @@ def csa_attend(q, entries, window, dt, idx, scale=1.0, q_pos=None, win_pos0=0, W
     lse = np.empty((B, H), dtype=np.float64)
     _check(lib().cskv_oracle_csa_attend(_p(q), _p(entries), _p(window), dt, B, H, Ee, Dv, N, W,
                                         _p(idx), k, ent_bs, win_bs, win_rows, _p(qp), int(win_pos0),
-                                        float(scale), _p(_c(sink, np.float64)), _p(out), _p(lse)),
+                                        float(scale), _p(_c(sink, np.float64)),
+                                        -1.0 if norm_eps is None else float(norm_eps), _p(out), _p(lse)),
            "csa_attend")
     return out, lse
 
@@ -212,10 +215,12 @@ def hca_attend_mxfp4(q, ent_codes, ent_scales, **kw):
     return hca_attend(decode(q, BF16), mxfp4_decode(ent_codes, ent_scales), F64, **kw)
 
 
-def hca_attend(q, entries, dt, scale=1.0, per_seq=False, Dv=D, q_pos=None, m=None, sink=None):
+def hca_attend(q, entries, dt, scale=1.0, per_seq=False, Dv=D, q_pos=None, m=None, sink=None,
+               norm_eps=None):
     """Dense attention over the entries each query sees: all of them at
     decode (q_pos None); at a prefill chunk, entries i with (i+1)*m <=
-    q_pos[b] + 1.  Returns (out [B, H, Dv], lse [B, H])."""
+    q_pos[b] + 1; norm_eps as in csa_attend.  Returns (out [B, H, Dv],
+    lse [B, H])."""
     q, entries = _c(q), _c(entries)
     B, H, Ee = q.shape
     N = entries.shape[-2]
@@ -225,6 +230,8 @@ def hca_attend(q, entries, dt, scale=1.0, per_seq=False, Dv=D, q_pos=None, m=Non
     _check(lib().cskv_oracle_hca_attend(_p(q), _p(entries), dt, B, H, Ee, Dv, N,
                                         N * Ee if per_seq else 0, _p(qp),
                                         int(m) if m is not None else 0, float(scale),
-                                        _p(_c(sink, np.float64)), _p(out), _p(lse)),
+                                        _p(_c(sink, np.float64)),
+                                        -1.0 if norm_eps is None else float(norm_eps), _p(out),
+                                        _p(lse)),
            "hca_attend")
     return out, lse

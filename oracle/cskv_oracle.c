@@ -38,6 +38,9 @@
  *  - CSA attention: one joint softmax over selected entries and window rows;
  *    logits use all 576 dims, values are dims 0..511;
  *  - attention-sink logits: one more softmax term per head with a zero value;
+ *  - query / compressed-entry normalisation (optional): unit root-mean-square
+ *    over all 576 dims with an epsilon argument, no learned gain; the
+ *    normalised entry is key and value; raw window rows are not normalised;
  *  - MXFP4 (named by [P1] for the indexer's QK path and, as FP4 with block
  *    scales, by "Compressed attention - CSA / HCA" section 3 for the V4.1 KV
  *    cache): the OCP Microscaling v1.0 format, element 2j in the low nibble
@@ -232,15 +235,37 @@ int cskv_oracle_topk(const double* scores, const uint8_t* visible, int64_t B, in
  * ("DeepSeek V4 comprimeix el context", section "CSA: buscar primer i
  * atendre despres": learned logits that absorb attention mass) is one more
  * softmax term with logit `sink` and a zero value: p_r = exp(l_r) /
- * (sum_r' exp(l_r') + exp(sink)).  sink = -inf: no sink. */
+ * (sum_r' exp(l_r') + exp(sink)).  sink = -inf: no sink.
+ *
+ * Normalisation of queries and compressed entries (the same section: the
+ * design normalises them to stabilise the logits).  With norm_eps >= 0 the
+ * query and every row flagged in is_entry are replaced by x / rms(x), rms(x)
+ * = sqrt(sum_e x[e]^2 / E + norm_eps) over all E dims; the normalised entry
+ * is both the key and the value.  Rows not flagged (raw window rows) are
+ * used as they are.  norm_eps < 0: no normalisation. */
+static double inv_rms(const void* buf, int64_t off, int64_t E, int dt, double eps) {
+  double ss = 0.0;
+  for (int64_t e = 0; e < E; ++e) {
+    const double x = ld(buf, off + e, dt);
+    ss += x * x;
+  }
+  return 1.0 / sqrt(ss / (double)E + eps);
+}
+
 static void attend_rows(const void* q, int64_t q_off, int dt, const void* const* row_buf,
-                        const int64_t* row_off, int64_t n_rows, int64_t E, int64_t Dv,
-                        double scale, double sink, double* out, double* lse) {
+                        const int64_t* row_off, const unsigned char* is_entry, int64_t n_rows,
+                        int64_t E, int64_t Dv, double scale, double sink, double norm_eps,
+                        double* out, double* lse) {
   double* l = (double*)malloc(sizeof(double) * (n_rows > 0 ? n_rows : 1));
+  double* g = (double*)malloc(sizeof(double) * (n_rows > 0 ? n_rows : 1));   /* row factors */
+  const int norm = norm_eps >= 0.0;
+  const double gq = norm ? inv_rms(q, q_off, E, dt, norm_eps) : 1.0;
   double mx = sink;
   for (int64_t r = 0; r < n_rows; ++r) {
+    g[r] = (norm && is_entry[r]) ? inv_rms(row_buf[r], row_off[r], E, dt, norm_eps) : 1.0;
     double acc = 0.0;
-    for (int64_t e = 0; e < E; ++e) acc += ld(q, q_off + e, dt) * ld(row_buf[r], row_off[r] + e, dt);
+    for (int64_t e = 0; e < E; ++e)
+      acc += (gq * ld(q, q_off + e, dt)) * (g[r] * ld(row_buf[r], row_off[r] + e, dt));
     l[r] = scale * acc;
     if (l[r] > mx) mx = l[r];
   }
@@ -248,17 +273,19 @@ static void attend_rows(const void* q, int64_t q_off, int dt, const void* const*
     for (int64_t d = 0; d < Dv; ++d) out[d] = 0.0;
     *lse = -INFINITY;
     free(l);
+    free(g);
     return;
   }
   double den = sink == -INFINITY ? 0.0 : exp(sink - mx);
   for (int64_t r = 0; r < n_rows; ++r) { l[r] = exp(l[r] - mx); den += l[r]; }
   for (int64_t d = 0; d < Dv; ++d) {
     double acc = 0.0;
-    for (int64_t r = 0; r < n_rows; ++r) acc += l[r] * ld(row_buf[r], row_off[r] + d, dt);
+    for (int64_t r = 0; r < n_rows; ++r) acc += l[r] * (g[r] * ld(row_buf[r], row_off[r] + d, dt));
     out[d] = acc / den;
   }
   *lse = mx + log(den);
   free(l);
+  free(g);
 }
 
 /* CSA: rows of query b = entries[idx[b][j]] for idx >= 0 (in list order),
@@ -271,8 +298,8 @@ int cskv_oracle_csa_attend(const void* q, const void* entries, const void* windo
                            int64_t B, int64_t H, int64_t E, int64_t Dv, int64_t N, int64_t W,
                            const int32_t* idx, int64_t k, int64_t ent_bstride,
                            int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
-                           int64_t win_pos0, double scale, const double* sink, double* out,
-                           double* lse) {
+                           int64_t win_pos0, double scale, const double* sink, double norm_eps,
+                           double* out, double* lse) {
   if (!q || !entries || !idx || !out || !lse || B < 0 || H <= 0 || E <= 0 || Dv <= 0 ||
       Dv > E || N < 0 || W < 0 || k <= 0 || !dt_ok(dt))
     return -1;
@@ -292,12 +319,14 @@ int cskv_oracle_csa_attend(const void* q, const void* entries, const void* windo
       int64_t cap = k + W;
       const void** buf = (const void**)malloc(sizeof(void*) * cap);
       int64_t* off = (int64_t*)malloc(sizeof(int64_t) * cap);
+      unsigned char* ent = (unsigned char*)malloc(cap);
       int64_t n = 0;
       for (int64_t j = 0; j < k; ++j) {
         int32_t i = idx[b * k + j];
         if (i < 0) continue;
         buf[n] = entries;
         off[n] = b * ent_bstride + (int64_t)i * E;
+        ent[n] = 1;
         ++n;
       }
       if (W > 0) {
@@ -314,13 +343,15 @@ int cskv_oracle_csa_attend(const void* q, const void* entries, const void* windo
         for (int64_t r = lo; r <= hi; ++r) {
           buf[n] = window;
           off[n] = b * win_bstride + r * E;
+          ent[n] = 0;
           ++n;
         }
       }
-      attend_rows(q, (b * H + h) * E, dt, buf, off, n, E, Dv, scale, sink ? sink[h] : -INFINITY,
-                  out + (b * H + h) * Dv, lse + b * H + h);
+      attend_rows(q, (b * H + h) * E, dt, buf, off, ent, n, E, Dv, scale,
+                  sink ? sink[h] : -INFINITY, norm_eps, out + (b * H + h) * Dv, lse + b * H + h);
       free(buf);
       free(off);
+      free(ent);
     }
   }
   return 0;
@@ -334,7 +365,7 @@ int cskv_oracle_csa_attend(const void* q, const void* entries, const void* windo
 int cskv_oracle_hca_attend(const void* q, const void* entries, int dt, int64_t B, int64_t H,
                            int64_t E, int64_t Dv, int64_t N, int64_t ent_bstride,
                            const int64_t* q_pos, int m, double scale, const double* sink,
-                           double* out, double* lse) {
+                           double norm_eps, double* out, double* lse) {
   if (!q || !entries || !out || !lse || B < 0 || H <= 0 || E <= 0 || Dv <= 0 || Dv > E ||
       N < 0 || !dt_ok(dt))
     return -1;
@@ -349,14 +380,17 @@ int cskv_oracle_hca_attend(const void* q, const void* entries, int dt, int64_t B
       }
       const void** buf = (const void**)malloc(sizeof(void*) * (n > 0 ? n : 1));
       int64_t* off = (int64_t*)malloc(sizeof(int64_t) * (n > 0 ? n : 1));
+      unsigned char* ent = (unsigned char*)malloc(n > 0 ? n : 1);
       for (int64_t i = 0; i < n; ++i) {
         buf[i] = entries;
         off[i] = b * ent_bstride + i * E;
+        ent[i] = 1;
       }
-      attend_rows(q, (b * H + h) * E, dt, buf, off, n, E, Dv, scale, sink ? sink[h] : -INFINITY,
-                  out + (b * H + h) * Dv, lse + b * H + h);
+      attend_rows(q, (b * H + h) * E, dt, buf, off, ent, n, E, Dv, scale,
+                  sink ? sink[h] : -INFINITY, norm_eps, out + (b * H + h) * Dv, lse + b * H + h);
       free(buf);
       free(off);
+      free(ent);
     }
   }
   return 0;

@@ -55,3 +55,9 @@ def attend(qv, rows, Dv=512, scale=1.0, sink=None):
     p = np.exp(logits - mx)
     den = p.sum(axis=1, keepdims=True)
     return (p / den) @ values, (mx + np.log(den))[:, 0]
+
+
+def rms_normalize(x, eps):
+    """x / sqrt(mean(x^2) + eps) along the last axis (unit root-mean-square)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)

@@ -637,3 +637,97 @@ def test_prefill_window_positions():
     np.testing.assert_allclose(lse, np.log(4), rtol=1e-12)
     with pytest.raises(ValueError):                           # window outside the buffer
         oracle.csa_attend(q, ent, src, F32, idx, q_pos=np.array([102, 109]), win_pos0=100, W=W, Dv=Dv)
+
+
+# ------------------------------------------- query / entry normalisation
+# ("DeepSeek V4 comprimeix el context", section "CSA: buscar primer i atendre
+# despres": queries and compressed entries are normalised to stabilise the
+# logits.  Reading: unit root-mean-square over the 576 dims, x / sqrt(mean(x^2)
+# + eps), no learned gain; the normalised entry is key and value; raw window
+# rows stay as they are.)
+
+def _norm_inputs(seed, B=2, H=3, N=40, W=6, k=9, dt=wl.DT_BF16):
+    rng = np.random.default_rng(seed)
+    q = wl.encode(rng.standard_normal((B, H, 576)) * rng.uniform(0.01, 0.2, (B, H, 1)), dt).raw
+    ent = wl.encode(rng.standard_normal((N, 576)) * rng.uniform(0.2, 5.0, (N, 1)), dt).raw
+    win = wl.encode(rng.standard_normal((W, 576)) * 0.7, dt).raw
+    idx = np.stack([rng.choice(N, k, replace=False) for _ in range(B)]).astype(np.int32)
+    idx[0, 2] = -1
+    return q, ent, win, idx
+
+
+def test_norm_single_row_is_that_row_over_its_rms():
+    """One selected entry and no window: every weight is 1, so the output is
+    the normalised entry's value part, whatever the query."""
+    eps = 1e-6
+    q, ent, win, idx = _norm_inputs(11)
+    idx1 = idx[:, :1]
+    out, lse = oracle.csa_attend(q, ent, None, wl.DT_BF16, idx1, W=0, norm_eps=eps)
+    dec = oracle.decode(ent, wl.DT_BF16)
+    for b in range(q.shape[0]):
+        row = dec[idx1[b, 0]]
+        want = row[:512] / math.sqrt(float(np.mean(row * row)) + eps)
+        np.testing.assert_allclose(out[b], np.tile(want, (q.shape[1], 1)), rtol=1e-13, atol=1e-15)
+
+
+def test_norm_equals_attention_over_prenormalised_rows():
+    """The oracle's folded factors equal a NumPy attention over rows that were
+    normalised first (entries only; window rows as given), with and without a
+    sink, for CSA and HCA."""
+    eps = 1e-5
+    q, ent, win, idx = _norm_inputs(12)
+    qv = oracle.decode(q, wl.DT_BF16)
+    ev = oracle.decode(ent, wl.DT_BF16)
+    wv = oracle.decode(win, wl.DT_BF16)
+    sink = np.array([0.3, -1.0, 2.0])
+    for s in (None, sink):
+        out, lse = oracle.csa_attend(q, ent, win, wl.DT_BF16, idx, scale=0.05, norm_eps=eps, sink=s)
+        for b in range(q.shape[0]):
+            sel = idx[b][idx[b] >= 0]
+            rows = np.concatenate([numpy_ref.rms_normalize(ev[sel], eps), wv])
+            ro, rl = numpy_ref.attend(numpy_ref.rms_normalize(qv[b], eps), rows, scale=0.05, sink=s)
+            np.testing.assert_allclose(out[b], ro, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(lse[b], rl, rtol=1e-12)
+        out, lse = oracle.hca_attend(q, ent, wl.DT_BF16, scale=0.05, norm_eps=eps, sink=s)
+        for b in range(q.shape[0]):
+            ro, rl = numpy_ref.attend(numpy_ref.rms_normalize(qv[b], eps),
+                                      numpy_ref.rms_normalize(ev, eps), scale=0.05, sink=s)
+            np.testing.assert_allclose(out[b], ro, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(lse[b], rl, rtol=1e-12)
+
+
+def test_norm_of_unit_rms_inputs_is_the_plain_path():
+    """Elements of +-1 have a root-mean-square of exactly 1: with eps = 0 the
+    normalised attention is the plain one."""
+    rng = np.random.default_rng(13)
+    B, H, N, W, k = 2, 4, 30, 5, 7
+    q = rng.choice([-1.0, 1.0], (B, H, 576)).astype(np.float32)
+    ent = rng.choice([-1.0, 1.0], (N, 576)).astype(np.float32)
+    win = rng.standard_normal((W, 576)).astype(np.float32)
+    idx = np.stack([rng.choice(N, k, replace=False) for _ in range(B)]).astype(np.int32)
+    a = oracle.csa_attend(q, ent, win, wl.DT_F32, idx, scale=1 / 24, norm_eps=0.0)
+    b = oracle.csa_attend(q, ent, win, wl.DT_F32, idx, scale=1 / 24)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-14)
+
+
+def test_norm_scale_invariance():
+    """With eps = 0 the result does not change when a query head or an entry
+    row is multiplied by a positive factor (powers of two keep the bf16
+    inputs exact); scaling a window row does change it, since raw window
+    rows are not normalised."""
+    q, ent, win, idx = _norm_inputs(14)
+    rng = np.random.default_rng(15)
+    qf = oracle.decode(q, wl.DT_BF16) * 2.0 ** rng.integers(-3, 4, (q.shape[0], q.shape[1], 1))
+    ef = oracle.decode(ent, wl.DT_BF16) * 2.0 ** rng.integers(-3, 4, (ent.shape[0], 1))
+    q2, e2 = wl.bf16_bits(qf.astype(np.float32)), wl.bf16_bits(ef.astype(np.float32))
+    a = oracle.csa_attend(q, ent, win, wl.DT_BF16, idx, scale=0.04, norm_eps=0.0)
+    b = oracle.csa_attend(q2, e2, win, wl.DT_BF16, idx, scale=0.04, norm_eps=0.0)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-12)
+    w2 = wl.bf16_bits((oracle.decode(win, wl.DT_BF16) * 2.0).astype(np.float32))
+    c = oracle.csa_attend(q, ent, w2, wl.DT_BF16, idx, scale=0.04, norm_eps=0.0)
+    assert np.abs(c[0] - a[0]).max() > 1e-3
+    h1 = oracle.hca_attend(q, ent, wl.DT_BF16, scale=0.04, norm_eps=0.0)
+    h2 = oracle.hca_attend(q2, e2, wl.DT_BF16, scale=0.04, norm_eps=0.0)
+    np.testing.assert_allclose(h1[0], h2[0], rtol=1e-12, atol=1e-14)
