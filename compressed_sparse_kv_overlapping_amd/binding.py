@@ -51,21 +51,22 @@ _SIGS = {
                                  _vp, _vp], ctypes.c_int),
     "cskv_attend_workspace_size": ([_i64, _i32, _i64], _sz),
     "cskv_sparse_attend": ([_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i64, _i64, _i64,
-                            _vp, _i64, _f32, _vp, ctypes.c_int, _vp, _vp, _vp, _sz, _vp],
+                            _vp, _i64, _f32, _vp, _f32, ctypes.c_int, _vp, _vp, _vp, _sz, _vp],
                            ctypes.c_int),
     "cskv_csa_workspace_size": ([_i64, _i32, _i64, _i32, _i32], _sz),
     "cskv_csa_attend": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i32, _i64, _i64,
-                         _i64, _i64, _vp, _i64, _f32, _vp, _f32, ctypes.c_int, ctypes.c_int, _vp,
-                         _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+                         _i64, _i64, _vp, _i64, _f32, _vp, _f32, _f32, ctypes.c_int, ctypes.c_int,
+                         _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "cskv_hca_workspace_size": ([_i64, _i32, _i64], _sz),
-    "cskv_hca_attend": ([_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, _vp, ctypes.c_int, _vp,
-                         _vp, _vp, _sz, _vp], ctypes.c_int),
+    "cskv_hca_attend": ([_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, _vp, _f32, ctypes.c_int,
+                         _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "cskv_sparse_attend_mxfp4_workspace_size": ([_i64, _i32, _i32, _i32], _sz),
     "cskv_hca_attend_mxfp4_workspace_size": ([_i64, _i32, _i64, _i32], _sz),
     "cskv_sparse_attend_mxfp4": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i64, _i64,
-                                  _i64, _vp, _i64, _f32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
-    "cskv_hca_attend_mxfp4": ([_vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, _vp, _vp, _vp,
-                               _vp, _sz, _vp], ctypes.c_int),
+                                  _i64, _vp, _i64, _f32, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+                                 ctypes.c_int),
+    "cskv_hca_attend_mxfp4": ([_vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, _vp, _f32, _vp,
+                               _vp, _vp, _sz, _vp], ctypes.c_int),
     "cskv_merge": ([_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
@@ -313,10 +314,23 @@ def attend_workspace_size(B, H, rows_per_query):
     return library().cskv_attend_workspace_size(B, H, rows_per_query)
 
 
+def _eps(norm_eps):
+    """The ABI's norm_eps: the epsilon of the query / entry normalisation, or
+    -1 for none."""
+    if norm_eps is None:
+        return -1.0
+    if not norm_eps >= 0.0:
+        raise ValueError("norm_eps must be >= 0 (None: no normalisation)")
+    return float(norm_eps)
+
+
 def sparse_attend(q, entries, window, idx, q_pos=None, win_pos0=0, W=None, scale=1.0,
-                  per_seq=False, out=None, lse=None, workspace=None, stream=None, sink=None):
+                  per_seq=False, out=None, lse=None, workspace=None, stream=None, sink=None,
+                  norm_eps=None):
     """Attention of q [B, H, 576] over entries[idx] plus the raw window;
-    sink: per-head attention-sink logits, fp32 [H] (None: no sink)."""
+    sink: per-head attention-sink logits, fp32 [H] (None: no sink);
+    norm_eps: normalise the queries and the selected entries to unit RMS
+    with this epsilon (None: no normalisation)."""
     _need(q, "q", _VAL_DT, (None, None, E))
     B, H = q.shape[0], q.shape[1]
     _kv(entries, "entries", per_seq, B, E, q.dtype)
@@ -340,7 +354,7 @@ def sparse_attend(q, entries, window, idx, q_pos=None, win_pos0=0, W=None, scale
         workspace = _workspace(attend_workspace_size(B, H, k + W), q.device)
     _call("cskv_sparse_attend", _ptr(q), _ptr(entries), _ptr(window), _ptr(idx), B, H, N, W, k,
           N * E if per_seq else 0, win_rows * E if per_seq else 0, win_rows, _ptr(q_pos),
-          int(win_pos0), float(scale), _sink(sink, H), _dt(q), _ptr(out), _ptr(lse),
+          int(win_pos0), float(scale), _sink(sink, H), _eps(norm_eps), _dt(q), _ptr(out), _ptr(lse),
           _ptr(workspace), workspace.numel(), _stream(stream))
     return out, lse
 
@@ -351,8 +365,9 @@ def csa_workspace_size(B, H, N, W, k):
 
 def csa_attend(q, q_idx, entries, idx_keys, window, k, m=4, q_pos=None, win_pos0=0, W=None,
                scale=1.0, idx_scale=1.0, per_seq=False, out=None, lse=None, idx_out=None,
-               workspace=None, stream=None, sink=None):
-    """CSA: indexer top-k then attention over the selection plus the window.
+               workspace=None, stream=None, sink=None, norm_eps=None):
+    """CSA: indexer top-k then attention over the selection plus the window
+    (sink, norm_eps as in sparse_attend).
     Returns (out [B, H, 512], lse [B, H], idx [B, k])."""
     _need(q, "q", _VAL_DT, (None, None, E))
     B, H = q.shape[0], q.shape[1]
@@ -383,7 +398,7 @@ def csa_attend(q, q_idx, entries, idx_keys, window, k, m=4, q_pos=None, win_pos0
     _call("cskv_csa_attend", _ptr(q), _ptr(q_idx), _ptr(entries), _ptr(idx_keys), _ptr(window),
           B, H, N, W, k, m, N * E if per_seq else 0, N * I if per_seq else 0,
           win_rows * E if per_seq else 0, win_rows, _ptr(q_pos), int(win_pos0), float(scale),
-          _sink(sink, H), float(idx_scale), _dt(q), _dt(q_idx), _ptr(out), _ptr(lse),
+          _sink(sink, H), _eps(norm_eps), float(idx_scale), _dt(q), _dt(q_idx), _ptr(out), _ptr(lse),
           _ptr(idx_out),
           _ptr(workspace), workspace.numel(), _stream(stream))
     return out, lse, idx_out
@@ -394,7 +409,7 @@ def hca_workspace_size(B, H, N):
 
 
 def hca_attend(q, entries, scale=1.0, per_seq=False, q_pos=None, m=None, out=None, lse=None,
-               workspace=None, stream=None, sink=None):
+               workspace=None, stream=None, sink=None, norm_eps=None):
     """HCA: dense attention of q [B, H, 576] over the entries [N, 576] each
     query sees: all of them (q_pos None), or at a prefill chunk those with
     (i+1)*m <= q_pos[b] + 1 (q_pos [B] int64 on the device)."""
@@ -416,8 +431,9 @@ def hca_attend(q, entries, scale=1.0, per_seq=False, q_pos=None, m=None, out=Non
     if workspace is None:
         workspace = _workspace(hca_workspace_size(B, H, N), q.device)
     _call("cskv_hca_attend", _ptr(q), _ptr(entries), B, H, N, N * E if per_seq else 0,
-          _ptr(q_pos), int(m) if q_pos is not None else 0, float(scale), _sink(sink, H), _dt(q),
-          _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
+          _ptr(q_pos), int(m) if q_pos is not None else 0, float(scale), _sink(sink, H),
+          _eps(norm_eps), _dt(q), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+          _stream(stream))
     return out, lse
 
 
@@ -432,7 +448,7 @@ def _mx_entries(codes, scales, per_seq, B):
 
 def sparse_attend_mxfp4(q, ent_codes, ent_scales, window, idx, q_pos=None, win_pos0=0, W=None,
                         scale=1.0, per_seq=False, out=None, lse=None, workspace=None, stream=None,
-                        sink=None):
+                        sink=None, norm_eps=None):
     """sparse_attend over MXFP4 entries: codes uint8 [N, 288] and E8M0
     scales uint8 [N, 18] (with a leading batch dimension per sequence); q,
     window and out are bf16."""
@@ -459,13 +475,13 @@ def sparse_attend_mxfp4(q, ent_codes, ent_scales, window, idx, q_pos=None, win_p
         workspace = _workspace(need, q.device)
     _call("cskv_sparse_attend_mxfp4", _ptr(q), _ptr(ent_codes), _ptr(ent_scales), _ptr(window),
           _ptr(idx), B, H, N, W, k, N if per_seq else 0, win_rows * E if per_seq else 0, win_rows,
-          _ptr(q_pos), int(win_pos0), float(scale), _sink(sink, H), _ptr(out), _ptr(lse),
-          _ptr(workspace), workspace.numel(), _stream(stream))
+          _ptr(q_pos), int(win_pos0), float(scale), _sink(sink, H), _eps(norm_eps), _ptr(out),
+          _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
     return out, lse
 
 
 def hca_attend_mxfp4(q, ent_codes, ent_scales, scale=1.0, per_seq=False, q_pos=None, m=None,
-                     out=None, lse=None, workspace=None, stream=None, sink=None):
+                     out=None, lse=None, workspace=None, stream=None, sink=None, norm_eps=None):
     """hca_attend over MXFP4 entries (codes [N, 288], scales [N, 18])."""
     if q_pos is not None and m is None:
         raise ValueError("hca_attend_mxfp4: q_pos needs the block size m")
@@ -486,7 +502,7 @@ def hca_attend_mxfp4(q, ent_codes, ent_scales, scale=1.0, per_seq=False, q_pos=N
         workspace = _workspace(need, q.device)
     _call("cskv_hca_attend_mxfp4", _ptr(q), _ptr(ent_codes), _ptr(ent_scales), B, H, N,
           N if per_seq else 0, _ptr(q_pos), int(m) if q_pos is not None else 0, float(scale),
-          _sink(sink, H), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+          _sink(sink, H), _eps(norm_eps), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
           _stream(stream))
     return out, lse
 

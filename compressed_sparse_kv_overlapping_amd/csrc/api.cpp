@@ -224,10 +224,12 @@ size_t cskv_attend_workspace_size(int64_t B, int32_t H, int64_t rows_per_query) 
 static int check_attend(const char* fn, const void* q, const void* entries, const void* window,
                         int64_t B, int32_t H, int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
                         int64_t win_bstride, int64_t win_rows, cskv_dtype dt, const void* out,
-                        float scale) {
+                        float scale, float norm_eps) {
   if (!q || !entries || !out) return fail(CSKV_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (!(scale >= 0.f) || scale > 3.0e38f)
     return fail(CSKV_ERR_INVALID_ARG, "%s: scale must be non-negative and finite", fn);
+  if (norm_eps != norm_eps || norm_eps > 3.0e38f)
+    return fail(CSKV_ERR_INVALID_ARG, "%s: norm_eps must be finite (negative: no normalisation)", fn);
   if (W > 0 && !window) return fail(CSKV_ERR_INVALID_ARG, "%s: W=%d without a window", fn, W);
   if (B < 1 || H < 1 || N < 0 || W < 0 || k < 0 || ent_bstride < 0 || win_bstride < 0 ||
       win_rows < 0)
@@ -247,10 +249,11 @@ static int check_attend(const char* fn, const void* q, const void* entries, cons
 int cskv_sparse_attend(const void* q, const void* entries, const void* window, const int32_t* idx,
                        int64_t B, int32_t H, int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
                        int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
-                       int64_t win_pos0, float scale, const float* sink, cskv_dtype dt, void* out,
-                       float* lse, void* workspace, size_t ws_bytes, void* stream) {
+                       int64_t win_pos0, float scale, const float* sink, float norm_eps,
+                       cskv_dtype dt, void* out, float* lse, void* workspace, size_t ws_bytes,
+                       void* stream) {
   int st = check_attend("cskv_sparse_attend", q, entries, window, B, H, N, W, k, ent_bstride,
-                        win_bstride, win_rows, dt, out, scale);
+                        win_bstride, win_rows, dt, out, scale, norm_eps);
   if (st) return st;
   if (k > 0 && !idx) return fail(CSKV_ERR_INVALID_ARG, "cskv_sparse_attend: null idx");
   if (!q_pos && W > win_rows)
@@ -261,7 +264,7 @@ int cskv_sparse_attend(const void* q, const void* entries, const void* window, c
     return fail(CSKV_ERR_WORKSPACE, "cskv_sparse_attend: workspace %zu bytes, need %zu", ws_bytes,
                 need);
   cskv::AttendParams p{(int)dt, q, entries, window, idx, q_pos, B, N, ent_bstride, win_bstride,
-                       win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0, sink};
+                       win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0, sink, norm_eps};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), "cskv_sparse_attend");
 }
 
@@ -275,14 +278,14 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
                     const void* window, int64_t B, int32_t H, int64_t N, int32_t W, int32_t k,
                     int32_t m, int64_t ent_bstride, int64_t key_bstride, int64_t win_bstride,
                     int64_t win_rows, const int64_t* q_pos, int64_t win_pos0, float scale,
-                    const float* sink, float idx_scale, cskv_dtype dt, cskv_dtype idx_dt,
-                    void* out, float* lse,
-                    int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+                    const float* sink, float norm_eps, float idx_scale, cskv_dtype dt,
+                    cskv_dtype idx_dt, void* out, float* lse, int32_t* idx_out, void* workspace,
+                    size_t ws_bytes, void* stream) {
   int st = check_topk("cskv_csa_attend", q_idx, idx_keys, B, N, k, key_bstride, q_pos, m,
                       idx_scale, idx_dt, idx_out);
   if (st) return st;
   st = check_attend("cskv_csa_attend", q, entries, window, B, H, N, W, k, ent_bstride, win_bstride,
-                    win_rows, dt, out, scale);
+                    win_rows, dt, out, scale, norm_eps);
   if (st) return st;
   if (!q_pos && W > win_rows)
     return fail(CSKV_ERR_INVALID_ARG, "cskv_csa_attend: W=%d > window rows %lld", W,
@@ -296,7 +299,8 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
   hipError_t e = cskv::launch_topk(tp, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "cskv_csa_attend (top-k)");
   cskv::AttendParams ap{(int)dt, q, entries, window, idx_out, q_pos, B, N, ent_bstride,
-                        win_bstride, win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0, sink};
+                        win_bstride, win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0, sink,
+                        norm_eps};
   return hip_status(cskv::launch_attend(ap, (char*)workspace + topk_bytes, (hipStream_t)stream),
                     "cskv_csa_attend (attention)");
 }
@@ -308,17 +312,17 @@ size_t cskv_hca_workspace_size(int64_t B, int32_t H, int64_t N) {
 
 int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, int64_t N,
                     int64_t ent_bstride, const int64_t* q_pos, int32_t m, float scale,
-                    const float* sink, cskv_dtype dt, void* out, float* lse, void* workspace,
-                    size_t ws_bytes, void* stream) {
+                    const float* sink, float norm_eps, cskv_dtype dt, void* out, float* lse,
+                    void* workspace, size_t ws_bytes, void* stream) {
   int st = check_attend("cskv_hca_attend", q, entries, nullptr, B, H, N, 0, 0, ent_bstride, 0, 0,
-                        dt, out, scale);
+                        dt, out, scale, norm_eps);
   if (st) return st;
   if (q_pos && m < 1) return fail(CSKV_ERR_INVALID_ARG, "cskv_hca_attend: m=%d with q_pos", m);
   const size_t need = cskv::attend_partial_bytes((int)dt, B, H, N);
   if (need && (!workspace || ws_bytes < need || !aligned16(workspace)))
     return fail(CSKV_ERR_WORKSPACE, "cskv_hca_attend: workspace %zu bytes, need %zu", ws_bytes, need);
   cskv::AttendParams p{(int)dt, q, entries, nullptr, nullptr, q_pos, B, N, ent_bstride, 0, 0, 0,
-                       H, 0, 0, scale, out, lse, 1, q_pos ? m : 0, sink};
+                       H, 0, 0, scale, out, lse, 1, q_pos ? m : 0, sink, norm_eps};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), "cskv_hca_attend");
 }
 
@@ -355,13 +359,14 @@ int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t
                              const void* window, const int32_t* idx, int64_t B, int32_t H,
                              int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
                              int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
-                             int64_t win_pos0, float scale, const float* sink, void* out,
-                             float* lse, void* workspace, size_t ws_bytes, void* stream) {
+                             int64_t win_pos0, float scale, const float* sink, float norm_eps,
+                             void* out, float* lse, void* workspace, size_t ws_bytes,
+                             void* stream) {
   const char* fn = "cskv_sparse_attend_mxfp4";
   int st = check_mxfp4_entries(fn, ent_codes, ent_scales, ent_bstride);
   if (st) return st;
   st = check_attend(fn, q, ent_codes, window, B, H, N, W, k, ent_bstride * 576, win_bstride,
-                    win_rows, CSKV_BF16, out, scale);
+                    win_rows, CSKV_BF16, out, scale, norm_eps);
   if (st) return st;
   if (k > 0 && !idx) return fail(CSKV_ERR_INVALID_ARG, "%s: null idx", fn);
   if (!q_pos && W > win_rows)
@@ -376,19 +381,20 @@ int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t
                                       ent_bstride, rows, sel, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, fn);
   cskv::AttendParams p{1, q, rows, window, sel, q_pos, B, k, (int64_t)k * 576, win_bstride,
-                       win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0, sink};
+                       win_pos0, win_rows, H, W, k, scale, out, lse, 0, 0, sink, norm_eps};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), fn);
 }
 
 int cskv_hca_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
                           int64_t B, int32_t H, int64_t N, int64_t ent_bstride,
                           const int64_t* q_pos, int32_t m, float scale, const float* sink,
-                          void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+                          float norm_eps, void* out, float* lse, void* workspace, size_t ws_bytes,
+                          void* stream) {
   const char* fn = "cskv_hca_attend_mxfp4";
   int st = check_mxfp4_entries(fn, ent_codes, ent_scales, ent_bstride);
   if (st) return st;
   st = check_attend(fn, q, ent_codes, nullptr, B, H, N, 0, 0, ent_bstride * 576, 0, 0, CSKV_BF16,
-                    out, scale);
+                    out, scale, norm_eps);
   if (st) return st;
   if (q_pos && m < 1) return fail(CSKV_ERR_INVALID_ARG, "%s: m=%d with q_pos", fn, m);
   const bool per_seq = ent_bstride > 0;
@@ -401,7 +407,7 @@ int cskv_hca_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* e
                                       (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, fn);
   cskv::AttendParams p{1, q, rows, nullptr, nullptr, q_pos, B, N, per_seq ? N * 576 : 0, 0, 0, 0,
-                       H, 0, 0, scale, out, lse, 1, q_pos ? m : 0, sink};
+                       H, 0, 0, scale, out, lse, 1, q_pos ? m : 0, sink, norm_eps};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), fn);
 }
 

@@ -59,6 +59,7 @@ struct AttnArgs {
   int dense;                 // 1: all N entries, no window (HCA)
   int hm;                    // dense with q_pos: entry i visible iff (i+1)*hm <= q_pos[b]+1
   const float* sink;         // [H] attention-sink logits (nullable), applied where splits end
+  float norm_eps;            // query / entry normalisation epsilon (kernels instantiated for it)
   int B, H, W, k, nslots, slots_per_split, nsplit;
   float c;                   // scale * log2(e)
   void* out;                 // [B][H][512] when nsplit == 1
@@ -181,8 +182,11 @@ template <> __device__ __forceinline__ void store_out4<float>(float* p, float a,
 __device__ __forceinline__ int srow(int g, int i) { return 16 * (i >> 2) + 4 * g + (i & 3); }
 
 // HB = head blocks of 16 per wave.  With HB = 2 every K and V^T fragment read
-// from LDS feeds two MFMAs, which halves the LDS traffic per flop.
-template <class T, int HB>
+// from LDS feeds two MFMAs, which halves the LDS traffic per flop.  NORM:
+// queries and compressed entries normalised to unit root-mean-square (as in
+// the wide kernel below; the tile's row factors are computed from its
+// staged rows, two lanes a row).
+template <class T, int HB, bool NORM>
 __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a) {
   typedef AttnCfg<T> C;
   constexpr int MN = 16, NW = C::NW, NT = 64 * NW;
@@ -193,6 +197,7 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
   __shared__ __attribute__((aligned(16))) T Vt[kDv * C::VP];
   __shared__ int64_t row_off[2][kTile];
   __shared__ int row_ok[2][kTile];
+  __shared__ float row_g[kTile];                             // row factors (NORM)
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
@@ -220,6 +225,23 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
         Frag<T> z{};
         qf[j][ks] = z;
       }
+    }
+  }
+  // each head's softmax scale, with its query's factor (NORM): a head's 576
+  // dims are spread over the lanes col, col+16, col+32, col+48
+  float c_h[HB];
+#pragma unroll
+  for (int j = 0; j < HB; ++j) {
+    c_h[j] = a.c;
+    if constexpr (NORM) {
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ss = fmaf((float)qf[j][ks].v[t], (float)qf[j][ks].v[t], ss);
+      ss += shfl_xor(ss, 16);
+      ss += shfl_xor(ss, 32);
+      c_h[j] = a.c * __frsqrt_rn(ss * (1.f / kE) + a.norm_eps);
     }
   }
   f32x4 O[HB][NDB];
@@ -351,6 +373,25 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
       __syncthreads();
     }
     const int* tile_ok = row_ok[slot];
+    if constexpr (NORM) {
+      // row factor of row r: threads 2r and 2r+1 sum the squares of its two
+      // halves; 1 for raw window rows
+      for (int r0 = 0; r0 < kTile; r0 += NT / 2) {
+        const int r = r0 + threadIdx.x / 2, h = threadIdx.x & 1;
+        float ss = 0.f;
+        if (r < kTile) {
+          const T* rp = Ks + r * C::KP + h * (kE / 2);
+          for (int e = 0; e < kE / 2; ++e) ss = fmaf((float)rp[e], (float)rp[e], ss);
+        }
+        ss += __shfl_xor(ss, 1, 64);
+        const int sl = t0 + r;
+        // absent rows (zero-filled) take 1, so that their zero weight stays 0
+        if (r < kTile && h == 0)
+          row_g[r] = (tile_ok[r] && (a.dense || sl < a.k)) ? __frsqrt_rn(ss * (1.f / kE) + a.norm_eps)
+                                                           : 1.f;
+      }
+      __syncthreads();
+    }
     // logits S^T[row, head]: rows 0..15 in S0, 16..31 in S1
     f32x4 S0[HB], S1[HB];
 #pragma unroll
@@ -379,7 +420,8 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
       float tmax = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        sv[i] = tile_ok[srow(g, i)] ? sv[i] * a.c : -INFINITY;
+        const float c = NORM ? c_h[j] * row_g[srow(g, i)] : a.c;
+        sv[i] = tile_ok[srow(g, i)] ? sv[i] * c : -INFINITY;
         tmax = fmaxf(tmax, sv[i]);
       }
       tmax = fmaxf(tmax, shfl_xor(tmax, 16));
@@ -405,6 +447,11 @@ __global__ __launch_bounds__(64 * AttnCfg<T>::NW) void attend_kernel(AttnArgs a)
         psum += sv[i];
       }
       l_run[j] += psum;
+      if constexpr (NORM) {
+        // the weighted sum takes the normalised rows; the sum above does not
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sv[i] *= row_g[srow(g, i)];
+      }
       p_frag(pf[j], sv);
     }
 
@@ -562,6 +609,7 @@ struct WideShared {
   __attribute__((aligned(16))) char kbuf[kBufs][kTileBytes];
   const char* row_ptr[kRing][kTile];
   int flag[kWideWaves];
+  __attribute__((aligned(16))) float rho[2][kTile];          // row factors (normalisation)
 };
 
 // Lane offsets of the LDS read patterns.  Derived from the lane id where
@@ -605,6 +653,14 @@ __device__ __forceinline__ ValOffs val_offs() {
     }
   return o;
 }
+// acc + the sum of squares of the two bf16 in w.  w is taken by value: a
+// bit cast applied directly to an element of a vector register tuple reads
+// element 0 whatever the index.
+__device__ __forceinline__ float sumsq_bf16x2(uint32_t w, float acc) {
+  const hw_bf16x2_t x = __builtin_bit_cast(hw_bf16x2_t, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
+}
+
 // x in the lanes of m, y in the others (one v_cndmask on a scalar lane mask)
 __device__ __forceinline__ float sel_lanes(float x, float y, uint64_t m) {
   float r;
@@ -616,7 +672,17 @@ __device__ __forceinline__ float sel_lanes(float x, float y, uint64_t m) {
 // writing anything, when a logit left its head's reference band.  EXACT =
 // true: the split again, first for each head's exact maximum, then
 // accumulating against it, one tile at a time.
-template <bool EXACT>
+//
+// NORM: queries and compressed entries are normalised to unit root-mean-
+// square over their 576 dims ("DeepSeek V4 comprimeix el context", section
+// "CSA: buscar primer i atendre despres": normalisation of queries and
+// compressed entries stabilises the logits).  A head's factor 1/rms(q)
+// joins its softmax scale; a row's factor g = 1/rms(row) (1 for raw window
+// rows) multiplies its logit and, since the normalised entry is also the
+// value, its weight in the weighted sum, while the normaliser sums the
+// weights without it.  Each tile's g are computed from the tile in LDS by
+// all four waves (8 lanes a row) one tile ahead and kept in LDS.
+template <bool EXACT, bool NORM>
 __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   auto& kbuf = sh.kbuf;
   auto& row_ptr = sh.row_ptr;
@@ -645,6 +711,17 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     const bf16_t* qp = q + ((int64_t)b * a.H + (hok ? head : 0)) * kE + 8 * lh;
 #pragma unroll
     for (int s = 0; s < kQSteps; ++s) frag_load(qf[s], qp + 16 * s);
+  }
+  // the head's softmax scale (log2 units), with its query's factor
+  float c_head = c_log2;
+  if constexpr (NORM) {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < kQSteps; ++s)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) ss = sumsq_bf16x2(qf[s].v[w], ss);
+    ss += __shfl_xor(ss, 32, 64);                            // the head's other 288 dims
+    c_head = c_log2 * __frsqrt_rn(ss * (1.f / kE) + a.norm_eps);
   }
 
   f32x16 O[kVBlocks];
@@ -802,6 +879,39 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     }
   };
 
+  // Row factors of tile t (NORM) from its image kb in LDS, in 11 pieces:
+  // wave w takes rows 8w .. 8w+7, 8 lanes a row, each lane 9 chunks of 8
+  // elements (piece p loads chunk p and sums the squares of chunk p-1);
+  // piece 10 reduces over the row's lanes and writes g: 1 for window rows
+  // and for rows the tile's mask leaves out (whose zero weights must stay 0).
+  struct RhoSt { u32x4 x; float ss; unsigned base; };
+  auto rho_piece = [&](int p, const char* kb, int t, uint32_t mask, RhoSt& rs, float* dst) {
+    const int r = 8 * wave + (lane >> 3);
+    if (p == 0) {
+      rs.ss = 0.f;
+      rs.base = lds_offset(kb) + kRowBytes * r + 16 * ((lane & 7) ^ row_swz(r));
+    }
+    if (p >= 1 && p <= 9) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) rs.ss = sumsq_bf16x2(rs.x[w], rs.ss);
+    }
+    if (p <= 8) rs.x = *reinterpret_cast<const lds_u32x4_t*>((uintptr_t)(rs.base + 128 * p));
+    if (p == 10) {
+      float ss = rs.ss;
+      ss += __shfl_xor(ss, 1, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      ss += __shfl_xor(ss, 4, 64);
+      const int sl = s_begin + t * kTile + r;
+      const bool entry_row = ((mask >> r) & 1u) && (a.dense || sl < a.k);
+      if ((lane & 7) == 0) dst[r] = entry_row ? __frsqrt_rn(ss * (1.f / kE) + a.norm_eps) : 1.f;
+    }
+  };
+  auto rho_all = [&](const char* kb, int t, uint32_t mask, float* dst) {
+    RhoSt rs;
+#pragma unroll
+    for (int p = 0; p < 11; ++p) rho_piece(p, kb, t, mask, rs, dst);
+  };
+
   // Softmax of one tile in pieces (piece s runs after logit k-step s of the
   // next tile): masked, scaled logits; the tile maximum of the head; the
   // reference (check: the main pass, which sets references and flags logits
@@ -811,13 +921,26 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     float mx, m_use, psum;
     int flagged;
     Frag<bf16_t> P[2];
+    float rv[2][4], rr[2];                                   // row factors in use (NORM)
   };
   // mask: the tile's row mask (uniform).  Logits stay unscaled until the
   // exponent: c >= 0, so the head's maximum of c l is c times its maximum of
   // l, and exp2(c l - m) is one FMA and the exponential.  The weights' sum is
   // taken over their bf16 values, the ones the weighted sum uses.
-  auto soft_piece = [&](int s, const f32x16& S, uint32_t mask, Soft& st, bool check) {
+  // rt: the tile's row factors (NORM): register i of a lane belongs to row
+  // 8 (i / 4) + 4 (l / 32) + i % 4.
+  auto soft_piece = [&](int s, const f32x16& S, uint32_t mask, Soft& st, bool check,
+                        const float* rt) {
     if (s < 4) {
+      if constexpr (NORM) {
+        // factors of register group s, loaded one piece ahead
+        auto ld4 = [&](int gidx, float* d) {
+          const float4 v = *reinterpret_cast<const float4*>(rt + 8 * gidx + 4 * lh);
+          d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        };
+        if (s == 0) ld4(0, st.rv[0]);
+        if (s < 3) ld4(s + 1, st.rv[(s + 1) & 1]);
+      }
 #pragma unroll
       for (int i = 4 * s; i < 4 * s + 4; ++i) {
         // register i holds row 8 (i / 4) + 4 (l / 32) + i % 4: lanes 0..31
@@ -825,7 +948,8 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
         const int b = 8 * (i >> 2) + (i & 3);
         const uint64_t lo = (mask >> b) & 1u ? 0xffffffffull : 0ull;
         const uint64_t hi = (mask >> (b + 4)) & 1u ? 0xffffffff00000000ull : 0ull;
-        st.sv[i] = sel_lanes(S[i], ninf, lo | hi);
+        const float l = NORM ? S[i] * st.rv[s & 1][i & 3] : S[i];
+        st.sv[i] = sel_lanes(l, ninf, lo | hi);
       }
     } else if (s == 4) {
       float m = -INFINITY;
@@ -834,7 +958,7 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
       st.mx = m;
     } else if (s == 5) {
       const float m = max_xor32(st.mx);
-      st.mx = m == -INFINITY ? m : m * c_log2;               // the head's tile maximum of c l
+      st.mx = m == -INFINITY ? m : m * c_head;               // the head's tile maximum of c l
     } else if (s == 6) {
       if (check) {
         const bool first = (m_ref == -INFINITY);
@@ -845,21 +969,36 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
       st.psum = 0.f;
     } else if (s >= 7 && s < 23) {
       const int i = s - 7;
-      st.sv[i] = __builtin_amdgcn_exp2f(fmaf(st.sv[i], c_log2, st.m_use));
+      st.sv[i] = __builtin_amdgcn_exp2f(fmaf(st.sv[i], c_head, st.m_use));
+      if constexpr (NORM) {
+        if (!(i & 1)) {                                      // factors of rows i, i+1
+          const float2 v = *reinterpret_cast<const float2*>(rt + 8 * (i >> 2) + 4 * lh + (i & 3));
+          st.rr[0] = v.x;
+          st.rr[1] = v.y;
+        }
+      }
       if (i & 1) {
         const int k = i >> 1;                                // pair k: slot pair of P[k / 4]
-        const uint32_t pk = pack_bf16x2(st.sv[i - 1], st.sv[i]);
-        st.P[k >> 2].v[k & 3] = pk;
-        st.psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(hw_bf16x2_t, pk), ones_bf16x2,
-                                                  st.psum, false);
+        if constexpr (NORM) {
+          // the weighted sum takes the normalised rows (weight times the
+          // row factor); the normaliser sums the weights themselves
+          const uint32_t pk = pack_bf16x2(st.sv[i - 1] * st.rr[0], st.sv[i] * st.rr[1]);
+          st.P[k >> 2].v[k & 3] = pk;
+          st.psum += st.sv[i - 1] + st.sv[i];
+        } else {
+          const uint32_t pk = pack_bf16x2(st.sv[i - 1], st.sv[i]);
+          st.P[k >> 2].v[k & 3] = pk;
+          st.psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(hw_bf16x2_t, pk), ones_bf16x2,
+                                                    st.psum, false);
+        }
       }
     } else if (s == 23) {
       l_run += st.psum;
     }
   };
-  auto soft_all = [&](const f32x16& S, uint32_t mask, Soft& st, bool check) {
+  auto soft_all = [&](const f32x16& S, uint32_t mask, Soft& st, bool check, const float* rt) {
 #pragma unroll
-    for (int s = 0; s < 24; ++s) soft_piece(s, S, mask, st, check);
+    for (int s = 0; s < 24; ++s) soft_piece(s, S, mask, st, check, rt);
   };
   auto any_flag = [&]() {
     int any = 0;
@@ -893,7 +1032,12 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
       }
       static_assert(kCopies == 9, "the wait above counts one tile's copies");
       __syncthreads();                                       // tile 0 landed
-      qk(kbuf[0], S, [](int) {});
+      RhoSt rs0;
+      qk(kbuf[0], S, [&](int s) {
+        if constexpr (NORM) {
+          if (s < 11) rho_piece(s, kbuf[0], 0, mk[0], rs0, sh.rho[0]);
+        }
+      });
     }
     // A logit past its band sets the wave's flag; the split then runs to the
     // end and the block redoes it (the accumulated values are dropped).
@@ -919,18 +1063,26 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
         asm volatile("" : "+v"(S));
         f32x16 Sn;
         qk(kbuf[(t + 1) % kBufs], Sn, [&](int s) {
-          soft_piece(s, S, mtp, st, true);
+          soft_piece(s, S, mtp, st, true, sh.rho[t & 1]);
           if ((s & 3) == 0 && (s >> 2) < kCopies) rp = copy_row(t + 2, s >> 2);
           if ((s & 3) == 2 && (s >> 2) < kCopies) copy_issue(rp + copy_off(s >> 2), kn, s >> 2);
         });
         S = Sn;
       } else {
-        soft_all(S, mt, st, true);
+        soft_all(S, mt, st, true, sh.rho[t & 1]);
       }
+      // the row factors of tile t+1 (landed at this tile's barrier), read
+      // by its softmax in the next tile
+      RhoSt rs;
+      const bool next_rho = NORM && t + 1 < ntiles;
       pv(kbuf[t % kBufs], st.P, [&](int j) {
         if (j == 8) {
           mk[3] = resolve(t + 3, e_next);
           e_next = sel_load(t + 4);
+        }
+        if constexpr (NORM) {
+          if (next_rho && j >= 12 && j < 23)
+            rho_piece(j - 12, kbuf[(t + 1) % kBufs], t + 1, mk[1], rs, sh.rho[(t + 1) & 1]);
         }
       });
       mk[0] = mk[1];
@@ -938,7 +1090,10 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
       mk[2] = mk[3];
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (lane == 0) flag[wave] = __any(st.flagged);
+    // the wave's vote is taken with every lane active (inside the lane-0
+    // branch it would see lane 0's heads alone)
+    const bool wave_flagged = __any(st.flagged);
+    if (lane == 0) flag[wave] = wave_flagged;
     __syncthreads();
     const bool redo = ntiles > 0 && any_flag();
     if (redo) return true;
@@ -953,24 +1108,33 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
       __syncthreads();
       return m;
     };
+    // the row factors of the loaded tile (NORM), in sh.rho[0]
+    auto tile_rho = [&](int t, uint32_t mask) {
+      if constexpr (NORM) {
+        rho_all(kbuf[0], t, mask, sh.rho[0]);
+        __syncthreads();
+      }
+    };
     float mx = -INFINITY;
     for (int t = 0; t < ntiles; ++t) {
       const uint32_t mt = load_tile(t);
+      tile_rho(t, mt);
       f32x16 S;
       qk(kbuf[0], S, [](int) {});
       Soft st;
 #pragma unroll
-      for (int s = 0; s < 6; ++s) soft_piece(s, S, mt, st, false);
+      for (int s = 0; s < 6; ++s) soft_piece(s, S, mt, st, false, sh.rho[0]);
       mx = fmaxf(mx, st.mx);
     }
     m_ref = mx;
     for (int t = 0; t < ntiles; ++t) {
       const uint32_t mt = load_tile(t);
+      tile_rho(t, mt);
       f32x16 S;
       qk(kbuf[0], S, [](int) {});
       Soft st;
       st.flagged = 0;
-      soft_all(S, mt, st, false);
+      soft_all(S, mt, st, false, sh.rho[0]);
       pv(kbuf[0], st.P, [](int) {});
     }
   }
@@ -1008,19 +1172,21 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   return false;
 }
 
+template <bool NORM>
 __device__ __noinline__ void wide_split_exact(const AttnArgs& a, WideShared& sh) {
-  wide_split<true>(a, sh);
+  wide_split<true, NORM>(a, sh);
 }
 
+template <bool NORM>
 __global__ __launch_bounds__(64 * kWideWaves) void attend_wide_kernel(AttnArgs a) {
   __shared__ WideShared sh;
   __shared__ AttnArgs args;
-  if (wide_split<false>(a, sh)) {                            // rare
+  if (wide_split<false, NORM>(a, sh)) {                      // rare
     // the arguments reach the out-of-line pass through LDS, so that the
     // main pass never needs an addressable copy of them
     if (threadIdx.x == 0) args = a;
     __syncthreads();
-    wide_split_exact(args, sh);
+    wide_split_exact<NORM>(args, sh);
   }
 }
 
@@ -1151,10 +1317,15 @@ static hipError_t launch_attend_t(const AttendParams& p, void* ws, hipStream_t s
   a.lse_part = a.o_part + (size_t)p.B * p.H * S * kDv;
   const int hpb = attend_heads_per_block(p.dt, p.H);
   dim3 grid(S, (p.H + hpb - 1) / hpb, (unsigned)p.B);
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL(attend_wide_kernel, grid, dim3(64 * kWideWaves), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attend_kernel<T, 1>), grid, dim3(64 * C::NW), 0, stream, a);
+  const bool norm = p.norm_eps >= 0.f;
+  a.norm_eps = norm ? p.norm_eps : 0.f;
+  if constexpr (sizeof(T) == 2) {
+    if (norm) hipLaunchKernelGGL(attend_wide_kernel<true>, grid, dim3(64 * kWideWaves), 0, stream, a);
+    else hipLaunchKernelGGL(attend_wide_kernel<false>, grid, dim3(64 * kWideWaves), 0, stream, a);
+  } else {
+    if (norm) hipLaunchKernelGGL((attend_kernel<T, 1, true>), grid, dim3(64 * C::NW), 0, stream, a);
+    else hipLaunchKernelGGL((attend_kernel<T, 1, false>), grid, dim3(64 * C::NW), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t BH = p.B * p.H;

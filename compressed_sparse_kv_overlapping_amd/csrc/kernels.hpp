@@ -31,6 +31,7 @@ struct AttendParams {
   int dense;                 // 1: rows = all N entries, no window
   int hm;                    // dense with q_pos: entry i visible iff (i+1)*hm <= q_pos[b]+1
   const float* sink;         // [H] attention-sink logits, or NULL
+  float norm_eps = -1.f;     // >= 0: queries and compressed entries normalised (unit RMS, this epsilon)
 };
 
 int attend_splits(int dt, int64_t B, int H, int64_t nslots);

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define CSKV_VERSION 10400 /* major*10000 + minor*100: 1.4 (MXFP4 indexer and entries) */
+#define CSKV_VERSION 10500 /* major*10000 + minor*100: 1.5 (query / entry normalisation) */
 
 typedef enum cskv_dtype {
   CSKV_F32 = 0,       /* IEEE binary32 */
@@ -222,18 +222,26 @@ int cskv_index_topk_mxfp4(const void* q_codes, const uint8_t* q_scales, const vo
  * logits ("DeepSeek V4 comprimeix el context", section "CSA: buscar primer i
  * atendre despres": learned logits that absorb attention mass), in the
  * units of l; a query with no rows then gets out = 0 and lse = sink[h].
+ * norm_eps >= 0 normalises the queries and the compressed entries (the same
+ * section: their normalisation stabilises the logits): q[b][h] and every
+ * selected entry row are divided by sqrt(mean over their 576 dims of x^2 +
+ * norm_eps) before the formulas above, so a normalised entry is both the
+ * key and the value; raw window rows are used as given.  norm_eps < 0: no
+ * normalisation.
  *   idx [B][k] int32 (-1 = no entry; any order); q, entries, window, out in dt
  *   (F32 or BF16); workspace: cskv_attend_workspace_size(...) bytes.
  * scale must be >= 0 and finite (0 gives uniform weights over the rows).
  * Errors: INVALID_ARG (null pointers, sizes < 0, window positions outside the
- * buffer, scale < 0 or not finite); UNSUPPORTED (dt not F32/BF16); WORKSPACE.
+ * buffer, scale < 0 or not finite, norm_eps NaN or infinite); UNSUPPORTED (dt
+ * not F32/BF16); WORKSPACE.
  */
 size_t cskv_attend_workspace_size(int64_t B, int32_t H, int64_t rows_per_query);
 int cskv_sparse_attend(const void* q, const void* entries, const void* window, const int32_t* idx,
                        int64_t B, int32_t H, int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
                        int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
-                       int64_t win_pos0, float scale, const float* sink, cskv_dtype dt, void* out,
-                       float* lse, void* workspace, size_t ws_bytes, void* stream);
+                       int64_t win_pos0, float scale, const float* sink, float norm_eps,
+                       cskv_dtype dt, void* out, float* lse, void* workspace, size_t ws_bytes,
+                       void* stream);
 
 /*
  * CSA: cskv_index_topk followed by cskv_sparse_attend, on one stream, with
@@ -245,9 +253,9 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
                     const void* window, int64_t B, int32_t H, int64_t N, int32_t W, int32_t k,
                     int32_t m, int64_t ent_bstride, int64_t key_bstride, int64_t win_bstride,
                     int64_t win_rows, const int64_t* q_pos, int64_t win_pos0, float scale,
-                    const float* sink, float idx_scale, cskv_dtype dt, cskv_dtype idx_dt,
-                    void* out, float* lse,
-                    int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream);
+                    const float* sink, float norm_eps, float idx_scale, cskv_dtype dt,
+                    cskv_dtype idx_dt, void* out, float* lse, int32_t* idx_out, void* workspace,
+                    size_t ws_bytes, void* stream);
 
 /*
  * HCA ("Frontier Techniques", 2.2; "DeepSeek V4 comprimeix el context",
@@ -259,13 +267,14 @@ int cskv_csa_attend(const void* q, const void* q_idx, const void* entries, const
  *   (i+1)*m <= q_pos[b] + 1, the causal rule of the indexer (an entry
  *   exists once its block of m tokens is complete).  A query that sees no
  *   entry gets a zero output and lse = -inf.
+ * norm_eps as in cskv_sparse_attend (every row is a compressed entry).
  * Errors as cskv_sparse_attend, plus INVALID_ARG for m < 1 with q_pos.
  */
 size_t cskv_hca_workspace_size(int64_t B, int32_t H, int64_t N);
 int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, int64_t N,
                     int64_t ent_bstride, const int64_t* q_pos, int32_t m, float scale,
-                    const float* sink, cskv_dtype dt, void* out, float* lse, void* workspace,
-                    size_t ws_bytes, void* stream);
+                    const float* sink, float norm_eps, cskv_dtype dt, void* out, float* lse,
+                    void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * CSA sparse attention and HCA dense attention over MXFP4 entries
@@ -294,12 +303,14 @@ int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t
                              const void* window, const int32_t* idx, int64_t B, int32_t H,
                              int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
                              int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
-                             int64_t win_pos0, float scale, const float* sink, void* out,
-                             float* lse, void* workspace, size_t ws_bytes, void* stream);
+                             int64_t win_pos0, float scale, const float* sink, float norm_eps,
+                             void* out, float* lse, void* workspace, size_t ws_bytes,
+                             void* stream);
 int cskv_hca_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
                           int64_t B, int32_t H, int64_t N, int64_t ent_bstride,
                           const int64_t* q_pos, int32_t m, float scale, const float* sink,
-                          void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
+                          float norm_eps, void* out, float* lse, void* workspace, size_t ws_bytes,
+                          void* stream);
 
 /*
  * Merge of split-KV partial results: for each (b, h) with S partial results

@@ -35,7 +35,7 @@ def test_header_functions_are_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.cskv_version() == 10400
+    assert lib.cskv_version() == 10500
     assert lib.cskv_status_string(OK) == b"ok"
     for code in (INVALID, UNSUPPORTED, WORKSPACE, -4):
         assert lib.cskv_status_string(code) not in (b"ok", b"unknown status")
@@ -125,14 +125,15 @@ def test_attend_mxfp4_errors(lib):
     ws = lib.cskv_attend_workspace_size(8, 128, 1152)
 
     def sp(q=P, c=P, sc=P, w=P, idx=P, B=8, H=128, N=16384, W=128, k=1024, eb=0, wr=128, wsb=ws):
-        return s(q, c, sc, w, idx, B, H, N, W, k, eb, 0, wr, NULL, 0, 1.0, NULL, P, P, P, wsb, NULL)
+        return s(q, c, sc, w, idx, B, H, N, W, k, eb, 0, wr, NULL, 0, 1.0, NULL, -1.0, P, P, P, wsb,
+                 NULL)
     assert sp(sc=NULL) == INVALID and sp(c=NULL) == INVALID and sp(q=NULL) == INVALID
     assert sp(idx=NULL) == INVALID and sp(W=200) == INVALID and sp(eb=-1) == INVALID
     assert sp(B=0) == INVALID and sp(wsb=16) == WORKSPACE
     hws = lib.cskv_hca_workspace_size(8, 128, 8192)
 
     def hc(c=P, sc=P, B=8, N=8192, eb=0, qp=NULL, m=0, wsb=hws):
-        return h(P, c, sc, B, 128, N, eb, qp, m, 1.0, NULL, P, P, P, wsb, NULL)
+        return h(P, c, sc, B, 128, N, eb, qp, m, 1.0, NULL, -1.0, P, P, P, wsb, NULL)
     assert hc(sc=NULL) == INVALID and hc(c=NULL) == INVALID and hc(eb=-3) == INVALID
     assert hc(qp=P, m=0) == INVALID and hc(wsb=16) == WORKSPACE
 
@@ -142,7 +143,7 @@ def test_attend_errors(lib):
     ws = lib.cskv_attend_workspace_size(8, 128, 1152)
     assert ws > 0
     args = dict(q=P, e=P, w=P, idx=P, B=8, H=128, N=16384, W=128, k=1024, eb=0, wb=0, wr=128,
-                qp=NULL, wp0=0, sc=1.0, sink=NULL, dt=1, out=P, lse=P, ws=P, wsb=ws, st=NULL)
+                qp=NULL, wp0=0, sc=1.0, sink=NULL, ne=-1.0, dt=1, out=P, lse=P, ws=P, wsb=ws, st=NULL)
 
     def call(**kw):
         a = dict(args, **kw)
@@ -156,12 +157,15 @@ def test_attend_errors(lib):
     assert call(sc=-0.5) == INVALID                                   # negative scale
     assert call(sc=float("inf")) == INVALID
     assert call(sc=float("nan")) == INVALID
+    assert call(ne=float("nan")) == INVALID                           # normalisation epsilon
+    assert call(ne=float("inf")) == INVALID
     h = lib.cskv_hca_attend
     hws = lib.cskv_hca_workspace_size(32, 128, 8192)
-    assert h(P, P, 32, 128, 8192, 0, NULL, 0, 1.0, NULL, 1, P, P, NULL, hws, NULL) == WORKSPACE
-    assert h(P, P, 32, 128, 8192, 0, NULL, 0, 1.0, NULL, 2, P, P, P, hws, NULL) == UNSUPPORTED
-    assert h(P, P, 32, 128, 8192, 0, NULL, 0, -1.0, NULL, 1, P, P, P, hws, NULL) == INVALID
-    assert h(P, P, 32, 128, 8192, 0, P, 0, 1.0, NULL, 1, P, P, P, hws, NULL) == INVALID  # m < 1
+    assert h(P, P, 32, 128, 8192, 0, NULL, 0, 1.0, NULL, -1.0, 1, P, P, NULL, hws, NULL) == WORKSPACE
+    assert h(P, P, 32, 128, 8192, 0, NULL, 0, 1.0, NULL, -1.0, 2, P, P, P, hws, NULL) == UNSUPPORTED
+    assert h(P, P, 32, 128, 8192, 0, NULL, 0, -1.0, NULL, -1.0, 1, P, P, P, hws, NULL) == INVALID
+    assert h(P, P, 32, 128, 8192, 0, P, 0, 1.0, NULL, -1.0, 1, P, P, P, hws, NULL) == INVALID  # m < 1
+    assert h(P, P, 32, 128, 8192, 0, NULL, 0, 1.0, NULL, float("nan"), 1, P, P, P, hws, NULL) == INVALID
     m = lib.cskv_merge
     assert m(P, P, 2, 4, 0, NULL, P, P, 1, NULL) == INVALID
     assert m(P, P, 2, 4, 3, NULL, P, P, 2, NULL) == UNSUPPORTED
@@ -171,8 +175,8 @@ def test_csa_workspace_covers_parts(lib):
     B, H, N, W, k = 32, 128, 262144, 128, 1024
     total = lib.cskv_csa_workspace_size(B, H, N, W, k)
     assert total >= lib.cskv_index_topk_workspace_size(B, N, k) + lib.cskv_attend_workspace_size(B, H, k + W)
-    assert lib.cskv_csa_attend(P, P, P, P, P, B, H, N, W, k, 4, 0, 0, 0, W, NULL, 0, 1.0, NULL, 1.0,
-                               1, 1, P, P, P, P, total - 1, NULL) == WORKSPACE
+    assert lib.cskv_csa_attend(P, P, P, P, P, B, H, N, W, k, 4, 0, 0, 0, W, NULL, 0, 1.0, NULL, -1.0,
+                               1.0, 1, 1, P, P, P, P, total - 1, NULL) == WORKSPACE
 
 
 def test_binding_refuses_missing_library(monkeypatch, tmp_path):

@@ -164,6 +164,38 @@ def test_logits_past_reference_band(N):
     _check_attn(out, lse, ro, rl, dt)
 
 
+@pytest.mark.parametrize("norm", [False, True])
+def test_logits_past_reference_band_in_some_heads(norm):
+    """Only the odd heads of each wave have logits past the band a split
+    accumulates against (rows of the later tiles along their queries); head
+    0 of every wave stays inside it.  The redo must be triggered by any
+    head's excess, not by head 0's alone; HCA and sparse attention must match
+    the oracle, with and without the query / entry normalisation."""
+    dt, B, H, N = wl.DT_BF16, 2, 128, 600
+    rng = np.random.default_rng(17)
+    qf = 0.05 * rng.standard_normal((B, H, E))
+    qf[:, 1::2] = 0.5 + 0.01 * rng.standard_normal((B, H // 2, E))
+    ef = 0.1 * rng.standard_normal((N, E))
+    big = np.arange(32 + 5, N, 32)
+    ef[big] = 0.5 + 0.01 * rng.standard_normal((len(big), E))
+    q, ent = wl.encode(qf, dt).raw, wl.encode(ef, dt).raw
+    eps = 1e-6 if norm else None
+    scale = 0.3 if norm else 1.0
+    out, lse = _cskv().hca_attend(dev(q), dev(ent), scale=scale, norm_eps=eps)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q, ent, dt, scale=scale, norm_eps=eps)
+    _check_attn(out, lse, ro, rl, dt)
+    W = 128
+    win = wl.encode(0.1 * rng.standard_normal((W, E)), dt).raw
+    idx = np.tile(np.arange(N, dtype=np.int32), (B, 1))
+    idx[1, 40:100] = -1
+    out, lse = _cskv().sparse_attend(dev(q), dev(ent), dev(win), torch.from_numpy(idx).cuda(),
+                                     scale=scale, norm_eps=eps)
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend(q, ent, win, dt, idx, scale=scale, norm_eps=eps)
+    _check_attn(out, lse, ro, rl, dt)
+
+
 @pytest.mark.parametrize("dt", [wl.DT_F32, wl.DT_BF16])
 def test_attention_sink(dt):
     """Per-head attention-sink logits: split paths (the merge adds the sink)
@@ -529,4 +561,124 @@ def test_attend_mxfp4_per_sequence_hca_and_window_only():
     torch.cuda.synchronize()
     # the oracle takes k >= 1: one empty slot (-1) is the same window-only attention
     ro, rl = oracle.csa_attend_mxfp4(q, codes[0], scales[0], win, np.full((B, 1), -1, np.int32))
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+
+
+# ------------------------------------- query / entry normalisation (norm_eps)
+
+def _scaled_rows(cfg_id, seed, tid, shape, dt, lo, hi):
+    """~N(0,1) rows times a per-row factor in [lo, hi): the normalisation
+    factors then differ widely between rows."""
+    v = wl.normal(cfg_id, seed, tid, shape)
+    f = np.random.default_rng(seed * 7 + tid).uniform(lo, hi, shape[:-1] + (1,))
+    return wl.encode((v * f).astype(np.float32), dt).raw
+
+
+@pytest.mark.parametrize("dt", [wl.DT_F32, wl.DT_BF16])
+def test_normalised_attention(dt):
+    """Queries and compressed entries normalised to unit RMS: sparse attention
+    over a selection with -1 holes plus raw window rows (not normalised),
+    with and without a sink; HCA at decode (several splits), at a prefill
+    chunk and over per-sequence entries."""
+    cskv = _cskv()
+    eps = 1e-6
+    H = 128 if dt == wl.DT_BF16 else 16
+    B, N, W, k = 3, 3000, 128, 300
+    q = _scaled_rows(110, 0, 1, (B, H, E), dt, 0.1, 4.0)
+    ent = _scaled_rows(110, 0, 2, (N, E), dt, 0.05, 20.0)
+    win = _rand(110, 0, 3, (W, E), dt)
+    rng = np.random.default_rng(1)
+    idx = np.stack([rng.choice(N, k, replace=False) for _ in range(B)]).astype(np.int32)
+    idx[1, 7:90] = -1
+    sink_h = rng.uniform(-1.0, 3.0, H)
+    for sk in (None, sink_h):
+        st = None if sk is None else torch.from_numpy(sk.astype(np.float32)).cuda()
+        out, lse = cskv.sparse_attend(dev(q), dev(ent), dev(win), torch.from_numpy(idx).cuda(),
+                                      scale=1 / 24, norm_eps=eps, sink=st)
+        torch.cuda.synchronize()
+        ro, rl = oracle.csa_attend(q, ent, win, dt, idx, scale=1 / 24, norm_eps=eps, sink=sk)
+        _check_attn(out, lse, ro, rl, dt)
+    out, lse = cskv.hca_attend(dev(q), dev(ent), scale=1 / 24, norm_eps=eps)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q, ent, dt, scale=1 / 24, norm_eps=eps)
+    _check_attn(out, lse, ro, rl, dt)
+    m = 128
+    pos = np.array([0, 127, 1000, 40 * m + 3, N * m + 5], np.int64)
+    q5 = _scaled_rows(110, 0, 4, (5, H, E), dt, 0.1, 4.0)
+    out, lse = cskv.hca_attend(dev(q5), dev(ent[:600]), scale=1 / 24, norm_eps=eps,
+                               q_pos=torch.from_numpy(pos).cuda(), m=m)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q5, ent[:600], dt, scale=1 / 24, norm_eps=eps, q_pos=pos, m=m)
+    _check_attn(out[1:], lse[1:], ro[1:], rl[1:], dt)
+    assert (host_f64(out)[0] == 0).all()
+    eps2 = _scaled_rows(110, 0, 5, (B, 500, E), dt, 0.05, 20.0)
+    out, lse = cskv.hca_attend(dev(q), dev(eps2), scale=1 / 24, norm_eps=0.0, per_seq=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q, eps2, dt, scale=1 / 24, norm_eps=0.0, per_seq=True)
+    _check_attn(out, lse, ro, rl, dt)
+
+
+@pytest.mark.parametrize("N", [300, 8192])
+def test_normalised_attention_past_reference_band(N):
+    """Normalised rows of tile 0 nearly orthogonal to the query, and one row
+    in every later tile along it: their logits (scale 0.3 x up to 576) are far
+    past the band a split accumulates against, so splits redo their rows
+    exactly; HCA and sparse attention must still match the oracle."""
+    dt, B, H = wl.DT_BF16, 2, 128
+    rng = np.random.default_rng(N + 1)
+    qf = 0.5 + 0.01 * rng.standard_normal((B, H, E))
+    ef = 0.1 * rng.standard_normal((N, E))
+    big = np.arange(32 + 5, N, 32)
+    ef[big] = (0.5 + 0.01 * rng.standard_normal((len(big), E))) * rng.uniform(0.1, 10, (len(big), 1))
+    q, ent = wl.encode(qf, dt).raw, wl.encode(ef, dt).raw
+    out, lse = _cskv().hca_attend(dev(q), dev(ent), scale=0.3, norm_eps=1e-6)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend(q, ent, dt, scale=0.3, norm_eps=1e-6)
+    _check_attn(out, lse, ro, rl, dt)
+    W = 128
+    win = wl.encode(0.1 * rng.standard_normal((W, E)), dt).raw
+    k = min(N, 1024)
+    idx = np.tile(np.arange(k, dtype=np.int32), (B, 1))
+    out, lse = _cskv().sparse_attend(dev(q), dev(ent), dev(win), torch.from_numpy(idx).cuda(),
+                                     scale=0.3, norm_eps=1e-6)
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend(q, ent, win, dt, idx, scale=0.3, norm_eps=1e-6)
+    _check_attn(out, lse, ro, rl, dt)
+
+
+def test_normalised_csa_decode_workload():
+    """The fused CSA call with normalisation on the 16,384-entry decode
+    workload (8 queries x 128 heads, top-1024 + 128 window rows): every
+    query's attention over the GPU's own selection."""
+    cfg = wl.CONFIGS["csa_decode"]
+    inp = wl.make_inputs(cfg, seed=0)
+    out, lse, idx = _cskv().csa_attend(dev(inp["q"]), dev(inp["qI"]), dev(inp["entries"]),
+                                       dev(inp["kI"]), dev(inp["window"]), cfg.k, scale=1 / 24,
+                                       norm_eps=1e-6)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    s, v = oracle.index_scores(inp["qI"].raw, inp["kI"].raw, cfg.idx_dt)
+    check_selection(idx, s, v, cfg.k)
+    ro, rl = oracle.csa_attend(inp["q"].raw, inp["entries"].raw, inp["window"].raw, cfg.dt, idx,
+                               scale=1 / 24, norm_eps=1e-6)
+    _check_attn(out, lse, ro, rl, cfg.dt)
+
+
+def test_normalised_attention_mxfp4_entries():
+    """Normalisation over MXFP4 entries (decoded exactly, then normalised):
+    sparse attention with bf16 window rows, and HCA."""
+    B, H, N, W, k = 2, 128, 900, 128, 200
+    q = _rand(111, 0, 1, (B, H, E), wl.DT_BF16, 1 / 24)
+    codes, scales = _mx_entries(111, 0, (N, E))
+    win = _rand(111, 0, 3, (W, E), wl.DT_BF16)
+    rng = np.random.default_rng(2)
+    idx = np.stack([np.sort(rng.choice(N, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    out, lse = _cskv().sparse_attend_mxfp4(dev(q), _up(codes), _up(scales), dev(win), _up(idx),
+                                           scale=1 / 24, norm_eps=1e-6)
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend_mxfp4(q, codes, scales, win, idx, scale=1 / 24, norm_eps=1e-6)
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+    out, lse = _cskv().hca_attend_mxfp4(dev(q), _up(codes), _up(scales), scale=1 / 24, norm_eps=1e-6)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend_mxfp4(q, codes, scales, scale=1 / 24, norm_eps=1e-6)
     _check_attn(out, lse, ro, rl, wl.DT_BF16)
