@@ -50,6 +50,7 @@ def lib():
         L.cskv_oracle_e8m0_value.argtypes = [ctypes.c_uint8]
         L.cskv_oracle_e8m0_value.restype = dbl
         L.cskv_oracle_mxfp4_decode.argtypes = [vp, vp, i64, i32, vp]
+        L.cskv_oracle_mxfp8_decode.argtypes = [vp, vp, i64, i32, vp]
         L.cskv_oracle_num_entries.argtypes = [i64, i32]
         L.cskv_oracle_num_entries.restype = i64
         L.cskv_oracle_compress.argtypes = [vp, vp, i32, vp, i64, i64, i32, vp, i64, vp]
@@ -157,6 +158,22 @@ def mxfp4_decode(codes, scales):
     return out
 
 
+def mxfp8_decode(codes, scales):
+    """MXFP8 (E4M3) rows of C elements (C a multiple of 32) -> float64
+    [..., C] (codes uint8 [..., C], scales uint8 [..., C/32])."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    lead = codes.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    cols = codes.shape[-1]
+    if cols % 32 or scales.shape != lead + (cols // 32,):
+        raise ValueError("mxfp8 rows: codes [..., C] and scales [..., C/32], C % 32 == 0")
+    out = np.empty(lead + (cols,), dtype=np.float64)
+    _check(lib().cskv_oracle_mxfp8_decode(_p(codes), _p(scales), rows, cols, _p(out)),
+           "mxfp8_decode")
+    return out
+
+
 def index_scores_mxfp4(q_codes, q_scales, k_codes, k_scales, scale=1.0, q_pos=None, m=4,
                        per_seq=False):
     """Indexer scores of MXFP4 queries and keys: the rows are decoded exactly,
@@ -208,6 +225,18 @@ def csa_attend_mxfp4(q, ent_codes, ent_scales, window, idx, **kw):
     attended in fp64."""
     win = None if window is None else decode(window, BF16)
     return csa_attend(decode(q, BF16), mxfp4_decode(ent_codes, ent_scales), win, F64, idx, **kw)
+
+
+def csa_attend_mxfp8(q, ent_codes, ent_scales, window, idx, **kw):
+    """csa_attend with MXFP8 entries (codes [.., N, 576], scales [.., N, 18])
+    and bf16 queries and window rows, every input decoded exactly."""
+    win = None if window is None else decode(window, BF16)
+    return csa_attend(decode(q, BF16), mxfp8_decode(ent_codes, ent_scales), win, F64, idx, **kw)
+
+
+def hca_attend_mxfp8(q, ent_codes, ent_scales, **kw):
+    """hca_attend with MXFP8 entries and bf16 queries."""
+    return hca_attend(decode(q, BF16), mxfp8_decode(ent_codes, ent_scales), F64, **kw)
 
 
 def hca_attend_mxfp4(q, ent_codes, ent_scales, **kw):

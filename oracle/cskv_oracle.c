@@ -44,7 +44,9 @@
  *  - MXFP4 (named by [P1] for the indexer's QK path and, as FP4 with block
  *    scales, by "Compressed attention - CSA / HCA" section 3 for the V4.1 KV
  *    cache): the OCP Microscaling v1.0 format, element 2j in the low nibble
- *    of byte j, one E8M0 scale per 32 elements in a separate array.
+ *    of byte j, one E8M0 scale per 32 elements in a separate array;
+ *  - FP8 entry rows with block scales: the OCP MXFP8 format with E4M3
+ *    elements, one byte an element, one E8M0 scale per 32 elements.
  *
  * All functions return 0 on success and a negative value on bad arguments.
  */
@@ -113,6 +115,22 @@ int cskv_oracle_mxfp4_decode(const uint8_t* codes, const uint8_t* scales, int64_
       out[r * cols + i] =
           cskv_oracle_e8m0_value(scales[r * (cols / 32) + i / 32]) * cskv_oracle_e2m1_value(code);
     }
+  return 0;
+}
+
+/* ---- MXFP8 entry rows ("Compressed attention - CSA / HCA", section 3: the
+ * compressed KV cache is kept in low-bit floating point with block scales).
+ * FP8 with block scales is read as the OCP Microscaling v1.0 MXFP8 format
+ * with E4M3 elements: a block of 32 E4M3 elements shares one E8M0 scale,
+ * and element i of a block is worth scale * E4M3 value.  Codes [rows][cols]
+ * (one byte an element), scales [rows][cols/32].  out [rows][cols]. */
+int cskv_oracle_mxfp8_decode(const uint8_t* codes, const uint8_t* scales, int64_t rows, int cols,
+                             double* out) {
+  if (!codes || !scales || !out || rows < 0 || cols <= 0 || cols % 32) return -1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int i = 0; i < cols; ++i)
+      out[r * cols + i] = cskv_oracle_e8m0_value(scales[r * (cols / 32) + i / 32]) *
+                          cskv_oracle_e4m3_value(codes[r * cols + i]);
   return 0;
 }
 

@@ -731,3 +731,69 @@ def test_norm_scale_invariance():
     h1 = oracle.hca_attend(q, ent, wl.DT_BF16, scale=0.04, norm_eps=0.0)
     h2 = oracle.hca_attend(q2, e2, wl.DT_BF16, scale=0.04, norm_eps=0.0)
     np.testing.assert_allclose(h1[0], h2[0], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------ MXFP8 (E4M3) entry rows
+# (FP8 storage of the compressed entries with block scales, "Compressed
+# attention - CSA / HCA", section 3; read as OCP MXFP8: 32 E4M3 elements per
+# E8M0 scale, one byte an element.)
+
+def test_mxfp8_element_placement_in_entry_rows():
+    """Element i of a 576-element row is code byte i and takes the scale of
+    block i // 32: one non-zero code lands at i with that block's power of
+    two times its E4M3 value (from the OCP table pinned above), nowhere else."""
+    rng = np.random.default_rng(21)
+    xs = rng.integers(100, 150, 18).astype(np.uint8)
+    for i in list(range(0, 576, 11)) + [31, 32, 63, 64, 543, 544, 575]:
+        for code in (0x38, 0xC5, 0x01, 0x7E):                  # 1.0, -3.25, 2^-9, 448
+            codes = np.zeros((1, 576), np.uint8)
+            codes[0, i] = code
+            row = oracle.mxfp8_decode(codes, xs[None])[0]
+            want = np.zeros(576)
+            want[i] = oracle.e4m3_value(code) * 2.0 ** (int(xs[i // 32]) - 127)
+            assert np.array_equal(row, want), (i, code)
+    assert oracle.e4m3_value(0x38) == 1.0 and oracle.e4m3_value(0x7E) == 448.0
+
+
+def test_mxfp8_encoder_roundtrip_and_nearest():
+    """Values on a block's grid (an E4M3 value times the block's power of two)
+    decode back exactly; other values decode to the nearest grid point."""
+    rng = np.random.default_rng(22)
+    grid = np.array([oracle.e4m3_value(c) for c in range(127)])
+    ex = rng.integers(-20, 20, (6, 18))
+    vals = rng.choice(grid, (6, 18, 32)) * rng.choice([-1, 1], (6, 18, 32))
+    vals[:, :, 0] = 448.0                                    # fixes each block's exponent at 8
+    vals = (vals * np.ldexp(1.0, ex)[..., None]).reshape(6, 576)
+    codes, scales = wl.mxfp8_encode(vals)
+    assert np.array_equal(oracle.mxfp8_decode(codes, scales), vals)
+    v = rng.standard_normal((4, 576)) * 3
+    codes, scales = wl.mxfp8_encode(v)
+    dec = oracle.mxfp8_decode(codes, scales)
+    s = np.ldexp(1.0, scales.astype(int) - 127).repeat(32, axis=1)
+    allv = np.concatenate([-grid[::-1], grid])
+    nearest = np.abs((v / s)[..., None] - allv).min(axis=-1) * s
+    np.testing.assert_allclose(np.abs(dec - v), nearest, rtol=0, atol=1e-12)
+
+
+def test_mxfp8_entries_attend_like_bf16_rows():
+    """MXFP8 entries holding bf16-exact values attend exactly like those
+    values stored as bf16 (CSA over a selection with the window, and HCA)."""
+    rng = np.random.default_rng(23)
+    B, H, N, W, k = 2, 3, 40, 5, 7
+    q = wl.bf16_bits(rng.standard_normal((B, H, 576)).astype(np.float32) / 24)
+    grid = np.array([oracle.e4m3_value(c) for c in range(0, 127, 3)])
+    vals = rng.choice(grid, (N, 576)) * rng.choice([-1, 1], (N, 576))
+    vals[:, ::32] = 448.0                 # each block's maximum: its scale is 2^0 (then x 2^-6)
+    vals *= 2.0 ** -6
+    ent = wl.bf16_bits(vals.astype(np.float32))
+    assert np.array_equal(oracle.decode(ent, BF16), vals)
+    codes, scales = wl.mxfp8_encode(vals)
+    assert np.array_equal(oracle.mxfp8_decode(codes, scales), vals)
+    win = wl.bf16_bits(rng.standard_normal((W, 576)).astype(np.float32))
+    idx = np.sort(rng.choice(N, (B, k)), axis=1).astype(np.int32)
+    o1, l1 = oracle.csa_attend(q, ent, win, BF16, idx)
+    o2, l2 = oracle.csa_attend_mxfp8(q, codes, scales, win, idx)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    h1, hl1 = oracle.hca_attend(q, ent, BF16)
+    h2, hl2 = oracle.hca_attend_mxfp8(q, codes, scales)
+    assert np.array_equal(h1, h2) and np.array_equal(hl1, hl2)

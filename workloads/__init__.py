@@ -13,13 +13,13 @@ drawn in fp32.  Large tensors are drawn in fixed-size chunks, chunk ``c``
 from ``SeedSequence([config_id, seed, tensor_id, c])``, so that they can be
 generated in parallel and any row range can be regenerated on its own.
 """
-from .formats import (bf16_bits, bf16_bits_to_f32, e4m3_encode, e4m3_scale, mxfp4_encode,
+from .formats import (bf16_bits, bf16_bits_to_f32, e4m3_encode, e4m3_scale, mxfp4_encode, mxfp8_encode,
                       DT_F32, DT_BF16, DT_E4M3, dtype_name)
 from .gen import normal, Tensor, encode
 from .configs import CONFIGS, Config, make_inputs
 
 __all__ = [
-    "bf16_bits", "bf16_bits_to_f32", "e4m3_encode", "e4m3_scale",
+    "bf16_bits", "bf16_bits_to_f32", "e4m3_encode", "e4m3_scale", "mxfp4_encode", "mxfp8_encode",
     "DT_F32", "DT_BF16", "DT_E4M3", "dtype_name",
     "normal", "Tensor", "encode", "CONFIGS", "Config", "make_inputs",
 ]

@@ -1,5 +1,6 @@
-"""Storage formats of the inputs: bf16 (round to nearest even), OCP fp8 e4m3
-and OCP MXFP4 (32-element blocks of FP4 E2M1 sharing an E8M0 scale).
+"""Storage formats of the inputs: bf16 (round to nearest even), OCP fp8 e4m3,
+OCP MXFP4 (32-element blocks of FP4 E2M1 sharing an E8M0 scale) and OCP
+MXFP8 (32-element blocks of FP8 E4M3 sharing an E8M0 scale).
 
 These are input-preparation encoders only.  The oracle and the GPU library
 each decode the stored bytes with their own code.
@@ -100,3 +101,26 @@ def mxfp4_encode(a):
     code = code.reshape(lead + (C,))
     packed = (code[..., 0::2] | (code[..., 1::2] << np.uint8(4))).astype(np.uint8)
     return np.ascontiguousarray(packed), np.ascontiguousarray(scales)
+
+
+def mxfp8_encode(a):
+    """Quantise rows of C values (C a multiple of 32) to MXFP8 with E4M3
+    elements: codes uint8 [..., C] (one byte an element) and E8M0 scales
+    uint8 [..., C/32], one per 32-element block.  The scale exponent is
+    floor(log2(amax)) - 8 (the largest E4M3 exponent), so the block's largest
+    value lands in [256, 512) before rounding; elements round to the nearest
+    E4M3 value, ties to the even code, saturating at 448.  All-zero blocks
+    get scale 2^0."""
+    v = np.asarray(a, dtype=np.float64)
+    C = v.shape[-1]
+    if C % 32:
+        raise ValueError("mxfp8 rows are whole 32-element blocks")
+    lead = v.shape[:-1]
+    blk = v.reshape(lead + (C // 32, 32))
+    amax = np.abs(blk).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        ex = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, 0)
+    ex = np.clip(ex, -127, 127).astype(np.int64)
+    scales = (ex + 127).astype(np.uint8)
+    codes = e4m3_encode(blk / np.ldexp(1.0, ex)[..., None], 1.0).reshape(lead + (C,))
+    return np.ascontiguousarray(codes), np.ascontiguousarray(scales)
