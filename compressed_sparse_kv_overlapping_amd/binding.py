@@ -67,6 +67,11 @@ _SIGS = {
                                  ctypes.c_int),
     "cskv_hca_attend_mxfp4": ([_vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, _vp, _f32, _vp,
                                _vp, _vp, _sz, _vp], ctypes.c_int),
+    "cskv_sparse_attend_mxfp8": ([_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i64, _i64,
+                                  _i64, _vp, _i64, _f32, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+                                 ctypes.c_int),
+    "cskv_hca_attend_mxfp8": ([_vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp, _i32, _f32, _vp, _f32, _vp,
+                               _vp, _vp, _sz, _vp], ctypes.c_int),
     "cskv_merge": ([_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
 }
 EXPORTS = tuple(_SIGS)
@@ -437,24 +442,25 @@ def hca_attend(q, entries, scale=1.0, per_seq=False, q_pos=None, m=None, out=Non
     return out, lse
 
 
-def _mx_entries(codes, scales, per_seq, B):
-    """MXFP4 entry rows: codes uint8 [N, 288] and scales uint8 [N, 18], with
-    a leading batch dimension per sequence.  Returns N."""
-    _kv(codes, "ent_codes", per_seq, B, E // 2, torch.uint8)
+def _mx_entries(codes, scales, per_seq, B, bits=4):
+    """MX entry rows: codes uint8 [N, 288] (MXFP4) or [N, 576] (MXFP8) and
+    scales uint8 [N, 18], with a leading batch dimension per sequence.
+    Returns N."""
+    _kv(codes, "ent_codes", per_seq, B, E * bits // 8, torch.uint8)
     N = codes.shape[-2]
     _need(scales, "ent_scales", torch.uint8, (B, N, E // 32) if per_seq else (N, E // 32))
     return N
 
 
-def sparse_attend_mxfp4(q, ent_codes, ent_scales, window, idx, q_pos=None, win_pos0=0, W=None,
-                        scale=1.0, per_seq=False, out=None, lse=None, workspace=None, stream=None,
-                        sink=None, norm_eps=None):
+def _sparse_attend_mx(bits, q, ent_codes, ent_scales, window, idx, q_pos=None, win_pos0=0, W=None,
+                      scale=1.0, per_seq=False, out=None, lse=None, workspace=None, stream=None,
+                      sink=None, norm_eps=None):
     """sparse_attend over MXFP4 entries: codes uint8 [N, 288] and E8M0
     scales uint8 [N, 18] (with a leading batch dimension per sequence); q,
     window and out are bf16."""
     _need(q, "q", torch.bfloat16, (None, None, E))
     B, H = q.shape[0], q.shape[1]
-    N = _mx_entries(ent_codes, ent_scales, per_seq, B)
+    N = _mx_entries(ent_codes, ent_scales, per_seq, B, bits)
     _kv(window, "window", per_seq, B, E, torch.bfloat16)
     _need(idx, "idx", torch.int32, (B, None))
     _need(q_pos, "q_pos", torch.int64, (B,))
@@ -473,21 +479,21 @@ def sparse_attend_mxfp4(q, ent_codes, ent_scales, window, idx, q_pos=None, win_p
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = _workspace(need, q.device)
-    _call("cskv_sparse_attend_mxfp4", _ptr(q), _ptr(ent_codes), _ptr(ent_scales), _ptr(window),
+    _call(f"cskv_sparse_attend_mxfp{bits}", _ptr(q), _ptr(ent_codes), _ptr(ent_scales), _ptr(window),
           _ptr(idx), B, H, N, W, k, N if per_seq else 0, win_rows * E if per_seq else 0, win_rows,
           _ptr(q_pos), int(win_pos0), float(scale), _sink(sink, H), _eps(norm_eps), _ptr(out),
           _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
     return out, lse
 
 
-def hca_attend_mxfp4(q, ent_codes, ent_scales, scale=1.0, per_seq=False, q_pos=None, m=None,
-                     out=None, lse=None, workspace=None, stream=None, sink=None, norm_eps=None):
+def _hca_attend_mx(bits, q, ent_codes, ent_scales, scale=1.0, per_seq=False, q_pos=None, m=None,
+                   out=None, lse=None, workspace=None, stream=None, sink=None, norm_eps=None):
     """hca_attend over MXFP4 entries (codes [N, 288], scales [N, 18])."""
     if q_pos is not None and m is None:
-        raise ValueError("hca_attend_mxfp4: q_pos needs the block size m")
+        raise ValueError("hca_attend_mx: q_pos needs the block size m")
     _need(q, "q", torch.bfloat16, (None, None, E))
     B, H = q.shape[0], q.shape[1]
-    N = _mx_entries(ent_codes, ent_scales, per_seq, B)
+    N = _mx_entries(ent_codes, ent_scales, per_seq, B, bits)
     _need(q_pos, "q_pos", torch.int64, (B,))
     _need(out, "out", torch.bfloat16, (B, H, D))
     _need(lse, "lse", torch.float32, (B, H))
@@ -500,11 +506,34 @@ def hca_attend_mxfp4(q, ent_codes, ent_scales, scale=1.0, per_seq=False, q_pos=N
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = _workspace(need, q.device)
-    _call("cskv_hca_attend_mxfp4", _ptr(q), _ptr(ent_codes), _ptr(ent_scales), B, H, N,
+    _call(f"cskv_hca_attend_mxfp{bits}", _ptr(q), _ptr(ent_codes), _ptr(ent_scales), B, H, N,
           N if per_seq else 0, _ptr(q_pos), int(m) if q_pos is not None else 0, float(scale),
           _sink(sink, H), _eps(norm_eps), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
           _stream(stream))
     return out, lse
+
+
+def sparse_attend_mxfp4(q, ent_codes, ent_scales, window, idx, **kw):
+    """sparse_attend over MXFP4 entries: codes uint8 [N, 288] and E8M0
+    scales uint8 [N, 18] (with a leading batch dimension per sequence); q,
+    window and out are bf16; other arguments as sparse_attend."""
+    return _sparse_attend_mx(4, q, ent_codes, ent_scales, window, idx, **kw)
+
+
+def hca_attend_mxfp4(q, ent_codes, ent_scales, **kw):
+    """hca_attend over MXFP4 entries (codes [N, 288], scales [N, 18])."""
+    return _hca_attend_mx(4, q, ent_codes, ent_scales, **kw)
+
+
+def sparse_attend_mxfp8(q, ent_codes, ent_scales, window, idx, **kw):
+    """sparse_attend over MXFP8 entries: E4M3 codes uint8 [N, 576] and E8M0
+    scales uint8 [N, 18] (with a leading batch dimension per sequence)."""
+    return _sparse_attend_mx(8, q, ent_codes, ent_scales, window, idx, **kw)
+
+
+def hca_attend_mxfp8(q, ent_codes, ent_scales, **kw):
+    """hca_attend over MXFP8 entries (codes [N, 576], scales [N, 18])."""
+    return _hca_attend_mx(8, q, ent_codes, ent_scales, **kw)
 
 
 def merge(o_part, lse_part, dtype=torch.bfloat16, out=None, lse=None, stream=None, sink=None):

@@ -326,9 +326,10 @@ int cskv_hca_attend(const void* q, const void* entries, int64_t B, int32_t H, in
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), "cskv_hca_attend");
 }
 
-// MXFP4 entries: the codes and scales of row i of sequence b start at
-// (b * ent_bstride + i) * 288 and * 18 bytes.  The rows an attention call
-// reads are first decoded to bf16 rows in the workspace (each row once: the
+// MX entries: the codes and scales of row i of sequence b start at
+// (b * ent_bstride + i) * 288 (MXFP4) or * 576 (MXFP8) and * 18 bytes.  The
+// rows an attention call reads are first decoded to bf16 rows in the
+// workspace (each row once: the
 // selected rows of every query, or all rows for dense attention), then the
 // bf16 attention kernels run on them.  Workspace: [partials][bf16 rows][row
 // table].
@@ -355,14 +356,17 @@ size_t cskv_hca_attend_mxfp4_workspace_size(int64_t B, int32_t H, int64_t N, int
          round256((size_t)(per_sequence ? B : 1) * N * 576 * 2);
 }
 
-int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
-                             const void* window, const int32_t* idx, int64_t B, int32_t H,
-                             int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
-                             int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
-                             int64_t win_pos0, float scale, const float* sink, float norm_eps,
-                             void* out, float* lse, void* workspace, size_t ws_bytes,
-                             void* stream) {
-  const char* fn = "cskv_sparse_attend_mxfp4";
+// MX entries (bits 4: MXFP4, 288 code bytes a row; bits 8: MXFP8 with E4M3
+// elements, 576 code bytes a row; 18 E8M0 scale bytes a row either way):
+// the rows a call reads are decoded to bf16 rows in the workspace first,
+// then the bf16 attention kernels run on them.
+static int sparse_attend_mx(const char* fn, int bits, const void* q, const void* ent_codes,
+                            const uint8_t* ent_scales, const void* window, const int32_t* idx,
+                            int64_t B, int32_t H, int64_t N, int32_t W, int32_t k,
+                            int64_t ent_bstride, int64_t win_bstride, int64_t win_rows,
+                            const int64_t* q_pos, int64_t win_pos0, float scale, const float* sink,
+                            float norm_eps, void* out, float* lse, void* workspace, size_t ws_bytes,
+                            void* stream) {
   int st = check_mxfp4_entries(fn, ent_codes, ent_scales, ent_bstride);
   if (st) return st;
   st = check_attend(fn, q, ent_codes, window, B, H, N, W, k, ent_bstride * 576, win_bstride,
@@ -377,7 +381,7 @@ int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t
   char* w = (char*)workspace;
   char* rows = w + round256(cskv::attend_partial_bytes(1, B, H, (int64_t)k + W));
   int32_t* sel = (int32_t*)(rows + round256((size_t)B * k * 576 * 2));
-  hipError_t e = cskv::launch_mx_rows((const uint8_t*)ent_codes, ent_scales, idx, B * k, k, N,
+  hipError_t e = cskv::launch_mx_rows(bits, (const uint8_t*)ent_codes, ent_scales, idx, B * k, k, N,
                                       ent_bstride, rows, sel, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, fn);
   cskv::AttendParams p{1, q, rows, window, sel, q_pos, B, k, (int64_t)k * 576, win_bstride,
@@ -385,12 +389,11 @@ int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), fn);
 }
 
-int cskv_hca_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
-                          int64_t B, int32_t H, int64_t N, int64_t ent_bstride,
-                          const int64_t* q_pos, int32_t m, float scale, const float* sink,
-                          float norm_eps, void* out, float* lse, void* workspace, size_t ws_bytes,
-                          void* stream) {
-  const char* fn = "cskv_hca_attend_mxfp4";
+static int hca_attend_mx(const char* fn, int bits, const void* q, const void* ent_codes,
+                         const uint8_t* ent_scales, int64_t B, int32_t H, int64_t N,
+                         int64_t ent_bstride, const int64_t* q_pos, int32_t m, float scale,
+                         const float* sink, float norm_eps, void* out, float* lse, void* workspace,
+                         size_t ws_bytes, void* stream) {
   int st = check_mxfp4_entries(fn, ent_codes, ent_scales, ent_bstride);
   if (st) return st;
   st = check_attend(fn, q, ent_codes, nullptr, B, H, N, 0, 0, ent_bstride * 576, 0, 0, CSKV_BF16,
@@ -402,13 +405,55 @@ int cskv_hca_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* e
   if (!workspace || ws_bytes < need || !aligned16(workspace))
     return fail(CSKV_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   char* rows = (char*)workspace + round256(cskv::attend_partial_bytes(1, B, H, N));
-  hipError_t e = cskv::launch_mx_rows((const uint8_t*)ent_codes, ent_scales, nullptr,
+  hipError_t e = cskv::launch_mx_rows(bits, (const uint8_t*)ent_codes, ent_scales, nullptr,
                                       (per_seq ? B : 1) * N, 0, N, ent_bstride, rows, nullptr,
                                       (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, fn);
   cskv::AttendParams p{1, q, rows, nullptr, nullptr, q_pos, B, N, per_seq ? N * 576 : 0, 0, 0, 0,
                        H, 0, 0, scale, out, lse, 1, q_pos ? m : 0, sink, norm_eps};
   return hip_status(cskv::launch_attend(p, workspace, (hipStream_t)stream), fn);
+}
+
+int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
+                             const void* window, const int32_t* idx, int64_t B, int32_t H,
+                             int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
+                             int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
+                             int64_t win_pos0, float scale, const float* sink, float norm_eps,
+                             void* out, float* lse, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  return sparse_attend_mx("cskv_sparse_attend_mxfp4", 4, q, ent_codes, ent_scales, window, idx, B,
+                          H, N, W, k, ent_bstride, win_bstride, win_rows, q_pos, win_pos0, scale,
+                          sink, norm_eps, out, lse, workspace, ws_bytes, stream);
+}
+
+int cskv_hca_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
+                          int64_t B, int32_t H, int64_t N, int64_t ent_bstride,
+                          const int64_t* q_pos, int32_t m, float scale, const float* sink,
+                          float norm_eps, void* out, float* lse, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  return hca_attend_mx("cskv_hca_attend_mxfp4", 4, q, ent_codes, ent_scales, B, H, N, ent_bstride,
+                       q_pos, m, scale, sink, norm_eps, out, lse, workspace, ws_bytes, stream);
+}
+
+int cskv_sparse_attend_mxfp8(const void* q, const void* ent_codes, const uint8_t* ent_scales,
+                             const void* window, const int32_t* idx, int64_t B, int32_t H,
+                             int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
+                             int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
+                             int64_t win_pos0, float scale, const float* sink, float norm_eps,
+                             void* out, float* lse, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  return sparse_attend_mx("cskv_sparse_attend_mxfp8", 8, q, ent_codes, ent_scales, window, idx, B,
+                          H, N, W, k, ent_bstride, win_bstride, win_rows, q_pos, win_pos0, scale,
+                          sink, norm_eps, out, lse, workspace, ws_bytes, stream);
+}
+
+int cskv_hca_attend_mxfp8(const void* q, const void* ent_codes, const uint8_t* ent_scales,
+                          int64_t B, int32_t H, int64_t N, int64_t ent_bstride,
+                          const int64_t* q_pos, int32_t m, float scale, const float* sink,
+                          float norm_eps, void* out, float* lse, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  return hca_attend_mx("cskv_hca_attend_mxfp8", 8, q, ent_codes, ent_scales, B, H, N, ent_bstride,
+                       q_pos, m, scale, sink, norm_eps, out, lse, workspace, ws_bytes, stream);
 }
 
 int cskv_merge(const float* o_part, const float* lse_part, int64_t B, int32_t H, int32_t S,

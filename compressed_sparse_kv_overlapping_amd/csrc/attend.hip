@@ -1334,12 +1334,16 @@ static hipError_t launch_attend_t(const AttendParams& p, void* ws, hipStream_t s
   return hipGetLastError();
 }
 
-// MXFP4 entry rows -> bf16 rows for the attention kernels, one 8-element
-// chunk (a 32-bit code word and its block's scale) per thread, 72 per row.
+// MX entry rows -> bf16 rows for the attention kernels, one 8-element
+// chunk (its codes and its block's scale) per thread, 72 per row.  BITS = 4:
+// MXFP4 (a 32-bit code word, E2M1 elements); BITS = 8: MXFP8 with E4M3
+// elements (two 32-bit code words).  The scaled conversions of gfx950 give
+// the exact products while they are bf16 normals.
 // Dense (idx == NULL): output row r = b * N + i is entry i of sequence b
 // (ent_bstride rows apart; one sequence when it is 0).  Gathered: output row
 // r = b * k + j is entry idx[b][j] of sequence b, and idx_out[r] = j, or -1
 // with a zero row where the selection holds no entry.
+template <int BITS>
 __global__ __launch_bounds__(256) void mx_rows_kernel(const uint8_t* codes, const uint8_t* scales,
                                                       const int32_t* idx, int64_t rows, int k,
                                                       int64_t N, int64_t ent_bstride,
@@ -1360,19 +1364,30 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const uint8_t* codes, cons
   }
   u32x4 v = u32x4{0u, 0u, 0u, 0u};
   if (src >= 0) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + src * (kE / 2) + 4 * c);
-    v = fp4x8_to_bf16(w, __uint_as_float(e8m0_f32_bits(scales[src * (kE / 32) + c / 4])));
+    const float sc = __uint_as_float(e8m0_f32_bits(scales[src * (kE / 32) + c / 4]));
+    if constexpr (BITS == 4) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + src * (kE / 2) + 4 * c);
+      v = fp4x8_to_bf16(w, sc);
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(codes + src * kE + 8 * c);
+      v = fp8x8_to_bf16(w.x, w.y, sc);
+    }
   }
   *reinterpret_cast<u32x4*>(out + r * kE + 8 * c) = v;
 }
 
-hipError_t launch_mx_rows(const uint8_t* codes, const uint8_t* scales, const int32_t* idx,
+hipError_t launch_mx_rows(int bits, const uint8_t* codes, const uint8_t* scales, const int32_t* idx,
                           int64_t rows, int k, int64_t N, int64_t ent_bstride, void* out,
                           int32_t* idx_out, hipStream_t stream) {
   const int64_t threads = rows * (kE / 8);
   if (threads == 0) return hipSuccess;
-  hipLaunchKernelGGL(mx_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                     codes, scales, idx, rows, k, N, ent_bstride, (bf16_t*)out, idx_out);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (bits == 8)
+    hipLaunchKernelGGL(mx_rows_kernel<8>, grid, dim3(256), 0, stream, codes, scales, idx, rows, k,
+                       N, ent_bstride, (bf16_t*)out, idx_out);
+  else
+    hipLaunchKernelGGL(mx_rows_kernel<4>, grid, dim3(256), 0, stream, codes, scales, idx, rows, k,
+                       N, ent_bstride, (bf16_t*)out, idx_out);
   return hipGetLastError();
 }
 

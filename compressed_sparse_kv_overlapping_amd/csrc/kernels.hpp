@@ -37,10 +37,10 @@ struct AttendParams {
 int attend_splits(int dt, int64_t B, int H, int64_t nslots);
 size_t attend_partial_bytes(int dt, int64_t B, int H, int64_t nslots);
 hipError_t launch_attend(const AttendParams& p, void* ws, hipStream_t stream);
-// MXFP4 entry rows (codes [.][288], E8M0 scales [.][18]) decoded to bf16
-// rows of 576: dense (idx NULL) rows b * N + i, or gathered rows b * k + j
-// with idx_out[b][j] = j or -1.
-hipError_t launch_mx_rows(const uint8_t* codes, const uint8_t* scales, const int32_t* idx,
+// MX entry rows (bits 4: MXFP4 codes [.][288]; bits 8: MXFP8 codes [.][576];
+// E8M0 scales [.][18]) decoded to bf16 rows of 576: dense (idx NULL) rows
+// b * N + i, or gathered rows b * k + j with idx_out[b][j] = j or -1.
+hipError_t launch_mx_rows(int bits, const uint8_t* codes, const uint8_t* scales, const int32_t* idx,
                           int64_t rows, int k, int64_t N, int64_t ent_bstride, void* out,
                           int32_t* idx_out, hipStream_t stream);
 hipError_t launch_merge(int dt, const float* o_part, const float* lse_part, int64_t BH, int S,

@@ -26,6 +26,8 @@
  * elements per E8M0 scale): a row of C elements is C/2 code bytes (element
  * 2j in the low nibble of byte j) plus C/32 scale bytes in a separate array;
  *   entry codes / scales [N][288] / [N][18];  key codes / scales [N][32] / [N][2].
+ * MXFP8 storage (the *_mxfp8 calls; 32 FP8 E4M3 elements per E8M0 scale):
+ *   entry codes / scales [N][576] / [N][18].
  * Per-query caches: *_bstride gives the element offset between the caches of
  * consecutive queries (0 = one cache shared by all queries).
  *
@@ -307,6 +309,35 @@ int cskv_sparse_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t
                              void* out, float* lse, void* workspace, size_t ws_bytes,
                              void* stream);
 int cskv_hca_attend_mxfp4(const void* q, const void* ent_codes, const uint8_t* ent_scales,
+                          int64_t B, int32_t H, int64_t N, int64_t ent_bstride,
+                          const int64_t* q_pos, int32_t m, float scale, const float* sink,
+                          float norm_eps, void* out, float* lse, void* workspace, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * CSA sparse attention and HCA dense attention over MXFP8 entries: the
+ * compressed entries stored in FP8 with block scales ("Compressed attention
+ * · CSA / HCA và hai trục nén", section 3: the compressed KV cache in
+ * low-bit floating point with block scales), read as the OCP Microscaling
+ * v1.0 MXFP8 format with E4M3 elements: 32 elements share one E8M0 scale
+ * 2^(X-127), element value = scale * E4M3 value.  Same calls, arguments,
+ * results and errors as the *_mxfp4 calls above, with
+ *   ent_codes [N][576] bytes: one E4M3 code an element.  16-byte aligned.
+ *   ent_scales [N][18] bytes: the scale of elements 32b .. 32b+31.
+ *   workspace: the size of the matching *_mxfp4 call
+ *     (cskv_sparse_attend_mxfp4_workspace_size, cskv_hca_attend_mxfp4_workspace_size):
+ *     the rows a call reads are decoded into it as bf16 first.
+ * The entries decode to bf16 exactly while every decoded value lies in
+ * bf16's normal range.
+ */
+int cskv_sparse_attend_mxfp8(const void* q, const void* ent_codes, const uint8_t* ent_scales,
+                             const void* window, const int32_t* idx, int64_t B, int32_t H,
+                             int64_t N, int32_t W, int32_t k, int64_t ent_bstride,
+                             int64_t win_bstride, int64_t win_rows, const int64_t* q_pos,
+                             int64_t win_pos0, float scale, const float* sink, float norm_eps,
+                             void* out, float* lse, void* workspace, size_t ws_bytes,
+                             void* stream);
+int cskv_hca_attend_mxfp8(const void* q, const void* ent_codes, const uint8_t* ent_scales,
                           int64_t B, int32_t H, int64_t N, int64_t ent_bstride,
                           const int64_t* q_pos, int32_t m, float scale, const float* sink,
                           float norm_eps, void* out, float* lse, void* workspace, size_t ws_bytes,

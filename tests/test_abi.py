@@ -27,7 +27,7 @@ def declared():
 
 def test_header_functions_are_exported(lib):
     names = declared()
-    assert len(names) == 23
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), f"{n} declared in cskv.h but not exported"
     from compressed_sparse_kv_overlapping_amd import binding

@@ -682,3 +682,93 @@ def test_normalised_attention_mxfp4_entries():
     torch.cuda.synchronize()
     ro, rl = oracle.hca_attend_mxfp4(q, codes, scales, scale=1 / 24, norm_eps=1e-6)
     _check_attn(out, lse, ro, rl, wl.DT_BF16)
+
+
+# ------------------------------------------------------- MXFP8 entries
+
+def _mx8_entries(cfg_id, seed, shape):
+    """Entries drawn ~N(0,1) in fp32 and quantised to MXFP8 (E4M3 codes, scales)."""
+    return wl.mxfp8_encode(wl.normal(cfg_id, seed, 2, shape))
+
+
+@pytest.mark.parametrize("B,H,N,W,k", [(2, 128, 5000, 128, 1024), (3, 80, 700, 16, 37),
+                                       (1, 16, 40, 0, 40), (4, 128, 300, 5, 1)])
+def test_sparse_attend_mxfp8_matches_oracle(B, H, N, W, k):
+    """CSA over MXFP8 entries plus bf16 window rows; some selections hold -1."""
+    rng = np.random.default_rng(B * 1000 + k + 7)
+    q = _rand(112, N, 1, (B, H, E), wl.DT_BF16, 1 / 24)
+    codes, scales = _mx8_entries(112, N, (N, E))
+    win = _rand(112, N, 3, (max(W, 1), E), wl.DT_BF16)
+    idx = np.stack([np.sort(rng.choice(N, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    idx[0, -1] = -1
+    out, lse = _cskv().sparse_attend_mxfp8(dev(q), _up(codes), _up(scales), dev(win), _up(idx), W=W)
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend_mxfp8(q, codes, scales, win, idx, W=W)
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+
+
+def test_attend_mxfp8_prefill_sink_per_sequence_and_norm():
+    """Prefill windows over per-sequence MXFP8 entries with sinks; HCA decode
+    (several splits), prefill visibility and per-sequence entries; and the
+    query / entry normalisation."""
+    cskv = _cskv()
+    rng = np.random.default_rng(4)
+    B, H, N, W, k = 3, 128, 900, 128, 64
+    q = _rand(113, 0, 1, (B, H, E), wl.DT_BF16, 1 / 24)
+    codes, scales = _mx8_entries(113, 0, (B, N, E))
+    pos0, rows = 1000, 300
+    win = _rand(113, 0, 3, (B, rows, E), wl.DT_BF16)
+    qp = np.array([pos0 + W - 1, pos0 + 200, pos0 + rows - 1], np.int64)
+    idx = np.stack([np.sort(rng.choice(N, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    sink = rng.standard_normal(H) * 2
+    st = torch.from_numpy(sink).float().cuda()
+    sk = sink.astype(np.float32).astype(np.float64)
+    out, lse = cskv.sparse_attend_mxfp8(dev(q), _up(codes), _up(scales), dev(win), _up(idx),
+                                        q_pos=_up(qp), win_pos0=pos0, W=W, per_seq=True, sink=st)
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend_mxfp8(q, codes, scales, win, idx, q_pos=qp, win_pos0=pos0, W=W,
+                                     per_seq=True, sink=sk)
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+    out, lse = cskv.hca_attend_mxfp8(dev(q), _up(codes[0]), _up(scales[0]), sink=st)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend_mxfp8(q, codes[0], scales[0], sink=sk)
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+    out, lse = cskv.hca_attend_mxfp8(dev(q), _up(codes), _up(scales), per_seq=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend_mxfp8(q, codes, scales, per_seq=True)
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+    m = 128
+    hp = np.array([0, 127, 40000], np.int64)
+    out, lse = cskv.hca_attend_mxfp8(dev(q), _up(codes[1]), _up(scales[1]), q_pos=_up(hp), m=m)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca_attend_mxfp8(q, codes[1], scales[1], q_pos=hp, m=m)
+    assert (host_f64(out)[0] == 0).all()
+    _check_attn(out[1:], lse[1:], ro[1:], rl[1:], wl.DT_BF16)
+    out, lse = cskv.sparse_attend_mxfp8(dev(q), _up(codes[2]), _up(scales[2]), dev(win[0]),
+                                        _up(idx), scale=1 / 24, norm_eps=1e-6)
+    torch.cuda.synchronize()
+    ro, rl = oracle.csa_attend_mxfp8(q, codes[2], scales[2], win[0], idx, scale=1 / 24, norm_eps=1e-6)
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+
+
+def test_attend_mxfp8_decode_workload_sampled():
+    """The 1M-token decode shapes with MXFP8 entries: HCA over 8,192 entries
+    and CSA over 1,024 selected of 262,144 plus 128 window rows, 32 queries x
+    128 heads, checked on sampled queries."""
+    cfg = wl.CONFIGS["layer_1m"]
+    B, H, k, W = cfg.B, cfg.H, cfg.k, cfg.W
+    rng = np.random.default_rng(12)
+    q = _rand(cfg.config_id, 0, 1, (B, H, E), wl.DT_BF16, 1 / 24)
+    c128, s128 = _mx8_entries(cfg.config_id, 3, (cfg.N_hca, E))
+    out, lse = _cskv().hca_attend_mxfp8(dev(q), _up(c128), _up(s128))
+    c4, s4 = _mx8_entries(cfg.config_id, 4, (cfg.N_csa, E))
+    win = _rand(cfg.config_id, 0, 3, (W, E), wl.DT_BF16)
+    idx = np.stack([np.sort(rng.choice(cfg.N_csa, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    o2, l2 = _cskv().sparse_attend_mxfp8(dev(q), _up(c4), _up(s4), dev(win), _up(idx))
+    torch.cuda.synchronize()
+    rows = np.array([0, 17, B - 1])
+    sel = torch.from_numpy(rows).cuda()
+    ro, rl = oracle.hca_attend_mxfp8(q[rows], c128, s128)
+    _check_attn(out[sel], lse[sel], ro, rl, wl.DT_BF16)
+    ro, rl = oracle.csa_attend_mxfp8(q[rows], c4, s4, win, idx[rows])
+    _check_attn(o2[sel], l2[sel], ro, rl, wl.DT_BF16)
