@@ -22,6 +22,10 @@
 //     only within each range).  If the candidate list overflowed (e.g. massive
 //     score ties), the query is resolved by a self-contained streaming radix
 //     select over all its entries instead.
+#include <float.h>
+
+#include <type_traits>
+
 #include "common.hpp"
 #include "fp4.hpp"
 #include "kernels.hpp"
@@ -484,6 +488,327 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Many-query score passes on 32x32 MFMA tiles.
+//
+// A block of four waves takes one chunk of entries and 4 x 32 NQB queries:
+// wave w owns queries q0 + 32 NQB w + 32 j + (l % 32), j < NQB, and the four
+// waves read the same key rows, staged in LDS in 16 KB stages exactly as in
+// the kernel above.  A tile is 32 entries:
+//   S[j] = keys (32 x 64) . queries_j^T (64 x 32)
+// one MFMA over all 64 dims for fp8 and MXFP4 (v_mfma_scale 32x32x64 with
+// the f8f6f4 operand formats: each lane supplies 32 consecutive dims of its
+// row, dims 32 (l / 32) .. + 31, i.e. one MX block, with that block's E8M0
+// scale; for fp8 the scales are 2^0), four 32x32x16 MFMAs for bf16.  Lane l
+// then holds query l % 32 and the 16 entries 8 (i / 4) + 4 (l / 32) + i % 4
+// of the tile, so a lane reduces 16 scores of one query.
+//
+// MODE 0: group maxima (GS >= 32, groups aligned to tiles): a running
+// maximum over the lane's scores (v_max3), the two lane halves joined with a
+// permlane swap at the end of a group; lane half g keeps group 2n + g and
+// writes it every second group.  MODE 1: candidates >= the threshold: the
+// lane's 16 scores of a tile are reduced to their maximum the same way, and
+// a lane whose maximum reaches its query's threshold (a few lanes per tile)
+// queues the 16 scores as one block in LDS; when the queue fills, and at the
+// end, every lane takes one block and appends the entries that qualify to
+// the per-(query, chunk) candidate regions.  The hit test costs no more than
+// the group maximum, and per-score work is left to the few queued blocks.
+template <class T> struct Tile32;
+template <> struct Tile32<e4m3_t> {
+  using BFrag = v8i32_t;
+  static constexpr int kFmt = 0;
+};
+template <> struct Tile32<fp4x2_t> {
+  using BFrag = v8i32_t;
+  static constexpr int kFmt = 4;
+};
+template <> struct Tile32<bf16_t> {
+  struct BFrag { u32x4 s[4]; };
+  static constexpr int kFmt = 1;
+};
+
+// The lane's operand of row `row` of a 64-dim row image at p (global memory
+// or a staged row whose 16-byte chunk c sits at chunk c ^ sw).
+template <class T>
+__device__ __forceinline__ void tile32_frag(typename Tile32<T>::BFrag& f, const char* row, int sw,
+                                            int g);
+template <>
+__device__ __forceinline__ void tile32_frag<e4m3_t>(v8i32_t& f, const char* row, int sw, int g) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(row + 16 * ((2 * g) ^ sw));
+  const u32x4 b = *reinterpret_cast<const u32x4*>(row + 16 * ((2 * g + 1) ^ sw));
+  f = v8i32_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+template <>
+__device__ __forceinline__ void tile32_frag<fp4x2_t>(v8i32_t& f, const char* row, int sw, int g) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(row + 16 * (g ^ sw));
+  f = v8i32_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+}
+template <>
+__device__ __forceinline__ void tile32_frag<bf16_t>(Tile32<bf16_t>::BFrag& f, const char* row, int sw,
+                                                    int g) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) f.s[s] = *reinterpret_cast<const u32x4*>(row + 16 * ((2 * s + g) ^ sw));
+}
+
+// S = A . B over the 64 dims (sa, sb: E8M0 scales of the lanes' blocks, MXFP4 only)
+template <class T>
+__device__ __forceinline__ f32x16 tile32_mma(const typename Tile32<T>::BFrag& a,
+                                             const typename Tile32<T>::BFrag& b, int sa, int sb) {
+  const f32x16 z = {};
+  if constexpr (Tile32<T>::kFmt == 0) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
+  } else {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, z, 4, 4, 0, sa, 0, sb);
+  }
+}
+template <>
+__device__ __forceinline__ f32x16 tile32_mma<bf16_t>(const Tile32<bf16_t>::BFrag& a,
+                                                     const Tile32<bf16_t>::BFrag& b, int, int) {
+  f32x16 c = {};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.s[s]),
+                                                __builtin_bit_cast(bf16x8, b.s[s]), c, 0, 0, 0);
+  return c;
+}
+
+constexpr int kQB = 64;                      // per-wave queue of lane blocks (one tile's worst case)
+
+template <class T, int NQB, int MODE, int GSL>
+__global__ __launch_bounds__(256) void idx_score32_kernel(IdxArgs a) {
+  using KT = KeyTiles<T>;
+  using F = typename Tile32<T>::BFrag;
+  constexpr int kT32 = KT::kStage / (32 * KT::kRow);          // 32-row tiles per stage
+  constexpr int QW = 32 * NQB;                                // queries per wave
+  constexpr int QB = MODE == 1 ? kQB : 1;
+  __shared__ __attribute__((aligned(16))) char kst[2][KT::kStage];
+  __shared__ uint32_t lcnt[4 * QW];
+  // MODE 1: queued lane blocks (a lane's 16 scores of one tile), their
+  // first entry and query slot, and the raw threshold of each query slot
+  __shared__ __attribute__((aligned(16))) float qs[4][QB][16];
+  __shared__ uint32_t qm[4][QB];
+  __shared__ float qt[4][MODE == 1 ? QW : 1];
+  __shared__ int sh_end[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hq = lane & 31, g = lane >> 5;
+  const int qw0 = blockIdx.y * a.qpb + wave * QW;              // this wave's first query
+  if (MODE == 1) {
+    for (int i = threadIdx.x; i < 4 * QW; i += 256) lcnt[i] = 0;
+  }
+
+  // the lane's queries: operands, visible counts, thresholds
+  F qf[NQB];
+  int qb[NQB], nvis[NQB], qsc[NQB];
+  float traw[NQB];
+  int blk_vis = 0, min_vis = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < NQB; ++j) {
+    const int q = qw0 + 32 * j + hq;
+    const bool ok = q < a.B;
+    qb[j] = ok ? q : -1;
+    nvis[j] = ok ? n_visible(a, q) : 0;
+    blk_vis = max(blk_vis, nvis[j]);
+    min_vis = min(min_vis, ok ? nvis[j] : 0x7fffffff);
+    const char* qrow = reinterpret_cast<const char*>(a.q) + (int64_t)(ok ? q : 0) * KT::kRow;
+    tile32_frag<T>(qf[j], qrow, 0, g);
+    if (!ok) qf[j] = F{};
+    qsc[j] = 127;
+    if constexpr (Tile32<T>::kFmt == 4) qsc[j] = ok ? a.qsc[(int64_t)q * 2 + g] : 127;
+    float tscore = -INFINITY;                                // threshold 0: take all
+    if (MODE == 1 && ok && a.thr[q] != 0u) tscore = key_score(a.thr[q]);
+    // rows past the visible count score -inf and never qualify, also when
+    // every visible entry does (scores are finite)
+    traw[j] = MODE == 1 && ok ? fmaxf(raw_threshold(tscore, a.scale), -FLT_MAX) : INFINITY;
+    if (MODE == 1) qt[wave][32 * j + hq] = traw[j];
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    blk_vis = max(blk_vis, __shfl_xor(blk_vis, off, 64));
+    min_vis = min(min_vis, __shfl_xor(min_vis, off, 64));
+  }
+  blk_vis = __builtin_amdgcn_readfirstlane(blk_vis);
+  min_vis = __builtin_amdgcn_readfirstlane(min_vis);
+
+  const int e_w0 = blockIdx.x * a.tiles_per_wave * 16;
+  const int e_w1 = min(e_w0 + a.tiles_per_wave * 16, MODE == 0 ? a.G * a.GS : blk_vis);
+  if (lane == 0) sh_end[wave] = e_w1;
+  __syncthreads();
+  const int e_b1 = max(max(sh_end[0], sh_end[1]), max(sh_end[2], sh_end[3]));
+  const int nst = e_b1 > e_w0 ? (e_b1 - e_w0 + 32 * kT32 - 1) / (32 * kT32) : 0;
+  const char* keys = reinterpret_cast<const char*>(a.keys);
+  const int64_t krow0 = 0;                                   // shared keys (per-sequence keys take the other kernels)
+  const uint8_t* ksc = a.ksc;
+
+  // MODE 0 state: running maxima; a stage's closed groups wait in registers
+  // (lane half g keeps groups 2n + g) and are stored early in the next
+  // stage, so that the stage's wait for its key tiles does not wait for them
+  constexpr int GS = 1 << GSL;
+  constexpr int kPend = MODE == 0 ? 16 * kT32 / GS : 1;      // groups per stage per lane half
+  static_assert(MODE == 1 || (GS >= 32 && 32 * kT32 % (2 * GS) == 0), "groups of whole tiles, even per stage");
+  float gm[NQB], pend[NQB][kPend];
+#pragma unroll
+  for (int j = 0; j < NQB; ++j) {
+    gm[j] = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kPend; ++s) pend[j][s] = -INFINITY;
+  }
+  const int g_end = e_w1 >> GSL;                             // groups [.., g_end) are computed
+  auto store_stage = [&](const int st) {
+    const int g0 = (e_w0 + st * 32 * kT32) >> GSL;
+#pragma unroll
+    for (int s = 0; s < kPend; ++s) {
+      const int gw = g0 + 2 * s + g;
+#pragma unroll
+      for (int j = 0; j < NQB; ++j)
+        if (qb[j] >= 0 && gw < g_end)
+          a.gmax[(int64_t)qb[j] * a.G + gw] = pend[j][s] == -INFINITY ? 0u : score_key(pend[j][s] * a.scale);
+    }
+  };
+  // MODE 1 state: the wave's queue fill (uniform)
+  int qn = 0;
+  auto flush = [&]() {
+    // a lane a block: the registers at or above the query's threshold, then
+    // one candidate slot per such register
+    for (int b0 = 0; b0 < qn; b0 += 64) {
+      const int i = b0 + lane;
+      if (i < qn) {
+        const uint32_t meta = qm[wave][i];
+        const int ql = (int)(meta >> 24), e0 = (int)(meta & 0xffffffu);
+        const float t = qt[wave][ql];
+        uint32_t hits = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&qs[wave][i][4 * c]);
+          hits |= ((uint32_t)(v.x >= t) | ((uint32_t)(v.y >= t) << 1) | ((uint32_t)(v.z >= t) << 2) |
+                   ((uint32_t)(v.w >= t) << 3)) << (4 * c);
+        }
+        uint64_t* dst = a.cand + ((int64_t)(qw0 + ql) * a.chunks + blockIdx.x) * a.region;
+        while (hits) {
+          const int r = __builtin_ctz(hits);
+          hits &= hits - 1u;
+          const int e = e0 + 8 * (r >> 2) + (r & 3);
+          const uint32_t key = score_key(qs[wave][i][r] * a.scale);
+          const uint32_t slot = atomicAdd(&lcnt[wave * QW + ql], 1u);
+          if (slot < (uint32_t)a.region) dst[slot] = ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+        }
+      }
+    }
+    qn = 0;
+  };
+
+  // one 32-entry tile: both column blocks' products first, so that they
+  // overlap; rows past a query's visible count masked (register i holds row
+  // et + 4 g + 8 (i / 4) + i % 4); then the lane's maximum: the group maximum
+  // (MODE 0) or the hit test (MODE 1: a lane whose 16 scores reach the
+  // threshold queues all of them; one reservation per tile, few lanes
+  // qualify)
+  auto tile = [&](const int et, const F& kf, const int ksa) {
+    if (et >= blk_vis) return;
+    f32x16 SS[NQB];
+#pragma unroll
+    for (int j = 0; j < NQB; ++j) SS[j] = tile32_mma<T>(kf, qf[j], ksa, qsc[j]);
+    if (et + 32 > min_vis) {
+#pragma unroll
+      for (int j = 0; j < NQB; ++j) {
+        const int lim = nvis[j] - et - 4 * g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) SS[j][i] = 8 * (i >> 2) + (i & 3) < lim ? SS[j][i] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NQB; ++j) {
+      const f32x16& S = SS[j];
+      float m = MODE == 0 ? gm[j] : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) m = fmaxf(fmaxf(m, S[i]), S[i + 1]);
+      if (MODE == 0) {
+        gm[j] = m;
+      } else {
+        const bool hit = m >= traw[j];
+        const uint64_t hm = __ballot(hit);
+        if (hm) {
+          const int n = __builtin_popcountll(hm);
+          if (qn + n > kQB) flush();
+          if (hit) {
+            const int pos = qn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hm >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)hm, 0u));
+            f32x4* d = reinterpret_cast<f32x4*>(&qs[wave][pos][0]);
+            d[0] = f32x4{S[0], S[1], S[2], S[3]};
+            d[1] = f32x4{S[4], S[5], S[6], S[7]};
+            d[2] = f32x4{S[8], S[9], S[10], S[11]};
+            d[3] = f32x4{S[12], S[13], S[14], S[15]};
+            qm[wave][pos] = (uint32_t)(et + 4 * g) | ((uint32_t)(32 * j + hq) << 24);
+          }
+          qn += n;
+        }
+      }
+    }
+  };
+  // MODE 0: tile t of a stage closes group (32 t) / GS of the stage when
+  // 32 (t + 1) is a multiple of GS: the two lane halves are joined
+  auto close = [&](const int t) {
+    if (MODE == 0 && (32 * (t + 1)) % GS == 0) {
+      const int lg = (32 * t) / GS;
+#pragma unroll
+      for (int j = 0; j < NQB; ++j) {
+        const float v = max_xor32(gm[j]);                     // both lane halves' rows
+        if ((lg & 1) == g) pend[j][lg >> 1] = v;
+        gm[j] = -INFINITY;
+      }
+    }
+  };
+
+  auto issue = [&](const int st) {
+    char* buf = kst[st & 1];
+#pragma unroll
+    for (int n = 0; n < KT::kStage / 4096; ++n) {
+      const int pos = (n * 4 + wave) * 1024 + lane * 16;     // byte in the stage
+      const int r = pos / KT::kRow, c = (pos % KT::kRow) / 16;
+      int row = e_w0 + st * 32 * kT32 + r;
+      row = row < a.N ? row : a.N - 1;
+      const char* src = keys + (krow0 + row) * KT::kRow + 16 * (c ^ KT::swz(r));
+      dma16(src, (unsigned)__builtin_amdgcn_readfirstlane(lds_offset(buf + (n * 4 + wave) * 1024)));
+    }
+  };
+  if (nst > 0) issue(0);
+  for (int st = 0; st < nst; ++st) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                                         // stage st landed; st - 1 read
+    if (st + 1 < nst) issue(st + 1);
+    if (MODE == 0 && st > 0) store_stage(st - 1);
+    // the lane's row in a staged tile is 32 t + l % 32, whose swizzle does
+    // not depend on t
+    const char* buf = kst[st & 1] + hq * KT::kRow;
+    const int sw = KT::swz(hq);
+    // MXFP4: the key block scales, fetched one tile ahead
+    int ksa_next = 127;
+    if constexpr (Tile32<T>::kFmt == 4) ksa_next = ksc[(krow0 + min(e_w0 + st * kT32 * 32 + hq, a.N - 1)) * 2 + g];
+    // the next tile's key operand is read from LDS while a tile computes
+    F kf, kn;
+    tile32_frag<T>(kn, buf, sw, g);
+#pragma unroll
+    for (int t = 0; t < kT32; ++t) {
+      const int et = e_w0 + (st * kT32 + t) * 32;
+      if (et >= e_w1) break;
+      kf = kn;
+      if (t + 1 < kT32) tile32_frag<T>(kn, buf + (t + 1) * 32 * KT::kRow, sw, g);
+      const int ksa = ksa_next;
+      if constexpr (Tile32<T>::kFmt == 4)
+        ksa_next = ksc[(krow0 + min(et + 32 + hq, a.N - 1)) * 2 + g];
+      tile(et, kf, ksa);
+      close(t);
+    }
+  }
+  if (MODE == 0 && nst > 0) store_stage(nst - 1);
+  if (MODE == 1) {
+    flush();
+    __syncthreads();
+    for (int c = threadIdx.x; c < 4 * QW; c += 256) {
+      const int q = blockIdx.y * a.qpb + c;
+      if (q < a.B) a.cnt[(int64_t)q * a.chunks + blockIdx.x] = lcnt[c];
+    }
+  }
+}
+
 // Collect pass from kept scores (per-sequence keys): the same candidates as
 // the MODE 1 score pass, read from the raw scores the group-maximum pass
 // stored instead of recomputed from the keys, so every key is read once.
@@ -627,45 +952,89 @@ __device__ uint32_t block_kth_largest(KeyAt key_at, int n, uint32_t kk, uint32_t
   return lo;
 }
 
-// A lower bound of the k-th largest of the G group maxima of each query (0
-// if fewer than k non-empty groups or fewer than k visible entries).  The
-// maxima are read from L2; only the histogram lives in LDS.
+// The k-th largest of the G group maxima of each query (0 if fewer than k
+// non-empty groups or fewer than k visible entries): at least k groups, hence
+// k entries, reach it, and no coarse bin lets extra entries in (one group
+// whose maximum is near zero, e.g. at the causal edge, would otherwise widen
+// the key range and with it the bins).  Up to 16 maxima a thread stay in
+// registers (else they are re-read from L2): one histogram of 4096 bins over
+// their key range, then the few maxima in the bin that holds the k-th are
+// ranked directly (a crowded bin takes further histogram passes).
 template <int NT>
 __global__ __launch_bounds__(NT) void idx_threshold_kernel(IdxArgs a) {
+  constexpr int kPer = 16;
+  constexpr uint32_t kRank = 128;                            // bin members ranked directly
   __shared__ uint32_t hist[4096], part[NT / 32];
-  __shared__ uint32_t sh_digit, sh_above;
-  const int b = blockIdx.x;
+  __shared__ uint32_t sh_digit, sh_above, sh_n, sh_tau;
+  const int b = blockIdx.x, t = threadIdx.x;
   const uint32_t* gm = a.gmax + (int64_t)b * a.G;
-  uint32_t ne = 0, mn = 0xffffffffu, mx = 0u;
-  for (int i = threadIdx.x; i < a.G; i += NT) {
-    const uint32_t v = gm[i];
-    if (v != 0u) { ++ne; mn = min(mn, v); mx = max(mx, v); }
+  const bool held = a.G <= kPer * NT;
+  uint32_t v[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = t + r * NT;
+    v[r] = held && i < a.G ? gm[i] : 0u;
   }
+  auto each = [&](auto&& f) {                                // every non-empty group's maximum
+    if (held) {
+#pragma unroll
+      for (int r = 0; r < kPer; ++r)
+        if (v[r] != 0u) f(v[r]);
+    } else {
+      for (int i = t; i < a.G; i += NT) {
+        const uint32_t x = gm[i];
+        if (x != 0u) f(x);
+      }
+    }
+  };
+  uint32_t ne = 0, mn = 0xffffffffu, mx = 0u;
+  each([&](uint32_t x) { ++ne; mn = min(mn, x); mx = max(mx, x); });
   uint32_t nonempty;
   block_excl_scan<NT>(ne, part, &nonempty);
   uint32_t lo, hi;
   block_minmax<NT>(mn, mx, part, &lo, &hi);
   const int nv = n_visible(a, b);
   if (nv <= a.k || nonempty < (uint32_t)a.k) {
-    if (threadIdx.x == 0) a.thr[b] = 0u;
+    if (t == 0) a.thr[b] = 0u;
     return;
   }
-  // one pass over 4096 bins of the key range: the lower edge of the bin that
-  // holds the k-th largest maximum is at most that maximum, so at least k
-  // groups (hence k entries) still reach it; a bin's width of extra
-  // candidates is all it costs
   const uint32_t range = hi - lo;
   const int bits = range ? 32 - __clz((int)range) : 0;     // range < 2^bits
   const int shift = bits > 12 ? bits - 12 : 0;
-  for (int i = threadIdx.x; i < 4096; i += NT) hist[i] = 0;
+  for (int i = t; i < 4096; i += NT) hist[i] = 0;
+  if (t == 0) sh_n = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < a.G; i += NT) {
-    const uint32_t v = gm[i];
-    if (v != 0u) atomicAdd(&hist[(v - lo) >> shift], 1u);
-  }
+  each([&](uint32_t x) { atomicAdd(&hist[(x - lo) >> shift], 1u); });
   __syncthreads();
   find_kth_bin<NT>(hist, 4096, (uint32_t)a.k, &sh_digit, &sh_above, part);
-  if (threadIdx.x == 0) a.thr[b] = lo + (sh_digit << shift);
+  const uint32_t bin = sh_digit, kk = (uint32_t)a.k - sh_above, nbin = hist[bin];
+  __syncthreads();                                           // hist is read; it holds the members next
+  if (nbin <= kRank) {
+    each([&](uint32_t x) {
+      if (((x - lo) >> shift) == bin) hist[atomicAdd(&sh_n, 1u)] = x;
+    });
+    __syncthreads();
+    // the member with fewer than kk larger ones and at least kk at or above
+    for (uint32_t m = t; m < nbin; m += NT) {
+      const uint32_t x = hist[m];
+      uint32_t gt = 0, ge = 0;
+      for (uint32_t j = 0; j < nbin; ++j) {
+        gt += hist[j] > x;
+        ge += hist[j] >= x;
+      }
+      if (gt < kk && kk <= ge) sh_tau = x;                   // equal maxima write the same value
+    }
+    __syncthreads();
+    if (t == 0) a.thr[b] = sh_tau;
+    return;
+  }
+  const uint32_t blo = lo + (bin << shift), span = (1u << shift) - 1u;
+  const uint32_t bhi = hi - blo > span ? blo + span : hi;
+  uint32_t above;
+  const uint32_t tau = block_kth_largest<12, NT>(
+      [&](int i, uint32_t& key) { key = gm[i]; return key != 0u; }, a.G, kk, blo, bhi, hist, part,
+      &sh_digit, &sh_above, &above);
+  if (t == 0) a.thr[b] = tau;
 }
 
 // ----------------------------------------------------------------- final
@@ -742,10 +1111,15 @@ __device__ __forceinline__ float entry_dot<fp4x2_t>(const IdxArgs& a, int b, int
 constexpr int kMaxChunks = 2048;
 constexpr int kFinalBB = 11;                 // histogram of 2^11 bins
 constexpr int kMem = 512;                    // bin members ranked exactly
-template <class T, int NT>
+//
+// CAP: candidate capacity in LDS (2048 for k <= 1024, so that five blocks fit
+// on a compute unit; 8192 otherwise).  A query with more candidates takes
+// the streaming path, with the same result.
+template <class T, int NT, int CAP>
 __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
-  // candidates (list) or, on overflow, the k selected indices
-  __shared__ union { uint64_t cand[kCap]; int32_t sel[kMaxK]; } cs;
+  static_assert(CAP <= kCap && CAP / 2 <= kMaxK, "capacity");
+  // candidates (list) or, on overflow, the k <= CAP / 2 selected indices
+  __shared__ union { uint64_t cand[CAP]; int32_t sel[CAP / 2]; } cs;
   // the histogram, then the members of the k-th bin, then the chunks' output
   // offsets
   __shared__ union { uint32_t hist[1 << kFinalBB]; uint64_t mem[kMem]; uint16_t csel[kMaxChunks]; } hs;
@@ -781,7 +1155,7 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
   if (full) sh_over = 1;
   uint32_t total;
   const uint32_t base = block_excl_scan<NT>(mine, part, &total);
-  const bool overflow = sh_over != 0 || total > (uint32_t)kCap;
+  const bool overflow = sh_over != 0 || total > (uint32_t)CAP;
   if (!overflow) {
     // chunk offsets in the list, then a copy spread over the whole block:
     // list slot j belongs to the last chunk whose offset is <= j
@@ -947,7 +1321,7 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
     const float s = entry_dot<T>(a, b, e) * a.scale;
     if (composite(score_key(s), e) >= thr) {
       const uint32_t at = atomicAdd(&sh_nsel, 1u);
-      if (at < (uint32_t)kMaxK) sel[at] = e;
+      if (at < (uint32_t)(CAP / 2)) sel[at] = e;
     }
   }
   __syncthreads();
@@ -1065,8 +1439,17 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
   dim3 grid(chunks, qblocks);
 #define CSKV_SCORE(NQB, MODE, WQ) \
   hipLaunchKernelGGL((idx_score_kernel<T, NQB, MODE, WQ>), grid, dim3(256), 0, stream, a)
+  // many queries on 32x32 tiles (fp8, bf16, MXFP4 keys; groups of >= 32)
+  constexpr bool kTile32 = !std::is_same<T, float>::value;
+  const bool tile32 = kTile32 && g.wq == 4 && g.GS >= 32;
+#define CSKV_SCORE32(MODE)                                                                   \
+  if (MODE == 1 || g.GS == 64)                                                               \
+    hipLaunchKernelGGL((idx_score32_kernel<T, 2, MODE, 6>), grid, dim3(256), 0, stream, a);  \
+  else                                                                                       \
+    hipLaunchKernelGGL((idx_score32_kernel<T, 2, MODE, 5>), grid, dim3(256), 0, stream, a)
 #define CSKV_SCORE_PASS(MODE)                                                  \
-  if (g.wq == 4) CSKV_SCORE(4, MODE, 4);                                       \
+  if (tile32) { if constexpr (kTile32) CSKV_SCORE32(MODE); }                   \
+  else if (g.wq == 4) CSKV_SCORE(4, MODE, 4);                                  \
   else if (nqb == 1) CSKV_SCORE(1, MODE, 1);                                   \
   else if (nqb == 2) CSKV_SCORE(2, MODE, 1);                                   \
   else CSKV_SCORE(4, MODE, 1)
@@ -1083,9 +1466,17 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
   else
     CSKV_SCORE_PASS(1);
 #undef CSKV_SCORE_PASS
+#undef CSKV_SCORE32
 #undef CSKV_SCORE
-  if (wide) hipLaunchKernelGGL((idx_final_kernel<T, 1024>), dim3((unsigned)p.B), dim3(1024), 0, stream, a);
-  else hipLaunchKernelGGL((idx_final_kernel<T, 256>), dim3((unsigned)p.B), dim3(256), 0, stream, a);
+  const bool small = p.k <= 1024;                            // 2048 candidates in LDS
+  if (wide && small)
+    hipLaunchKernelGGL((idx_final_kernel<T, 1024, 2048>), dim3((unsigned)p.B), dim3(1024), 0, stream, a);
+  else if (wide)
+    hipLaunchKernelGGL((idx_final_kernel<T, 1024, kCap>), dim3((unsigned)p.B), dim3(1024), 0, stream, a);
+  else if (small)
+    hipLaunchKernelGGL((idx_final_kernel<T, 256, 2048>), dim3((unsigned)p.B), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((idx_final_kernel<T, 256, kCap>), dim3((unsigned)p.B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -291,3 +291,68 @@ def test_topk_per_sequence_keys_read_once_or_twice():
     s, v = oracle.index_scores(wl.bf16_bits(q), wl.bf16_bits(kk), wl.DT_BF16, q_pos=pos, m=m,
                                per_seq=True)
     check_selection(b, s, v, k)
+
+
+# ------------------------------------- many queries on 32x32 tiles (GS >= 32)
+
+def _sample_rows(B, n=96):
+    return np.unique(np.concatenate([[0, 1, B - 1], np.linspace(0, B - 1, n).round().astype(int)]))
+
+
+@pytest.mark.parametrize("dt", [wl.DT_BF16, wl.DT_E4M3])
+def test_topk_many_queries_groups_of_32_and_more(dt):
+    """1,100 causal queries over 70,000 keys, top-512: the many-query score
+    passes on 32x32 MFMA tiles (groups of 32 entries), with queries whose
+    visible prefix ends inside a tile, at the first entry and past the end."""
+    B, N, k, m = 1100, 70000, 512, 4
+    q = wl.normal(105, 0, 1, (B, 64))
+    kk = wl.normal(105, 0, 2, (N, 64))
+    pos = np.random.default_rng(5).integers(0, N * m, B)
+    pos[:6] = [0, 3, 4, 2047, N * m - 1, N * m + 77]
+    if dt == wl.DT_E4M3:
+        sq, sk = wl.e4m3_scale(q), wl.e4m3_scale(kk)
+        qI, kI, scale = wl.e4m3_encode(q, sq), wl.e4m3_encode(kk, sk), sq * sk
+    else:
+        qI, kI, scale = wl.bf16_bits(q), wl.bf16_bits(kk), 0.37
+    rows = _sample_rows(B)
+    for qp in (pos, None):
+        cskv = _cskv()
+        qpt = None if qp is None else torch.from_numpy(qp).cuda()
+        idx = cskv.index_topk(dev(qI), dev(kI), k, q_pos=qpt, m=m, idx_scale=scale).cpu().numpy()
+        s, v = oracle.index_scores(qI[rows], kI, dt, scale, q_pos=None if qp is None else qp[rows], m=m)
+        check_selection(idx[rows], s, v, k)
+
+
+def test_topk_many_queries_exact_ties():
+    """Small-integer keys and queries (exact scores, many ties) for 1,024
+    queries over 40,000 keys: the 32x32-tile passes must give the oracle's
+    set exactly, ties resolved by index."""
+    rng = np.random.default_rng(6)
+    B, N, k = 1024, 40000, 300
+    qI = rng.integers(-2, 3, (B, 64)).astype(np.float32)
+    kI = rng.integers(-2, 3, (N, 64)).astype(np.float32)
+    for dt in (wl.DT_BF16, wl.DT_E4M3):
+        qe = wl.bf16_bits(qI) if dt == wl.DT_BF16 else wl.e4m3_encode(qI, 1.0)
+        ke = wl.bf16_bits(kI) if dt == wl.DT_BF16 else wl.e4m3_encode(kI, 1.0)
+        idx = _cskv().index_topk(dev(qe), dev(ke), k).cpu().numpy()
+        rows = _sample_rows(B, 64)
+        s, v = oracle.index_scores(qe[rows], ke, dt)
+        ref = oracle.topk(s, v, k)
+        np.testing.assert_array_equal(idx[rows], np.sort(ref, axis=1))
+
+
+def test_topk_mxfp4_many_queries_groups_of_32():
+    """MXFP4 queries and keys (per-block scales) for 1,100 causal queries over
+    70,000 keys: the scaled 32x32x64 MFMA path, exact against the oracle."""
+    B, N, k, m = 1100, 70000, 512, 4
+    qc, qs = wl.mxfp4_encode(wl.normal(106, 0, 1, (B, 64)))
+    kc, ks = wl.mxfp4_encode(wl.normal(106, 0, 2, (N, 64)))
+    pos = np.random.default_rng(7).integers(0, N * m, B)
+    pos[:4] = [0, 5, N * m - 1, 2047]
+    cskv = _cskv()
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    idx = cskv.index_topk_mxfp4(up(qc), up(qs), up(kc), up(ks), k, q_pos=up(pos), m=m,
+                                idx_scale=0.5).cpu().numpy()
+    rows = _sample_rows(B)
+    s, v = oracle.index_scores_mxfp4(qc[rows], qs[rows], kc, ks, 0.5, q_pos=pos[rows], m=m)
+    _exact(idx[rows], s, v, k)
