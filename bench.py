@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the tiny, CSA-decode and HCA-decode workload legs")
     return ap.parse_args()
 
 
@@ -119,17 +121,34 @@ def main():
     for _ in range(args.warmup):
         step(events())
     torch.cuda.synchronize()
-    evs = [events() for _ in range(args.steps)]
+    # warm cache (reported, labelled): the steps back to back, so what one
+    # step leaves in the 256 MB last-level cache (the queries, keys and HCA
+    # entries) is still there for the next
+    wevs = [events() for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step(evs[i])
+        step(wevs[i])
     stop.record()
     torch.cuda.synchronize()
+    warm_ms = start.elapsed_time(stop) / args.steps
+    warm_parts = {p: round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in wevs])), 4)
+                  for j, p in enumerate(parts)}
+    # cold cache (the headline): before every step 1 GiB is written to a
+    # scratch buffer, outside the step's events, which evicts the last-level
+    # cache; each step is timed by its own events
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    evs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        scratch.fill_(i & 0xff)
+        step(evs[i])
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(stop) / args.steps
+    del scratch
+    ms_step = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs]))
     part_ms = {p: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
                for j, p in enumerate(parts)}
     # per-step latency: first launch to last completion of each step
@@ -143,12 +162,13 @@ def main():
     pairs = B * k + B * N128
     value = pairs / (ms_step * 1e-3)
 
-    # algorithmic bytes / flops per launch (inputs once, outputs once, gathers per query)
+    # algorithmic bytes / flops per launch (inputs once, outputs once; the
+    # selected entries are gathered per query, the shared window once)
     bx = 2 * T * D * 2
     alg = {
         "compress": {"bytes": bx + (N4 + N128) * D * 2},
         "csa_topk": {"bytes": N4 * I * 2 + B * I * 2 + B * k * 4, "flops": 2 * B * N4 * I},
-        "csa_attend": {"bytes": B * (k + W) * E * 2 + B * H * E * 2 + B * H * D * 2,
+        "csa_attend": {"bytes": B * k * E * 2 + W * E * 2 + B * H * E * 2 + B * H * D * 2,
                        "flops": 2 * B * H * (k + W) * (E + D)},
         "hca_attend": {"bytes": N128 * E * 2 + B * H * E * 2 + B * H * D * 2,
                        "flops": 2 * B * H * N128 * (E + D)},
@@ -183,6 +203,11 @@ def main():
                    "queries": B, "heads": H, "top_k": k, "window": W,
                    "pairs_per_step": pairs, "kv": "shared context"},
         "roofline": roofline,
+        "cache": ("cold: 1 GiB written to a scratch buffer before each step, outside the "
+                  "step's events; each step timed by its own events"),
+        "warm_cache": {"ms_per_step": round(warm_ms, 4), "parts_ms": warm_parts,
+                       "value": round(pairs / (warm_ms * 1e-3), 1),
+                       "note": "the same steps back to back (inputs left in the last-level cache)"},
         "latency_ms": latency,
         "cache_bytes": cache_accounting(T, W, k),
         "run": {"device": torch.cuda.get_device_name(0), "hip": torch.version.hip, "streams": 1,
@@ -191,7 +216,8 @@ def main():
         "attention_GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
         "decode_only_entries_per_s": round(pairs / (attn_ms * 1e-3), 1),
         "parts": detail,
-        "wall_s_timed": round(wall, 3), "input_gen_s": round(gen_s, 1),
+        "wall_s_timed": round(wall, 3), "wall_note": "the timed steps with the scratch writes between them",
+        "input_gen_s": round(gen_s, 1),
     }
     del x, z
     torch.cuda.empty_cache()
@@ -206,9 +232,129 @@ def main():
         torch.cuda.empty_cache()
         result["per_sequence"] = bench_per_sequence(args, cskv, inp, cfg, dev, torch)
         torch.cuda.empty_cache()
+    if not args.no_configs:
+        result["configs"] = bench_configs(args, cskv, wl, dev, torch, np)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, inp, cfg, ms_step, np)
     print(json.dumps(result), flush=True)
+
+
+def _time_leg(fn, outs, torch, np, iters=50):
+    """Time a call sequence eagerly (events around back-to-back calls, inputs
+    warm) and as a replayed HIP graph of one sequence.  Every checked replay
+    starts from cleared outputs (eager work between replays) and must give
+    the eager result bit for bit."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) / iters * 1e3
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            if not torch.equal(o, r):
+                raise RuntimeError("a replayed graph differs from the eager result")
+    e0.record()
+    for _ in range(iters):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) / iters * 1e3
+    del g
+    return eager_us, graph_us
+
+
+def bench_configs(args, cskv, wl, dev, torch, np):
+    """The three small workloads, each timed eagerly and as a replayed HIP
+    graph (one call sequence captured; replays checked against the eager
+    result): the tiny fp32 layer (both scales compressed from 4,096 raw
+    tokens, CSA top-64 + 128 window rows and HCA over 32 entries, 1 query x 16
+    heads), CSA decode (8 queries x 128 heads, top-1024 of 16,384 entries +
+    128 window rows) and HCA decode (16 queries x 128 heads over 8,192
+    entries), bf16."""
+    res = {"note": "eager: events around 50 back-to-back calls (inputs warm); graph: one call "
+                   "sequence captured in a HIP graph and replayed 50 times"}
+    f32, bf = torch.float32, torch.bfloat16
+    # tiny
+    cfg = wl.CONFIGS["tiny"]
+    inp = wl.make_inputs(cfg, seed=args.seed)
+    B, H, k, T = cfg.B, cfg.H, cfg.k, cfg.T
+    x, z, b4, b128 = dev(inp["x"]), dev(inp["z"]), dev(inp["b4"]), dev(inp["b128"])
+    e4 = torch.zeros((T // 4, E), dtype=f32, device="cuda")
+    e128 = torch.zeros((T // 128, E), dtype=f32, device="cuda")
+    e4[:, D:] = dev(inp["rope4"])
+    e128[:, D:] = dev(inp["rope128"])
+    q, qI, kI, win, qh = (dev(inp[n]) for n in ("q", "qI", "kI", "window", "q_hca"))
+    o1 = torch.empty((B, H, D), dtype=f32, device="cuda")
+    o2 = torch.empty((B, H, D), dtype=f32, device="cuda")
+    l1 = torch.empty((B, H), dtype=f32, device="cuda")
+    l2 = torch.empty((B, H), dtype=f32, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    wsc = torch.empty(cskv.compress2_workspace_size(T, 128), dtype=torch.uint8, device="cuda")
+    wsa = torch.empty(cskv.csa_workspace_size(B, H, T // 4, cfg.W, k), dtype=torch.uint8, device="cuda")
+    wsh = torch.empty(max(1, cskv.hca_workspace_size(B, H, T // 128)), dtype=torch.uint8, device="cuda")
+
+    def tiny():
+        cskv.compress2(x, z, b4, 4, b128, 128, out_small=e4, out_large=e128, workspace=wsc)
+        cskv.csa_attend(q, qI, e4, kI, win, k, out=o1, lse=l1, idx_out=idx, workspace=wsa)
+        cskv.hca_attend(qh, e128, out=o2, lse=l2, workspace=wsh)
+    eu, gu = _time_leg(tiny, [e4, e128, o1, l1, o2, l2, idx], torch, np)
+    pairs = B * k + B * (T // 128)
+    res["tiny"] = {"workload": "tiny", "dtype": "f32", "launches": "compress2 + csa_attend + hca_attend",
+                   "eager_us": round(eu, 2), "graph_us": round(gu, 2),
+                   "entries_attended_per_s_graph": round(pairs / (gu * 1e-6), 1),
+                   "bound": "launch latency (about 30 kB of inputs per step)"}
+    # CSA decode
+    cfg = wl.CONFIGS["csa_decode"]
+    inp = wl.make_inputs(cfg, seed=args.seed)
+    B, H, k, W, N = cfg.B, cfg.H, cfg.k, cfg.W, cfg.N_csa
+    q, qI, kI, ent, win = (dev(inp[n]) for n in ("q", "qI", "kI", "entries", "window"))
+    o = torch.empty((B, H, D), dtype=bf, device="cuda")
+    l = torch.empty((B, H), dtype=f32, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    wsa = torch.empty(cskv.csa_workspace_size(B, H, N, W, k), dtype=torch.uint8, device="cuda")
+    eu, gu = _time_leg(lambda: cskv.csa_attend(q, qI, ent, kI, win, k, out=o, lse=l, idx_out=idx,
+                                               workspace=wsa), [o, l, idx], torch, np)
+    nbytes = N * I * 2 + B * I * 2 + B * k * E * 2 + W * E * 2 + B * H * E * 2 + B * H * D * 2
+    res["csa_decode"] = {"workload": "csa_decode", "dtype": "bf16", "launches": "csa_attend",
+                         "eager_us": round(eu, 2), "graph_us": round(gu, 2),
+                         "entries_attended_per_s_graph": round(B * k / (gu * 1e-6), 1),
+                         "roofline": {"bound": "hbm", "achieved": round(nbytes / (gu * 1e-6) / 1e9, 1),
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": round(nbytes / (gu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                      "alg_bytes": nbytes}}
+    # HCA decode
+    cfg = wl.CONFIGS["hca_decode"]
+    inp = wl.make_inputs(cfg, seed=args.seed)
+    B, H, N = cfg.B, cfg.H, cfg.N_hca
+    q, ent = dev(inp["q_hca"]), dev(inp["entries_hca"])
+    o = torch.empty((B, H, D), dtype=bf, device="cuda")
+    l = torch.empty((B, H), dtype=f32, device="cuda")
+    wsh = torch.empty(max(1, cskv.hca_workspace_size(B, H, N)), dtype=torch.uint8, device="cuda")
+    eu, gu = _time_leg(lambda: cskv.hca_attend(q, ent, out=o, lse=l, workspace=wsh), [o, l], torch, np)
+    flops = 2 * B * H * N * (E + D)
+    res["hca_decode"] = {"workload": "hca_decode", "dtype": "bf16", "launches": "hca_attend",
+                         "eager_us": round(eu, 2), "graph_us": round(gu, 2),
+                         "entries_attended_per_s_graph": round(B * N / (gu * 1e-6), 1),
+                         "roofline": {"bound": "mfma", "achieved": round(flops / (gu * 1e-6) / 1e12, 1),
+                                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(flops / (gu * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
+    return res
 
 
 def bench_per_sequence(args, cskv, inp, cfg, dev, torch):
@@ -516,6 +662,19 @@ def cpu_baseline(args, inp, cfg, gpu_ms, np):
         runs.append(run(frac))
     reps = len(runs)
     sample_s = time.perf_counter() - t0
+    # one core: a sample sized for about half the budget (the all-core
+    # calibration times the thread count), the same parts scaled to the step
+    oracle.set_threads(1)
+    try:
+        f1 = min(1.0, 0.5 * args.cpu_seconds / max(sum(est) * threads, 1e-9))
+        f1 = max(f1, 1.0 / 4096)
+        t1 = time.perf_counter()
+        r1 = run(f1)
+        s1 = time.perf_counter() - t1
+    finally:
+        oracle.set_threads(threads)
+    step1 = float(sum(r1[0]))
+    n4s, n128s, nqs, nhs = r1[1]
     (n4, n128, nq, nh) = runs[0][1]
     parts = tuple(float(np.mean([r[0][i] for r in runs])) for i in range(5))
     t_c4, t_c128, t_sel, t_csa, t_hca = parts
@@ -534,6 +693,16 @@ def cpu_baseline(args, inp, cfg, gpu_ms, np):
                     "csa_topk": round(t_sel, 2), "csa_attend": round(t_csa, 2),
                     "hca_attend": round(t_hca, 2)},
         "gpu_speedup": round(step_s / (gpu_ms * 1e-3), 1),
+        "single_core": {
+            "value": round(pairs / step1, 2), "unit": "entries/s", "cores": 1, "kind": "oracle",
+            "sample": (f"compress {n4s} of {N4} m=4 entries and {n128s} of {N128} m'=128 entries; "
+                       f"indexer+top-k and CSA attention for {nqs} of {B} queries; HCA for {nqs} "
+                       f"queries x {nhs} of {H} heads; each part scaled to the full step "
+                       f"({s1:.1f} s of oracle time on one thread)"),
+            "step_s_extrapolated": round(step1, 2),
+            "parts_s": dict(zip(("compress_m4", "compress_m128", "csa_topk", "csa_attend",
+                                 "hca_attend"), (round(float(v), 2) for v in r1[0]))),
+        },
     }
 
 if __name__ == "__main__":

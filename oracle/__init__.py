@@ -61,6 +61,7 @@ def lib():
         L.cskv_oracle_hca_attend.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, vp, i32, dbl,
                                              vp, dbl, vp, vp]
         L.cskv_oracle_max_threads.restype = i32
+        L.cskv_oracle_set_threads.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -80,6 +81,12 @@ def _check(rc, what):
 
 def max_threads():
     return lib().cskv_oracle_max_threads()
+
+
+def set_threads(n):
+    """Thread count of the oracle's OpenMP loops (the results do not depend
+    on it)."""
+    lib().cskv_oracle_set_threads(int(n))
 
 
 def e4m3_value(code):

@@ -414,6 +414,16 @@ int cskv_oracle_hca_attend(const void* q, const void* entries, int dt, int64_t B
   return 0;
 }
 
+/* Thread count of the OpenMP loops (results do not depend on it). */
+void cskv_oracle_set_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int cskv_oracle_max_threads(void) {
 #ifdef _OPENMP
   extern int omp_get_max_threads(void);
