@@ -1147,27 +1147,43 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
                                              : -INFINITY;
   float inv, lse2;
   head_norm(l, m_ref, s2, &inv, &lse2);
-  if (!hok) return false;
-  // lane l holds head l % 32, dims 32 db + 8 q + 4 (l / 32) + 0..3 in
-  // registers 4 q .. 4 q + 3 of block db
-  if (a.nsplit == 1) {
-    bf16_t* o = reinterpret_cast<bf16_t*>(a.out) + ((int64_t)b * a.H + head) * kDv + 4 * lh;
+  // Output rows (the result, or with several splits this split's
+  // normalised partial, kept in bf16, the output's precision).  Lane l holds
+  // head l % 32, dims 32 db + 8 q + 4 (l / 32) + 0..3 in registers 4 q ..
+  // 4 q + 3 of block db, so stores straight from the registers would write 8
+  // scattered bytes a lane; instead each wave stages its 32 heads through
+  // LDS (the tile buffers, free once every wave is past its last tile), 256
+  // dims at a time, with 16-byte chunk c of row r at chunk c ^ r, and stores
+  // whole 512-byte row segments.
+  const bool part = a.nsplit > 1;
+  bf16_t* orow0 = part ? reinterpret_cast<bf16_t*>(a.o_part) : reinterpret_cast<bf16_t*>(a.out);
+  char* stage = sh.kbuf[0] + 16384 * wave;
+  __syncthreads();
 #pragma unroll
-    for (int db = 0; db < kVBlocks; ++db)
+  for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        store_out4<bf16_t>(o + 32 * db + 8 * qq, O[db][4 * qq] * inv, O[db][4 * qq + 1] * inv,
-                           O[db][4 * qq + 2] * inv, O[db][4 * qq + 3] * inv);
-    if (a.lse && lh == 0) a.lse[(int64_t)b * a.H + head] = lse2 * LN2;
-  } else {
-    float* o = a.o_part + (((int64_t)b * a.H + head) * a.nsplit + split) * kDv + 4 * lh;
+    for (int d8 = 0; d8 < 8; ++d8)
 #pragma unroll
-    for (int db = 0; db < kVBlocks; ++db)
+      for (int qq = 0; qq < 4; ++qq) {
+        const f32x16& o = O[8 * hh + d8];
+        const uint2 w = make_uint2(pack_bf16x2(o[4 * qq] * inv, o[4 * qq + 1] * inv),
+                                   pack_bf16x2(o[4 * qq + 2] * inv, o[4 * qq + 3] * inv));
+        *reinterpret_cast<uint2*>(stage + 512 * hl + 16 * ((4 * d8 + qq) ^ hl) + 8 * lh) = w;
+      }
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        store_out4<float>(o + 32 * db + 8 * qq, O[db][4 * qq] * inv, O[db][4 * qq + 1] * inv,
-                          O[db][4 * qq + 2] * inv, O[db][4 * qq + 3] * inv);
-    if (lh == 0) a.lse_part[((int64_t)b * a.H + head) * a.nsplit + split] = lse2 * LN2;
+    for (int i = 0; i < 16; ++i) {
+      const int r = 2 * i + lh;                               // row (head) r, chunk hl
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 512 * r + 16 * (hl ^ r));
+      const int hd = hg * kWideHeads + wave * 32 + r;
+      if (hd < a.H) {
+        const int64_t row = part ? ((int64_t)b * a.H + hd) * a.nsplit + split : (int64_t)b * a.H + hd;
+        *reinterpret_cast<u32x4*>(orow0 + row * kDv + 256 * hh + 8 * hl) = v;
+      }
+    }
+  }
+  if (hok && lh == 0) {
+    if (part) a.lse_part[((int64_t)b * a.H + head) * a.nsplit + split] = lse2 * LN2;
+    else if (a.lse) a.lse[(int64_t)b * a.H + head] = lse2 * LN2;
   }
   return false;
 }
@@ -1194,9 +1210,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void attend_wide_kernel(AttnArgs a
 // out = sum_s exp(lse_s - lse) o_s (the partials carry no sink; sink may be
 // NULL).  Lane l takes the lse of splits l, l + 64, ...; the partial rows
 // are loaded eight splits at a time and accumulated in split order, so the
-// result does not depend on timing.
-template <class T>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
+// result does not depend on timing.  P: the partials' type (fp32, or bf16
+// for the bf16 attention's own splits).
+template <class T, class P>
+__global__ __launch_bounds__(256) void merge_kernel(const P* __restrict__ o_part,
                                                     const float* __restrict__ lse_part, int64_t BH,
                                                     int S, const float* __restrict__ sink, int H,
                                                     T* __restrict__ out,
@@ -1225,7 +1242,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
         for (int u = 0; u < 8; ++u) {
           w[u] = __shfl(wl, j + u, 64);
           if (j + u < n) {
-            Row8<float>::load(o_part + (bh * S + s0 + j + u) * kDv + lane * 8, v[u]);
+            Row8<P>::load(o_part + (bh * S + s0 + j + u) * kDv + lane * 8, v[u]);
           } else {
 #pragma unroll
             for (int d = 0; d < 8; ++d) v[u][d] = 0.f;
@@ -1288,10 +1305,11 @@ int attend_splits(int dt, int64_t B, int H, int64_t nslots) {
   return (int)((tiles + per - 1) / per);
 }
 
+// partial outputs (fp32; bf16 for bf16 calls) and their lse (fp32)
 size_t attend_partial_bytes(int dt, int64_t B, int H, int64_t nslots) {
   const int S = attend_splits(dt, B, H, nslots);
   if (S <= 1) return 0;
-  return (size_t)B * H * S * (kDv + 1) * sizeof(float) + 256;
+  return (size_t)B * H * S * (kDv * (dt == 0 ? 4 : 2) + 4) + 256;
 }
 
 template <class T>
@@ -1313,8 +1331,8 @@ static hipError_t launch_attend_t(const AttendParams& p, void* ws, hipStream_t s
   const int64_t tiles = (a.nslots + kTile - 1) / kTile;
   a.nsplit = S;
   a.slots_per_split = (int)(((tiles + S - 1) / S) * kTile);
-  a.o_part = (float*)ws;
-  a.lse_part = a.o_part + (size_t)p.B * p.H * S * kDv;
+  a.o_part = (float*)ws;                                     // bf16 partials for bf16 calls
+  a.lse_part = (float*)((char*)ws + (size_t)p.B * p.H * S * kDv * sizeof(T));
   const int hpb = attend_heads_per_block(p.dt, p.H);
   dim3 grid(S, (p.H + hpb - 1) / hpb, (unsigned)p.B);
   const bool norm = p.norm_eps >= 0.f;
@@ -1329,8 +1347,8 @@ static hipError_t launch_attend_t(const AttendParams& p, void* ws, hipStream_t s
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t BH = p.B * p.H;
-  hipLaunchKernelGGL(merge_kernel<T>, dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, stream,
-                     a.o_part, a.lse_part, BH, S, p.sink, p.H, (T*)p.out, p.lse);
+  hipLaunchKernelGGL((merge_kernel<T, T>), dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, stream,
+                     reinterpret_cast<const T*>(a.o_part), a.lse_part, BH, S, p.sink, p.H, (T*)p.out, p.lse);
   return hipGetLastError();
 }
 
@@ -1399,10 +1417,10 @@ hipError_t launch_attend(const AttendParams& p, void* ws, hipStream_t stream) {
 hipError_t launch_merge(int dt, const float* o_part, const float* lse_part, int64_t BH, int S,
                         const float* sink, int H, void* out, float* lse, hipStream_t stream) {
   if (dt == 0)
-    hipLaunchKernelGGL(merge_kernel<float>, dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((merge_kernel<float, float>), dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, stream,
                        o_part, lse_part, BH, S, sink, H, (float*)out, lse);
   else
-    hipLaunchKernelGGL(merge_kernel<bf16_t>, dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((merge_kernel<bf16_t, float>), dim3((unsigned)((BH + 3) / 4)), dim3(256), 0, stream,
                        o_part, lse_part, BH, S, sink, H, (bf16_t*)out, lse);
   return hipGetLastError();
 }
