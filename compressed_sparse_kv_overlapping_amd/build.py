@@ -5,6 +5,9 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libcskv.so")
+# the streaming probe (a measurement tool of profiling.py, outside the path)
+PROBE_SRC = os.path.join(HERE, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libcskv_probe.so")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          # packed fp32 math is kept off on these GPUs
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -49,12 +52,15 @@ def build(verbose=False):
         flags = [f for f in FLAGS if f != "-shared"]
         cmds.append(["hipcc"] + flags + EXTRA.get(name, []) + ["-c", "-o", obj, src])
         objs.append(obj)
+    probe_tmp = PROBE_LIB + ".tmp"
+    cmds.append(["hipcc"] + FLAGS + ["-o", probe_tmp, PROBE_SRC])
     msgs = _run(cmds)
     tmp = LIB + ".tmp"
     msgs += _run([["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs])
     if verbose and any(m.strip() for m in msgs):
         print("\n".join(m for m in msgs if m.strip()))
     os.replace(tmp, LIB)
+    os.replace(probe_tmp, PROBE_LIB)
     return LIB
 
 

@@ -24,6 +24,11 @@ program profiled for the indexer's SQ counters and kernel trace), and
 ``sq <pmc_dir> <title> <command>`` prints every counter of a --pmc run per
 kernel.
 
+``floor`` times the streaming probe (libcskv_probe.so: the compressor's
+reads and writes at 1M tokens with none of its arithmetic, in four mixes)
+beside the fused compressor itself, and prints the table kept in
+profiles/compress_floor_probe.txt.
+
 ``trace <results.db> <command>`` prints, from a ``rocprofv3 --kernel-trace``
 database, each library kernel's dispatch count and average / min / max
 duration per grid shape, with the profiled command in the header.
@@ -106,6 +111,77 @@ def indexer():
         torch.cuda.synchronize()
         print(json.dumps({"queries": B, "entries": N, "k": k, "dtype": str(dt),
                           "ms_per_selection": round(e0.elapsed_time(e1) / 5, 4)}), flush=True)
+
+
+def floor(reps=7):
+    """The compressor against what the memory system delivers for its
+    traffic: the streaming probe's four mixes (reads only; reads with the
+    entry rows written as they stream; the writes only; reads, then the
+    writes) and compress2 on the same 1M-token shapes, each the median of
+    reps launches timed by events."""
+    import ctypes
+    import statistics
+    import torch
+    import compressed_sparse_kv_overlapping_amd as cskv
+    from compressed_sparse_kv_overlapping_amd.build import PROBE_LIB
+    lib = ctypes.CDLL(PROBE_LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.cskv_probe_stream.argtypes = [ctypes.c_int, vp, vp, i64, vp, vp, vp, vp]
+    lib.cskv_probe_stream.restype = ctypes.c_int
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn(T_TOKENS, D, device="cuda", generator=g).bfloat16()
+    z = torch.randn(T_TOKENS, D, device="cuda", generator=g).bfloat16()
+    o4 = torch.empty(T_TOKENS // 4, D, dtype=torch.bfloat16, device="cuda")
+    o128 = torch.empty(T_TOKENS // 128, D, dtype=torch.bfloat16, device="cuda")
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def probe(mode):
+        st = lib.cskv_probe_stream(mode, x.data_ptr(), z.data_ptr(), T_TOKENS, o4.data_ptr(),
+                                   o128.data_ptr(), sink.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError(f"probe launch failed ({st})")
+
+    b4 = 0.1 * torch.randn(8, D, device="cuda", generator=g)
+    b128 = 0.1 * torch.randn(256, D, device="cuda", generator=g)
+    e4 = torch.empty(T_TOKENS // 4, 576, dtype=torch.bfloat16, device="cuda")
+    e128 = torch.empty(T_TOKENS // 128, 576, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(cskv.compress2_workspace_size(T_TOKENS, 128), dtype=torch.uint8, device="cuda")
+
+    def compress():
+        cskv.compress2(x, z, b4, 4, b128, 128, out_small=e4, out_large=e128, workspace=ws)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3)
+        return statistics.median(out)
+
+    rd = 2 * T_TOKENS * D * 2
+    wr = (T_TOKENS // 4 + T_TOKENS // 128) * D * 2
+    rows = [("reads only", lambda: probe(0), rd),
+            ("reads + entry writes as they stream", lambda: probe(1), rd + wr),
+            ("entry writes only", lambda: probe(2), wr),
+            ("reads, then each wave's writes", lambda: probe(3), rd + wr),
+            ("compress2 (fused kernel + table + join)", compress, rd + wr)]
+    print(f"# streaming probe vs the fused compressor, {T_TOKENS} tokens x {D} dims bf16 "
+          f"(reads {rd / 1e9:.3f} GB, entry writes {wr / 1e9:.3f} GB), median of {reps} launches")
+    print("# command: python -m compressed_sparse_kv_overlapping_amd.profiling floor")
+    res = {}
+    for name, fn, nbytes in rows:
+        us = timed(fn)
+        res[name] = us
+        print(f"{name:42s} {us:9.1f} us  {nbytes / (us * 1e-6) / 1e12:6.2f} TB/s")
+    mix = res["reads + entry writes as they stream"]
+    print(f"compressor / streaming mix: {res[rows[-1][0]] / mix:.3f}")
+    return res
 
 
 def sq_summary(directory, title, command):
@@ -221,6 +297,8 @@ if __name__ == "__main__":
         summarize(sys.argv[2], sys.argv[3], sys.argv[4] if len(sys.argv) > 4 else None)
     elif len(sys.argv) == 2 and sys.argv[1] == "indexer":
         indexer()
+    elif len(sys.argv) == 2 and sys.argv[1] == "floor":
+        floor()
     elif len(sys.argv) == 5 and sys.argv[1] == "sq":
         sq_summary(sys.argv[2], sys.argv[3], sys.argv[4])
     elif len(sys.argv) == 4 and sys.argv[1] == "trace":
