@@ -1156,6 +1156,10 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
   uint32_t total;
   const uint32_t base = block_excl_scan<NT>(mine, part, &total);
   const bool overflow = sh_over != 0 || total > (uint32_t)CAP;
+  // list slots of this thread (gather and output), and the chunk of p0
+  const uint32_t per = (total + NT - 1) / NT;
+  const uint32_t p0 = min(total, t * per), p1 = min(total, p0 + per);
+  int ch0 = 0;
   if (!overflow) {
     // chunk offsets in the list, then a copy spread over the whole block:
     // list slot j belongs to the last chunk whose offset is <= j
@@ -1167,13 +1171,36 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
     }
     if (t == 0) coff[a.chunks] = (uint16_t)total;
     __syncthreads();
-    for (uint32_t j = t; j < total; j += NT) {
-      int lo = 0, hi = a.chunks;                             // coff[lo] <= j < coff[hi]
+    // thread t copies list slots [p0, p1): the chunk of p0 by binary search,
+    // then a walk (chunks are contiguous in the list), the loads issued
+    // eight at a time
+    if (p0 < p1) {
+      int lo = 0, hi = a.chunks;                             // coff[lo] <= p0 < coff[hi]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (coff[mid] <= j) lo = mid; else hi = mid;
+        if (coff[mid] <= p0) lo = mid; else hi = mid;
       }
-      cand[j] = a.cand[((int64_t)b * a.chunks + lo) * a.region + (j - coff[lo])];
+      ch0 = lo;
+      int c = lo;
+      uint32_t cb = coff[c], ce = coff[c + 1];
+      for (uint32_t p = p0; p < p1; p += 8) {
+        uint64_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t q = p + u;
+          if (q < p1) {
+            while (q >= ce) {
+              ++c;
+              cb = ce;
+              ce = coff[c + 1];
+            }
+            v[u] = a.cand[((int64_t)b * a.chunks + c) * a.region + (q - cb)];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (p + u < p1) cand[p + u] = v[u];
+      }
     }
   }
   const int nc = overflow ? 0 : (int)total;
@@ -1280,10 +1307,22 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
     // per-chunk counts of selected candidates -> output offsets; then each
     // selected candidate goes to its chunk's offset plus its rank by index
     // among the chunk's selected ones (chunks are ascending entry ranges)
+    // selected ones among slots [i0, i1) with an index below that of v
+    // (larger low word), or all of them (v = 0); reads eight at a time
+    auto count_sel = [&](uint32_t i0, uint32_t i1, uint64_t v) {
+      uint32_t n = 0;
+      for (uint32_t i = i0; i < i1; i += 8) {
+        uint64_t w[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) w[u] = i + u < i1 ? cand[i + u] : 0ull;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) n += (w[u] >= thr) && (uint32_t)w[u] > (uint32_t)v;
+      }
+      return n;
+    };
     uint32_t mine_sel = 0;
     for (int c = c0; c < c1; ++c) {
-      uint32_t m = 0;
-      for (uint32_t j = coff[c]; j < coff[c + 1]; ++j) m += cand[j] >= thr;
+      const uint32_t m = count_sel(coff[c], coff[c + 1], 0ull);
       hs.csel[c] = (uint16_t)m;
       mine_sel += m;
     }
@@ -1295,20 +1334,20 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
       ob += m;
     }
     __syncthreads();
-    for (uint32_t j = t; j < total; j += NT) {
+    // this thread's slots again, walking the chunks from that of p0; a
+    // selected candidate goes to its chunk's offset plus the number of
+    // selected ones of its chunk with a smaller index
+    int c = ch0;
+    uint32_t cb = p0 < p1 ? coff[c] : 0, ce = p0 < p1 ? coff[c + 1] : 0;
+    for (uint32_t j = p0; j < p1; ++j) {
+      while (j >= ce) {
+        ++c;
+        cb = ce;
+        ce = coff[c + 1];
+      }
       const uint64_t v = cand[j];
       if (v < thr) continue;
-      int lo = 0, hi = a.chunks;                             // chunk of slot j
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (coff[mid] <= j) lo = mid; else hi = mid;
-      }
-      uint32_t rank = 0;                                     // selected with a smaller index
-      for (uint32_t i = coff[lo]; i < coff[lo + 1]; ++i) {
-        const uint64_t w = cand[i];
-        rank += (w >= thr) && ((uint32_t)w > (uint32_t)v);  // larger low word = smaller index
-      }
-      const uint32_t o = hs.csel[lo] + rank;
+      const uint32_t o = hs.csel[c] + count_sel(cb, ce, v);
       if (o < (uint32_t)a.k) out[o] = (int32_t)(0xffffffffu - (uint32_t)v);
     }
     for (int j = (int)nsel + t; j < a.k; j += NT) out[j] = -1;
