@@ -190,17 +190,16 @@ def sq_summary(directory, title, command):
     if not files:
         raise SystemExit(f"no counter_collection.csv under {directory}")
     acc = {}
-    grid = {}
     for f in files:
         with open(f) as fh:
             for r in csv.DictReader(fh):
-                key = r["Kernel_Name"]
+                key = (r["Kernel_Name"], r.get("Grid_Size", ""), r.get("Workgroup_Size", ""))
                 acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-                grid[key] = (r.get("Grid_Size", ""), r.get("Workgroup_Size", ""))
-    print(f"# {title}\n# command: {command}\n# per dispatch, averaged over the dispatches of each kernel")
+    print(f"# {title}\n# command: {command}\n# per dispatch, averaged over the dispatches of each kernel "
+          f"and grid (grid in threads)")
     for key in sorted(acc):
-        g, w = grid[key]
-        print(f"\n{key}  (grid {g}, workgroup {w})")
+        name, g, w = key
+        print(f"\n{name}  (grid {g}, workgroup {w})")
         for c, v in sorted(acc[key].items()):
             print(f"  {c:28s} {sum(v) / len(v):16.1f}")
 
