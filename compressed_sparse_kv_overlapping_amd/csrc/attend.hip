@@ -1222,6 +1222,48 @@ __global__ __launch_bounds__(256) void merge_kernel(const P* __restrict__ o_part
   const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (bh >= BH) return;
   const float* lp = lse_part + bh * S;
+  if (S <= 8) {
+    // up to eight splits: the partial rows are loaded together with the lse
+    // values rather than after them (one memory latency, not two).  When
+    // every split is empty all weights are 0 and the rows (zeros) add 0.
+    float v[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < S) {
+        Row8<P>::load(o_part + (bh * S + u) * kDv + lane * 8, v[u]);
+      } else {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) v[u][d] = 0.f;
+      }
+    }
+    const float ls = lane < S ? lp[lane] : -INFINITY;
+    float m8 = ls;
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) m8 = fmaxf(m8, __shfl_xor(m8, off, 64));
+    m8 = __shfl(m8, 0, 64);                                  // lanes 0..7 hold the splits
+    const float sk = sink ? sink[bh % H] : -INFINITY;
+    m8 = fmaxf(m8, sk);
+    const bool any = m8 != -INFINITY;
+    const float wl = (any && lane < S) ? __expf(ls - m8) : 0.f;
+    float t8 = wl;
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) t8 += __shfl_xor(t8, off, 64);
+    t8 = __shfl(t8, 0, 64);
+    if (any && sk != -INFINITY) t8 += __expf(sk - m8);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = __shfl(wl, u, 64);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[d] = fmaf(w, v[u][d], acc[d]);
+    }
+    const float inv = t8 > 0.f ? 1.f / t8 : 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[d] *= inv;
+    Row8<T>::store(out + bh * kDv + lane * 8, acc);
+    if (lse && lane == 0) lse[bh] = t8 > 0.f ? m8 + __logf(t8) : -INFINITY;
+    return;
+  }
   float mx = -INFINITY;
   for (int s = lane; s < S; s += 64) mx = fmaxf(mx, lp[s]);
 #pragma unroll

@@ -249,10 +249,12 @@ def test_attention_sink(dt):
     np.testing.assert_allclose(lse.cpu().numpy(), np.tile(sink_h, (Bs, 1)), rtol=1e-6)
 
 
-def test_merge_of_split_partials():
+@pytest.mark.parametrize("S", [7, 12])
+def test_merge_of_split_partials(S):
     """cskv_merge combines oracle partials over a row partition into the
-    oracle's unsplit result."""
-    B, H, N, S = 2, 32, 300, 7
+    oracle's unsplit result (up to eight splits load every row with the lse
+    values; more take the lse first)."""
+    B, H, N = 2, 32, 300
     q = _rand(98, 0, 1, (B, H, E), wl.DT_F32, 1 / 24)
     ent = _rand(98, 0, 2, (N, E), wl.DT_F32)
     parts = np.array_split(np.arange(N), S - 1)
@@ -280,6 +282,25 @@ def test_merge_of_split_partials():
     ro, rl = oracle.hca_attend(q, ent, wl.DT_F32, sink=sink_h)
     assert rowwise_err(host_f64(out), ro) <= 1e-5
     np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=1e-5)
+
+
+@pytest.mark.parametrize("S", [3, 12])
+def test_merge_of_empty_splits(S):
+    """Every split empty (lse -inf, zero rows): the output is 0 and the lse
+    -inf, or with a sink, the sink's logit."""
+    B, H = 2, 8
+    o_part = torch.zeros(B, H, S, 512, dtype=torch.float32, device="cuda")
+    l_part = torch.full((B, H, S), -np.inf, dtype=torch.float32, device="cuda")
+    out, lse = _cskv().merge(o_part, l_part, dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert (host_f64(out) == 0).all()
+    assert np.isneginf(lse.cpu().numpy()).all()
+    sink_h = np.linspace(-1.0, 3.0, H)
+    out, lse = _cskv().merge(o_part, l_part, dtype=torch.float32,
+                             sink=torch.from_numpy(sink_h.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    assert (host_f64(out) == 0).all()
+    np.testing.assert_allclose(lse.cpu().numpy(), np.tile(sink_h, (B, 1)), rtol=1e-6)
 
 
 def prefill_sample(B, n=64):
