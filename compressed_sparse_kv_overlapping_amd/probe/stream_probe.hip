@@ -6,7 +6,9 @@
 //
 // Layout of the work as in the fused compressor: 256 blocks of 16 waves,
 // each wave streaming a contiguous range of rows, one 16-byte load a lane
-// per row and array, eight rows in flight.  Modes:
+// per row and array, eight rows in flight.  The rows are read with
+// non-temporal loads, as the compressor reads them (read once, no cache
+// allocation); the entry rows are written with ordinary stores.  Modes:
 //   0  reads only
 //   1  reads, with the entry rows written as the rows stream (the mix)
 //   2  the entry-row writes only
@@ -32,6 +34,11 @@ __global__ __launch_bounds__(64 * kWaves) void stream_probe_kernel(const uint4* 
   const int64_t r0 = wave * per, r1 = r0 + per < rows ? r0 + per : rows;
   uint32_t acc = 0;
   auto fold = [&](uint4 v) { acc ^= v.x ^ (v.y << 1) ^ (v.z << 2) ^ (v.w << 3); };
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  auto ld = [](const uint4* p) {
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+  };
   auto put = [&](int64_t r) {                                 // entry rows closed at row r
     const uint4 w = make_uint4(acc, acc + 1, acc + 2, acc + 3);
     if ((r & 3) == 3) o4[(r >> 2) * 64 + lane] = w;
@@ -45,8 +52,8 @@ __global__ __launch_bounds__(64 * kWaves) void stream_probe_kernel(const uint4* 
     for (int i = 0; i < kDepth; ++i) {
       const int64_t r = r0 + i;
       if (r < r1) {
-        bx[i] = x[r * 64 + lane];
-        bz[i] = z[r * 64 + lane];
+        bx[i] = ld(x + r * 64 + lane);
+        bz[i] = ld(z + r * 64 + lane);
       }
     }
     for (int64_t rb = r0; rb < r1; rb += kDepth) {
@@ -59,8 +66,8 @@ __global__ __launch_bounds__(64 * kWaves) void stream_probe_kernel(const uint4* 
           if (mode == 1) put(r);
           const int64_t rn = r + kDepth;
           if (rn < r1) {
-            bx[i] = x[rn * 64 + lane];
-            bz[i] = z[rn * 64 + lane];
+            bx[i] = ld(x + rn * 64 + lane);
+            bz[i] = ld(z + rn * 64 + lane);
           }
         }
       }
