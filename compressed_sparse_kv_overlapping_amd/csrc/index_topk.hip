@@ -960,20 +960,42 @@ __device__ uint32_t block_kth_largest(KeyAt key_at, int n, uint32_t kk, uint32_t
 // registers (else they are re-read from L2): one histogram of 4096 bins over
 // their key range, then the few maxima in the bin that holds the k-th are
 // ranked directly (a crowded bin takes further histogram passes).
-template <int NT>
-__global__ __launch_bounds__(NT) void idx_threshold_kernel(IdxArgs a) {
+// Loads and stores of data that other blocks of the same launch write or
+// read (COH): system-scope accesses, which write through and read past the
+// XCD's L2, so that no cache write-back or invalidation is needed between
+// the phases of the fused decode kernel.  Plain accesses otherwise.
+template <bool COH, class U>
+__device__ __forceinline__ U ld_c(const U* p) {
+  if constexpr (COH) return __hip_atomic_load(const_cast<U*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  else return *p;
+}
+template <bool COH, class U>
+__device__ __forceinline__ void st_c(U* p, U v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  else *p = v;
+}
+
+template <int NT> struct ThrLds {
+  uint32_t hist[4096], part[NT / 32];
+  uint32_t sh_digit, sh_above, sh_n, sh_tau;
+};
+
+// the threshold of query b, by a block of NT threads (LDS in s)
+template <int NT, bool COH = false>
+__device__ void threshold_query(const IdxArgs& a, const int b, ThrLds<NT>& s) {
   constexpr int kPer = 16;
   constexpr uint32_t kRank = 128;                            // bin members ranked directly
-  __shared__ uint32_t hist[4096], part[NT / 32];
-  __shared__ uint32_t sh_digit, sh_above, sh_n, sh_tau;
-  const int b = blockIdx.x, t = threadIdx.x;
+  uint32_t* hist = s.hist;
+  uint32_t* part = s.part;
+  uint32_t &sh_digit = s.sh_digit, &sh_above = s.sh_above, &sh_n = s.sh_n, &sh_tau = s.sh_tau;
+  const int t = threadIdx.x;
   const uint32_t* gm = a.gmax + (int64_t)b * a.G;
   const bool held = a.G <= kPer * NT;
   uint32_t v[kPer];
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int i = t + r * NT;
-    v[r] = held && i < a.G ? gm[i] : 0u;
+    v[r] = held && i < a.G ? ld_c<COH>(gm + i) : 0u;
   }
   auto each = [&](auto&& f) {                                // every non-empty group's maximum
     if (held) {
@@ -982,7 +1004,7 @@ __global__ __launch_bounds__(NT) void idx_threshold_kernel(IdxArgs a) {
         if (v[r] != 0u) f(v[r]);
     } else {
       for (int i = t; i < a.G; i += NT) {
-        const uint32_t x = gm[i];
+        const uint32_t x = ld_c<COH>(gm + i);
         if (x != 0u) f(x);
       }
     }
@@ -995,7 +1017,7 @@ __global__ __launch_bounds__(NT) void idx_threshold_kernel(IdxArgs a) {
   block_minmax<NT>(mn, mx, part, &lo, &hi);
   const int nv = n_visible(a, b);
   if (nv <= a.k || nonempty < (uint32_t)a.k) {
-    if (t == 0) a.thr[b] = 0u;
+    if (t == 0) st_c<COH>(a.thr + b, 0u);
     return;
   }
   const uint32_t range = hi - lo;
@@ -1025,16 +1047,22 @@ __global__ __launch_bounds__(NT) void idx_threshold_kernel(IdxArgs a) {
       if (gt < kk && kk <= ge) sh_tau = x;                   // equal maxima write the same value
     }
     __syncthreads();
-    if (t == 0) a.thr[b] = sh_tau;
+    if (t == 0) st_c<COH>(a.thr + b, sh_tau);
     return;
   }
   const uint32_t blo = lo + (bin << shift), span = (1u << shift) - 1u;
   const uint32_t bhi = hi - blo > span ? blo + span : hi;
   uint32_t above;
   const uint32_t tau = block_kth_largest<12, NT>(
-      [&](int i, uint32_t& key) { key = gm[i]; return key != 0u; }, a.G, kk, blo, bhi, hist, part,
+      [&](int i, uint32_t& key) { key = ld_c<COH>(gm + i); return key != 0u; }, a.G, kk, blo, bhi, hist, part,
       &sh_digit, &sh_above, &above);
-  if (t == 0) a.thr[b] = tau;
+  if (t == 0) st_c<COH>(a.thr + b, tau);
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void idx_threshold_kernel(IdxArgs a) {
+  __shared__ ThrLds<NT> s;
+  threshold_query<NT>(a, blockIdx.x, s);
 }
 
 // ----------------------------------------------------------------- final
@@ -1115,22 +1143,30 @@ constexpr int kMem = 512;                    // bin members ranked exactly
 // CAP: candidate capacity in LDS (2048 for k <= 1024, so that five blocks fit
 // on a compute unit; 8192 otherwise).  A query with more candidates takes
 // the streaming path, with the same result.
-template <class T, int NT, int CAP>
-__global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
-  static_assert(CAP <= kCap && CAP / 2 <= kMaxK, "capacity");
+template <int NT, int CAP> struct FinalLds {
   // candidates (list) or, on overflow, the k <= CAP / 2 selected indices
-  __shared__ union { uint64_t cand[CAP]; int32_t sel[CAP / 2]; } cs;
+  union { uint64_t cand[CAP]; int32_t sel[CAP / 2]; } cs;
   // the histogram, then the members of the k-th bin, then the chunks' output
   // offsets
-  __shared__ union { uint32_t hist[1 << kFinalBB]; uint64_t mem[kMem]; uint16_t csel[kMaxChunks]; } hs;
-  __shared__ uint16_t coff[kMaxChunks + 1];                  // list offset of each chunk
-  __shared__ uint32_t part[NT / 32];
-  __shared__ uint32_t sh_digit, sh_above, sh_nsel, sh_over;
-  __shared__ uint64_t sh_thr;
-  uint64_t* cand = cs.cand;
-  int32_t* sel = cs.sel;
+  union { uint32_t hist[1 << kFinalBB]; uint64_t mem[kMem]; uint16_t csel[kMaxChunks]; } hs;
+  uint16_t coff[kMaxChunks + 1];                             // list offset of each chunk
+  uint32_t part[NT / 32];
+  uint32_t sh_digit, sh_above, sh_nsel, sh_over;
+  uint64_t sh_thr;
+};
+
+// the selection of query b, by a block of NT threads (LDS in s)
+template <class T, int NT, int CAP, bool COH = false>
+__device__ void final_query(const IdxArgs& a, const int b, FinalLds<NT, CAP>& s) {
+  static_assert(CAP <= kCap && CAP / 2 <= kMaxK, "capacity");
+  uint64_t* cand = s.cs.cand;
+  int32_t* sel = s.cs.sel;
+  auto& hs = s.hs;
   uint32_t* hist = hs.hist;
-  const int b = blockIdx.x;
+  uint16_t* coff = s.coff;
+  uint32_t* part = s.part;
+  uint32_t &sh_digit = s.sh_digit, &sh_above = s.sh_above, &sh_nsel = s.sh_nsel, &sh_over = s.sh_over;
+  uint64_t& sh_thr = s.sh_thr;
   const int t = threadIdx.x;
   const int nv = n_visible(a, b);
   int32_t* out = a.out + (int64_t)b * a.k;
@@ -1147,7 +1183,7 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
   uint32_t mine = 0;
   bool full = !listed;
   for (int c = c0; c < c1; ++c) {
-    const uint32_t n = a.cnt[(int64_t)b * a.chunks + c];
+    const uint32_t n = ld_c<COH>(a.cnt + (int64_t)b * a.chunks + c);
     full |= n > (uint32_t)a.region;
     mine += n > (uint32_t)a.region ? (uint32_t)a.region : n;
   }
@@ -1166,7 +1202,7 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
     uint32_t at = base;
     for (int c = c0; c < c1; ++c) {
       coff[c] = (uint16_t)at;
-      const uint32_t n = a.cnt[(int64_t)b * a.chunks + c];
+      const uint32_t n = ld_c<COH>(a.cnt + (int64_t)b * a.chunks + c);
       at += n > (uint32_t)a.region ? (uint32_t)a.region : n;
     }
     if (t == 0) coff[a.chunks] = (uint16_t)total;
@@ -1194,7 +1230,7 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
               cb = ce;
               ce = coff[c + 1];
             }
-            v[u] = a.cand[((int64_t)b * a.chunks + c) * a.region + (q - cb)];
+            v[u] = ld_c<COH>(a.cand + ((int64_t)b * a.chunks + c) * a.region + (q - cb));
           }
         }
 #pragma unroll
@@ -1383,6 +1419,242 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
   for (int j = t; j < a.k; j += NT) out[j] = sel[j];
 }
 
+template <class T, int NT, int CAP>
+__global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
+  __shared__ FinalLds<NT, CAP> s;
+  final_query<T, NT, CAP>(a, blockIdx.x, s);
+}
+
+// ------------------------------------------------------------ decode, fused
+//
+// The decode selection (up to 32 queries over one shared, fully visible key
+// set) in a single launch: the four steps above run as phases of one kernel,
+// separated by grid-wide barriers, with one block of 1024 threads resident
+// on every compute unit.  Block c owns the C keys [c C, c C + C):
+//  A. scores its keys for every query (the same 16x16 MFMA steps as the
+//     score passes, so the same raw scores), keeps the raw scores in LDS and
+//     writes its groups' maxima;
+//  B. (blocks b < B) the threshold of query b, as idx_threshold_kernel;
+//  C. appends its candidates, read from LDS rather than recomputed, to the
+//     per-(query, block) regions;
+//  D. (blocks b < B) the exact selection of query b, as idx_final_kernel.
+// The result is that of the four launches.  The barrier counts arrivals in
+// the workspace (zeroed by a one-block kernel just before); its wait is
+// bounded, so a grid that is not resident ends with an error flag set
+// instead of hanging.
+constexpr int kDecThreads = 1024;
+constexpr int kDecPad = 4;                                   // row pad of the score array (floats)
+constexpr int kDecScores = 32 * (1024 + kDecPad);            // 128.5 KB of raw scores
+constexpr uint32_t kDecSpin = 1u << 20;                      // barrier polls before giving up
+
+constexpr int kDecMaxBlocks = 256;                           // flag words: four a lane of one wave
+constexpr int kDecFlagStride = 16;                           // flag words 64 bytes apart
+
+struct DecodeBar {
+  uint32_t err, pad0[15], go, pad1[15];
+  uint32_t flags[kDecMaxBlocks * kDecFlagStride];
+};
+
+__global__ void idx_decode_reset_kernel(DecodeBar* bar) {
+  for (int i = threadIdx.x; i < kDecMaxBlocks * kDecFlagStride; i += blockDim.x) bar->flags[i] = 0u;
+  if (threadIdx.x == 0) { bar->err = 0u; bar->go = 0u; }
+}
+
+// Every block's writes before it are visible to every block after it,
+// for the data the blocks exchange through system-scope accesses (ld_c /
+// st_c with COH): those write through and read past the L2s, so the
+// barrier needs no cache write-back or invalidation, only that each wave's
+// stores have completed (a block barrier alone does not wait for them).
+// Block c then publishes barrier number `epoch` in its own flag word (no
+// shared counter: same-address atomics from every block serialise); block 0
+// polls all the flags, four a lane, and raises the go word, which the other
+// blocks poll with one lane.  Every wait is bounded: past the limit the
+// error word is set and the block goes on.
+__device__ __forceinline__ void grid_barrier(DecodeBar* bar, uint32_t epoch) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int nblk = gridDim.x;
+  if (threadIdx.x == 0) st_c<true>(&bar->flags[blockIdx.x * kDecFlagStride], epoch);
+  if (threadIdx.x < 64) {
+    uint32_t spins = 0;
+    if (blockIdx.x == 0) {
+      const int f0 = 4 * threadIdx.x;
+      for (;;) {
+        bool done = true;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (f0 + u < nblk) done &= ld_c<true>(&bar->flags[(f0 + u) * kDecFlagStride]) >= epoch;
+        if (__all(done)) break;
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins == kDecSpin) {
+          if (threadIdx.x == 0) st_c<true>(&bar->err, 1u);
+          break;
+        }
+      }
+      if (threadIdx.x == 0) st_c<true>(&bar->go, epoch);
+    } else if (threadIdx.x == 0) {
+      while (ld_c<true>(&bar->go) < epoch) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins == kDecSpin) {
+          st_c<true>(&bar->err, 1u);
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int CAP> struct DecodeLds {
+  union {
+    float sc[kDecScores];                                    // raw scores [16 NQB][C + kDecPad]
+    FinalLds<kDecThreads, CAP> fin;                          // phase D (the scores are done)
+  } u;
+  ThrLds<kDecThreads> thr;                                   // phase B
+  uint32_t lcnt[32];                                         // phase C: candidates per query
+  float traw[32];                                            // phase C: raw thresholds
+};
+
+// C keys a block (a multiple of 256: whole 16-key tiles for each of the 16
+// waves); bar: the barrier words.
+template <class T, int NQB, int CAP>
+__global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int C, DecodeBar* bar) {
+  static_assert(sizeof(FinalLds<kDecThreads, CAP>) <= sizeof(float) * kDecScores, "LDS union");
+  __shared__ DecodeLds<CAP> sh;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int blk = blockIdx.x;
+  const int P = C + kDecPad;                                 // score row pitch
+  const int64_t c0 = (int64_t)blk * C;
+  float* sc = sh.u.sc;
+
+  // A. raw scores of the block's keys: wave w takes keys c0 + w C/16 + ...
+  {
+    typename Elem<T>::QF qf[NQB][2];
+#pragma unroll
+    for (int j = 0; j < NQB; ++j) {
+      const int q = 16 * j + col;
+      if (q < a.B) {
+        query_frags<T>(qf[j], a, q, g);
+      } else {
+        typename Elem<T>::QF z{};
+        qf[j][0] = z;
+        qf[j][1] = z;
+      }
+    }
+    const char* kb = reinterpret_cast<const char*>(a.keys);
+    const int per = C / 16;                                  // keys per wave (a multiple of 16 and of GS)
+    float pinf = INFINITY;
+    asm volatile("" : "+v"(pinf));
+    const int GS = a.GS;
+    // group maxima as the tiles go: a lane's four scores of a tile lie in one
+    // group (GS >= 4); GS = 8 joins lane groups g and g ^ 1, GS >= 16 all
+    // four, and larger groups run across the wave's consecutive tiles
+    float gm[NQB];
+#pragma unroll
+    for (int j = 0; j < NQB; ++j) gm[j] = -INFINITY;
+    auto put_max = [&](const int q, const int64_t key, const float m) {
+      const int64_t gi = key >> a.gs_shift;
+      if (q < a.B && gi < a.G)
+        st_c<true>(a.gmax + (int64_t)q * a.G + gi, (m == -INFINITY) ? 0u : score_key(m * a.scale));
+    };
+    // tiles in flight a wave (fp32 fragments are twice the registers)
+    constexpr int TF = sizeof(T) == 4 ? 2 : 4;
+    for (int t0 = 0; t0 < per; t0 += 16 * TF) {
+      Frag<T> kf[TF][2];
+#pragma unroll
+      for (int u = 0; u < TF; ++u) {
+        const int64_t er = c0 + wave * per + t0 + 16 * u + col;
+        if (t0 + 16 * u < per && er < a.N) {
+          key_frags<T>(kf[u], kb, a.ksc, er, g);
+        } else {
+          Frag<T> z{};
+          kf[u][0] = z;
+          kf[u][1] = z;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < TF; ++u) {
+        const int el = wave * per + t0 + 16 * u;             // first key of the tile, in the block
+        if (t0 + 16 * u < per) {
+          typename Elem<T>::QF kd[2];
+          key_decode<T>(kd, kf[u]);
+#pragma unroll
+          for (int j = 0; j < NQB; ++j) {
+            f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f};
+            mma16(S, kd[0], qf[j][0]);
+            mma16(S, kd[1], qf[j][1]);
+            // S[i]: query 16 j + col, key c0 + el + 4 g + i (-inf past N)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (c0 + el + 4 * g + i >= a.N) S[i] = -INFINITY;
+            *reinterpret_cast<f32x4*>(sc + (16 * j + col) * P + el + 4 * g) = S;
+            float m = max_raw(max_raw(S[0], S[1], pinf), max_raw(S[2], S[3], pinf), pinf);
+            if (GS == 4) {
+              put_max(16 * j + col, c0 + el + 4 * g, m);
+            } else if (GS == 8) {
+              m = max_raw(m, __shfl_xor(m, 16, 64), pinf);
+              if ((g & 1) == 0) put_max(16 * j + col, c0 + el + 4 * g, m);
+            } else {
+              m = max_raw(m, __shfl_xor(m, 16, 64), pinf);
+              m = max_raw(m, __shfl_xor(m, 32, 64), pinf);
+              gm[j] = max_raw(gm[j], m, pinf);
+              if (((el + 16) & (GS - 1)) == 0) {             // the tile closes a group
+                if (g == 0) put_max(16 * j + col, c0 + el, gm[j]);
+                gm[j] = -INFINITY;
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  grid_barrier(bar, 1u);
+
+  // B. thresholds: query q in block q
+  if (blk < a.B) threshold_query<kDecThreads, true>(a, blk, sh.thr);
+  grid_barrier(bar, 2u);
+
+  // C. candidates >= the threshold, from the scores in LDS
+  if (threadIdx.x < a.B) {
+    const uint32_t th = ld_c<true>(a.thr + threadIdx.x);
+    sh.traw[threadIdx.x] = raw_threshold(th != 0u ? key_score(th) : -INFINITY, a.scale);
+    sh.lcnt[threadIdx.x] = 0u;
+  }
+  __syncthreads();
+  {
+    // each lane reads back the scores it wrote in phase A
+    const int per = C / 16;
+    for (int t = 0; t < per; t += 16) {
+      const int el = wave * per + t;
+#pragma unroll
+      for (int j = 0; j < NQB; ++j) {
+        const int q = 16 * j + col;
+        if (q >= a.B) continue;
+        const f32x4 S = *reinterpret_cast<const f32x4*>(sc + q * P + el + 4 * g);
+        const float tr = sh.traw[q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t e = c0 + el + 4 * g + i;
+          if (S[i] >= tr && e < a.N) {
+            const uint32_t slot = atomicAdd(&sh.lcnt[q], 1u);
+            if (slot < (uint32_t)a.region)
+              st_c<true>(a.cand + ((int64_t)q * a.chunks + blk) * a.region + slot,
+                         composite(score_key(S[i] * a.scale), (int)e));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < a.B) st_c<true>(a.cnt + (int64_t)threadIdx.x * a.chunks + blk, sh.lcnt[threadIdx.x]);
+  grid_barrier(bar, 3u);
+
+  // D. the selections: query q in block q
+  if (blk < a.B) final_query<T, kDecThreads, CAP, true>(a, blk, sh.u.fin);
+}
+
 // ------------------------------------------------------------------ host
 
 // Group size: about 4k groups per query (so the k-th largest group maximum
@@ -1451,6 +1723,62 @@ constexpr int64_t kWideBelow = 256;
 int topk_max_k() { return kMaxK; }
 int64_t topk_max_entries() { return (int64_t)kMaxGroups * 64; }
 
+// The fused decode selection when it applies: shared, fully visible keys;
+// up to 32 queries; one resident block a compute unit holding its keys' raw
+// scores in LDS; its workspace layout within topk_workspace_bytes.  Returns
+// hipErrorNotSupported (nothing launched) when it does not apply.
+template <class T>
+static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, hipStream_t stream) {
+  if (p.B > 32 || p.k > kMaxK) return hipErrorNotSupported;
+  const int nqb = p.B <= 16 ? 1 : 2;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return hipErrorNotSupported;
+  // keys a block: a multiple of 256, as few blocks as give every compute unit
+  // at most one
+  int64_t C = ((p.N + cus - 1) / cus + 255) / 256 * 256;
+  if (C < 16 * (int64_t)a.GS) C = 16 * (int64_t)a.GS;       // a wave's keys hold whole groups
+  C = (C + 255) / 256 * 256;
+  const int64_t nb = (p.N + C - 1) / C;
+  // at least one block a query (a block takes one query's threshold and
+  // selection)
+  if (16 * nqb * (C + kDecPad) > kDecScores || nb < p.B || nb < 2 || nb > kDecMaxBlocks)
+    return hipErrorNotSupported;
+  const void* kern = nullptr;
+  const bool small = p.k <= 1024;
+  if (nqb == 1) kern = small ? (const void*)idx_decode_kernel<T, 1, 2048> : (const void*)idx_decode_kernel<T, 1, kCap>;
+  else kern = small ? (const void*)idx_decode_kernel<T, 2, 2048> : (const void*)idx_decode_kernel<T, 2, kCap>;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kDecThreads, 0) != hipSuccess ||
+      (int64_t)per_cu * cus < nb)
+    return hipErrorNotSupported;
+  // candidate regions: room for 16x each block's share of about 1.2k, at
+  // least 32 slots, at most the block's keys
+  int64_t r = (16 * (int64_t)p.k + nb - 1) / nb;
+  r = r < 32 ? 32 : (r > C ? C : r);
+  a.chunks = (int)nb;
+  a.region = (int)r;
+  char* w = (char*)ws;
+  a.cand = (uint64_t*)w;            w += (size_t)p.B * nb * r * 8;
+  a.gmax = (uint32_t*)w;            w += (size_t)p.B * a.G * 4;
+  a.thr = (uint32_t*)w;             w += (size_t)p.B * 4;
+  a.cnt = (uint32_t*)w;             w += (size_t)p.B * nb * 4;
+  w = (char*)(((uintptr_t)w + 255) & ~(uintptr_t)255);
+  DecodeBar* bar = (DecodeBar*)w;   w += sizeof(DecodeBar);
+  if ((size_t)(w - (char*)ws) > topk_workspace_bytes(p.B, p.N, p.k)) return hipErrorNotSupported;
+  a.sraw = nullptr;
+  hipLaunchKernelGGL(idx_decode_reset_kernel, dim3(1), dim3(256), 0, stream, bar);
+#define CSKV_DECODE(NQB, CAPV) \
+  hipLaunchKernelGGL((idx_decode_kernel<T, NQB, CAPV>), dim3((unsigned)nb), dim3(kDecThreads), 0, stream, a, (int)C, bar)
+  if (nqb == 1 && small) CSKV_DECODE(1, 2048);
+  else if (nqb == 1) CSKV_DECODE(1, kCap);
+  else if (small) CSKV_DECODE(2, 2048);
+  else CSKV_DECODE(2, kCap);
+#undef CSKV_DECODE
+  return hipGetLastError();
+}
+
 template <class T>
 static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t stream) {
   IdxArgs a;
@@ -1497,6 +1825,10 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
   // that each query's serial steps run on a whole compute unit; 256 threads
   // otherwise (two blocks per compute unit)
   const bool wide = p.B < kWideBelow;
+  if (!per_seq && !p.q_pos) {
+    const hipError_t e = launch_decode_fused<T>(p, a, ws, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
   CSKV_SCORE_PASS(0);
   if (wide) hipLaunchKernelGGL(idx_threshold_kernel<1024>, dim3((unsigned)p.B), dim3(1024), 0, stream, a);
   else hipLaunchKernelGGL(idx_threshold_kernel<256>, dim3((unsigned)p.B), dim3(256), 0, stream, a);

@@ -145,6 +145,13 @@ int cskv_compress2(const void* raw_kv, const void* score_logits, int64_t T,
  *     cskv_index_topk_per_seq_workspace_size(B, N, k) bytes also keeps the
  *     raw scores between the selection's two passes, so that every key is
  *     read from memory once instead of twice (same result).
+ *   Decode selections (q_pos == NULL, shared keys, B <= 32, at least one
+ *   compute unit per query, and up to 1,024 keys per compute unit for 17 to
+ *   32 queries, 2,048 for 16 or fewer) run as one kernel whose phases meet
+ *   at grid-wide barriers: one block of 1024 threads per compute unit,
+ *   every block resident at once (blocks that start late, behind other work
+ *   on the GPU, are waited for).  Same result as the multi-launch path; the
+ *   same workspace.
  * Errors: INVALID_ARG (null pointers, B < 1, N < 1, k < 1, m < 1 with q_pos);
  * UNSUPPORTED (k > 4096); WORKSPACE.
  */

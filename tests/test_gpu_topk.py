@@ -356,3 +356,36 @@ def test_topk_mxfp4_many_queries_groups_of_32():
     rows = _sample_rows(B)
     s, v = oracle.index_scores_mxfp4(qc[rows], qs[rows], kc, ks, 0.5, q_pos=pos[rows], m=m)
     _exact(idx[rows], s, v, k)
+
+
+@pytest.mark.parametrize("dt", [wl.DT_BF16, wl.DT_E4M3, wl.DT_F32])
+@pytest.mark.parametrize("B,N,k", [(32, 1 << 18, 1024), (20, 100003, 333), (7, 30000, 64)])
+def test_topk_decode_one_launch_equals_four(dt, B, N, k):
+    """Up to 32 queries over shared keys with every entry visible run the
+    selection in one launch (its phases separated by grid barriers);
+    positions that make every entry visible take the four launches instead.
+    Both compute the same scores in the same order, so the selections are
+    identical, and the one-launch result matches the oracle."""
+    rng_cfg = 105
+    q = wl.normal(rng_cfg, N, 1, (B, 64))
+    kk = wl.normal(rng_cfg, N, 2, (N, 64))
+    if dt == wl.DT_E4M3:
+        sq, sk = wl.e4m3_scale(q), wl.e4m3_scale(kk)
+        qI, kI, scale = wl.e4m3_encode(q, sq), wl.e4m3_encode(kk, sk), sq * sk
+    else:
+        qI, kI, scale = wl.encode(q, dt).raw, wl.encode(kk, dt).raw, 0.61
+    idx1, s, v = _run(qI, kI, dt, k, scale=scale)
+    check_selection(idx1, s, v, k)
+    idx4, _, _ = _run(qI, kI, dt, k, scale=scale, q_pos=np.full(B, 4 * N - 1), m=4)
+    np.testing.assert_array_equal(idx1, idx4)
+
+
+def test_topk_mxfp4_decode_one_launch_equals_four():
+    """The same for MXFP4 keys at the 1M-token decode shape."""
+    B, N, k = 32, 1 << 18, 1024
+    qc, qs = wl.mxfp4_encode(wl.normal(106, 0, 1, (B, 64)))
+    kc, ks = wl.mxfp4_encode(wl.normal(106, 0, 2, (N, 64)))
+    idx1, s, v = _run_mx(qc, qs, kc, ks, k)
+    _exact(idx1, s, v, k)
+    idx4, _, _ = _run_mx(qc, qs, kc, ks, k, q_pos=np.full(B, 4 * N - 1), m=4)
+    np.testing.assert_array_equal(idx1, idx4)
