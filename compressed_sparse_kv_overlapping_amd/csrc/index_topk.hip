@@ -975,19 +975,15 @@ __device__ __forceinline__ void st_c(U* p, U v) {
   else *p = v;
 }
 
-template <int NT> struct ThrLds {
-  uint32_t hist[4096], part[NT / 32];
-  uint32_t sh_digit, sh_above, sh_n, sh_tau;
-};
-
-// the threshold of query b, by a block of NT threads (LDS in s)
+// The threshold of query b, by a block of NT threads.  LDS: hist[4096],
+// part[NT / 32] and four words, each its own __shared__ object in the
+// caller (inlined there, so the compiler sees that they do not overlap).
 template <int NT, bool COH = false>
-__device__ void threshold_query(const IdxArgs& a, const int b, ThrLds<NT>& s) {
+__device__ __forceinline__ void threshold_query(const IdxArgs& a, const int b, uint32_t* hist, uint32_t* part,
+                                                uint32_t& sh_digit, uint32_t& sh_above, uint32_t& sh_n,
+                                                uint32_t& sh_tau) {
   constexpr int kPer = 16;
   constexpr uint32_t kRank = 128;                            // bin members ranked directly
-  uint32_t* hist = s.hist;
-  uint32_t* part = s.part;
-  uint32_t &sh_digit = s.sh_digit, &sh_above = s.sh_above, &sh_n = s.sh_n, &sh_tau = s.sh_tau;
   const int t = threadIdx.x;
   const uint32_t* gm = a.gmax + (int64_t)b * a.G;
   const bool held = a.G <= kPer * NT;
@@ -1061,8 +1057,9 @@ __device__ void threshold_query(const IdxArgs& a, const int b, ThrLds<NT>& s) {
 
 template <int NT>
 __global__ __launch_bounds__(NT) void idx_threshold_kernel(IdxArgs a) {
-  __shared__ ThrLds<NT> s;
-  threshold_query<NT>(a, blockIdx.x, s);
+  __shared__ uint32_t hist[4096], part[NT / 32];
+  __shared__ uint32_t sh_digit, sh_above, sh_n, sh_tau;
+  threshold_query<NT>(a, blockIdx.x, hist, part, sh_digit, sh_above, sh_n, sh_tau);
 }
 
 // ----------------------------------------------------------------- final
@@ -1143,30 +1140,26 @@ constexpr int kMem = 512;                    // bin members ranked exactly
 // CAP: candidate capacity in LDS (2048 for k <= 1024, so that five blocks fit
 // on a compute unit; 8192 otherwise).  A query with more candidates takes
 // the streaming path, with the same result.
-template <int NT, int CAP> struct FinalLds {
-  // candidates (list) or, on overflow, the k <= CAP / 2 selected indices
-  union { uint64_t cand[CAP]; int32_t sel[CAP / 2]; } cs;
-  // the histogram, then the members of the k-th bin, then the chunks' output
-  // offsets
-  union { uint32_t hist[1 << kFinalBB]; uint64_t mem[kMem]; uint16_t csel[kMaxChunks]; } hs;
-  uint16_t coff[kMaxChunks + 1];                             // list offset of each chunk
-  uint32_t part[NT / 32];
-  uint32_t sh_digit, sh_above, sh_nsel, sh_over;
-  uint64_t sh_thr;
-};
+// candidates (list) or, on overflow, the k <= CAP / 2 selected indices
+template <int CAP> union FinalCands { uint64_t cand[CAP]; int32_t sel[CAP / 2]; };
+// the histogram, then the members of the k-th bin, then the chunks' output
+// offsets
+union FinalHist { uint32_t hist[1 << kFinalBB]; uint64_t mem[kMem]; uint16_t csel[kMaxChunks]; };
 
-// the selection of query b, by a block of NT threads (LDS in s)
+// The selection of query b, by a block of NT threads.  LDS: the candidate
+// and histogram unions, coff[kMaxChunks + 1] (list offset of each chunk),
+// part[NT / 32] and five words, separate __shared__ objects in the callers
+// that can have them (inlined there, so the compiler sees that they do not
+// overlap).
 template <class T, int NT, int CAP, bool COH = false>
-__device__ void final_query(const IdxArgs& a, const int b, FinalLds<NT, CAP>& s) {
+__device__ __forceinline__ void final_query(const IdxArgs& a, const int b, FinalCands<CAP>& cs, FinalHist& hs,
+                                            uint16_t* coff, uint32_t* part, uint32_t& sh_digit,
+                                            uint32_t& sh_above, uint32_t& sh_nsel, uint32_t& sh_over,
+                                            uint64_t& sh_thr) {
   static_assert(CAP <= kCap && CAP / 2 <= kMaxK, "capacity");
-  uint64_t* cand = s.cs.cand;
-  int32_t* sel = s.cs.sel;
-  auto& hs = s.hs;
+  uint64_t* cand = cs.cand;
+  int32_t* sel = cs.sel;
   uint32_t* hist = hs.hist;
-  uint16_t* coff = s.coff;
-  uint32_t* part = s.part;
-  uint32_t &sh_digit = s.sh_digit, &sh_above = s.sh_above, &sh_nsel = s.sh_nsel, &sh_over = s.sh_over;
-  uint64_t& sh_thr = s.sh_thr;
   const int t = threadIdx.x;
   const int nv = n_visible(a, b);
   int32_t* out = a.out + (int64_t)b * a.k;
@@ -1421,8 +1414,13 @@ __device__ void final_query(const IdxArgs& a, const int b, FinalLds<NT, CAP>& s)
 
 template <class T, int NT, int CAP>
 __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
-  __shared__ FinalLds<NT, CAP> s;
-  final_query<T, NT, CAP>(a, blockIdx.x, s);
+  __shared__ FinalCands<CAP> cs;
+  __shared__ FinalHist hs;
+  __shared__ uint16_t coff[kMaxChunks + 1];
+  __shared__ uint32_t part[NT / 32];
+  __shared__ uint32_t sh_digit, sh_above, sh_nsel, sh_over;
+  __shared__ uint64_t sh_thr;
+  final_query<T, NT, CAP>(a, blockIdx.x, cs, hs, coff, part, sh_digit, sh_above, sh_nsel, sh_over, sh_thr);
 }
 
 // ------------------------------------------------------------ decode, fused
@@ -1505,28 +1503,28 @@ __device__ __forceinline__ void grid_barrier(DecodeBar* bar, uint32_t epoch) {
   __syncthreads();
 }
 
-template <int CAP> struct DecodeLds {
-  union {
-    float sc[kDecScores];                                    // raw scores [16 NQB][C + kDecPad]
-    FinalLds<kDecThreads, CAP> fin;                          // phase D (the scores are done)
-  } u;
-  ThrLds<kDecThreads> thr;                                   // phase B
-  uint32_t lcnt[32];                                         // phase C: candidates per query
-  float traw[32];                                            // phase C: raw thresholds
+// raw scores [16 NQB][C + kDecPad] (phases A to C), then phase D's lists
+template <int CAP> union DecodeScores {
+  float sc[kDecScores];
+  struct { FinalCands<CAP> cs; FinalHist hs; uint16_t coff[kMaxChunks + 1]; } fin;
 };
 
 // C keys a block (a multiple of 256: whole 16-key tiles for each of the 16
 // waves); bar: the barrier words.
 template <class T, int NQB, int CAP>
 __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int C, DecodeBar* bar) {
-  static_assert(sizeof(FinalLds<kDecThreads, CAP>) <= sizeof(float) * kDecScores, "LDS union");
-  __shared__ DecodeLds<CAP> sh;
+  __shared__ DecodeScores<CAP> u;
+  __shared__ uint32_t thist[4096], part[kDecThreads / 32];   // phases B and D
+  __shared__ uint32_t sh_digit, sh_above, sh_n, sh_tau, sh_over;
+  __shared__ uint64_t sh_thr;
+  __shared__ uint32_t lcnt[32];                              // phase C: candidates per query
+  __shared__ float traw[32];                                 // phase C: raw thresholds
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int blk = blockIdx.x;
   const int P = C + kDecPad;                                 // score row pitch
   const int64_t c0 = (int64_t)blk * C;
-  float* sc = sh.u.sc;
+  float* sc = u.sc;
 
   // A. raw scores of the block's keys: wave w takes keys c0 + w C/16 + ...
   {
@@ -1613,14 +1611,14 @@ __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int 
   grid_barrier(bar, 1u);
 
   // B. thresholds: query q in block q
-  if (blk < a.B) threshold_query<kDecThreads, true>(a, blk, sh.thr);
+  if (blk < a.B) threshold_query<kDecThreads, true>(a, blk, thist, part, sh_digit, sh_above, sh_n, sh_tau);
   grid_barrier(bar, 2u);
 
   // C. candidates >= the threshold, from the scores in LDS
   if (threadIdx.x < a.B) {
     const uint32_t th = ld_c<true>(a.thr + threadIdx.x);
-    sh.traw[threadIdx.x] = raw_threshold(th != 0u ? key_score(th) : -INFINITY, a.scale);
-    sh.lcnt[threadIdx.x] = 0u;
+    traw[threadIdx.x] = raw_threshold(th != 0u ? key_score(th) : -INFINITY, a.scale);
+    lcnt[threadIdx.x] = 0u;
   }
   __syncthreads();
   {
@@ -1633,12 +1631,12 @@ __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int 
         const int q = 16 * j + col;
         if (q >= a.B) continue;
         const f32x4 S = *reinterpret_cast<const f32x4*>(sc + q * P + el + 4 * g);
-        const float tr = sh.traw[q];
+        const float tr = traw[q];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t e = c0 + el + 4 * g + i;
           if (S[i] >= tr && e < a.N) {
-            const uint32_t slot = atomicAdd(&sh.lcnt[q], 1u);
+            const uint32_t slot = atomicAdd(&lcnt[q], 1u);
             if (slot < (uint32_t)a.region)
               st_c<true>(a.cand + ((int64_t)q * a.chunks + blk) * a.region + slot,
                          composite(score_key(S[i] * a.scale), (int)e));
@@ -1648,11 +1646,13 @@ __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int 
     }
   }
   __syncthreads();
-  if (threadIdx.x < a.B) st_c<true>(a.cnt + (int64_t)threadIdx.x * a.chunks + blk, sh.lcnt[threadIdx.x]);
+  if (threadIdx.x < a.B) st_c<true>(a.cnt + (int64_t)threadIdx.x * a.chunks + blk, lcnt[threadIdx.x]);
   grid_barrier(bar, 3u);
 
   // D. the selections: query q in block q
-  if (blk < a.B) final_query<T, kDecThreads, CAP, true>(a, blk, sh.u.fin);
+  if (blk < a.B)
+    final_query<T, kDecThreads, CAP, true>(a, blk, u.fin.cs, u.fin.hs, u.fin.coff, part, sh_digit, sh_above,
+                                           sh_n, sh_over, sh_thr);
 }
 
 // ------------------------------------------------------------------ host
