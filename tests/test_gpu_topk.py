@@ -389,3 +389,42 @@ def test_topk_mxfp4_decode_one_launch_equals_four():
     _exact(idx1, s, v, k)
     idx4, _, _ = _run_mx(qc, qs, kc, ks, k, q_pos=np.full(B, 4 * N - 1), m=4)
     np.testing.assert_array_equal(idx1, idx4)
+
+
+def test_topk_decode_in_a_replayed_graph():
+    """The one-launch decode selection (a reset kernel, then the selection
+    kernel) captured in a HIP graph with the workspace and allocation-free
+    entry points: every replay, with new queries copied in and the outputs
+    cleared in between and eager calls between the replays, equals the eager
+    result."""
+    cskv = _cskv()
+    B, N, k = 20, 100003, 333
+    kk = torch.from_numpy(wl.bf16_bits(wl.normal(107, 0, 2, (N, 64))).view(np.int16)).cuda()
+    keys = kk.view(torch.bfloat16)
+    q = torch.empty(B, 64, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(B, k, dtype=torch.int32, device="cuda")
+    out_na = torch.empty(B, k, dtype=torch.int32, device="cuda")
+    ref = torch.empty(B, k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(cskv.index_topk_workspace_size(B, N, k), dtype=torch.uint8, device="cuda")
+    ws_e = torch.empty_like(ws)
+
+    def draw(i):
+        return torch.from_numpy(wl.bf16_bits(wl.normal(107, i, 1, (B, 64))).view(np.int16)).cuda().view(torch.bfloat16)
+
+    q.copy_(draw(0))
+    cskv.index_topk(q, keys, k, idx_out=out, workspace=ws)          # warm up outside the capture
+    cskv.index_topk_noalloc(q, keys, k, idx_out=out_na)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cskv.index_topk(q, keys, k, idx_out=out, workspace=ws)
+        cskv.index_topk_noalloc(q, keys, k, idx_out=out_na)
+    for i in range(1, 5):
+        q.copy_(draw(i))
+        out.fill_(-7)
+        out_na.fill_(-7)
+        g.replay()
+        cskv.index_topk(q, keys, k, idx_out=ref, workspace=ws_e)       # eager, between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
+        assert torch.equal(out_na, ref), f"replay {i} (allocation-free)"
