@@ -24,6 +24,7 @@
 //     select over all its entries instead.
 #include <float.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1443,7 +1444,7 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
 constexpr int kDecThreads = 1024;
 constexpr int kDecPad = 4;                                   // row pad of the score array (floats)
 constexpr int kDecScores = 32 * (1024 + kDecPad);            // 128.5 KB of raw scores
-constexpr uint32_t kDecSpin = 1u << 20;                      // barrier polls before giving up
+constexpr uint32_t kDecSpin = 1u << 24;                      // barrier polls (tens of seconds) before giving up
 
 constexpr int kDecMaxBlocks = 256;                           // flag words: four a lane of one wave
 constexpr int kDecFlagStride = 16;                           // flag words 64 bytes apart
@@ -1723,6 +1724,18 @@ constexpr int64_t kWideBelow = 256;
 int topk_max_k() { return kMaxK; }
 int64_t topk_max_entries() { return (int64_t)kMaxGroups * 64; }
 
+// Per-device record of the last one-launch selection (see below).
+constexpr int kDecDevices = 64;
+struct DecodeGuard {
+  std::mutex mu;
+  hipStream_t stream = nullptr;
+  hipEvent_t ev = nullptr;
+};
+static DecodeGuard& decode_guard(int dev) {
+  static DecodeGuard guards[kDecDevices];
+  return guards[dev];
+}
+
 // The fused decode selection when it applies: shared, fully visible keys;
 // up to 32 queries; one resident block a compute unit holding its keys' raw
 // scores in LDS; its workspace layout within topk_workspace_bytes.  Returns
@@ -1731,9 +1744,15 @@ template <class T>
 static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, hipStream_t stream) {
   if (p.B > 32 || p.k > kMaxK) return hipErrorNotSupported;
   const int nqb = p.B <= 16 ? 1 : 2;
+  // Not under stream capture: the multi-launch path is captured instead
+  // (a replayed graph runs whenever its caller launches it, with no record
+  // below to keep two of these kernels apart).
   int dev = 0, cus = 0;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0 ||
+      hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone ||
+      dev < 0 || dev >= kDecDevices)
     return hipErrorNotSupported;
   // keys a block: a multiple of 256, as few blocks as give every compute unit
   // at most one
@@ -1768,6 +1787,23 @@ static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, 
   DecodeBar* bar = (DecodeBar*)w;   w += sizeof(DecodeBar);
   if ((size_t)(w - (char*)ws) > topk_workspace_bytes(p.B, p.N, p.k)) return hipErrorNotSupported;
   a.sraw = nullptr;
+  // Two of these kernels must not run at once: each could hold part of
+  // the chip while it waits for blocks of its own that cannot start.  Per
+  // device, the stream and completion event of the last launch are kept; a
+  // call on another stream while that launch may still run takes the
+  // multi-launch path.  (Kernels of other kinds running beside it only delay
+  // its barriers: their blocks finish and free their compute units.)
+  DecodeGuard& gd = decode_guard(dev);
+  std::lock_guard<std::mutex> lock(gd.mu);
+  if (gd.ev != nullptr && gd.stream != stream && hipEventQuery(gd.ev) != hipSuccess) {
+    (void)hipGetLastError();
+    return hipErrorNotSupported;
+  }
+  if (gd.ev == nullptr && hipEventCreateWithFlags(&gd.ev, hipEventDisableTiming) != hipSuccess) {
+    gd.ev = nullptr;
+    (void)hipGetLastError();
+    return hipErrorNotSupported;
+  }
   hipLaunchKernelGGL(idx_decode_reset_kernel, dim3(1), dim3(256), 0, stream, bar);
 #define CSKV_DECODE(NQB, CAPV) \
   hipLaunchKernelGGL((idx_decode_kernel<T, NQB, CAPV>), dim3((unsigned)nb), dim3(kDecThreads), 0, stream, a, (int)C, bar)
@@ -1776,7 +1812,10 @@ static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, 
   else if (small) CSKV_DECODE(2, 2048);
   else CSKV_DECODE(2, kCap);
 #undef CSKV_DECODE
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  gd.stream = stream;
+  return hipEventRecord(gd.ev, stream);
 }
 
 template <class T>

@@ -428,3 +428,30 @@ def test_topk_decode_in_a_replayed_graph():
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {i}"
         assert torch.equal(out_na, ref), f"replay {i} (allocation-free)"
+
+
+def test_topk_decode_on_two_streams_at_once():
+    """Decode selections issued on two streams at once (each with its own
+    workspace) equal the same selections run one at a time.  Two one-launch
+    selection kernels must never run together (each could hold part of the
+    chip while it waits for blocks of its own), so the second stream's call
+    takes the multi-launch path while the first may still be running."""
+    cskv = _cskv()
+    B, N, k = 32, 1 << 18, 1024
+    keys = torch.from_numpy(wl.bf16_bits(wl.normal(108, 0, 2, (N, 64))).view(np.int16)).cuda().view(torch.bfloat16)
+    qs = [torch.from_numpy(wl.bf16_bits(wl.normal(108, i, 1, (B, 64))).view(np.int16)).cuda().view(torch.bfloat16)
+          for i in (1, 2)]
+    wss = [torch.empty(cskv.index_topk_workspace_size(B, N, k), dtype=torch.uint8, device="cuda") for _ in qs]
+    refs = [cskv.index_topk(q, keys, k) for q in qs]
+    outs = [torch.empty(B, k, dtype=torch.int32, device="cuda") for _ in qs]
+    streams = [torch.cuda.Stream() for _ in qs]
+    torch.cuda.synchronize()
+    for it in range(8):
+        for o in outs:
+            o.fill_(-7)
+        torch.cuda.synchronize()
+        for q, ws, o, st in zip(qs, wss, outs, streams):
+            cskv.index_topk(q, keys, k, idx_out=o, workspace=ws, stream=st)
+        torch.cuda.synchronize()
+        for o, r in zip(outs, refs):
+            assert torch.equal(o, r), f"iteration {it}"
