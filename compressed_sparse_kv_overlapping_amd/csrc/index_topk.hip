@@ -1724,12 +1724,13 @@ constexpr int64_t kWideBelow = 256;
 int topk_max_k() { return kMaxK; }
 int64_t topk_max_entries() { return (int64_t)kMaxGroups * 64; }
 
-// Per-device record of the last one-launch selection (see below).
+// Per-device record of the stream that one-launch selections run on (see
+// below).
 constexpr int kDecDevices = 64;
 struct DecodeGuard {
   std::mutex mu;
+  bool used = false, several = false;
   hipStream_t stream = nullptr;
-  hipEvent_t ev = nullptr;
 };
 static DecodeGuard& decode_guard(int dev) {
   static DecodeGuard guards[kDecDevices];
@@ -1788,21 +1789,22 @@ static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, 
   if ((size_t)(w - (char*)ws) > topk_workspace_bytes(p.B, p.N, p.k)) return hipErrorNotSupported;
   a.sraw = nullptr;
   // Two of these kernels must not run at once: each could hold part of
-  // the chip while it waits for blocks of its own that cannot start.  Per
-  // device, the stream and completion event of the last launch are kept; a
-  // call on another stream while that launch may still run takes the
-  // multi-launch path.  (Kernels of other kinds running beside it only delay
-  // its barriers: their blocks finish and free their compute units.)
+  // the chip while it waits for blocks of its own that cannot start.  They
+  // therefore run on one stream per device, whose order keeps them apart:
+  // the first call's.  Once a call comes on another stream, this and every
+  // later selection on the device take the multi-launch path.  (Kernels of
+  // other kinds running beside one only delay its barriers: their blocks
+  // finish and free their compute units.)
   DecodeGuard& gd = decode_guard(dev);
-  std::lock_guard<std::mutex> lock(gd.mu);
-  if (gd.ev != nullptr && gd.stream != stream && hipEventQuery(gd.ev) != hipSuccess) {
-    (void)hipGetLastError();
-    return hipErrorNotSupported;
-  }
-  if (gd.ev == nullptr && hipEventCreateWithFlags(&gd.ev, hipEventDisableTiming) != hipSuccess) {
-    gd.ev = nullptr;
-    (void)hipGetLastError();
-    return hipErrorNotSupported;
+  {
+    std::lock_guard<std::mutex> lock(gd.mu);
+    if (!gd.used) {
+      gd.used = true;
+      gd.stream = stream;
+    } else if (gd.stream != stream) {
+      gd.several = true;
+    }
+    if (gd.several) return hipErrorNotSupported;
   }
   hipLaunchKernelGGL(idx_decode_reset_kernel, dim3(1), dim3(256), 0, stream, bar);
 #define CSKV_DECODE(NQB, CAPV) \
@@ -1812,10 +1814,7 @@ static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, 
   else if (small) CSKV_DECODE(2, 2048);
   else CSKV_DECODE(2, kCap);
 #undef CSKV_DECODE
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  gd.stream = stream;
-  return hipEventRecord(gd.ev, stream);
+  return hipGetLastError();
 }
 
 template <class T>

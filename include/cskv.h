@@ -37,8 +37,8 @@
  *    frees nothing and keeps no device state between calls (the one
  *    exception is the allocation-free selection call, which uses a fixed
  *    scratch array of the library's on each GPU).  On the host it keeps, per
- *    GPU, the stream and a completion event of its last one-launch decode
- *    selection (see cskv_index_topk).
+ *    GPU, the stream its one-launch decode selections run on (see
+ *    cskv_index_topk).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream) and never synchronize the device.
  *  - All arguments are validated before anything is launched: on error
@@ -153,9 +153,10 @@ int cskv_compress2(const void* raw_kv, const void* score_logits, int64_t T,
  *   at grid-wide barriers: one block of 1024 threads per compute unit,
  *   every block resident at once (blocks that start late, behind other work
  *   on the GPU, are waited for).  Two such kernels must not run at once, so
- *   a call on another stream while the last one may still be running, and
- *   a call under stream capture, take the multi-launch path.  Same result
- *   either way; the same workspace.
+ *   they run on one stream per GPU, that of the first such call: once a call
+ *   comes on another stream, it and every later decode selection on that
+ *   GPU take the multi-launch path, as do calls under stream capture.  Same
+ *   result either way; the same workspace.
  * Errors: INVALID_ARG (null pointers, B < 1, N < 1, k < 1, m < 1 with q_pos);
  * UNSUPPORTED (k > 4096); WORKSPACE.
  */

@@ -434,8 +434,8 @@ def test_topk_decode_on_two_streams_at_once():
     """Decode selections issued on two streams at once (each with its own
     workspace) equal the same selections run one at a time.  Two one-launch
     selection kernels must never run together (each could hold part of the
-    chip while it waits for blocks of its own), so the second stream's call
-    takes the multi-launch path while the first may still be running."""
+    chip while it waits for blocks of its own), so once calls come on a
+    second stream every later decode selection takes the multi-launch path."""
     cskv = _cskv()
     B, N, k = 32, 1 << 18, 1024
     keys = torch.from_numpy(wl.bf16_bits(wl.normal(108, 0, 2, (N, 64))).view(np.int16)).cuda().view(torch.bfloat16)
