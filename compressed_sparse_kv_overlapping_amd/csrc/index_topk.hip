@@ -25,6 +25,7 @@
 #include <float.h>
 
 #include <mutex>
+#include <random>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1437,9 +1438,11 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
 //  C. appends its candidates, read from LDS rather than recomputed, to the
 //     per-(query, block) regions;
 //  D. (blocks b < B) the exact selection of query b, as idx_final_kernel.
-// The result is that of the four launches.  The barrier counts arrivals in
-// the workspace (zeroed by a one-block kernel just before); its wait is
-// bounded, so a grid that is not resident ends with an error flag set
+// The result is that of the four launches.  The barriers' words live in
+// the workspace, which holds whatever its last user left: each launch
+// passes a 64-bit tag of its own and barrier i waits for words equal to
+// tag + i, which stale contents match with probability about 2^-64.  Waits
+// are bounded, so a grid that is not resident ends with the error word set
 // instead of hanging.
 constexpr int kDecThreads = 1024;
 constexpr int kDecPad = 4;                                   // row pad of the score array (floats)
@@ -1447,33 +1450,29 @@ constexpr int kDecScores = 32 * (1024 + kDecPad);            // 128.5 KB of raw 
 constexpr uint32_t kDecSpin = 1u << 24;                      // barrier polls (tens of seconds) before giving up
 
 constexpr int kDecMaxBlocks = 256;                           // flag words: four a lane of one wave
-constexpr int kDecFlagStride = 16;                           // flag words 64 bytes apart
+constexpr int kDecFlagStride = 8;                            // 64-bit flag words 64 bytes apart
 
 struct DecodeBar {
-  uint32_t err, pad0[15], go, pad1[15];
-  uint32_t flags[kDecMaxBlocks * kDecFlagStride];
+  uint64_t err, pad0[7], go, pad1[7];
+  uint64_t flags[kDecMaxBlocks * kDecFlagStride];
 };
-
-__global__ void idx_decode_reset_kernel(DecodeBar* bar) {
-  for (int i = threadIdx.x; i < kDecMaxBlocks * kDecFlagStride; i += blockDim.x) bar->flags[i] = 0u;
-  if (threadIdx.x == 0) { bar->err = 0u; bar->go = 0u; }
-}
 
 // Every block's writes before it are visible to every block after it,
 // for the data the blocks exchange through system-scope accesses (ld_c /
 // st_c with COH): those write through and read past the L2s, so the
 // barrier needs no cache write-back or invalidation, only that each wave's
 // stores have completed (a block barrier alone does not wait for them).
-// Block c then publishes barrier number `epoch` in its own flag word (no
-// shared counter: same-address atomics from every block serialise); block 0
-// polls all the flags, four a lane, and raises the go word, which the other
-// blocks poll with one lane.  Every wait is bounded: past the limit the
+// Block c then publishes the barrier's value (the launch's tag + barrier
+// number) in its own flag word (no shared counter: same-address atomics
+// from every block serialise); block 0 polls all the flags, four a lane,
+// and raises the go word, which the other blocks poll with one lane.  Every
+// wait is bounded: past the limit the
 // error word is set and the block goes on.
-__device__ __forceinline__ void grid_barrier(DecodeBar* bar, uint32_t epoch) {
+__device__ __forceinline__ void grid_barrier(DecodeBar* bar, uint64_t value) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   const int nblk = gridDim.x;
-  if (threadIdx.x == 0) st_c<true>(&bar->flags[blockIdx.x * kDecFlagStride], epoch);
+  if (threadIdx.x == 0) st_c<true>(&bar->flags[blockIdx.x * kDecFlagStride], value);
   if (threadIdx.x < 64) {
     uint32_t spins = 0;
     if (blockIdx.x == 0) {
@@ -1482,20 +1481,20 @@ __device__ __forceinline__ void grid_barrier(DecodeBar* bar, uint32_t epoch) {
         bool done = true;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (f0 + u < nblk) done &= ld_c<true>(&bar->flags[(f0 + u) * kDecFlagStride]) >= epoch;
+          if (f0 + u < nblk) done &= ld_c<true>(&bar->flags[(f0 + u) * kDecFlagStride]) == value;
         if (__all(done)) break;
         __builtin_amdgcn_s_sleep(2);
         if (++spins == kDecSpin) {
-          if (threadIdx.x == 0) st_c<true>(&bar->err, 1u);
+          if (threadIdx.x == 0) st_c<true>(&bar->err, value);
           break;
         }
       }
-      if (threadIdx.x == 0) st_c<true>(&bar->go, epoch);
+      if (threadIdx.x == 0) st_c<true>(&bar->go, value);
     } else if (threadIdx.x == 0) {
-      while (ld_c<true>(&bar->go) < epoch) {
+      while (ld_c<true>(&bar->go) != value) {
         __builtin_amdgcn_s_sleep(2);
         if (++spins == kDecSpin) {
-          st_c<true>(&bar->err, 1u);
+          st_c<true>(&bar->err, value);
           break;
         }
       }
@@ -1513,7 +1512,8 @@ template <int CAP> union DecodeScores {
 // C keys a block (a multiple of 256: whole 16-key tiles for each of the 16
 // waves); bar: the barrier words.
 template <class T, int NQB, int CAP>
-__global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int C, DecodeBar* bar) {
+__global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int C, DecodeBar* bar,
+                                                                uint64_t tag) {
   __shared__ DecodeScores<CAP> u;
   __shared__ uint32_t thist[4096], part[kDecThreads / 32];   // phases B and D
   __shared__ uint32_t sh_digit, sh_above, sh_n, sh_tau, sh_over;
@@ -1609,11 +1609,11 @@ __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int 
     }
   }
   __syncthreads();
-  grid_barrier(bar, 1u);
+  grid_barrier(bar, tag + 1u);
 
   // B. thresholds: query q in block q
   if (blk < a.B) threshold_query<kDecThreads, true>(a, blk, thist, part, sh_digit, sh_above, sh_n, sh_tau);
-  grid_barrier(bar, 2u);
+  grid_barrier(bar, tag + 2u);
 
   // C. candidates >= the threshold, from the scores in LDS
   if (threadIdx.x < a.B) {
@@ -1648,7 +1648,7 @@ __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int 
   }
   __syncthreads();
   if (threadIdx.x < a.B) st_c<true>(a.cnt + (int64_t)threadIdx.x * a.chunks + blk, lcnt[threadIdx.x]);
-  grid_barrier(bar, 3u);
+  grid_barrier(bar, tag + 3u);
 
   // D. the selections: query q in block q
   if (blk < a.B)
@@ -1731,10 +1731,25 @@ struct DecodeGuard {
   std::mutex mu;
   bool used = false, several = false;
   hipStream_t stream = nullptr;
+  uint64_t seq = 0;                                          // launches so far
 };
 static DecodeGuard& decode_guard(int dev) {
   static DecodeGuard guards[kDecDevices];
   return guards[dev];
+}
+
+// The barrier tag of a device's n-th launch: a 64-bit mix (splitmix64's
+// finaliser) of a per-process random salt, the device and n.  Successive
+// tags differ by far more than the 3 their barriers add.
+static uint64_t decode_tag(int dev, uint64_t n) {
+  static const uint64_t salt = [] {
+    std::random_device rd;
+    return ((uint64_t)rd() << 32) ^ (uint64_t)rd();
+  }();
+  uint64_t z = salt + 0x9e3779b97f4a7c15ull * (n + ((uint64_t)dev << 48));
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
 }
 
 // The fused decode selection when it applies: shared, fully visible keys;
@@ -1796,6 +1811,7 @@ static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, 
   // other kinds running beside one only delay its barriers: their blocks
   // finish and free their compute units.)
   DecodeGuard& gd = decode_guard(dev);
+  uint64_t tag;
   {
     std::lock_guard<std::mutex> lock(gd.mu);
     if (!gd.used) {
@@ -1805,10 +1821,10 @@ static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, 
       gd.several = true;
     }
     if (gd.several) return hipErrorNotSupported;
+    tag = decode_tag(dev, ++gd.seq);
   }
-  hipLaunchKernelGGL(idx_decode_reset_kernel, dim3(1), dim3(256), 0, stream, bar);
 #define CSKV_DECODE(NQB, CAPV) \
-  hipLaunchKernelGGL((idx_decode_kernel<T, NQB, CAPV>), dim3((unsigned)nb), dim3(kDecThreads), 0, stream, a, (int)C, bar)
+  hipLaunchKernelGGL((idx_decode_kernel<T, NQB, CAPV>), dim3((unsigned)nb), dim3(kDecThreads), 0, stream, a, (int)C, bar, tag)
   if (nqb == 1 && small) CSKV_DECODE(1, 2048);
   else if (nqb == 1) CSKV_DECODE(1, kCap);
   else if (small) CSKV_DECODE(2, 2048);

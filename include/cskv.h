@@ -182,7 +182,9 @@ int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t 
  *   Every call on a GPU uses that GPU's one scratch array: calls that
  *   overlap on one GPU (different streams, or threads) race and must be
  *   serialised by the caller.  Every scratch byte a call reads it first
- *   writes, so nothing carries over from the previous call.
+ *   writes, except the barrier words of the one-launch decode selection,
+ *   which it compares with 64-bit values unique to the call; nothing
+ *   carries over from the previous call.
  * Arguments and the other errors are those of cskv_index_topk.
  */
 size_t cskv_index_topk_noalloc_max_bytes(void);
