@@ -1466,8 +1466,8 @@ struct DecodeBar {
 // number) in its own flag word (no shared counter: same-address atomics
 // from every block serialise); block 0 polls all the flags, four a lane,
 // and raises the go word, which the other blocks poll with one lane.  Every
-// wait is bounded: past the limit the
-// error word is set and the block goes on.
+// wait is bounded: past the limit the error word is set and the block goes
+// on.
 __device__ __forceinline__ void grid_barrier(DecodeBar* bar, uint64_t value) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -1509,8 +1509,9 @@ template <int CAP> union DecodeScores {
   struct { FinalCands<CAP> cs; FinalHist hs; uint16_t coff[kMaxChunks + 1]; } fin;
 };
 
-// C keys a block (a multiple of 256: whole 16-key tiles for each of the 16
-// waves); bar: the barrier words.
+// C keys a block (a multiple of 256 and of 16 GS: whole 16-key tiles for
+// each of the 16 waves, and whole groups in each wave's keys); bar: the
+// barrier words; tag: the launch's barrier tag.
 template <class T, int NQB, int CAP>
 __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int C, DecodeBar* bar,
                                                                 uint64_t tag) {
@@ -1770,11 +1771,11 @@ static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, 
       hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone ||
       dev < 0 || dev >= kDecDevices)
     return hipErrorNotSupported;
-  // keys a block: a multiple of 256, as few blocks as give every compute unit
-  // at most one
-  int64_t C = ((p.N + cus - 1) / cus + 255) / 256 * 256;
-  if (C < 16 * (int64_t)a.GS) C = 16 * (int64_t)a.GS;       // a wave's keys hold whole groups
-  C = (C + 255) / 256 * 256;
+  // keys a block: a multiple of 256 (whole 16-key tiles for its 16 waves)
+  // and of 16 GS (each wave's keys hold whole groups), as few blocks as give
+  // every compute unit at most one
+  const int64_t unit = 16 * (int64_t)a.GS > 256 ? 16 * (int64_t)a.GS : 256;
+  const int64_t C = ((p.N + cus - 1) / cus + unit - 1) / unit * unit;
   const int64_t nb = (p.N + C - 1) / C;
   // at least one block a query (a block takes one query's threshold and
   // selection)

@@ -359,7 +359,7 @@ def test_topk_mxfp4_many_queries_groups_of_32():
 
 
 @pytest.mark.parametrize("dt", [wl.DT_BF16, wl.DT_E4M3, wl.DT_F32])
-@pytest.mark.parametrize("B,N,k", [(32, 1 << 18, 1024), (20, 100003, 333), (7, 30000, 64)])
+@pytest.mark.parametrize("B,N,k", [(32, 1 << 18, 1024), (20, 100003, 333), (7, 30000, 64), (7, 300000, 512)])
 def test_topk_decode_one_launch_equals_four(dt, B, N, k):
     """Up to 32 queries over shared keys with every entry visible run the
     selection in one launch (its phases separated by grid barriers);
