@@ -20,7 +20,11 @@ int fail(int code, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
+  try {                                    // no exception may leave a C entry point
+    g_last_error = buf;
+  } catch (...) {
+    g_last_error.clear();
+  }
   return code;
 }
 

@@ -24,6 +24,7 @@
 //     select over all its entries instead.
 #include <float.h>
 
+#include <chrono>
 #include <mutex>
 #include <random>
 #include <type_traits>
@@ -1742,11 +1743,20 @@ static DecodeGuard& decode_guard(int dev) {
 // The barrier tag of a device's n-th launch: a 64-bit mix (splitmix64's
 // finaliser) of a per-process random salt, the device and n.  Successive
 // tags differ by far more than the 3 their barriers add.
-static uint64_t decode_tag(int dev, uint64_t n) {
-  static const uint64_t salt = [] {
+static uint64_t decode_salt() {
+  uint64_t s = 0;
+  try {
     std::random_device rd;
-    return ((uint64_t)rd() << 32) ^ (uint64_t)rd();
-  }();
+    s = ((uint64_t)rd() << 32) ^ (uint64_t)rd();
+  } catch (...) {
+  }
+  // also the clock and an address, should the random device give nothing
+  s ^= (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+  s ^= (uint64_t)(uintptr_t)&s << 17;
+  return s;
+}
+static uint64_t decode_tag(int dev, uint64_t n) {
+  static const uint64_t salt = decode_salt();
   uint64_t z = salt + 0x9e3779b97f4a7c15ull * (n + ((uint64_t)dev << 48));
   z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
   z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
@@ -1813,7 +1823,7 @@ static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, 
   // finish and free their compute units.)
   DecodeGuard& gd = decode_guard(dev);
   uint64_t tag;
-  {
+  try {                                                      // nothing may throw past the C entry points
     std::lock_guard<std::mutex> lock(gd.mu);
     if (!gd.used) {
       gd.used = true;
@@ -1823,6 +1833,8 @@ static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, 
     }
     if (gd.several) return hipErrorNotSupported;
     tag = decode_tag(dev, ++gd.seq);
+  } catch (...) {
+    return hipErrorNotSupported;
   }
 #define CSKV_DECODE(NQB, CAPV) \
   hipLaunchKernelGGL((idx_decode_kernel<T, NQB, CAPV>), dim3((unsigned)nb), dim3(kDecThreads), 0, stream, a, (int)C, bar, tag)

@@ -34,11 +34,15 @@ hipError_t noalloc_scratch(void** ptr) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::call_once(g_once[dev], [dev] {
-    void* p = nullptr;
-    g_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    g_ptr[dev] = g_err[dev] == hipSuccess ? p : nullptr;
-  });
+  try {                                    // no exception may leave a C entry point
+    std::call_once(g_once[dev], [dev] {
+      void* p = nullptr;
+      g_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      g_ptr[dev] = g_err[dev] == hipSuccess ? p : nullptr;
+    });
+  } catch (...) {
+    return hipErrorUnknown;
+  }
   *ptr = g_ptr[dev];
   return g_err[dev];
 }
