@@ -56,6 +56,8 @@ struct IdxArgs {
   uint64_t* cand;             // [B][chunks][region] candidate regions
   int32_t* out;               // [B][k]
   int chunks, region;         // score-pass chunks; slots per (query, chunk)
+  int csize;                  // entries per chunk: chunk c holds entries [c csize, (c+1) csize)
+  uint32_t cmagic;            // floor((2^32 - 1) / csize)
   float* sraw;                // per-sequence keys: raw scores [B][Np] kept between the passes, or NULL
   int64_t np;                 // row pitch of sraw (N rounded up to 16)
 };
@@ -1133,9 +1135,10 @@ __device__ __forceinline__ float entry_dot<fp4x2_t>(const IdxArgs& a, int b, int
 // ascending entry ranges.  The k-th largest composite is found with one
 // histogram of the score words over 2048 bins of their range; the few
 // candidates in the bin that holds it are ranked exactly by composite (a
-// crowded bin falls back to further passes).  Each selected candidate is then
-// written at its chunk's output offset plus its rank by index among the
-// chunk's selected ones, so the output is ascending without a global sort.
+// crowded bin falls back to further passes).  The selected candidates,
+// compacted in list order, are then in ascending order of chunk; each is
+// written at the start of its chunk's run plus its rank by index within that
+// run, so the output is ascending without a global sort.
 constexpr int kMaxChunks = 2048;
 constexpr int kFinalBB = 11;                 // histogram of 2^11 bins
 constexpr int kMem = 512;                    // bin members ranked exactly
@@ -1145,9 +1148,9 @@ constexpr int kMem = 512;                    // bin members ranked exactly
 // the streaming path, with the same result.
 // candidates (list) or, on overflow, the k <= CAP / 2 selected indices
 template <int CAP> union FinalCands { uint64_t cand[CAP]; int32_t sel[CAP / 2]; };
-// the histogram, then the members of the k-th bin, then the chunks' output
-// offsets
-union FinalHist { uint32_t hist[1 << kFinalBB]; uint64_t mem[kMem]; uint16_t csel[kMaxChunks]; };
+// the histogram, then the members of the k-th bin, then where each chunk's
+// selected candidates start and end in the compacted list
+union FinalHist { uint32_t hist[1 << kFinalBB]; uint64_t mem[kMem]; uint16_t seg[2][kMaxChunks]; };
 
 // The selection of query b, by a block of NT threads.  LDS: the candidate
 // and histogram unions, coff[kMaxChunks + 1] (list offset of each chunk),
@@ -1191,7 +1194,6 @@ __device__ __forceinline__ void final_query(const IdxArgs& a, const int b, Final
   // list slots of this thread (gather and output), and the chunk of p0
   const uint32_t per = (total + NT - 1) / NT;
   const uint32_t p0 = min(total, t * per), p1 = min(total, p0 + per);
-  int ch0 = 0;
   if (!overflow) {
     // chunk offsets in the list, then a copy spread over the whole block:
     // list slot j belongs to the last chunk whose offset is <= j
@@ -1212,7 +1214,6 @@ __device__ __forceinline__ void final_query(const IdxArgs& a, const int b, Final
         const int mid = (lo + hi) >> 1;
         if (coff[mid] <= p0) lo = mid; else hi = mid;
       }
-      ch0 = lo;
       int c = lo;
       uint32_t cb = coff[c], ce = coff[c + 1];
       for (uint32_t p = p0; p < p1; p += 8) {
@@ -1303,7 +1304,7 @@ __device__ __forceinline__ void final_query(const IdxArgs& a, const int b, Final
           },
           nc, kt, lo, hi, hist, part, &sh_digit, &sh_above, &above);
       prefix = ((uint64_t)th << 32) | tl;
-      __syncthreads();                                       // hist is read; csel reuses it
+      __syncthreads();                                       // hist is read; the placement reuses it
     }
   } else {
     // radix select over the recomputed composites, digits of 11, 11 and 10
@@ -1336,51 +1337,96 @@ __device__ __forceinline__ void final_query(const IdxArgs& a, const int b, Final
   // the final bucket); composites are distinct, so exactly k reach it
   const uint64_t thr = prefix;
   if (!overflow) {
-    // per-chunk counts of selected candidates -> output offsets; then each
-    // selected candidate goes to its chunk's offset plus its rank by index
-    // among the chunk's selected ones (chunks are ascending entry ranges)
-    // selected ones among slots [i0, i1) with an index below that of v
-    // (larger low word), or all of them (v = 0); reads eight at a time
-    auto count_sel = [&](uint32_t i0, uint32_t i1, uint64_t v) {
-      uint32_t n = 0;
-      for (uint32_t i = i0; i < i1; i += 8) {
-        uint64_t w[8];
+    // placement.  The list is in chunk order and chunks are ascending entry
+    // ranges, so the output (ascending indices) is the selected candidates in
+    // list order with each chunk's run sorted by index.  The selected low
+    // words are compacted in list order (each thread its own run of slots,
+    // one block scan), each chunk's run is delimited, and every selected
+    // candidate goes to its run's start plus the number of the run's members
+    // with a smaller index (a larger low word).
+    constexpr int U = CAP / NT;                              // list slots a thread holds at most
+    uint32_t los[U];
+    uint32_t selm = 0, nmine = 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) w[u] = i + u < i1 ? cand[i + u] : 0ull;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) n += (w[u] >= thr) && (uint32_t)w[u] > (uint32_t)v;
-      }
-      return n;
-    };
-    uint32_t mine_sel = 0;
-    for (int c = c0; c < c1; ++c) {
-      const uint32_t m = count_sel(coff[c], coff[c + 1], 0ull);
-      hs.csel[c] = (uint16_t)m;
-      mine_sel += m;
+    for (int u = 0; u < U; ++u) {
+      const uint32_t j = p0 + u;
+      const uint64_t v = cand[j < (uint32_t)CAP ? j : CAP - 1];
+      const bool s = j < p1 && v >= thr;
+      los[u] = (uint32_t)v;
+      selm |= (uint32_t)s << u;
+      nmine += s;
     }
     uint32_t nsel;
-    uint32_t ob = block_excl_scan<NT>(mine_sel, part, &nsel);
-    for (int c = c0; c < c1; ++c) {
-      const uint32_t m = hs.csel[c];
-      hs.csel[c] = (uint16_t)ob;
-      ob += m;
+    uint32_t at = block_excl_scan<NT>(nmine, part, &nsel);
+    // the scan's barriers order every read of the list before these writes
+    uint32_t* run = reinterpret_cast<uint32_t*>(cand);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if ((selm >> u) & 1u) run[at++] = los[u];
+    __syncthreads();
+    const uint32_t cs_ = (uint32_t)a.csize;
+    auto chunk_of = [&](const uint32_t lo) {
+      const uint32_t e = 0xffffffffu - lo;
+      uint32_t c = __umulhi(e, a.cmagic);                    // floor(e / csize) or one less
+      return c + (e - c * cs_ >= cs_ ? 1u : 0u);
+    };
+    // G list positions a thread at a time, their loads issued together;
+    // nl <= k <= CAP / 2 keeps every read below inside the list's storage
+    // (2 CAP words)
+    constexpr int G = CAP / 2 / NT < 4 ? CAP / 2 / NT : 4;
+    static_assert(G >= 1, "a position per thread");
+    const uint32_t nl = min(nsel, (uint32_t)a.k);
+    uint16_t* first = hs.seg[0];
+    uint16_t* last = hs.seg[1];
+    for (uint32_t i0 = t; i0 < nl; i0 += G * NT) {
+      uint32_t w0[G], w1[G], w2[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint32_t i = i0 + g * NT < nl ? i0 + g * NT : 0u;
+        w0[g] = run[i > 0 ? i - 1 : 0];
+        w1[g] = run[i];
+        w2[g] = run[i + 1];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint32_t i = i0 + g * NT;
+        if (i < nl) {
+          const uint32_t c = chunk_of(w1[g]);
+          if (i == 0 || chunk_of(w0[g]) != c) first[c] = (uint16_t)i;
+          if (i + 1 == nl || chunk_of(w2[g]) != c) last[c] = (uint16_t)(i + 1);
+        }
+      }
     }
     __syncthreads();
-    // this thread's slots again, walking the chunks from that of p0; a
-    // selected candidate goes to its chunk's offset plus the number of
-    // selected ones of its chunk with a smaller index
-    int c = ch0;
-    uint32_t cb = p0 < p1 ? coff[c] : 0, ce = p0 < p1 ? coff[c + 1] : 0;
-    for (uint32_t j = p0; j < p1; ++j) {
-      while (j >= ce) {
-        ++c;
-        cb = ce;
-        ce = coff[c + 1];
+    // rank within the run, eight words at a time; the words past a run (at
+    // most seven beyond the longest of the G) are not counted
+    for (uint32_t i0 = t; i0 < nl; i0 += G * NT) {
+      uint32_t lo[G], L[G], n[G], r[G];
+      uint32_t span = 0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) lo[g] = run[i0 + g * NT < nl ? i0 + g * NT : 0u];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint32_t c = chunk_of(lo[g]);
+        L[g] = first[c];
+        n[g] = i0 + g * NT < nl ? last[c] - L[g] : 0u;
+        r[g] = 0;
+        span = max(span, n[g]);
       }
-      const uint64_t v = cand[j];
-      if (v < thr) continue;
-      const uint32_t o = hs.csel[c] + count_sel(cb, ce, v);
-      if (o < (uint32_t)a.k) out[o] = (int32_t)(0xffffffffu - (uint32_t)v);
+      for (uint32_t j = 0; j < span; j += 8) {
+        uint32_t w[G][8];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) w[g][u] = run[L[g] + j + u];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) r[g] += (j + u < n[g] && w[g][u] > lo[g]) ? 1u : 0u;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        if (i0 + g * NT < nl && L[g] + r[g] < (uint32_t)a.k) out[L[g] + r[g]] = (int32_t)(0xffffffffu - lo[g]);
     }
     for (int j = (int)nsel + t; j < a.k; j += NT) out[j] = -1;
     return;
@@ -1674,7 +1720,7 @@ int topk_group_size(int64_t N, int k) {
 // launcher: entry chunks of tiles_per_wave 16-entry tiles per wave (times 4
 // when the waves split the chunk), and the candidate region of each (query,
 // chunk).
-struct TopkGeom { int GS, G, qpb, nqb, wq, qblocks, tpw, chunks, region; };
+struct TopkGeom { int GS, G, qpb, nqb, wq, qblocks, tpw, chunks, region, csize; };
 
 static TopkGeom topk_geom(int64_t B, int64_t N, int k, bool per_seq) {
   TopkGeom g;
@@ -1699,6 +1745,7 @@ static TopkGeom topk_geom(int64_t B, int64_t N, int k, bool per_seq) {
   r = r < 32 ? 32 : r;
   const int64_t csize = (int64_t)g.tpw * 16 * wsplit;
   g.region = (int)(r > csize ? csize : r);
+  g.csize = (int)csize;
   return g;
 }
 
@@ -1805,6 +1852,8 @@ static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, 
   r = r < 32 ? 32 : (r > C ? C : r);
   a.chunks = (int)nb;
   a.region = (int)r;
+  a.csize = (int)C;
+  a.cmagic = 0xffffffffu / (uint32_t)C;
   char* w = (char*)ws;
   a.cand = (uint64_t*)w;            w += (size_t)p.B * nb * r * 8;
   a.gmax = (uint32_t*)w;            w += (size_t)p.B * a.G * 4;
@@ -1858,6 +1907,7 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
   a.gs_shift = 0;
   while ((1 << a.gs_shift) < g.GS) ++a.gs_shift;             // group sizes are powers of two
   a.chunks = g.chunks; a.region = g.region;
+  a.csize = g.csize; a.cmagic = 0xffffffffu / (uint32_t)g.csize;
   char* w = (char*)ws;
   a.cand = (uint64_t*)w;            w += (size_t)p.B * g.chunks * g.region * 8;
   a.gmax = (uint32_t*)w;            w += (size_t)p.B * a.G * 4;
