@@ -1926,13 +1926,15 @@ static hipError_t launch_topk_t(const TopkParams& p, void* ws, hipStream_t strea
   // many queries on 32x32 tiles (fp8, bf16, MXFP4 keys; groups of >= 32)
   constexpr bool kTile32 = !std::is_same<T, float>::value;
   const bool tile32 = kTile32 && g.wq == 4 && g.GS >= 32;
-#define CSKV_SCORE32(MODE)                                                                   \
-  if (MODE == 1 || g.GS == 64)                                                               \
-    hipLaunchKernelGGL((idx_score32_kernel<T, 2, MODE, 6>), grid, dim3(256), 0, stream, a);  \
-  else                                                                                       \
-    hipLaunchKernelGGL((idx_score32_kernel<T, 2, MODE, 5>), grid, dim3(256), 0, stream, a)
+#define CSKV_SCORE32(MODE)                                                                     \
+  {                                                                                            \
+    if (MODE == 1 || g.GS == 64)                                                               \
+      hipLaunchKernelGGL((idx_score32_kernel<T, 2, MODE, 6>), grid, dim3(256), 0, stream, a);  \
+    else                                                                                       \
+      hipLaunchKernelGGL((idx_score32_kernel<T, 2, MODE, 5>), grid, dim3(256), 0, stream, a);  \
+  }
 #define CSKV_SCORE_PASS(MODE)                                                  \
-  if (tile32) { if constexpr (kTile32) CSKV_SCORE32(MODE); }                   \
+  if (tile32) { if constexpr (kTile32) { CSKV_SCORE32(MODE) } }               \
   else if (g.wq == 4) CSKV_SCORE(4, MODE, 4);                                  \
   else if (nqb == 1) CSKV_SCORE(1, MODE, 1);                                   \
   else if (nqb == 2) CSKV_SCORE(2, MODE, 1);                                   \
