@@ -1476,74 +1476,67 @@ __global__ __launch_bounds__(NT) void idx_final_kernel(IdxArgs a) {
 //
 // The decode selection (up to 32 queries over one shared, fully visible key
 // set) in a single launch: the four steps above run as phases of one kernel,
-// separated by grid-wide barriers, with one block of 1024 threads resident
-// on every compute unit.  Block c owns the C keys [c C, c C + C):
+// with one block of 1024 threads resident on every compute unit.  Block c
+// owns the C keys [c C, c C + C):
 //  A. scores its keys for every query (the same 16x16 MFMA steps as the
 //     score passes, so the same raw scores), keeps the raw scores in LDS and
 //     writes its groups' maxima;
-//  B. (blocks b < B) the threshold of query b, as idx_threshold_kernel;
-//  C. appends its candidates, read from LDS rather than recomputed, to the
-//     per-(query, block) regions;
-//  D. (blocks b < B) the exact selection of query b, as idx_final_kernel.
-// The result is that of the four launches.  The barriers' words live in
-// the workspace, which holds whatever its last user left: each launch
-// passes a 64-bit tag of its own and barrier i waits for words equal to
-// tag + i, which stale contents match with probability about 2^-64.  Waits
-// are bounded, so a grid that is not resident ends with the error word set
-// instead of hanging.
+//  B. (blocks b < B, once every block is past A) the threshold of query b,
+//     as idx_threshold_kernel;
+//  C. (once every threshold is out) appends its candidates, read from LDS
+//     rather than recomputed, to the per-(query, block) regions;
+//  D. (blocks b < B, once every block is past C) the exact selection of
+//     query b, as idx_final_kernel.
+// The result is that of the four launches.  The phase words live in the
+// workspace, which holds whatever its last user left: each launch passes a
+// 64-bit tag of its own and phase i publishes tag + i, which stale contents
+// match with probability about 2^-64.  Waits are bounded, so a grid that is
+// not resident ends with the error word set instead of hanging.
 constexpr int kDecThreads = 1024;
 constexpr int kDecPad = 4;                                   // row pad of the score array (floats)
 constexpr int kDecScores = 32 * (1024 + kDecPad);            // 128.5 KB of raw scores
-constexpr uint32_t kDecSpin = 1u << 24;                      // barrier polls (tens of seconds) before giving up
+constexpr uint32_t kDecSpin = 1u << 24;                      // polls of a wait (tens of seconds) before giving up
 
 constexpr int kDecMaxBlocks = 256;                           // flag words: four a lane of one wave
 constexpr int kDecFlagStride = 8;                            // 64-bit flag words 64 bytes apart
 
 struct DecodeBar {
-  uint64_t err, pad0[7], go, pad1[7];
-  uint64_t flags[kDecMaxBlocks * kDecFlagStride];
+  uint64_t err, pad0[7];
+  uint64_t a[kDecMaxBlocks * kDecFlagStride];                // block c's phase A is done
+  uint64_t b[32 * kDecFlagStride];                           // query q's threshold is out
+  uint64_t c[kDecMaxBlocks * kDecFlagStride];                // block c's phase C is done
 };
 
-// Every block's writes before it are visible to every block after it,
-// for the data the blocks exchange through system-scope accesses (ld_c /
-// st_c with COH): those write through and read past the L2s, so the
-// barrier needs no cache write-back or invalidation, only that each wave's
-// stores have completed (a block barrier alone does not wait for them).
-// Block c then publishes the barrier's value (the launch's tag + barrier
-// number) in its own flag word (no shared counter: same-address atomics
-// from every block serialise); block 0 polls all the flags, four a lane,
-// and raises the go word, which the other blocks poll with one lane.  Every
-// wait is bounded: past the limit the error word is set and the block goes
-// on.
-__device__ __forceinline__ void grid_barrier(DecodeBar* bar, uint64_t value) {
+// The blocks exchange data through system-scope accesses (ld_c / st_c with
+// COH), which write through and read past the L2s, so no cache write-back or
+// invalidation is needed between phases; only each wave's stores must have
+// completed (a block barrier alone does not wait for them).  A block then
+// publishes a phase's value (the launch's tag + phase number) in its own
+// word (no shared counter: same-address atomics from every block
+// serialise), and a block that needs the phase waits for exactly the words
+// it depends on, polled by one wave, four a lane: a single memory round trip
+// from the last publisher to the waiter.  Every wait is bounded: past the
+// limit the error word is set and the block goes on.
+__device__ __forceinline__ void dec_publish(uint64_t* word, uint64_t value) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  const int nblk = gridDim.x;
-  if (threadIdx.x == 0) st_c<true>(&bar->flags[blockIdx.x * kDecFlagStride], value);
+  if (threadIdx.x == 0) st_c<true>(word, value);
+}
+// words[i * kDecFlagStride] == value for every i < n (n <= 256)
+__device__ __forceinline__ void dec_wait(DecodeBar* bar, const uint64_t* words, int n, uint64_t value) {
   if (threadIdx.x < 64) {
+    const int f0 = 4 * threadIdx.x;
     uint32_t spins = 0;
-    if (blockIdx.x == 0) {
-      const int f0 = 4 * threadIdx.x;
-      for (;;) {
-        bool done = true;
+    for (;;) {
+      bool done = true;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (f0 + u < nblk) done &= ld_c<true>(&bar->flags[(f0 + u) * kDecFlagStride]) == value;
-        if (__all(done)) break;
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins == kDecSpin) {
-          if (threadIdx.x == 0) st_c<true>(&bar->err, value);
-          break;
-        }
-      }
-      if (threadIdx.x == 0) st_c<true>(&bar->go, value);
-    } else if (threadIdx.x == 0) {
-      while (ld_c<true>(&bar->go) != value) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins == kDecSpin) {
-          st_c<true>(&bar->err, value);
-          break;
-        }
+      for (int u = 0; u < 4; ++u)
+        if (f0 + u < n) done &= ld_c<true>(&words[(f0 + u) * kDecFlagStride]) == value;
+      if (__all(done)) break;
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins == kDecSpin) {
+        if (threadIdx.x == 0) st_c<true>(&bar->err, value);
+        break;
       }
     }
   }
@@ -1558,7 +1551,7 @@ template <int CAP> union DecodeScores {
 
 // C keys a block (a multiple of 256 and of 16 GS: whole 16-key tiles for
 // each of the 16 waves, and whole groups in each wave's keys); bar: the
-// barrier words; tag: the launch's barrier tag.
+// phase words; tag: the launch's tag.
 template <class T, int NQB, int CAP>
 __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int C, DecodeBar* bar,
                                                                 uint64_t tag) {
@@ -1656,12 +1649,15 @@ __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int 
       }
     }
   }
-  __syncthreads();
-  grid_barrier(bar, tag + 1u);
+  dec_publish(&bar->a[blk * kDecFlagStride], tag + 1u);
 
-  // B. thresholds: query q in block q
-  if (blk < a.B) threshold_query<kDecThreads, true>(a, blk, thist, part, sh_digit, sh_above, sh_n, sh_tau);
-  grid_barrier(bar, tag + 2u);
+  // B. thresholds: query q in block q, once every block's group maxima are out
+  if (blk < a.B) {
+    dec_wait(bar, bar->a, gridDim.x, tag + 1u);
+    threshold_query<kDecThreads, true>(a, blk, thist, part, sh_digit, sh_above, sh_n, sh_tau);
+    dec_publish(&bar->b[blk * kDecFlagStride], tag + 2u);
+  }
+  dec_wait(bar, bar->b, a.B, tag + 2u);
 
   // C. candidates >= the threshold, from the scores in LDS
   if (threadIdx.x < a.B) {
@@ -1696,12 +1692,14 @@ __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int 
   }
   __syncthreads();
   if (threadIdx.x < a.B) st_c<true>(a.cnt + (int64_t)threadIdx.x * a.chunks + blk, lcnt[threadIdx.x]);
-  grid_barrier(bar, tag + 3u);
+  dec_publish(&bar->c[blk * kDecFlagStride], tag + 3u);
 
-  // D. the selections: query q in block q
-  if (blk < a.B)
+  // D. the selections: query q in block q, once every block's candidates are out
+  if (blk < a.B) {
+    dec_wait(bar, bar->c, gridDim.x, tag + 3u);
     final_query<T, kDecThreads, CAP, true>(a, blk, u.fin.cs, u.fin.hs, u.fin.coff, part, sh_digit, sh_above,
                                            sh_n, sh_over, sh_thr);
+  }
 }
 
 // ------------------------------------------------------------------ host
@@ -1787,9 +1785,9 @@ static DecodeGuard& decode_guard(int dev) {
   return guards[dev];
 }
 
-// The barrier tag of a device's n-th launch: a 64-bit mix (splitmix64's
-// finaliser) of a per-process random salt, the device and n.  Successive
-// tags differ by far more than the 3 their barriers add.
+// The tag of a device's n-th launch: a 64-bit mix (splitmix64's finaliser)
+// of a per-process random salt, the device and n.  Successive tags differ by
+// far more than the 3 their phases add.
 static uint64_t decode_salt() {
   uint64_t s = 0;
   try {
@@ -1868,7 +1866,7 @@ static hipError_t launch_decode_fused(const TopkParams& p, IdxArgs a, void* ws, 
   // therefore run on one stream per device, whose order keeps them apart:
   // the first call's.  Once a call comes on another stream, this and every
   // later selection on the device take the multi-launch path.  (Kernels of
-  // other kinds running beside one only delay its barriers: their blocks
+  // other kinds running beside one only delay its waits: their blocks
   // finish and free their compute units.)
   DecodeGuard& gd = decode_guard(dev);
   uint64_t tag;

@@ -149,8 +149,8 @@ int cskv_compress2(const void* raw_kv, const void* score_logits, int64_t T,
  *     read from memory once instead of twice (same result).
  *   Decode selections (q_pos == NULL, shared keys, B <= 32, at least one
  *   compute unit per query, and up to 1,024 keys per compute unit for 17 to
- *   32 queries, 2,048 for 16 or fewer) run as one kernel whose phases meet
- *   at grid-wide barriers: one block of 1024 threads per compute unit,
+ *   32 queries, 2,048 for 16 or fewer) run as one kernel whose blocks wait
+ *   for each other between phases: one block of 1024 threads per compute unit,
  *   every block resident at once (blocks that start late, behind other work
  *   on the GPU, are waited for).  Two such kernels must not run at once, so
  *   they run on one stream per GPU, that of the first such call: once a call
@@ -182,7 +182,7 @@ int cskv_index_topk(const void* q_idx, const void* idx_keys, int64_t B, int64_t 
  *   Every call on a GPU uses that GPU's one scratch array: calls that
  *   overlap on one GPU (different streams, or threads) race and must be
  *   serialised by the caller.  Every scratch byte a call reads it first
- *   writes, except the barrier words of the one-launch decode selection,
+ *   writes, except the phase words of the one-launch decode selection,
  *   which it compares with 64-bit values unique to the call; nothing
  *   carries over from the previous call.
  * Arguments and the other errors are those of cskv_index_topk.

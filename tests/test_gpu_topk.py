@@ -362,7 +362,7 @@ def test_topk_mxfp4_many_queries_groups_of_32():
 @pytest.mark.parametrize("B,N,k", [(32, 1 << 18, 1024), (20, 100003, 333), (7, 30000, 64), (7, 300000, 512)])
 def test_topk_decode_one_launch_equals_four(dt, B, N, k):
     """Up to 32 queries over shared keys with every entry visible run the
-    selection in one launch (its phases separated by grid barriers);
+    selection in one launch (its blocks waiting for each other between phases);
     positions that make every entry visible take the four launches instead.
     Both compute the same scores in the same order, so the selections are
     identical, and the one-launch result matches the oracle."""
