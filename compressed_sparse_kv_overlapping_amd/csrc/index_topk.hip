@@ -920,6 +920,36 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, uint32_t*
   *out_mx = mx;
 }
 
+// Block sum of the counts and min and max of the keys in one exchange (NT
+// threads; part[] holds 3 NT / 64 values).
+template <int NT>
+__device__ __forceinline__ void block_count_minmax(uint32_t n, uint32_t mn, uint32_t mx, uint32_t* part,
+                                                   uint32_t* out_n, uint32_t* out_mn, uint32_t* out_mx) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    n += (uint32_t)__shfl_xor((int)n, off, 64);
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+  }
+  if (lane == 0) { part[w] = n; part[NW + w] = mn; part[2 * NW + w] = mx; }
+  __syncthreads();
+  n = part[0];
+  mn = part[NW];
+  mx = part[2 * NW];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    n += part[i];
+    mn = min(mn, part[NW + i]);
+    mx = max(mx, part[2 * NW + i]);
+  }
+  __syncthreads();
+  *out_n = n;
+  *out_mn = mn;
+  *out_mx = mx;
+}
+
 // kk-th largest (1-based) of the 32-bit keys that key_at(i) yields as valid,
 // i in [0, n), given their min lo and max hi.  Every pass spreads the
 // remaining range over 2^BB bins of equal width, so keys crowded into a few
@@ -981,7 +1011,7 @@ __device__ __forceinline__ void st_c(U* p, U v) {
 }
 
 // The threshold of query b, by a block of NT threads.  LDS: hist[4096],
-// part[NT / 32] and four words, each its own __shared__ object in the
+// part[3 NT / 64] and four words, each its own __shared__ object in the
 // caller (inlined there, so the compiler sees that they do not overlap).
 template <int NT, bool COH = false>
 __device__ __forceinline__ void threshold_query(const IdxArgs& a, const int b, uint32_t* hist, uint32_t* part,
@@ -998,6 +1028,9 @@ __device__ __forceinline__ void threshold_query(const IdxArgs& a, const int b, u
     const int i = t + r * NT;
     v[r] = held && i < a.G ? ld_c<COH>(gm + i) : 0u;
   }
+  // the histogram below, cleared while the maxima load
+  for (int i = t; i < 4096; i += NT) hist[i] = 0;
+  if (t == 0) sh_n = 0;
   auto each = [&](auto&& f) {                                // every non-empty group's maximum
     if (held) {
 #pragma unroll
@@ -1012,10 +1045,9 @@ __device__ __forceinline__ void threshold_query(const IdxArgs& a, const int b, u
   };
   uint32_t ne = 0, mn = 0xffffffffu, mx = 0u;
   each([&](uint32_t x) { ++ne; mn = min(mn, x); mx = max(mx, x); });
-  uint32_t nonempty;
-  block_excl_scan<NT>(ne, part, &nonempty);
-  uint32_t lo, hi;
-  block_minmax<NT>(mn, mx, part, &lo, &hi);
+  // (its block barriers also order the cleared histogram before its use)
+  uint32_t nonempty, lo, hi;
+  block_count_minmax<NT>(ne, mn, mx, part, &nonempty, &lo, &hi);
   const int nv = n_visible(a, b);
   if (nv <= a.k || nonempty < (uint32_t)a.k) {
     if (t == 0) st_c<COH>(a.thr + b, 0u);
@@ -1024,9 +1056,6 @@ __device__ __forceinline__ void threshold_query(const IdxArgs& a, const int b, u
   const uint32_t range = hi - lo;
   const int bits = range ? 32 - __clz((int)range) : 0;     // range < 2^bits
   const int shift = bits > 12 ? bits - 12 : 0;
-  for (int i = t; i < 4096; i += NT) hist[i] = 0;
-  if (t == 0) sh_n = 0;
-  __syncthreads();
   each([&](uint32_t x) { atomicAdd(&hist[(x - lo) >> shift], 1u); });
   __syncthreads();
   find_kth_bin<NT>(hist, 4096, (uint32_t)a.k, &sh_digit, &sh_above, part);
@@ -1062,7 +1091,7 @@ __device__ __forceinline__ void threshold_query(const IdxArgs& a, const int b, u
 
 template <int NT>
 __global__ __launch_bounds__(NT) void idx_threshold_kernel(IdxArgs a) {
-  __shared__ uint32_t hist[4096], part[NT / 32];
+  __shared__ uint32_t hist[4096], part[3 * NT / 64];
   __shared__ uint32_t sh_digit, sh_above, sh_n, sh_tau;
   threshold_query<NT>(a, blockIdx.x, hist, part, sh_digit, sh_above, sh_n, sh_tau);
 }
@@ -1194,6 +1223,7 @@ __device__ __forceinline__ void final_query(const IdxArgs& a, const int b, Final
   // list slots of this thread (gather and output), and the chunk of p0
   const uint32_t per = (total + NT - 1) / NT;
   const uint32_t p0 = min(total, t * per), p1 = min(total, p0 + per);
+  uint32_t mn = 0xffffffffu, mx = 0u;                        // score words of this thread's slots
   if (!overflow) {
     // chunk offsets in the list, then a copy spread over the whole block:
     // list slot j belongs to the last chunk whose offset is <= j
@@ -1232,30 +1262,29 @@ __device__ __forceinline__ void final_query(const IdxArgs& a, const int b, Final
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (p + u < p1) cand[p + u] = v[u];
+          if (p + u < p1) {
+            cand[p + u] = v[u];
+            mn = min(mn, (uint32_t)(v[u] >> 32));
+            mx = max(mx, (uint32_t)(v[u] >> 32));
+          }
       }
     }
+    // the histogram of the selection below, cleared while the copies land
+    for (int i = t; i < (1 << kFinalBB); i += NT) hist[i] = 0;
+    if (t == 0) { sh_nsel = 0; sh_thr = 0; }
   }
   const int nc = overflow ? 0 : (int)total;
-  __syncthreads();
 
   // the k-th largest composite
   uint64_t prefix = 0;
   if (!overflow) {
-    uint32_t mn = 0xffffffffu, mx = 0u;
-    for (int j = t; j < nc; j += NT) {
-      const uint32_t h = (uint32_t)(cand[j] >> 32);
-      mn = min(mn, h);
-      mx = max(mx, h);
-    }
+    // the block barriers of the range reduction also order the copies and
+    // the cleared histogram before their readers
     uint32_t lo, hi;
     block_minmax<NT>(mn, mx, part, &lo, &hi);
     const uint32_t range = hi - lo;
     const int bits = range ? 32 - __clz((int)range) : 0;   // range < 2^bits
     const int shift = bits > kFinalBB ? bits - kFinalBB : 0;
-    for (int i = t; i < (1 << kFinalBB); i += NT) hist[i] = 0;
-    if (t == 0) { sh_nsel = 0; sh_thr = 0; }
-    __syncthreads();
     for (int j = t; j < nc; j += NT)
       atomicAdd(&hist[((uint32_t)(cand[j] >> 32) - lo) >> shift], 1u);
     __syncthreads();
@@ -1556,7 +1585,7 @@ template <class T, int NQB, int CAP>
 __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int C, DecodeBar* bar,
                                                                 uint64_t tag) {
   __shared__ DecodeScores<CAP> u;
-  __shared__ uint32_t thist[4096], part[kDecThreads / 32];   // phases B and D
+  __shared__ uint32_t thist[4096], part[3 * kDecThreads / 64];  // phases B and D
   __shared__ uint32_t sh_digit, sh_above, sh_n, sh_tau, sh_over;
   __shared__ uint64_t sh_thr;
   __shared__ uint32_t lcnt[32];                              // phase C: candidates per query
