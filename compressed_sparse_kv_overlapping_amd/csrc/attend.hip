@@ -706,23 +706,61 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   // queries, the B operand of the logits: k-step s, lane l holds head l % 32
   // and dims 16 s + 8 (l / 32) .. + 7.  A head past H reads head 0 and
   // writes nothing.
+  //
+  // The main pass stages them through the tile buffers (free until the
+  // first tile copy), in two halves of 288 dims: each wave copies its 32
+  // heads' half rows (576 bytes each) into its own 18 KB region with whole
+  // 1 KB copies, then reads its fragments from there.  A fragment load from
+  // global memory touches 32 heads' rows at once, 32 bytes of a 128-byte
+  // line each, so four consecutive loads share every line and the lines
+  // come from L2 several times over.  Region row r holds chunk j of the half
+  // row in slot j ^ f(r), f(r) = (r / 4) % 4: the 16 rows a fragment read
+  // serves together then cover all 64 banks.
   Frag<bf16_t> qf[kQSteps];
-  {
+  auto q_row = [&](int r) {                                  // query row of the wave's head r
+    const int hd = hg * kWideHeads + wave * 32 + r;
+    return reinterpret_cast<const char*>(q + ((int64_t)b * a.H + (hd < a.H ? hd : 0)) * kE);
+  };
+  const unsigned q_region = lds_offset(kbuf[0]) + 18432 * wave;
+  auto q_stage = [&](int half) {
+#pragma unroll
+    for (int n = 0; n < 18; ++n) {
+      const int slot = 64 * n + lane, r = slot / 36, jj = slot - 36 * r;
+      const char* src = q_row(r) + 576 * half + 16 * (jj ^ ((r >> 2) & 3));
+      dma16(src, (unsigned)__builtin_amdgcn_readfirstlane(q_region + 1024 * n));
+    }
+  };
+  auto q_read = [&](int half) {
+    const int y = lh ^ ((hl >> 2) & 3);
+    const unsigned base = q_region + 576 * hl;
+    const unsigned o0 = base + 16 * y, o1 = base + 16 * (2 ^ y);
+#pragma unroll
+    for (int u = 0; u < 9; ++u) {
+      qf[18 * half + 2 * u].v = *reinterpret_cast<const lds_u32x4_t*>((uintptr_t)(o0 + 64 * u));
+      qf[18 * half + 2 * u + 1].v = *reinterpret_cast<const lds_u32x4_t*>((uintptr_t)(o1 + 64 * u));
+    }
+  };
+  if constexpr (EXACT) {
     const bf16_t* qp = q + ((int64_t)b * a.H + (hok ? head : 0)) * kE + 8 * lh;
 #pragma unroll
     for (int s = 0; s < kQSteps; ++s) frag_load(qf[s], qp + 16 * s);
+  } else {
+    q_stage(0);
   }
   // the head's softmax scale (log2 units), with its query's factor
   float c_head = c_log2;
-  if constexpr (NORM) {
-    float ss = 0.f;
+  auto q_norm = [&]() {
+    if constexpr (NORM) {
+      float ss = 0.f;
 #pragma unroll
-    for (int s = 0; s < kQSteps; ++s)
+      for (int s = 0; s < kQSteps; ++s)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) ss = sumsq_bf16x2(qf[s].v[w], ss);
-    ss += __shfl_xor(ss, 32, 64);                            // the head's other 288 dims
-    c_head = c_log2 * __frsqrt_rn(ss * (1.f / kE) + a.norm_eps);
-  }
+        for (int w = 0; w < 4; ++w) ss = sumsq_bf16x2(qf[s].v[w], ss);
+      ss += __shfl_xor(ss, 32, 64);                          // the head's other 288 dims
+      c_head = c_log2 * __frsqrt_rn(ss * (1.f / kE) + a.norm_eps);
+    }
+  };
+  if constexpr (EXACT) q_norm();
 
   f32x16 O[kVBlocks];
 #pragma unroll
@@ -1013,12 +1051,23 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     // every ring slot the loop reads holds valid row addresses: slots of
     // tiles past the split resolve to the safe row.  mk[i]: row mask of tile
     // t + i.
-    uint32_t mk[4];
-    mk[0] = resolve(0, sel_load(0));
-    mk[1] = resolve(1, sel_load(1));
-    mk[2] = resolve(2, sel_load(2));
+    // (the selections load while the first query half is in flight; the
+    // rows resolve while the second is)
+    const int e0 = sel_load(0), e1 = sel_load(1), e2 = sel_load(2);
     int e_next = sel_load(3);
-    __syncthreads();                                         // rows in LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");        // first query half staged
+    q_read(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      // read before it is overwritten
+    q_stage(1);
+    uint32_t mk[4];
+    mk[0] = resolve(0, e0);
+    mk[1] = resolve(1, e1);
+    mk[2] = resolve(2, e2);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");        // second query half staged
+    q_read(1);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    q_norm();
+    __syncthreads();                                         // rows in LDS; query regions free
     f32x16 S;
     if (ntiles > 0) {
       // tiles 0 and 1 in flight together; at most the kCopies copies of

@@ -705,6 +705,45 @@ def test_normalised_attention_mxfp4_entries():
     _check_attn(out, lse, ro, rl, wl.DT_BF16)
 
 
+def _scales_at(scales, off):
+    """The scale rows on the device, starting off bytes past a 16-byte
+    boundary (a view into a larger buffer)."""
+    flat = np.ascontiguousarray(scales).reshape(-1)
+    buf = torch.zeros(flat.size + 32, dtype=torch.uint8, device="cuda")
+    buf[off:off + flat.size] = torch.from_numpy(flat).cuda()
+    return buf[off:off + flat.size].view(scales.shape)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("off", [1, 2, 3])
+def test_attend_mx_scales_at_any_byte_offset(bits, off):
+    """Scale rows that start at any byte address: CSA with a selection that
+    is not a whole number of tiles (k = 45, some -1) plus window rows, and
+    HCA over a ragged entry count, per sequence."""
+    B, H, N, W, k = 2, 32, 301, 7, 45
+    rng = np.random.default_rng(off * 10 + bits)
+    q = _rand(131, N, 1, (B, H, E), wl.DT_BF16, 1 / 24)
+    enc = wl.mxfp4_encode if bits == 4 else wl.mxfp8_encode
+    codes, scales = enc(wl.normal(131, N + bits, 2, (B, N, E)))
+    win = _rand(131, N, 3, (W, E), wl.DT_BF16)
+    idx = np.stack([rng.choice(N, k, replace=False) for _ in range(B)]).astype(np.int32)
+    idx[1, 3] = -1
+    sc = _scales_at(scales, off)
+    cskv = _cskv()
+    sparse = cskv.sparse_attend_mxfp4 if bits == 4 else cskv.sparse_attend_mxfp8
+    hca = cskv.hca_attend_mxfp4 if bits == 4 else cskv.hca_attend_mxfp8
+    ocsa = oracle.csa_attend_mxfp4 if bits == 4 else oracle.csa_attend_mxfp8
+    ohca = oracle.hca_attend_mxfp4 if bits == 4 else oracle.hca_attend_mxfp8
+    out, lse = sparse(dev(q), _up(codes[0]), sc[0], dev(win), _up(idx), W=W)
+    torch.cuda.synchronize()
+    ro, rl = ocsa(q, codes[0], scales[0], win, idx, W=W)
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+    out, lse = hca(dev(q), _up(codes), sc, per_seq=True)
+    torch.cuda.synchronize()
+    ro, rl = ohca(q, codes, scales, per_seq=True)
+    _check_attn(out, lse, ro, rl, wl.DT_BF16)
+
+
 # ------------------------------------------------------- MXFP8 entries
 
 def _mx8_entries(cfg_id, seed, shape):
