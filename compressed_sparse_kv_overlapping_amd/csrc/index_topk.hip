@@ -78,38 +78,46 @@ template <> struct KeyFrag<e4m3_t> { static constexpr int bytes = 1; };
 // codes in 32 bytes, element 2j in the low nibble of byte j, and two E8M0
 // scales per row (elements 0..31, 32..63) in a separate byte array.
 struct fp4x2_t { uint8_t u; };
-template <> struct Frag<fp4x2_t> { uint32_t v; uint32_t s; };  // 8 codes; block scale as fp32 bits
+// MXFP4 on 16x16 tiles: the two halves f[0], f[1] of a lane's 16 codes (8
+// bytes: dims 16 g .. 16 g + 15 of its row, g = l / 16) and the E8M0 byte of
+// their block (g / 2), as the scaled MFMA takes it
+template <> struct Frag<fp4x2_t> { uint32_t v; uint32_t s; };
 
 // Bytes of a 64-element row, and the fragment type the MFMA consumes.
-// MXFP4 is decoded to bf16, which is exact: an E2M1 value times a power of
-// two has at most two significant bits (within bf16's exponent range).
 template <class T> struct Elem {
   static constexpr int kRowBytes = 64 * (int)sizeof(T);
   using QF = Frag<T>;
 };
 template <> struct Elem<fp4x2_t> {
   static constexpr int kRowBytes = 32;
-  using QF = Frag<bf16_t>;
+  using QF = Frag<fp4x2_t>;
 };
 
-// 8 E2M1 codes times their block scale, as 8 bf16 (gfx950 converts two
-// codes per instruction).  Queries and keys go through the same conversion,
-// so the pairing of slots in a dot product never depends on which nibble a
-// converted pair puts first.
-__device__ __forceinline__ void fp4_decode(Frag<bf16_t>& d, const Frag<fp4x2_t>& f) {
-  d.v = fp4x8_to_bf16(f.v, __uint_as_float(f.s));
-}
-
-// Key fragments as the MFMA takes them (a copy, or the MXFP4 decode).
+// Key fragments as the MFMA takes them.
 template <class T>
 __device__ __forceinline__ void key_decode(typename Elem<T>::QF* d, const Frag<T>* k) {
   d[0] = k[0];
   d[1] = k[1];
 }
+
+// S += keys . queries^T for one 16 x 16 tile over the 64 dims.  bf16, fp8,
+// fp32: two MFMAs, k-step ks taking dims 32 ks + 8 g .. + 7 in lane group g.
+// MXFP4: one v_mfma_scale 16x16x128 with E2M1 operands, lane group g
+// supplying its 16 codes of block g / 2 in K slots 0..15 of its 32 (the
+// other 16 zero) and that block's E8M0 scale, so each scale covers only its
+// own block's elements; the products are exact, as with every format here.
+template <class T>
+__device__ __forceinline__ void score16(f32x4& S, const typename Elem<T>::QF* k,
+                                        const typename Elem<T>::QF* q) {
+  mma16(S, k[0], q[0]);
+  mma16(S, k[1], q[1]);
+}
 template <>
-__device__ __forceinline__ void key_decode<fp4x2_t>(Frag<bf16_t>* d, const Frag<fp4x2_t>* k) {
-  fp4_decode(d[0], k[0]);
-  fp4_decode(d[1], k[1]);
+__device__ __forceinline__ void score16<fp4x2_t>(f32x4& S, const Frag<fp4x2_t>* k,
+                                                 const Frag<fp4x2_t>* q) {
+  const v8i32_t a = {(int)k[0].v, (int)k[1].v, 0, 0, 0, 0, 0, 0};
+  const v8i32_t b = {(int)q[0].v, (int)q[1].v, 0, 0, 0, 0, 0, 0};
+  S = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, S, 4, 4, 0, (int)k[0].s, 0, (int)q[0].s);
 }
 
 // Both k-step fragments (dims 0..31 and 32..63, slots 8g..8g+7) of row r,
@@ -124,22 +132,19 @@ __device__ __forceinline__ void key_frags(Frag<T>* f, const char* kb, const uint
 template <>
 __device__ __forceinline__ void key_frags<fp4x2_t>(Frag<fp4x2_t>* f, const char* kb, const uint8_t* sb,
                                                    int64_t r, int g) {
-  const char* p = kb + r * 32;
-  f[0].v = *reinterpret_cast<const uint32_t*>(p + 4 * g);
-  f[1].v = *reinterpret_cast<const uint32_t*>(p + 16 + 4 * g);
-  const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sb + 2 * r);
-  f[0].s = e8m0_f32_bits(s2 & 255u);
-  f[1].s = e8m0_f32_bits(s2 >> 8);
+  const uint2 w = *reinterpret_cast<const uint2*>(kb + r * 32 + 8 * g);
+  f[0].v = w.x;
+  f[1].v = w.y;
+  f[0].s = f[1].s = sb[2 * r + (g >> 1)];
 }
 
-// The block scales of row r for fragments whose codes came from LDS.
+// The block scale of row r for fragments whose codes came from LDS.
 template <class T>
-__device__ __forceinline__ void key_scales(Frag<T>* f, const uint8_t* sb, int64_t r) {}
+__device__ __forceinline__ void key_scales(Frag<T>* f, const uint8_t* sb, int64_t r, int g) {}
 template <>
-__device__ __forceinline__ void key_scales<fp4x2_t>(Frag<fp4x2_t>* f, const uint8_t* sb, int64_t r) {
-  const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sb + 2 * r);
-  f[0].s = e8m0_f32_bits(s2 & 255u);
-  f[1].s = e8m0_f32_bits(s2 >> 8);
+__device__ __forceinline__ void key_scales<fp4x2_t>(Frag<fp4x2_t>* f, const uint8_t* sb, int64_t r,
+                                                    int g) {
+  f[0].s = f[1].s = sb[2 * r + (g >> 1)];
 }
 
 // Query row r's fragments, decoded once per kernel.
@@ -199,7 +204,10 @@ template <class T> struct KeyTiles {
   static constexpr int kTiles = kStage / (16 * kRow);        // 16-row tiles per stage
   static __device__ __forceinline__ int swz(int r) { return (r / kRowsPer256) % kChunks; }
   // byte offset of the fragment of k-step ks, lane group g, in a row
-  static __device__ __forceinline__ int frag_off(int ks, int g) { return (32 * ks + 8 * g) * kRow / 64; }
+  static __device__ __forceinline__ int frag_off(int ks, int g) {
+    if constexpr (std::is_same<T, fp4x2_t>::value) return 8 * g + 4 * ks;   // the lane's 8 code bytes
+    return (32 * ks + 8 * g) * kRow / 64;
+  }
   // the 8-element fragment at byte offset off of a staged row
   static __device__ __forceinline__ void load(Frag<T>& f, const char* row, int off, int sw);
 };
@@ -308,8 +316,7 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
 #pragma unroll
     for (int j = 0; j < NQB; ++j) {
       S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma16(S[j], kd[0], qf[j][0]);
-      mma16(S[j], kd[1], qf[j][1]);
+      score16<T>(S[j], kd, qf[j]);
     }
     // S[j][i]: query qb[j], entry et + 4g + i
     if (MODE == 0 && NQB == 1 && a.sraw && qb[0] >= 0)         // one query per block
@@ -468,7 +475,7 @@ __global__ __launch_bounds__(256) void idx_score_kernel(IdxArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) KT::load(f[ks], rowp, KT::frag_off(ks, g), swz);
         const int row = e_w0 + (st * KT::kTiles + t) * 16 + col;   // as staged (clamped)
-        key_scales<T>(f, sbase, row < a.N ? row : a.N - 1);
+        key_scales<T>(f, sbase, row < a.N ? row : a.N - 1, g);
       };
       frags(0, kf[0]);
       static_assert(KT::kTiles % 2 == 0, "tiles per stage come in pairs");
@@ -1651,8 +1658,7 @@ __global__ __launch_bounds__(kDecThreads) void idx_decode_kernel(IdxArgs a, int 
 #pragma unroll
           for (int j = 0; j < NQB; ++j) {
             f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f};
-            mma16(S, kd[0], qf[j][0]);
-            mma16(S, kd[1], qf[j][1]);
+            score16<T>(S, kd, qf[j]);
             // S[i]: query 16 j + col, key c0 + el + 4 g + i (-inf past N)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
