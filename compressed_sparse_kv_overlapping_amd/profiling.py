@@ -29,9 +29,13 @@ reads and writes at 1M tokens with none of its arithmetic, in four mixes)
 beside the fused compressor itself, and prints the table kept in
 profiles/compress_floor_probe.txt.
 
-``trace <results.db> <command>`` prints, from a ``rocprofv3 --kernel-trace``
-database, each library kernel's dispatch count and average / min / max
-duration per grid shape, with the profiled command in the header.
+``trace <results.db> <command> [phases]`` prints, from a ``rocprofv3
+--kernel-trace`` database, each library kernel's dispatch count and average /
+min / max duration per grid shape, with the profiled command in the header.
+``phases`` (e.g. ``warmup:2,warm:10,cold:10,cold_dirty:10``, the order in
+which bench.py runs its steps) splits, for every kernel dispatched exactly
+that many times in all, its dispatches in start order into those phases and
+prints the average of each.
 """
 import csv
 import glob
@@ -268,12 +272,12 @@ def summarize(fetch_dir, write_dir, digest=None):
           f"{alg / 1e9:.4f} GB (ratio {total / alg:.3f})")
 
 
-def trace(db, command):
+def trace(db, command, phases=None):
     import sqlite3
     con = sqlite3.connect(db)
     q = ("select s.kernel_name, d.grid_size_x / d.workgroup_size_x, d.grid_size_y, "
          "d.grid_size_z, d.workgroup_size_x, d.end - d.start from rocpd_kernel_dispatch d "
-         "join rocpd_info_kernel_symbol s on d.kernel_id = s.id")
+         "join rocpd_info_kernel_symbol s on d.kernel_id = s.id order by d.start")
     agg = {}
     for name, gx, gy, gz, wx, dur in con.execute(q):
         if "cskv" not in name:
@@ -287,6 +291,19 @@ def trace(db, command):
     for (nm, grid, wx), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         print(f"{nm[:78]:78s} {grid:>14s} {wx:4d} {len(v):4d} {sum(v) / len(v):10.2f} "
               f"{min(v):10.2f} {max(v):10.2f}")
+    if not phases:
+        return
+    spec = [(n, int(c)) for n, c in (p.split(":") for p in phases.split(","))]
+    total = sum(c for _, c in spec)
+    print(f"# per phase, in dispatch order ({phases}): average microseconds")
+    for (nm, grid, wx), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        if len(v) != total:
+            continue
+        cols, i = [], 0
+        for n, c in spec:
+            cols.append(f"{n} {sum(v[i:i + c]) / c:.2f}")
+            i += c
+        print(f"{nm[:78]:78s} {grid:>14s}  " + "  ".join(cols))
 
 
 if __name__ == "__main__":
@@ -300,7 +317,7 @@ if __name__ == "__main__":
         floor()
     elif len(sys.argv) == 5 and sys.argv[1] == "sq":
         sq_summary(sys.argv[2], sys.argv[3], sys.argv[4])
-    elif len(sys.argv) == 4 and sys.argv[1] == "trace":
-        trace(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) in (4, 5) and sys.argv[1] == "trace":
+        trace(sys.argv[2], sys.argv[3], sys.argv[4] if len(sys.argv) == 5 else None)
     else:
         raise SystemExit(__doc__)
