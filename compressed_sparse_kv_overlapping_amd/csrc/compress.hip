@@ -11,7 +11,7 @@
 // Kernels: compress_small_kernel (m <= 4, the CSA scale) and
 // compress_large_kernel (m > 4, the HCA scale) stream one scale each;
 // compress_fused_kernel streams the raw rows once for both scales (with
-// beta_table_kernel before it and compress_join_kernel after it).  Every
+// compress_join_kernel after it).  Every
 // wave streams a contiguous range of entries and reads each raw row once;
 // adjacent ranges hand over the half window they share.  Blocks are mapped
 // so that consecutive ranges stay on one XCD and share its L2.
@@ -395,7 +395,8 @@ static hipError_t launch_large_t(const void* x, const void* z, const float* bias
 // (the constant factors cancel in each normalisation).  With ux = u x every
 // accumulation is one FMA.  A block takes 128 dimensions (2 per lane), so
 // that both weight tables of its dimensions fit LDS whole (beta_l: 2*ML rows,
-// precomputed into the workspace, 128 KB at ML = 128): the 16 waves stream
+// 128 KB at ML = 128, computed by the block from the bias before it
+// streams): the 16 waves stream
 // their ranges with no barrier.  A small block's large sums join the running
 // sums of its large block once, scaled by 2^(r - rl) with rl the large
 // block's raise-only reference.  Wave ranges hand their carried halves to the
@@ -418,33 +419,10 @@ constexpr int kFusedSW = 64 * kFusedDpl;       // dimensions per block
 constexpr int kFusedSlices = kD / kFusedSW;
 constexpr int kFusedMaxML = 128;               // largest large block whose weights fit LDS
 
-// beta[p][d] = 2^((bias[p][d] - max_p bias[p][d]) * log2e): a block takes 64
-// dimensions, its 16 row slices take every 16th row, and the column maxima
-// meet in LDS.
-constexpr int kBetaDims = 64, kBetaSlices = 16;
-__global__ __launch_bounds__(kBetaDims* kBetaSlices) void beta_table_kernel(
-    const float* __restrict__ bias, int rows, float* __restrict__ beta) {
-  __shared__ float part[kBetaSlices][kBetaDims];
-  const int dl = threadIdx.x % kBetaDims, sl = threadIdx.x / kBetaDims;
-  const int d = blockIdx.x * kBetaDims + dl;
-  const float L2E = 1.4426950408889634f;
-  float bm = -INFINITY;
-#pragma unroll 4
-  for (int p = sl; p < rows; p += kBetaSlices) bm = fmaxf(bm, bias[(int64_t)p * kD + d]);
-  part[sl][dl] = bm;
-  __syncthreads();
-  bm = part[0][dl];
-#pragma unroll
-  for (int i = 1; i < kBetaSlices; ++i) bm = fmaxf(bm, part[i][dl]);
-#pragma unroll 4
-  for (int p = sl; p < rows; p += kBetaSlices)
-    beta[(int64_t)p * kD + d] = __builtin_amdgcn_exp2f((bias[(int64_t)p * kD + d] - bm) * L2E);
-}
-
 template <class T, int MS>
 __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
     const T* __restrict__ x, const T* __restrict__ z, const float* __restrict__ bias_s,
-    const float* __restrict__ beta_l, int R, int64_t NL, int epw, T* __restrict__ out_s,
+    const float* __restrict__ bias_l, int R, int64_t NL, int epw, T* __restrict__ out_s,
     int64_t ld_s, T* __restrict__ out_l, int64_t ld_l, float* __restrict__ bnd) {
   constexpr int DPL = kFusedDpl, kSW = kFusedSW;
   const int ML = R * MS;
@@ -479,10 +457,33 @@ __global__ __launch_bounds__(64 * kFusedWaves) void compress_fused_kernel(
     for (int q = 1; q < 2 * MS; ++q) bm = fmaxf(bm, bias_s[(int64_t)q * kD + slice * kSW + d]);
     bs_lds[p][d] = __builtin_amdgcn_exp2f((bias_s[(int64_t)p * kD + slice * kSW + d] - bm) * L2E);
   }
-  for (int i = threadIdx.x; i < 2 * ML * kSW / 4; i += 64 * kFusedWaves) {
-    const int p = (4 * i) / kSW, d = (4 * i) % kSW;
-    *reinterpret_cast<float4*>(&bl_lds[p][d]) =
-        *reinterpret_cast<const float4*>(beta_l + (int64_t)p * kD + slice * kSW + d);
+  // the large scale's weights beta_l[p][d] = 2^((b[p][d] - max_p b[p][d]) log2e)
+  // of this block's dimensions: thread t takes dimension t % kSW and the
+  // rows of row group t / kSW (every kRG-th row), so each row load is one
+  // coalesced 512-byte run; the group maxima meet in LDS
+  {
+    constexpr int kRG = 64 * kFusedWaves / kSW;              // row groups (8)
+    constexpr int kRows = 2 * kFusedMaxML / kRG;             // rows a thread takes, at most (32)
+    __shared__ float gmx[kRG][kSW];
+    const int dd = threadIdx.x % kSW, rg = threadIdx.x / kSW;
+    const float* bcol = bias_l + slice * kSW + dd;
+    float bv[kRows];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int p = rg + kRG * i;
+      bv[i] = p < 2 * ML ? bcol[(int64_t)p * kD] : -INFINITY;
+      bm = fmaxf(bm, bv[i]);
+    }
+    gmx[rg][dd] = bm;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kRG; ++i) bm = fmaxf(bm, gmx[i][dd]);
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int p = rg + kRG * i;
+      if (p < 2 * ML) bl_lds[p][dd] = __builtin_amdgcn_exp2f((bv[i] - bm) * L2E);
+    }
   }
 
   // Small scale: carried first half cS/cA of the next entry with its
@@ -730,10 +731,7 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
                                  void* out_l, int64_t ld_l, void* ws, hipStream_t stream) {
   const int64_t NL = T_tokens / ml;
   const int R = ml / ms;
-  float* beta_l = (float*)ws;
-  float* bnd = beta_l + (size_t)2 * ml * kD;                 // per block: 12 x 512 boundary halves
-  hipLaunchKernelGGL(beta_table_kernel, dim3(kD / kBetaDims), dim3(kBetaDims * kBetaSlices), 0, stream,
-                     bias_l, 2 * ml, beta_l);
+  float* bnd = (float*)ws;                                   // per block: 12 x 512 boundary halves
   const T* xp = (const T*)x;
   const T* zp = (const T*)z;
   int epw = 2;
@@ -762,7 +760,7 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
 #define CSKV_FUSED(MS)                                                                            \
   pick((const void*)compress_fused_kernel<T, MS>);                                            \
   hipLaunchKernelGGL((compress_fused_kernel<T, MS>), dim3((unsigned)(groups * kFusedSlices)),     \
-                     dim3(64 * kFusedWaves), 0, stream, xp, zp, bias_s, beta_l, R, NL, epw,        \
+                     dim3(64 * kFusedWaves), 0, stream, xp, zp, bias_s, bias_l, R, NL, epw,        \
                      (T*)out_s, ld_s, (T*)out_l, ld_l, bnd)
   switch (ms) {
     case 1: CSKV_FUSED(1); break;
@@ -808,7 +806,8 @@ hipError_t launch_compress_fused(int dt, const void* x, const void* z, int64_t T
 size_t compress_fused_workspace_bytes(int64_t T_tokens, int ml) {
   const int64_t NL = T_tokens / ml;
   const int64_t groups = (NL + 2 * kFusedWaves - 1) / (2 * kFusedWaves);
-  return (size_t)2 * ml * kD * sizeof(float) + (size_t)groups * 12 * kD * sizeof(float) + 256;
+  (void)ml;
+  return (size_t)groups * 12 * kD * sizeof(float) + 256;
 }
 
 template <class T>

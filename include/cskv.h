@@ -115,9 +115,9 @@ int cskv_compress(const void* raw_kv, const void* score_logits, const float* pos
  * one read of raw_kv and score_logits instead of two.
  *   bias_small [2*m_small][512], bias_large [2*m_large][512] fp32;
  *   out_small / out_large rows of ld >= 512 (multiple of 8) in dt.
- *   workspace: cskv_compress2_workspace_size(T, m_large) bytes: the table of
- *   exponentiated large-scale biases and the half-window sums that join
- *   the entries at the boundaries between thread blocks.
+ *   workspace: cskv_compress2_workspace_size(T, m_large) bytes: the
+ *   half-window sums that join the entries at the boundaries between thread
+ *   blocks (when the two scales run as separate passes, none is used).
  * bias_large and out_large are not used (may be NULL) when T < m_large.
  * Errors: INVALID_ARG (null pointers, T < 0, m_large not a multiple of
  * m_small, ld < 512); UNSUPPORTED (m_small > 4, m_large > 65536, dt not
