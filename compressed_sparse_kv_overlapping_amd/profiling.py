@@ -239,7 +239,7 @@ def summarize(fetch_dir, write_dir, digest=None):
     f_scale = COPY_BYTES / (copy_f * 1024.0)
     w_scale = COPY_BYTES / (copy_w * 1024.0)
     parts = {}
-    for needle in ("beta_table_kernel", "compress_fused_kernel", "compress_join_kernel"):
+    for needle in ("compress_fused_kernel", "compress_join_kernel"):
         fb = _find(fetch, needle) * 1024.0 * f_scale
         wb = _find(write, needle) * 1024.0 * w_scale
         parts[needle] = {"fetch_bytes": round(fb), "write_bytes": round(wb)}
