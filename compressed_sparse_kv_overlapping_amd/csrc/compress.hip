@@ -738,7 +738,7 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
   int64_t groups = 0;
   auto pick = [&](const void* kern) {
     // Large entries per wave: the grid runs in rounds of the blocks that fit
-    // on the chip at once; take the epw (at least 2) that fills its last
+    // on the chip at once; take the epw (at least 1) that fills its last
     // round best, the largest of equals (fewest block boundaries to join).
     // The resident block count is queried on every call, for the current
     // device (host-side queries, no device work, nothing kept between calls).
@@ -749,7 +749,7 @@ static hipError_t launch_fused_t(const void* x, const void* z, int64_t T_tokens,
       nb = 0;
     const int slots = nb > 0 && cus > 0 ? nb * cus : 256;
     double best = -1.0;
-    for (int e = 2; e <= 64; ++e) {
+    for (int e = 1; e <= 64; ++e) {
       const int64_t per = (int64_t)kFusedWaves * e;
       const int64_t g = (NL + per - 1) / per;
       const double rounds = (double)(g * kFusedSlices) / slots;
@@ -805,7 +805,7 @@ hipError_t launch_compress_fused(int dt, const void* x, const void* z, int64_t T
 // most one block per 2 * kFusedWaves large entries).
 size_t compress_fused_workspace_bytes(int64_t T_tokens, int ml) {
   const int64_t NL = T_tokens / ml;
-  const int64_t groups = (NL + 2 * kFusedWaves - 1) / (2 * kFusedWaves);
+  const int64_t groups = (NL + kFusedWaves - 1) / kFusedWaves;  // at one large block a wave, the most
   (void)ml;
   return (size_t)groups * 12 * kD * sizeof(float) + 256;
 }
