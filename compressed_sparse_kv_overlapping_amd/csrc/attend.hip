@@ -1372,7 +1372,8 @@ int attend_splits(int dt, int64_t B, int H, int64_t nslots) {
   // compute unit): more splits than that only add partial outputs
   const int64_t target = dt == 0 ? 512 : 256;
   int64_t s = (target + blocks - 1) / blocks;
-  const int64_t cap = tiles / 2 > 1 ? tiles / 2 : 1;
+  // (fp32: one wave a block, so a tile a split when blocks are few)
+  const int64_t cap = dt == 0 ? tiles : (tiles / 2 > 1 ? tiles / 2 : 1);
   if (s > cap) s = cap;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
