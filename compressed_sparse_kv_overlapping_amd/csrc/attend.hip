@@ -707,8 +707,8 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   // and dims 16 s + 8 (l / 32) .. + 7.  A head past H reads head 0 and
   // writes nothing.
   //
-  // The main pass stages them through the tile buffers (free until the
-  // first tile copy), in two halves of 288 dims: each wave copies its 32
+  // The main pass stages them through tile buffers 1 and 2 (free until the
+  // second tile's copy), in two halves of 288 dims: each wave copies its 32
   // heads' half rows (576 bytes each) into its own 18 KB region with whole
   // 1 KB copies, then reads its fragments from there.  A fragment load from
   // global memory touches 32 heads' rows at once, 32 bytes of a 128-byte
@@ -721,7 +721,7 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     const int hd = hg * kWideHeads + wave * 32 + r;
     return reinterpret_cast<const char*>(q + ((int64_t)b * a.H + (hd < a.H ? hd : 0)) * kE);
   };
-  const unsigned q_region = lds_offset(kbuf[0]) + 18432 * wave;
+  const unsigned q_region = lds_offset(kbuf[1]) + 18432 * wave;    // buffers 1 and 2
   auto q_stage = [&](int half) {
 #pragma unroll
     for (int n = 0; n < 18; ++n) {
@@ -1051,11 +1051,15 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     // every ring slot the loop reads holds valid row addresses: slots of
     // tiles past the split resolve to the safe row.  mk[i]: row mask of tile
     // t + i.
-    // (the selections load while the first query half is in flight; the
-    // rows resolve while the second is)
-    const int e0 = sel_load(0), e1 = sel_load(1), e2 = sel_load(2);
+    // The selections load while the first query half is in flight; the rows
+    // resolve and tile 0 (into buffer 0, which the query does not use) is
+    // copied while the second half is.  The selections are settled after the
+    // first wait, so that no later use waits for the copies issued since
+    // (the compiler does not count them).
+    int e0 = sel_load(0), e1 = sel_load(1), e2 = sel_load(2);
     int e_next = sel_load(3);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");        // first query half staged
+    asm volatile("" : "+v"(e0), "+v"(e1), "+v"(e2), "+v"(e_next));
     q_read(0);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      // read before it is overwritten
     q_stage(1);
@@ -1063,16 +1067,21 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
     mk[0] = resolve(0, e0);
     mk[1] = resolve(1, e1);
     mk[2] = resolve(2, e2);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");        // second query half staged
+    __syncthreads();                                         // rows in LDS
+    if (ntiles > 0) {
+      issue(0, 0);
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");      // second query half staged (tile 0 may fly)
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     q_read(1);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     q_norm();
-    __syncthreads();                                         // rows in LDS; query regions free
+    __syncthreads();                                         // query regions free
     f32x16 S;
     if (ntiles > 0) {
       // tiles 0 and 1 in flight together; at most the kCopies copies of
       // tile 1 may still be outstanding once tile 0 has landed
-      issue(0, 0);
       if (ntiles > 1) {
         issue(1, 1);
         asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
