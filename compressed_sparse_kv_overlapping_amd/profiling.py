@@ -200,12 +200,42 @@ def sq_summary(directory, title, command):
                 key = (r["Kernel_Name"], r.get("Grid_Size", ""), r.get("Workgroup_Size", ""))
                 acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     print(f"# {title}\n# command: {command}\n# per dispatch, averaged over the dispatches of each kernel "
-          f"and grid (grid in threads)")
+          f"and grid (grid in threads)\n# derived: per wave = counter / SQ_WAVES; busy = SQ_BUSY_CYCLES / 32 "
+          f"shader engines; MFMA pipe = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / busy; attention tiles = "
+          f"MFMA per wave / 68\n# (36 logit + 32 weighted-sum MFMAs a 32-row tile; a 32x32x16 bf16 MFMA "
+          f"occupies its SIMD 32 cycles, so a tile's MFMAs take 2,176 cycles)")
     for key in sorted(acc):
         name, g, w = key
         print(f"\n{name}  (grid {g}, workgroup {w})")
-        for c, v in sorted(acc[key].items()):
-            print(f"  {c:28s} {sum(v) / len(v):16.1f}")
+        avg = {c: sum(v) / len(v) for c, v in acc[key].items()}
+        for c, v in sorted(avg.items()):
+            print(f"  {c:28s} {v:16.1f}")
+        _sq_derived(name, avg)
+
+
+def _sq_derived(name, avg):
+    """Per-wave instruction counts, busy cycles (SQ_BUSY_CYCLES over the 32
+    shader engines) and MFMA pipe use (SQ_VALU_MFMA_BUSY_CYCLES over the 1,024
+    SIMDs and the busy cycles); for the wide attention kernel also per
+    32-row tile (36 logit + 32 weighted-sum MFMAs a tile, 32 cycles each)."""
+    need = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_BUSY_CYCLES",
+            "SQ_VALU_MFMA_BUSY_CYCLES")
+    if not all(c in avg for c in need) or avg["SQ_WAVES"] <= 0:
+        return
+    w = avg["SQ_WAVES"]
+    valu, lds, mfma = avg["SQ_INSTS_VALU"] / w, avg["SQ_INSTS_LDS"] / w, avg["SQ_INSTS_MFMA"] / w
+    busy = avg["SQ_BUSY_CYCLES"] / 32
+    pipe = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / busy if busy > 0 else 0.0
+    print(f"  per wave: VALU {valu:.0f}, LDS {lds:.0f}, MFMA {mfma:.0f}")
+    line = f"  busy cycles: {busy:.0f}"
+    if "attend_wide" in name and mfma > 0:
+        tiles = mfma / 68
+        per_tile = busy / tiles
+        line += (f"; tiles per wave {tiles:.0f}; busy cycles per tile {per_tile:.0f} "
+                 f"({per_tile / 2176:.2f}x the MFMA cycles); VALU per wave per tile {valu / tiles:.0f}")
+    if mfma > 0:
+        line += f"; MFMA pipe {100 * pipe:.0f}%"
+    print(line)
 
 
 def _per_kernel(directory, counter):
