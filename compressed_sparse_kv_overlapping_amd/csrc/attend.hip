@@ -712,8 +712,8 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
   // heads' half rows (576 bytes each) into its own 18 KB region with whole
   // 1 KB copies, then reads its fragments from there.  A fragment load from
   // global memory touches 32 heads' rows at once, 32 bytes of a 128-byte
-  // line each, so four consecutive loads share every line and the lines
-  // come from L2 several times over.  Region row r holds chunk j of the half
+  // line each, so four consecutive loads share every line; a whole-line
+  // copy asks for each line once.  Region row r holds chunk j of the half
   // row in slot j ^ f(r), f(r) = (r / 4) % 4: the 16 rows a fragment read
   // serves together then cover all 64 banks.
   Frag<bf16_t> qf[kQSteps];
