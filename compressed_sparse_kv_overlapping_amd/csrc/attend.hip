@@ -95,6 +95,16 @@ __device__ __forceinline__ int dense_end(const AttnArgs& a, int b, int s_begin, 
   return vis < s_end ? (vis > s_begin ? (int)vis : s_begin) : s_end;
 }
 
+// Block order over the XCDs: the dispatcher deals linear block ids round-
+// robin over the 8 XCDs; logical block L = xcd_block(id, G) gives each XCD a
+// contiguous range of logical blocks, so the splits of one query (and, with
+// the same order in the merge, that query's merge blocks) share one XCD.
+__device__ __forceinline__ int xcd_block(int id, int G) {
+  const int q = G / 8, rem = G % 8;
+  const int x = id % 8, slot = id / 8;
+  return x * q + (x < rem ? x : rem) + slot;
+}
+
 // Keeps the scheduler from hoisting every LDS fragment load of an unrolled
 // loop to its top (which would need more registers than a wave has).
 __device__ __forceinline__ void fence_sched() { asm volatile("" ::: "memory"); }
@@ -694,7 +704,9 @@ __device__ __forceinline__ bool wide_split(const AttnArgs& a, WideShared& sh) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int nblk = gridDim.x * gridDim.y * gridDim.z;
+  const int lb = xcd_block(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), nblk);
+  const int split = lb % gridDim.x, hg = (lb / gridDim.x) % gridDim.y, b = lb / (gridDim.x * gridDim.y);
   const int hl = lane & 31, lh = lane >> 5;
   const int head = hg * kWideHeads + wave * 32 + hl;
   const bool hok = head < a.H;
@@ -1277,7 +1289,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const P* __restrict__ o_part
                                                     T* __restrict__ out,
                                                     float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
-  const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t bh = (int64_t)xcd_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
   if (bh >= BH) return;
   const float* lp = lse_part + bh * S;
   if (S <= 8) {
