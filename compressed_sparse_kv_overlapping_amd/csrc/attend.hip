@@ -43,7 +43,7 @@ template <> struct AttnCfg<bf16_t> {
   static constexpr int VP = kTile + 4;                       // V^T row pitch (elements)
 };
 template <> struct AttnCfg<float> {
-  static constexpr int NW = 1;                               // 16 heads per block
+  static constexpr int NW = 4;                               // 64 heads per block
   static constexpr int EPC = 8;
   static constexpr int KP = kE + 4;
   static constexpr int VP = kTile + 4;
